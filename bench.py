@@ -1,0 +1,190 @@
+"""Benchmark: RNN-T fwd+bwd lattice cells/s (B*T*(U+1)) at V=1024 and peak HBM bytes.
+
+One step = rnnt_loss_fwd + rnnt_loss_bwd over one batch of the workload, with
+inputs already resident in HBM. K steps are timed after W warm-up steps.
+Prints one JSON line. Per-kernel durations come from the library's launch
+timing (hipEvent pairs on the launch stream over the timed steps); the
+roofline object reports the dominant kernel. The fp64 CPU oracle is timed on
+a bounded sample of the same workload as cpu_baseline.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--config 5]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def mfma_flops(inp):
+    """Algorithmic FLOP of each MFMA kernel class over one step (valid cells only)."""
+    d = inp.dims
+    H, V, HA, HL = d["H"], d["V"], d["HA"], d["HL"]
+    Nc = inp.valid_cells
+    rows_a = int(np.sum(inp.T_len))
+    rows_l = int(np.sum(inp.U_len + 1))
+    pre = 2.0 * H * (rows_a * HA + rows_l * HL)
+    return {
+        "joint_fwd": 2.0 * H * V * Nc,   # scores for every valid cell
+        "joint_bwd": 2.0 * H * V * Nc,   # recomputed scores
+        "dz": 2.0 * H * V * Nc,          # dz = dh W^O
+        "dWO_gemm": 2.0 * H * V * Nc,    # dW^O = dh^T z
+        "preproj_gemm": pre,             # a = W^A h^A, l = W^L h^L
+        "dh_enc_gemm": pre,              # dh^A, dh^L
+        "dW_enc_gemm": pre,              # dW^A, dW^L
+    }
+
+
+def cpu_baseline(inp, budget_s: float):
+    """Time the oracle (as it stands) on single samples of the workload."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    order = np.argsort(inp.T_len * (inp.U_len + 1))  # smallest samples first
+    done_cells, t_used, used = 0, 0.0, []
+    for b in order:
+        t0 = time.perf_counter()
+        oracle.loss_and_grads(inp, samples=[int(b)])
+        t_used += time.perf_counter() - t0
+        done_cells += int(inp.T_len[b] * (inp.U_len[b] + 1))
+        used.append(int(b))
+        if t_used >= budget_s:
+            break
+    # extrapolate to the whole batch by valid cells, report in padded cells/s
+    t_batch = t_used * inp.valid_cells / done_cells
+    return {
+        "value": inp.padded_cells / t_batch,
+        "unit": "cells/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle fwd+bwd on {len(used)} sample(s) {used} of the workload "
+                   f"({done_cells} valid cells, {t_used:.1f} s), extrapolated by valid cells to the "
+                   f"batch ({inp.valid_cells} valid / {inp.padded_cells} padded cells)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--mode", default="tiled", choices=["tiled", "untiled"])
+    ap.add_argument("--tile", default="64x32")
+    ap.add_argument("--tiles-per-wave", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget; 0 = skip")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the batch shards by sample; see DESIGN.md for the multi-GPU design)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import rnn_loss_joint_amd as rl
+    from rnnt_inputs import WORKLOADS, workload_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    rl.load()
+    w = WORKLOADS[args.config]
+    tile = tuple(int(x) for x in args.tile.split("x"))
+    print(f"# generating {w.name} inputs", file=sys.stderr, flush=True)
+    inp = workload_inputs(args.config)
+    prob = rl.Problem(inp, mode=args.mode, tile=tile, tiles_per_wave=args.tiles_per_wave)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        prob.forward()
+        prob.backward()
+
+    print("# warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    rl.rnnt_profile_start()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = rl.rnnt_profile_stop()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    peak = torch.cuda.max_memory_allocated()
+    print(f"# timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.2f} s)", file=sys.stderr, flush=True)
+
+    flops = mfma_flops(inp)
+    dtype = inp.dtype
+    kernels = {}
+    for name, (launches, tot) in prof.items():
+        k = {"launches": launches // args.steps, "ms_per_step": tot / args.steps}
+        if name in flops and tot > 0:
+            k["tflops"] = flops[name] * args.steps / (tot * 1e-3) / 1e12
+        if name == "lattice" and tot > 0:
+            k["gbs"] = 24.0 * inp.valid_cells * args.steps / (tot * 1e-3) / 1e9
+        kernels[name] = k
+    mfma_names = [n for n in kernels if n in flops and n in ("joint_fwd", "joint_bwd", "dz", "dWO_gemm")]
+    dom = max(mfma_names, key=lambda n: kernels[n]["ms_per_step"])
+    dk = kernels[dom]
+    ach = dk["tflops"]
+    roof = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
+            "frac": ach / PEAK_TFLOPS[dtype], "traffic": None,
+            "per_launch": f"2*H*V*valid_cells / launches = {flops[dom] / max(1, dk['launches']):.4g} FLOP"}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inp, args.cpu_seconds)
+
+    d = inp.dims
+    value = inp.padded_cells / (ms * 1e-3)
+    out = {
+        "metric": "RNN-T fwd+bwd lattice cells/s (B*T*(U+1)) at V=1024; peak HBM bytes",
+        "value": value,
+        "unit": "cells/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "peak_hbm_bytes": int(peak),
+        "valid_cells_per_s": inp.valid_cells / (ms * 1e-3),
+        "config": {"workload": f"config {args.config} ({w.name})", "B": d["B"], "T": d["T"], "U": d["U"],
+                   "V": d["V"], "HA": d["HA"], "HL": d["HL"], "H": d["H"], "mode": args.mode,
+                   "tile": list(tile), "tiles_per_wave": args.tiles_per_wave,
+                   "padded_cells": inp.padded_cells, "valid_cells": inp.valid_cells,
+                   "saved_bytes": prob.saved_bytes, "workspace_bytes": prob.ws_bytes},
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+/*
+ * rnnt.h - C ABI of the MI355X (gfx950) RNN-T joint + loss library.
+ *
+ * The library computes, for a batch of B utterances, the RNN-T loss and its
+ * gradients through the joint network and output layer:
+ *
+ *   joint network   z[b,t,u] = tanh(W^A h^A[b,t] + W^L h^L[b,u] + b^Z)
+ *   output layer    h[b,t,u] = W^O z[b,t,u] + b^O              (V scores)
+ *   two log-probs   phi = h[blank] - logsumexp(h), psi = h[y[u+1]] - logsumexp(h)
+ *   lattice         alpha/beta forward-backward variables over t < T_b, u <= U_b
+ *   loss            cost_b = -ln P(y_b | x_b) = -(alpha(T_b-1,U_b) + phi(T_b-1,U_b))
+ *
+ * Definitions: "Neural transducer training: reduced memory consumption with
+ * sample-wise computation", section "Transducer training", Eqs. (3)-(10)
+ * (joint network f^J, output layer f^O, loss sub-functions f^W_1..4; the
+ * extraction lost Eq. (4), and tanh with a single bias b^Z is the reading this
+ * library implements). Tiled recompute, the fused joint kernel, the
+ * two-probability reduction, in-place gradients and the untiled mode follow
+ * "Flash RNN-T: making room to train speech recognition", sections "Compute
+ * it, use it, make room" and "Making each operation more efficient".
+ *
+ * Conventions shared by every entry point
+ *  - All device buffers are allocated and owned by the caller. The library
+ *    never allocates device memory; the bytes it needs beyond inputs and
+ *    outputs are exactly what rnnt_loss_query reports.
+ *  - Length arrays T_len_host / U_len_host are HOST int32 arrays [B], read
+ *    during the call and not retained (the forward copies them, with the tile
+ *    plan, into `saved`). 1 <= T_len[b] <= T, 0 <= U_len[b] <= U.
+ *  - Float inputs (h^A, h^L, W^A, W^L, b^Z, W^O, b^O) all have the dtype of
+ *    desc->dtype (fp32 or bf16), row-major, densely packed:
+ *      hA [B,T,HA], hL [B,U+1,HL], WA [H,HA], WL [H,HL], bZ [H], WO [V,H], bO [V].
+ *    labels is int32 [B,U+1] on the device; column 0 is the blank id, column
+ *    u+1 (u < U_len[b]) is the label emitted from lattice row u. Entries past
+ *    U_len[b] are never read. Label values must lie in [0,V) (precondition,
+ *    not checked on the device).
+ *    Padded positions (t >= T_len[b], u > U_len[b]) are never read.
+ *  - costs, dcosts and every gradient output are fp32. Gradients are
+ *    overwritten, not accumulated; padded rows of dhA/dhL are written as 0.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Every call enqueues
+ *    work on that stream and returns without synchronizing the device.
+ *  - Errors: every entry point validates its arguments on the host before
+ *    launching anything and returns a status; no exception or exit crosses
+ *    the ABI. rnnt_last_error() gives a thread-local description of the last
+ *    failure. Calls are reentrant given distinct saved/workspace buffers.
+ */
+#ifndef RNNT_MI355_H
+#define RNNT_MI355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RNNT_OK = 0,
+  RNNT_E_INVALID = -1,     /* bad dims, lengths, pointers or tile settings   */
+  RNNT_E_WORKSPACE = -2,   /* saved/workspace smaller than rnnt_loss_query   */
+  RNNT_E_HIP = -3,         /* a HIP runtime call or kernel launch failed      */
+  RNNT_E_UNSUPPORTED = -4  /* valid request outside this build's limits       */
+} rnnt_status;
+
+typedef enum { RNNT_F32 = 0, RNNT_BF16 = 1 } rnnt_dtype;
+
+/* Tiled: the joint/output intermediates exist one wave of tiles at a time and
+ * are recomputed in the backward. Untiled: the forward keeps z and the scores
+ * for every valid lattice cell in `saved` and the backward reuses them. */
+typedef enum { RNNT_TILED = 0, RNNT_UNTILED = 1 } rnnt_mode;
+
+typedef struct {
+  int32_t B, T, U, V, HA, HL, H; /* lattice per sample is T x (U+1)           */
+  int32_t blank;                 /* blank id, 0 <= blank < V                   */
+  int32_t dtype;                 /* rnnt_dtype of all float inputs             */
+  int32_t mode;                  /* rnnt_mode                                  */
+  int32_t tile_t, tile_u;        /* tile extent in t and u (tiled mode), > 0   */
+  int32_t tiles_per_wave;        /* tiles whose buffers coexist; 0 = default   */
+  int32_t reserved;              /* must be 0                                  */
+} rnnt_desc;
+
+/* Limits of this build (RNNT_E_UNSUPPORTED beyond them): H, HA, HL multiples
+ * of 8; H <= 768; U+1 <= 1024; V <= 65536; B*T*(U+1) <= 2^30. Any tile size
+ * is accepted; a tile's t extent is padded to a multiple of 32 rows inside the
+ * library, so tile_t values that are multiples of 32 waste nothing. */
+
+/* Bytes of `saved` (lives from rnnt_loss_fwd to rnnt_loss_bwd, must not be
+ * modified in between) and of `workspace` (scratch, reusable after each call)
+ * for this descriptor and these lengths. Host-only; launches nothing.
+ * Either output pointer may be NULL. */
+rnnt_status rnnt_loss_query(const rnnt_desc* desc, const int32_t* T_len_host,
+                            const int32_t* U_len_host, size_t* saved_bytes,
+                            size_t* workspace_bytes);
+
+/* Forward: per-sample costs[b] = -ln P(y_b | x_b) (fp32 [B], device).
+ * Fills `saved` with the tile plan, the joint pre-activations, the per-cell
+ * log-softmax denominators and two log-probs, alpha, beta and ln P (and, in
+ * untiled mode, z and the scores). workspace may be NULL in the forward. */
+rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
+                          const int32_t* labels, const int32_t* T_len_host,
+                          const int32_t* U_len_host, const void* WA, const void* WL,
+                          const void* bZ, const void* WO, const void* bO, float* costs,
+                          void* saved, size_t saved_bytes, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Backward: gradients of L = sum_b dcosts[b] * cost_b (dcosts fp32 [B] on the
+ * device; NULL means all ones, i.e. L = sum of costs) with respect to every
+ * input: dhA [B,T,HA], dhL [B,U+1,HL], dWA [H,HA], dWL [H,HL], dbZ [H],
+ * dWO [V,H], dbO [V], all fp32 on the device. The inputs must be the ones
+ * given to rnnt_loss_fwd, and `saved` the buffer it filled. In untiled mode
+ * the backward overwrites the scores kept in `saved` with their gradients
+ * (in place, as the scores are not needed afterwards), so it may run once
+ * per forward; in tiled mode `saved` is only read. */
+rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
+                          const int32_t* labels, const int32_t* T_len_host,
+                          const int32_t* U_len_host, const void* WA, const void* WL,
+                          const void* bZ, const void* WO, const void* bO,
+                          const float* dcosts, void* saved, size_t saved_bytes,
+                          void* workspace, size_t workspace_bytes, float* dhA, float* dhL,
+                          float* dWA, float* dWL, float* dbZ, float* dWO, float* dbO,
+                          void* stream);
+
+/* The lattice step alone (forward-backward variables, "Transducer training"
+ * Eqs. (8)-(9)) on caller-given two log-probs, for testing and for callers
+ * that produce phi/psi themselves. T_len_dev / U_len_dev are DEVICE int32
+ * arrays [B] (same ranges as above, not checked here). phi, psi, alpha, beta
+ * are fp32 [B, U+1, T] on the device (t fastest); psi at u = U_len[b] is
+ * never read. costs[b] = -(alpha(T_b-1,U_b) + phi(T_b-1,U_b)). Cells outside
+ * a sample's lattice are not written. desc supplies B, T, U (other fields
+ * are ignored). */
+rnnt_status rnnt_lattice(const rnnt_desc* desc, const int32_t* T_len_dev,
+                         const int32_t* U_len_dev, const float* phi, const float* psi,
+                         float* alpha, float* beta, float* costs, void* stream);
+
+/* Launch timing (tracing). rnnt_profile_start() clears previous records and
+ * makes every later launch record a hipEvent pair on its stream;
+ * rnnt_profile_stop() waits for those events, turns them into per-kernel
+ * totals (launch count and summed milliseconds, keyed by kernel name such as
+ * "joint_fwd", "joint_bwd", "dz", "dWO_gemm", "lattice") and sets
+ * *n_kernels; rnnt_profile_get(i, ...) reads entry i (0 <= i < n_kernels;
+ * the name stays valid until the next rnnt_profile_start). Process-global;
+ * not meant to be toggled while another thread is launching. */
+rnnt_status rnnt_profile_start(void);
+rnnt_status rnnt_profile_stop(int32_t* n_kernels);
+rnnt_status rnnt_profile_get(int32_t i, const char** name, int32_t* launches, double* total_ms);
+
+const char* rnnt_status_string(rnnt_status status);
+const char* rnnt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RNNT_MI355_H */

@@ -1,0 +1,648 @@
+// C ABI of the RNN-T joint + loss library: argument checks, the tile plan,
+// buffer layout and the launch sequence of the forward and backward passes.
+//
+// Forward ("Flash RNN-T", section "Compute it, use it, make room"; "Neural
+// transducer training ...", section "Transducer training", Eqs. (3)-(9)):
+//   1. a = W^A h^A + b^Z and l = W^L h^L              (MFMA GEMMs)
+//   2. per lattice cell: z, scores, logsumexp, phi, psi (fused kernel; scores
+//      and z kept only in untiled mode)
+//   3. alpha, beta, ln P and the costs                  (lattice kernel)
+// Backward (Eq. (10) and the gradient accumulation of the sample-wise
+// method, section "Sample-wise method"), one wave of tiles at a time:
+//   4. recompute scores, dh in place of them, z          (fused kernel)
+//   5. dz = dh W^O, ds = dz (1 - z^2), sums over u / t  (dz kernel)
+//   6. gA += sums over u, gL += sums over t             (ordered reductions)
+//   7. dW^O += dh^T z, db^O += sum dh                    (split-K GEMM)
+// then dh^A = gA W^A, dh^L = gL W^L, dW^A = gA^T h^A, dW^L = gL^T h^L,
+// db^Z = sum gA.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/rnnt.h"
+#include "common.hpp"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+static_assert(sizeof(rnnt::Tile) == sizeof(rnnt::TileH), "tile record layout");
+static_assert(sizeof(rnnt::Group) == sizeof(rnnt::GroupH), "group record layout");
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rnnt_status fail(rnnt_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+#define RNNT_HIP(call)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (call);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return fail(RNNT_E_HIP, std::string(#call) + ": " + hipGetErrorString(e_));     \
+  } while (0)
+
+rnnt_status to_dims(const rnnt_desc* desc, rnnt::Dims& d) {
+  if (!desc) return fail(RNNT_E_INVALID, "desc is null");
+  if (desc->dtype != RNNT_F32 && desc->dtype != RNNT_BF16) return fail(RNNT_E_INVALID, "unknown dtype");
+  if (desc->mode != RNNT_TILED && desc->mode != RNNT_UNTILED) return fail(RNNT_E_INVALID, "unknown mode");
+  if (desc->reserved != 0) return fail(RNNT_E_INVALID, "reserved field must be 0");
+  d = rnnt::Dims{desc->B, desc->T, desc->U, desc->V, desc->HA, desc->HL, desc->H, desc->blank,
+                 desc->dtype == RNNT_BF16, desc->mode == RNNT_UNTILED, desc->tile_t, desc->tile_u,
+                 desc->tiles_per_wave};
+  std::string err;
+  int st = 0;
+  if (!rnnt::check_dims(d, err, st)) return fail((rnnt_status)st, err);
+  return RNNT_OK;
+}
+
+rnnt_status prepare(const rnnt_desc* desc, const int32_t* T_len, const int32_t* U_len, rnnt::Plan& p,
+                    rnnt::Layout& L) {
+  rnnt::Dims d;
+  rnnt_status s = to_dims(desc, d);
+  if (s != RNNT_OK) return s;
+  std::string err;
+  if (!rnnt::check_lengths(d, T_len, U_len, err)) return fail(RNNT_E_INVALID, err);
+  int ks = rnnt::joint_ks_for(d.H);
+  if (ks < 0) return fail(RNNT_E_UNSUPPORTED, "H too large for the fused joint kernel");
+  rnnt::build_plan(d, T_len, U_len, ks * 16, p);
+  L = rnnt::make_layout(p);
+  return RNNT_OK;
+}
+
+// Pinned staging for the host -> device plan copy. The buffer is reused once
+// the previous copy (tracked by an event) has completed.
+struct Staging {
+  std::mutex mu;
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+Staging g_staging;
+
+rnnt_status upload(void* dst, const std::vector<char>& src, hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_staging.mu);
+  if (g_staging.pending) {
+    RNNT_HIP(hipEventSynchronize(g_staging.ev));
+    g_staging.pending = false;
+  }
+  if (!g_staging.ev) RNNT_HIP(hipEventCreateWithFlags(&g_staging.ev, hipEventDisableTiming));
+  if (g_staging.cap < src.size()) {
+    if (g_staging.host) RNNT_HIP(hipHostFree(g_staging.host));
+    g_staging.host = nullptr;
+    g_staging.cap = 0;
+    RNNT_HIP(hipHostMalloc(&g_staging.host, src.size(), hipHostMallocDefault));
+    g_staging.cap = src.size();
+  }
+  std::memcpy(g_staging.host, src.data(), src.size());
+  RNNT_HIP(hipMemcpyAsync(dst, g_staging.host, src.size(), hipMemcpyHostToDevice, st));
+  RNNT_HIP(hipEventRecord(g_staging.ev, st));
+  g_staging.pending = true;
+  return RNNT_OK;
+}
+
+// ---------------------------------------------------------------- launch timing
+// When enabled, every launch site records a hipEvent pair on the launch
+// stream; rnnt_profile_stop() resolves them into per-kernel totals.
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<ProfRec> recs;
+  std::vector<std::string> names;
+  std::vector<int> launches;
+  std::vector<double> total_ms;
+};
+Profiler g_prof;
+
+struct ProfScope {
+  hipStream_t st;
+  hipEvent_t b = nullptr;
+  ProfScope(const char* name, hipStream_t s) : st(s) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (!g_prof.on) return;
+    hipEvent_t a;
+    if (hipEventCreate(&a) != hipSuccess) return;
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      b = nullptr;
+      return;
+    }
+    (void)hipEventRecord(a, st);
+    g_prof.recs.push_back(ProfRec{name, a, b});
+  }
+  ~ProfScope() {
+    if (b) (void)hipEventRecord(b, st);
+  }
+};
+
+template <class T> T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+template <class T> const T* at(const void* base, size_t off) {
+  return reinterpret_cast<const T*>(static_cast<const char*>(base) + off);
+}
+
+struct Saved {
+  const int32_t* Tlen;
+  const int32_t* Ulen;
+  const rnnt::Tile* tiles;
+  const rnnt::Group* groups;
+  const int32_t* gidx;
+  float *a, *l, *lse, *phi, *psi, *alpha, *beta, *lnP;
+  void* logits;
+  void* z;
+};
+
+Saved saved_view(void* s, const rnnt::Layout& L) {
+  Saved v;
+  v.Tlen = at<int32_t>(s, L.off_Tlen);
+  v.Ulen = at<int32_t>(s, L.off_Ulen);
+  v.tiles = at<rnnt::Tile>(s, L.off_tiles);
+  v.groups = at<rnnt::Group>(s, L.off_groups);
+  v.gidx = at<int32_t>(s, L.off_gidx);
+  v.a = at<float>(s, L.off_a);
+  v.l = at<float>(s, L.off_l);
+  v.lse = at<float>(s, L.off_lse);
+  v.phi = at<float>(s, L.off_phi);
+  v.psi = at<float>(s, L.off_psi);
+  v.alpha = at<float>(s, L.off_alpha);
+  v.beta = at<float>(s, L.off_beta);
+  v.lnP = at<float>(s, L.off_lnP);
+  v.logits = L.off_logits ? at<char>(s, L.off_logits) : nullptr;
+  v.z = L.off_z ? at<char>(s, L.off_z) : nullptr;
+  return v;
+}
+
+rnnt::JointArgs joint_args(const rnnt::Plan& p, const Saved& sv, const int32_t* labels, const void* WO,
+                           const void* bO) {
+  rnnt::JointArgs a{};
+  a.tiles = sv.tiles;
+  a.T_len = sv.Tlen;
+  a.U_len = sv.Ulen;
+  a.labels = labels;
+  a.T = p.d.T;
+  a.U1 = p.U1;
+  a.V = p.d.V;
+  a.H = p.d.H;
+  a.H_pad = p.H_pad;
+  a.V_pad = p.V_pad;
+  a.blank = p.d.blank;
+  a.a = sv.a;
+  a.l = sv.l;
+  a.WO = WO;
+  a.bO = bO;
+  a.lse = sv.lse;
+  a.phi = sv.phi;
+  a.psi = sv.psi;
+  a.alpha = sv.alpha;
+  a.beta = sv.beta;
+  a.lnP = sv.lnP;
+  return a;
+}
+
+inline int rows_per_chunk(bool bf16) { return bf16 ? 32 : 16; }
+
+}  // namespace
+
+extern "C" {
+
+const char* rnnt_status_string(rnnt_status s) {
+  switch (s) {
+    case RNNT_OK: return "ok";
+    case RNNT_E_INVALID: return "invalid argument";
+    case RNNT_E_WORKSPACE: return "saved or workspace buffer too small";
+    case RNNT_E_HIP: return "HIP runtime error";
+    case RNNT_E_UNSUPPORTED: return "unsupported by this build";
+  }
+  return "unknown status";
+}
+
+const char* rnnt_last_error(void) { return g_last_error.c_str(); }
+
+rnnt_status rnnt_loss_query(const rnnt_desc* desc, const int32_t* T_len_host, const int32_t* U_len_host,
+                            size_t* saved_bytes, size_t* workspace_bytes) {
+  rnnt::Plan p;
+  rnnt::Layout L;
+  rnnt_status s = prepare(desc, T_len_host, U_len_host, p, L);
+  if (s != RNNT_OK) return s;
+  if (saved_bytes) *saved_bytes = L.saved_bytes;
+  if (workspace_bytes) *workspace_bytes = L.workspace_bytes;
+  return RNNT_OK;
+}
+
+rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL, const int32_t* labels,
+                          const int32_t* T_len_host, const int32_t* U_len_host, const void* WA,
+                          const void* WL, const void* bZ, const void* WO, const void* bO, float* costs,
+                          void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  rnnt::Plan p;
+  rnnt::Layout L;
+  rnnt_status s = prepare(desc, T_len_host, U_len_host, p, L);
+  if (s != RNNT_OK) return s;
+  if (!hA || !hL || !labels || !WA || !WL || !bZ || !WO || !bO || !costs || !saved)
+    return fail(RNNT_E_INVALID, "null input, output or saved pointer");
+  if (saved_bytes < L.saved_bytes) return fail(RNNT_E_WORKSPACE, "saved buffer smaller than rnnt_loss_query");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool bf = p.d.bf16;
+  const rnnt::Dims& d = p.d;
+
+  std::vector<char> host_plan;
+  rnnt::serialize_plan(p, L, T_len_host, U_len_host, host_plan);
+  s = upload(saved, host_plan, st);
+  if (s != RNNT_OK) return s;
+  Saved sv = saved_view(saved, L);
+
+  // 1. joint pre-activations
+  {
+    rnnt::GemmArgs g{};
+    g.A = rnnt::Operand{hA, d.HA, d.B * d.T, nullptr, 1, 0};
+    g.B = rnnt::Operand{WA, d.HA, d.H, nullptr, 1, 0};
+    g.M = d.B * d.T;
+    g.N = d.H;
+    g.K = d.HA;
+    g.k_per_split = d.HA;
+    g.C = sv.a;
+    g.ldc = p.H_pad;
+    g.c_cols = p.H_pad;
+    g.bias = bZ;
+    g.bias_bf16 = bf;
+    {
+      ProfScope ps_("preproj_gemm", st);
+      RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_KC_KC, bf, bf, bf, 1, st));
+    }
+    g.A = rnnt::Operand{hL, d.HL, d.B * p.U1, nullptr, 1, 0};
+    g.B = rnnt::Operand{WL, d.HL, d.H, nullptr, 1, 0};
+    g.M = d.B * p.U1;
+    g.K = d.HL;
+    g.k_per_split = d.HL;
+    g.C = sv.l;
+    g.bias = nullptr;
+    {
+      ProfScope ps_("preproj_gemm", st);
+      RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_KC_KC, bf, bf, bf, 1, st));
+    }
+  }
+  // 2. fused joint + output layer + log-softmax statistics
+  {
+    rnnt::JointArgs a = joint_args(p, sv, labels, WO, bO);
+    a.tile_begin = 0;
+    a.tile_end = (int)p.tiles.size();
+    a.row_begin = 0;
+    a.n_chunks = (int)(p.total_rows / rows_per_chunk(bf));
+    a.lse_out = sv.lse;
+    a.phi_out = sv.phi;
+    a.psi_out = sv.psi;
+    a.store = d.untiled ? 1 : 0;
+    a.logits_out = sv.logits;
+    a.z_out = sv.z;
+    a.buf_row_base = 0;
+    {
+      ProfScope ps_("joint_fwd", st);
+      RNNT_HIP(rnnt::launch_joint(a, bf, false, st));
+    }
+  }
+  // 3. lattice
+  {
+    rnnt::LatticeArgs la{sv.Tlen, sv.Ulen, sv.phi, sv.psi, sv.alpha, sv.beta, sv.lnP, costs, d.B, d.T, p.U1};
+    {
+      ProfScope ps_("lattice", st);
+      RNNT_HIP(rnnt::launch_lattice(la, p.U1, st));
+    }
+  }
+  return RNNT_OK;
+}
+
+rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL, const int32_t* labels,
+                          const int32_t* T_len_host, const int32_t* U_len_host, const void* WA,
+                          const void* WL, const void* bZ, const void* WO, const void* bO,
+                          const float* dcosts, void* saved, size_t saved_bytes, void* workspace,
+                          size_t workspace_bytes, float* dhA, float* dhL, float* dWA, float* dWL,
+                          float* dbZ, float* dWO, float* dbO, void* stream) {
+  (void)bZ;
+  rnnt::Plan p;
+  rnnt::Layout L;
+  rnnt_status s = prepare(desc, T_len_host, U_len_host, p, L);
+  if (s != RNNT_OK) return s;
+  if (!hA || !hL || !labels || !WA || !WL || !WO || !bO || !saved || !workspace || !dhA || !dhL || !dWA ||
+      !dWL || !dbZ || !dWO || !dbO)
+    return fail(RNNT_E_INVALID, "null input, output, saved or workspace pointer");
+  if (saved_bytes < L.saved_bytes) return fail(RNNT_E_WORKSPACE, "saved buffer smaller than rnnt_loss_query");
+  if (workspace_bytes < L.workspace_bytes)
+    return fail(RNNT_E_WORKSPACE, "workspace buffer smaller than rnnt_loss_query");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool bf = p.d.bf16;
+  const rnnt::Dims& d = p.d;
+  Saved sv = saved_view(saved, L);
+  float* gA = at<float>(workspace, L.w_gA);
+  float* gL = at<float>(workspace, L.w_gL);
+  float* PA = at<float>(workspace, L.w_PA);
+  float* PL = at<float>(workspace, L.w_PL);
+  float* PW = at<float>(workspace, L.w_PW);
+  float* PB = at<float>(workspace, L.w_PB);
+  void* dh_buf = d.untiled ? sv.logits : at<char>(workspace, L.w_dh);
+  void* z_buf = d.untiled ? sv.z : at<char>(workspace, L.w_z);
+
+  {
+    ProfScope ps_("fill", st);
+    RNNT_HIP(rnnt::launch_fill(gA, (int64_t)d.B * d.T * d.H, 0.0f, st));
+  }
+  {
+    ProfScope ps_("fill", st);
+    RNNT_HIP(rnnt::launch_fill(gL, (int64_t)d.B * p.U1 * d.H, 0.0f, st));
+  }
+  {
+    ProfScope ps_("fill", st);
+    RNNT_HIP(rnnt::launch_fill(dWO, (int64_t)d.V * d.H, 0.0f, st));
+  }
+  {
+    ProfScope ps_("fill", st);
+    RNNT_HIP(rnnt::launch_fill(dbO, d.V, 0.0f, st));
+  }
+
+  for (const rnnt::WaveInfo& wv : p.waves) {
+    const int wrows = wv.row_end - wv.row_begin;
+    const int buf_base = d.untiled ? 0 : wv.row_begin;
+    // 4. dh (and z) for the wave's cells
+    if (d.untiled) {
+      rnnt::DhInplaceArgs a{};
+      a.tiles = sv.tiles;
+      a.tile_begin = wv.tile_begin;
+      a.tile_end = wv.tile_end;
+      a.row_begin = wv.row_begin;
+      a.n_rows = wrows;
+      a.T_len = sv.Tlen;
+      a.U_len = sv.Ulen;
+      a.labels = labels;
+      a.T = d.T;
+      a.U1 = p.U1;
+      a.V = d.V;
+      a.V_pad = p.V_pad;
+      a.blank = d.blank;
+      a.logits = sv.logits;
+      a.buf_row_base = 0;
+      a.lse = sv.lse;
+      a.phi = sv.phi;
+      a.psi = sv.psi;
+      a.alpha = sv.alpha;
+      a.beta = sv.beta;
+      a.lnP = sv.lnP;
+      a.dcosts = dcosts;
+      {
+        ProfScope ps_("dh_inplace", st);
+        RNNT_HIP(rnnt::launch_dh_inplace(a, bf, st));
+      }
+    } else {
+      rnnt::JointArgs a = joint_args(p, sv, labels, WO, bO);
+      a.tile_begin = wv.tile_begin;
+      a.tile_end = wv.tile_end;
+      a.row_begin = wv.row_begin;
+      a.n_chunks = wrows / rows_per_chunk(bf);
+      a.logits_out = dh_buf;
+      a.z_out = z_buf;
+      a.buf_row_base = buf_base;
+      a.dcosts = dcosts;
+      {
+        ProfScope ps_("joint_bwd", st);
+        RNNT_HIP(rnnt::launch_joint(a, bf, true, st));
+      }
+    }
+    // 5. dz, dtanh and per-tile sums
+    {
+      rnnt::DzArgs a{};
+      a.tiles = sv.tiles;
+      a.tile_begin = wv.tile_begin;
+      a.tile_end = wv.tile_end;
+      a.strip_begin = wv.strip_begin;
+      a.n_strips = wv.strip_end - wv.strip_begin;
+      a.wave_row_base = buf_base;
+      a.dh = dh_buf;
+      a.z = z_buf;
+      a.WO = WO;
+      a.V = d.V;
+      a.V_pad = p.V_pad;
+      a.H = d.H;
+      a.H_pad = p.H_pad;
+      a.PA = PA;
+      a.PL = PL;
+      a.tile_tp = p.tile_tp;
+      a.tile_u = d.tile_u;
+      {
+        ProfScope ps_("dz", st);
+        RNNT_HIP(rnnt::launch_dz(a, bf, st));
+      }
+    }
+    // 6. gA / gL
+    {
+      rnnt::GroupReduceArgs r{};
+      r.tiles = sv.tiles;
+      r.groups = sv.groups + wv.gA_begin;
+      r.n_groups = wv.gA_end - wv.gA_begin;
+      r.idx = sv.gidx;
+      r.tile_begin = wv.tile_begin;
+      r.P = PA;
+      r.tile_stride = (int64_t)p.tile_tp * d.H;
+      r.n_sub = 0;
+      r.sub_stride = 0;
+      r.G = gA;
+      r.Gdim = d.T;
+      r.H = d.H;
+      r.max_len = wv.maxA_len;
+      {
+        ProfScope ps_("group_reduce", st);
+        RNNT_HIP(rnnt::launch_group_reduce(r, st));
+      }
+      r.groups = sv.groups + wv.gL_begin;
+      r.n_groups = wv.gL_end - wv.gL_begin;
+      r.P = PL;
+      r.tile_stride = (int64_t)(p.tile_tp / 32) * d.tile_u * d.H;
+      r.n_sub = 1;
+      r.sub_stride = (int64_t)d.tile_u * d.H;
+      r.G = gL;
+      r.Gdim = p.U1;
+      r.max_len = wv.maxL_len;
+      {
+        ProfScope ps_("group_reduce", st);
+        RNNT_HIP(rnnt::launch_group_reduce(r, st));
+      }
+    }
+    // 7. dW^O and db^O
+    {
+      rnnt::GemmArgs g{};
+      g.A = rnnt::Operand{dh_buf, p.V_pad, d.V, nullptr, 1, 0};
+      g.B = rnnt::Operand{z_buf, p.H_pad, d.H, nullptr, 1, 0};
+      g.M = d.V;
+      g.N = d.H;
+      g.K = wrows;
+      const int kst = bf ? 64 : 32;
+      g.k_per_split = (int)(((wrows + p.s6 - 1) / p.s6 + kst - 1) / kst * kst);
+      g.C = PW;
+      g.ldc = d.H;
+      g.split_stride = (int64_t)d.V * d.H;
+      g.c_cols = d.H;
+      g.colsum = PB;
+      // rows of the dh/z buffers start at the wave's first row
+      {
+        ProfScope ps_("dWO_gemm", st);
+        RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_MN_MN, bf, bf, bf, p.s6, st));
+      }
+      {
+        ProfScope ps_("split_reduce", st);
+        RNNT_HIP(rnnt::launch_split_reduce(dWO, PW, (int64_t)d.V * d.H, p.s6, (int64_t)d.V * d.H, true, st));
+      }
+      {
+        ProfScope ps_("split_reduce", st);
+        RNNT_HIP(rnnt::launch_split_reduce(dbO, PB, d.V, p.s6, d.V, true, st));
+      }
+    }
+  }
+
+  // 8. encodings and joint weights (fp32 MFMA)
+  {
+    rnnt::GemmArgs g{};
+    g.A = rnnt::Operand{gA, d.H, d.B * d.T, nullptr, 1, 0};
+    g.B = rnnt::Operand{WA, d.HA, d.HA, nullptr, 1, 0};
+    g.M = d.B * d.T;
+    g.N = d.HA;
+    g.K = d.H;
+    g.k_per_split = d.H;
+    g.C = dhA;
+    g.ldc = d.HA;
+    g.c_cols = d.HA;
+    {
+      ProfScope ps_("dh_enc_gemm", st);
+      RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_KC_MN, false, false, bf, 1, st));
+    }
+    g.A = rnnt::Operand{gL, d.H, d.B * p.U1, nullptr, 1, 0};
+    g.B = rnnt::Operand{WL, d.HL, d.HL, nullptr, 1, 0};
+    g.M = d.B * p.U1;
+    g.N = d.HL;
+    g.C = dhL;
+    g.ldc = d.HL;
+    g.c_cols = d.HL;
+    {
+      ProfScope ps_("dh_enc_gemm", st);
+      RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_KC_MN, false, false, bf, 1, st));
+    }
+  }
+  {
+    float* PWA = at<float>(workspace, L.w_PWA);
+    float* PBZ = at<float>(workspace, L.w_PBZ);
+    float* PWL = at<float>(workspace, L.w_PWL);
+    rnnt::GemmArgs g{};
+    g.A = rnnt::Operand{gA, d.H, d.H, nullptr, 1, 0};
+    g.B = rnnt::Operand{hA, d.HA, d.HA, sv.Tlen, d.T, 0};
+    g.M = d.H;
+    g.N = d.HA;
+    g.K = d.B * d.T;
+    g.k_per_split = (int)(((g.K + p.s7a - 1) / p.s7a + 31) / 32 * 32);
+    g.C = PWA;
+    g.ldc = d.HA;
+    g.split_stride = (int64_t)d.H * d.HA;
+    g.c_cols = d.HA;
+    g.colsum = PBZ;
+    {
+      ProfScope ps_("dW_enc_gemm", st);
+      RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_MN_MN, false, false, bf, p.s7a, st));
+    }
+    {
+      ProfScope ps_("split_reduce", st);
+      RNNT_HIP(rnnt::launch_split_reduce(dWA, PWA, (int64_t)d.H * d.HA, p.s7a, (int64_t)d.H * d.HA, false, st));
+    }
+    {
+      ProfScope ps_("split_reduce", st);
+      RNNT_HIP(rnnt::launch_split_reduce(dbZ, PBZ, d.H, p.s7a, d.H, false, st));
+    }
+    g.A = rnnt::Operand{gL, d.H, d.H, nullptr, 1, 0};
+    g.B = rnnt::Operand{hL, d.HL, d.HL, sv.Ulen, p.U1, 1};
+    g.N = d.HL;
+    g.K = d.B * p.U1;
+    g.k_per_split = (int)(((g.K + p.s7l - 1) / p.s7l + 31) / 32 * 32);
+    g.C = PWL;
+    g.ldc = d.HL;
+    g.split_stride = (int64_t)d.H * d.HL;
+    g.c_cols = d.HL;
+    g.colsum = nullptr;
+    {
+      ProfScope ps_("dW_enc_gemm", st);
+      RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_MN_MN, false, false, bf, p.s7l, st));
+    }
+    {
+      ProfScope ps_("split_reduce", st);
+      RNNT_HIP(rnnt::launch_split_reduce(dWL, PWL, (int64_t)d.H * d.HL, p.s7l, (int64_t)d.H * d.HL, false, st));
+    }
+  }
+  return RNNT_OK;
+}
+
+rnnt_status rnnt_profile_start(void) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (auto& r : g_prof.recs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_prof.recs.clear();
+  g_prof.names.clear();
+  g_prof.launches.clear();
+  g_prof.total_ms.clear();
+  g_prof.on = true;
+  return RNNT_OK;
+}
+
+rnnt_status rnnt_profile_stop(int32_t* n_kernels) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.on = false;
+  rnnt_status st = RNNT_OK;
+  for (auto& r : g_prof.recs) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) st = fail(RNNT_E_HIP, std::string("profile events: ") + hipGetErrorString(e));
+    size_t k = 0;
+    while (k < g_prof.names.size() && g_prof.names[k] != r.name) ++k;
+    if (k == g_prof.names.size()) {
+      g_prof.names.push_back(r.name);
+      g_prof.launches.push_back(0);
+      g_prof.total_ms.push_back(0.0);
+    }
+    g_prof.launches[k] += 1;
+    g_prof.total_ms[k] += ms;
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_prof.recs.clear();
+  if (n_kernels) *n_kernels = (int32_t)g_prof.names.size();
+  return st;
+}
+
+rnnt_status rnnt_profile_get(int32_t i, const char** name, int32_t* launches, double* total_ms) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (i < 0 || i >= (int32_t)g_prof.names.size()) return fail(RNNT_E_INVALID, "profile index out of range");
+  if (name) *name = g_prof.names[i].c_str();
+  if (launches) *launches = g_prof.launches[i];
+  if (total_ms) *total_ms = g_prof.total_ms[i];
+  return RNNT_OK;
+}
+
+rnnt_status rnnt_lattice(const rnnt_desc* desc, const int32_t* T_len_dev, const int32_t* U_len_dev,
+                         const float* phi, const float* psi, float* alpha, float* beta, float* costs,
+                         void* stream) {
+  if (!desc) return fail(RNNT_E_INVALID, "desc is null");
+  if (desc->B <= 0 || desc->T <= 0 || desc->U < 0) return fail(RNNT_E_INVALID, "need B, T > 0 and U >= 0");
+  if (desc->U + 1 > 1024) return fail(RNNT_E_UNSUPPORTED, "this build supports U + 1 <= 1024");
+  if (!T_len_dev || !U_len_dev || !phi || !psi || !alpha || !beta || !costs)
+    return fail(RNNT_E_INVALID, "null pointer");
+  rnnt::LatticeArgs la{T_len_dev, U_len_dev, phi, psi, alpha, beta, nullptr, costs, desc->B, desc->T, desc->U + 1};
+  RNNT_HIP(rnnt::launch_lattice(la, desc->U + 1, reinterpret_cast<hipStream_t>(stream)));
+  return RNNT_OK;
+}
+
+}  // extern "C"

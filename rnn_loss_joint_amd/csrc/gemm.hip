@@ -1,0 +1,521 @@
+// MFMA GEMMs for the joint pre-projections, the backward through the output
+// layer and joint network, and the deterministic reductions that follow them
+// ("Neural transducer training ...", section "Sample-wise method": the
+// per-piece gradients of the joint network and output layer are accumulated,
+// which gives the same result as one batched computation).
+//
+// Engine: 256 threads, 128 x 128 output tile, 2 x 2 waves of 64 x 64, k in
+// 128-byte LDS stages (64 bf16 or 32 fp32), double buffered. Operands are
+// staged into the swizzled [row][k] LDS layout of common.hpp either directly
+// (k-contiguous sources) or through a 4 x 8 / 4 x 4 register transpose
+// (m-contiguous sources), so every MFMA fragment is one 16-byte LDS read.
+#include "common.hpp"
+#include "kernels.hpp"
+
+#include <algorithm>
+
+namespace rnnt {
+
+namespace {
+
+constexpr int TM = 128;  // workgroup tile
+
+__device__ inline bool kvalid(const Operand& o, int k) {
+  if (!o.kv_len) return true;
+  int s = k / o.kv_T;
+  return (k - s * o.kv_T) < o.kv_len[s] + o.kv_add;
+}
+
+// k-contiguous operand: piece i of thread tid is row i*32 + tid/8, chunk tid%8.
+template <class M, class S>
+struct KcLoader {
+  using CT = typename M::CT;
+  static constexpr int KPL = M::KPL;
+  const S* rowp[4];
+  u32x4 v[4];
+  int c, K;
+  __device__ void init(int tid, int K_) {
+    c = tid & 7;
+    K = K_;
+  }
+  __device__ void set_row(int i, const S* p) { rowp[i] = p; }
+  __device__ void load(int k0) {
+    int k = k0 + c * KPL;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (rowp[i] && k < K) {
+        if constexpr (sizeof(S) == sizeof(CT)) {
+          v[i] = ldg<u32x4>(rowp[i] + k);
+        } else {  // bf16 source, fp32 compute: 4 bf16 -> 4 floats
+          bf16x4 x = ldg<bf16x4>(rowp[i] + k);
+          f32x4 f = {(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+          v[i] = __builtin_bit_cast(u32x4, f);
+        }
+      } else {
+        v[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+  __device__ void store(char* buf, int tid) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(buf + lds_off(i * 32 + (tid >> 3), c)) = v[i];
+  }
+};
+
+// m-contiguous operand: thread covers 4 k rows x ER consecutive m and writes
+// them transposed. bf16: ER = 8 (16 k-groups x 16 m-groups); fp32: ER = 4
+// (8 k-groups x 32 m-groups).
+template <class M, class S, bool COLSUM>
+struct MnLoader {
+  using CT = typename M::CT;
+  static constexpr int ER = (sizeof(CT) == 2) ? 8 : 4;
+  static constexpr int NRQ = TM / ER;
+  Operand o;
+  int K, m0, kq, rq;
+  CT val[4][ER];
+  float cs[ER];
+  __device__ void init(const Operand& op, int K_, int m0_, int tid) {
+    o = op;
+    K = K_;
+    m0 = m0_;
+    kq = tid / NRQ;
+    rq = tid % NRQ;
+#pragma unroll
+    for (int e = 0; e < ER; ++e) cs[e] = 0.0f;
+  }
+  __device__ void load(int k0) {
+    const int m = m0 + rq * ER;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int k = k0 + kq * 4 + i;
+      bool ok = k < K && kvalid(o, k);
+      const S* src = reinterpret_cast<const S*>(o.base) + (int64_t)k * o.ld + m;
+      if (ok && m + ER <= o.rows) {
+        if constexpr (sizeof(S) == 2 && ER == 8) {
+          bf16x8 x = ldg<bf16x8>(src);
+#pragma unroll
+          for (int e = 0; e < ER; ++e) val[i][e] = (CT)x[e];
+        } else if constexpr (sizeof(S) == 2) {
+          bf16x4 x = ldg<bf16x4>(src);
+#pragma unroll
+          for (int e = 0; e < ER; ++e) val[i][e] = (CT)(float)x[e];
+        } else {
+          f32x4 x = ldg<f32x4>(src);
+#pragma unroll
+          for (int e = 0; e < ER; ++e) val[i][e] = to_ct<CT>(x[e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < ER; ++e)
+          val[i][e] = (ok && m + e < o.rows) ? to_ct<CT>(to_f32(src[e])) : to_ct<CT>(0.0f);
+      }
+      if (COLSUM) {
+#pragma unroll
+        for (int e = 0; e < ER; ++e) cs[e] += to_f32(val[i][e]);
+      }
+    }
+  }
+  __device__ void store(char* buf, int) const {
+#pragma unroll
+    for (int e = 0; e < ER; ++e) {
+      int row = rq * ER + e;
+      if constexpr (sizeof(CT) == 2) {
+        bf16x4 w = {val[0][e], val[1][e], val[2][e], val[3][e]};
+        *reinterpret_cast<bf16x4*>(buf + lds_off(row, kq >> 1) + (kq & 1) * 8) = w;
+      } else {
+        f32x4 w = {val[0][e], val[1][e], val[2][e], val[3][e]};
+        *reinterpret_cast<f32x4*>(buf + lds_off(row, kq)) = w;
+      }
+    }
+  }
+};
+
+template <class M>
+struct WaveTile {
+  static constexpr int W = 64 / M::ROWS;  // blocks per wave in m and n
+  typename M::Acc acc[W][W];
+  __device__ void zero() {
+#pragma unroll
+    for (int i = 0; i < W; ++i)
+#pragma unroll
+      for (int j = 0; j < W; ++j) acc[i][j] = typename M::Acc{};
+  }
+  // one LDS stage: A rows [wr*64, +64), B rows [wc*64, +64)
+  __device__ void mma_stage(const char* abuf, const char* bbuf, int wr, int wc, int lane) {
+    using Frag = typename M::Frag;
+    constexpr int SPS = 8 / M::GROUPS;
+    const int r = lane % M::ROWS, g = lane / M::ROWS;
+#pragma unroll
+    for (int ss = 0; ss < SPS; ++ss) {
+      Frag af[W], bfr[W];
+#pragma unroll
+      for (int i = 0; i < W; ++i)
+        af[i] = *reinterpret_cast<const Frag*>(abuf + lds_off(wr * 64 + i * M::ROWS + r, ss * M::GROUPS + g));
+#pragma unroll
+      for (int j = 0; j < W; ++j)
+        bfr[j] = *reinterpret_cast<const Frag*>(bbuf + lds_off(wc * 64 + j * M::ROWS + r, ss * M::GROUPS + g));
+#pragma unroll
+      for (int i = 0; i < W; ++i)
+#pragma unroll
+        for (int j = 0; j < W; ++j) acc[i][j] = M::mma(af[i], bfr[j], acc[i][j]);
+    }
+  }
+};
+
+// Full k loop over [kb, ke) with double-buffered LDS stages.
+template <class M, class LA, class LB>
+__device__ void mainloop(WaveTile<M>& wt, LA& la, LB& lb, int kb, int ke, char* lds, int tid) {
+  constexpr int KST = 8 * M::KPL;
+  const int lane = tid & 63, wave = tid >> 6, wr = wave >> 1, wc = wave & 1;
+  // stage s: A at lds + s*TM*128, B at lds + (2+s)*TM*128 (offsets, so the
+  // compiler keeps the LDS address space)
+  constexpr int SB = TM * 128;
+  if (kb >= ke) return;
+  la.load(kb);
+  lb.load(kb);
+  la.store(lds, tid);
+  lb.store(lds + 2 * SB, tid);
+  __syncthreads();
+  int cur = 0;
+  for (int k0 = kb; k0 < ke; k0 += KST) {
+    const bool next = k0 + KST < ke;
+    if (next) {
+      la.load(k0 + KST);
+      lb.load(k0 + KST);
+    }
+    wt.mma_stage(lds + cur * SB, lds + (2 + cur) * SB, wr, wc, lane);
+    if (next) {
+      la.store(lds + (cur ^ 1) * SB, tid);
+      lb.store(lds + (2 + (cur ^ 1)) * SB, tid);
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- generic GEMM
+template <class M, int KIND, class SA, class SB, bool COLSUM>
+__global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) char lds[4 * TM * 128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wr = wave >> 1, wc = wave & 1;
+  const int n0 = blockIdx.x * TM, m0 = blockIdx.y * TM, split = blockIdx.z;
+  const int kb = split * g.k_per_split;
+  const int ke = min(g.K, kb + g.k_per_split);
+  WaveTile<M> wt;
+  wt.zero();
+  const bool do_cs = COLSUM && blockIdx.x == 0;
+
+  if constexpr (KIND == GEMM_KC_KC || KIND == GEMM_KC_MN) {
+    KcLoader<M, SA> la;
+    la.init(tid, g.K);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int m = m0 + i * 32 + (tid >> 3);
+      la.set_row(i, m < g.A.rows ? reinterpret_cast<const SA*>(g.A.base) + (int64_t)m * g.A.ld : nullptr);
+    }
+    if constexpr (KIND == GEMM_KC_KC) {
+      KcLoader<M, SB> lb;
+      lb.init(tid, g.K);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int n = n0 + i * 32 + (tid >> 3);
+        lb.set_row(i, n < g.B.rows ? reinterpret_cast<const SB*>(g.B.base) + (int64_t)n * g.B.ld : nullptr);
+      }
+      mainloop<M>(wt, la, lb, kb, ke, lds, tid);
+    } else {
+      MnLoader<M, SB, false> lb;
+      lb.init(g.B, g.K, n0, tid);
+      mainloop<M>(wt, la, lb, kb, ke, lds, tid);
+    }
+  } else {
+    MnLoader<M, SA, COLSUM> la;
+    la.init(g.A, g.K, m0, tid);
+    MnLoader<M, SB, false> lb;
+    lb.init(g.B, g.K, n0, tid);
+    mainloop<M>(wt, la, lb, kb, ke, lds, tid);
+    if constexpr (COLSUM) {
+      if (do_cs) {
+        // sum the per-thread column sums over the k groups
+        float* red = reinterpret_cast<float*>(lds);
+        constexpr int ER = MnLoader<M, SA, COLSUM>::ER;
+        constexpr int NKQ = 256 / (TM / ER);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < ER; ++e) red[la.kq * TM + la.rq * ER + e] = la.cs[e];
+        __syncthreads();
+        if (tid < TM && m0 + tid < g.M) {
+          float s = 0.0f;
+          for (int q = 0; q < NKQ; ++q) s += red[q * TM + tid];
+          g.colsum[(int64_t)split * g.M + m0 + tid] = s;
+        }
+      }
+    }
+  }
+
+  // epilogue: C[m, n] = acc (+ bias[n]); columns in [N, c_cols) get 0
+  constexpr int W = WaveTile<M>::W;
+  float* C = g.C + (int64_t)split * g.split_stride;
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    int n = n0 + wc * 64 + j * M::ROWS + M::col_of(lane);
+    if (n >= g.c_cols) continue;
+    float bias = 0.0f;
+    if (g.bias && n < g.N)
+      bias = g.bias_bf16 ? (float)reinterpret_cast<const bf16*>(g.bias)[n] : reinterpret_cast<const float*>(g.bias)[n];
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+#pragma unroll
+      for (int e = 0; e < M::NACC; ++e) {
+        int m = m0 + wr * 64 + i * M::ROWS + M::row_of(e, lane);
+        if (m < g.M) C[(int64_t)m * g.ldc + n] = (n < g.N) ? wt.acc[i][j][e] + bias : 0.0f;
+      }
+    }
+  }
+}
+
+template <class M, int KIND, class SA, class SB, bool CS>
+static void launch_gemm_t(const GemmArgs& g, int splits, hipStream_t st) {
+  dim3 grid((g.c_cols + TM - 1) / TM, (g.M + TM - 1) / TM, splits), block(256);
+  hipLaunchKernelGGL((gemm_kernel<M, KIND, SA, SB, CS>), grid, block, 0, st, g);
+}
+
+hipError_t launch_gemm(const GemmArgs& g, GemmKind kind, bool bf16_compute, bool a_bf16, bool b_bf16,
+                       int splits, hipStream_t st) {
+  if (g.M <= 0 || g.c_cols <= 0 || splits <= 0) return hipSuccess;
+  const bool cs = g.colsum != nullptr;
+  if (bf16_compute) {
+    if (!a_bf16 || !b_bf16) return hipErrorInvalidValue;
+    switch (kind) {
+      case GEMM_KC_KC: launch_gemm_t<MfmaBf16, GEMM_KC_KC, bf16, bf16, false>(g, splits, st); break;
+      case GEMM_KC_MN: launch_gemm_t<MfmaBf16, GEMM_KC_MN, bf16, bf16, false>(g, splits, st); break;
+      case GEMM_MN_MN:
+        if (cs) launch_gemm_t<MfmaBf16, GEMM_MN_MN, bf16, bf16, true>(g, splits, st);
+        else launch_gemm_t<MfmaBf16, GEMM_MN_MN, bf16, bf16, false>(g, splits, st);
+        break;
+    }
+  } else {
+#define RNNT_F32_CASES(SA, SB)                                                            \
+  switch (kind) {                                                                        \
+    case GEMM_KC_KC: launch_gemm_t<MfmaF32, GEMM_KC_KC, SA, SB, false>(g, splits, st); break; \
+    case GEMM_KC_MN: launch_gemm_t<MfmaF32, GEMM_KC_MN, SA, SB, false>(g, splits, st); break; \
+    case GEMM_MN_MN:                                                                     \
+      if (cs) launch_gemm_t<MfmaF32, GEMM_MN_MN, SA, SB, true>(g, splits, st);           \
+      else launch_gemm_t<MfmaF32, GEMM_MN_MN, SA, SB, false>(g, splits, st);             \
+      break;                                                                             \
+  }
+    if (!a_bf16 && !b_bf16) { RNNT_F32_CASES(float, float) }
+    else if (!a_bf16 && b_bf16) { RNNT_F32_CASES(float, bf16) }
+    else return hipErrorInvalidValue;
+#undef RNNT_F32_CASES
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- dz + dtanh + sums
+// Workgroup = one 32-row strip (32 consecutive t of one tile) x 128 columns
+// of H. It walks the tile's u values four at a time: rows of the 128-row
+// M-tile are (u = u0 + 4*ug + i/32, t = strip t + i%32). For each group it
+// computes dz = dh . W^O, ds = dz * (1 - z^2), adds ds over u into per-strip
+// gA sums held in registers, and writes the sum over the strip's t of ds for
+// every u (gL partial, one row per (strip, u)). The gA sums are written once
+// at the end. Every partial slot has exactly one writer.
+template <class M>
+__global__ void __launch_bounds__(256) dz_kernel(DzArgs p) {
+  using CT = typename M::CT;
+  constexpr int ROWS = M::ROWS, NACC = M::NACC;
+  constexpr int W = WaveTile<M>::W;
+  constexpr int TS = 32 / ROWS;  // M-blocks per 32-row strip
+  __shared__ __attribute__((aligned(16))) char lds[4 * TM * 128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wr = wave >> 1, wc = wave & 1;
+  const int strip = p.strip_begin + blockIdx.x;
+  const int h0 = blockIdx.y * TM;
+
+  int lo = p.tile_begin, hi = p.tile_end - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (p.tiles[mid].strip0 <= strip) lo = mid; else hi = mid - 1;
+  }
+  const Tile tl = p.tiles[lo];
+  const int slot = lo - p.tile_begin;
+  const int s_local = strip - tl.strip0;
+  const int tl0 = s_local * 32;
+  const int tile_row = tl.row0 - p.wave_row_base;
+  const CT* dh = reinterpret_cast<const CT*>(p.dh);
+  const CT* zb = reinterpret_cast<const CT*>(p.z);
+
+  float gacc[TS][W][NACC];
+#pragma unroll
+  for (int a = 0; a < TS; ++a)
+#pragma unroll
+    for (int j = 0; j < W; ++j)
+#pragma unroll
+      for (int e = 0; e < NACC; ++e) gacc[a][j][e] = 0.0f;
+
+  Operand wo{p.WO, p.H, p.H, nullptr, 1, 0};
+  const int ngroups = (tl.wu + 3) / 4;
+  for (int ug = 0; ug < ngroups; ++ug) {
+    KcLoader<M, CT> la;
+    la.init(tid, p.V_pad);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int row = i * 32 + (tid >> 3);
+      int ul = ug * 4 + row / 32;
+      la.set_row(i, ul < tl.wu ? dh + (int64_t)(tile_row + ul * tl.htp + tl0 + row % 32) * p.V_pad : nullptr);
+    }
+    MnLoader<M, CT, false> lb;
+    lb.init(wo, p.V, h0, tid);
+    WaveTile<M> wt;
+    wt.zero();
+    mainloop<M>(wt, la, lb, 0, p.V_pad, lds, tid);
+
+    // epilogue for this u group
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const int mrow = wr * 64 + i * ROWS;  // first M row of the block
+      const int ul = ug * 4 + mrow / 32;
+      const int ts = (mrow % 32) / ROWS;
+      const bool uok = ul < tl.wu;
+      const int64_t zrow0 = (int64_t)(tile_row + ul * tl.htp + tl0 + (mrow % 32));
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        const int h = h0 + wc * 64 + j * ROWS + M::col_of(lane);
+        float lsum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < NACC; ++e) {
+          float ds = 0.0f;
+          if (uok && h < p.H) {
+            float z = to_f32(zb[(zrow0 + M::row_of(e, lane)) * p.H_pad + h]);
+            ds = wt.acc[i][j][e] * (1.0f - z * z);
+          }
+          gacc[ts][j][e] += ds;
+          lsum += ds;
+        }
+        wt.acc[i][j][0] = lsum;  // stash per-block t-sum for the gL reduction below
+      }
+    }
+    // gL partial: sum over the strip's 32 t for each u (two u per wave row)
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) {
+      const int ul = ug * 4 + wr * 2 + uu;
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < W; ++i)
+          if ((i * ROWS) / 32 == uu) s += wt.acc[i][j][0];
+#pragma unroll
+        for (int off = ROWS; off < 64; off <<= 1) s += __shfl_xor(s, off);
+        const int h = h0 + wc * 64 + j * ROWS + M::col_of(lane);
+        if (lane < ROWS && ul < tl.wu && h < p.H)
+          p.PL[(((int64_t)slot * (p.tile_tp / 32) + s_local) * p.tile_u + ul) * p.H + h] = s;
+      }
+    }
+    __syncthreads();
+  }
+
+  // gA partial: combine the two wave rows, then one write per (t, h)
+  float* red = reinterpret_cast<float*>(lds);
+  constexpr int PER = TS * W * NACC;
+  if (wr == 1) {
+#pragma unroll
+    for (int a = 0; a < TS; ++a)
+#pragma unroll
+      for (int j = 0; j < W; ++j)
+#pragma unroll
+        for (int e = 0; e < NACC; ++e) red[((wc * PER) + (a * W + j) * NACC + e) * 64 + lane] = gacc[a][j][e];
+  }
+  __syncthreads();
+  if (wr == 0) {
+#pragma unroll
+    for (int a = 0; a < TS; ++a)
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        const int h = h0 + wc * 64 + j * ROWS + M::col_of(lane);
+#pragma unroll
+        for (int e = 0; e < NACC; ++e) {
+          float v = gacc[a][j][e] + red[((wc * PER) + (a * W + j) * NACC + e) * 64 + lane];
+          const int t = a * ROWS + M::row_of(e, lane);
+          if (h < p.H) p.PA[((int64_t)slot * p.tile_tp + tl0 + t) * p.H + h] = v;
+        }
+      }
+  }
+}
+
+hipError_t launch_dz(const DzArgs& a, bool bf16_mode, hipStream_t st) {
+  dim3 grid(a.n_strips, (a.H + TM - 1) / TM), block(256);
+  if (a.n_strips == 0) return hipSuccess;
+  if (bf16_mode) hipLaunchKernelGGL(dz_kernel<MfmaBf16>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(dz_kernel<MfmaF32>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- reductions
+__global__ void __launch_bounds__(256) group_reduce_kernel(GroupReduceArgs p) {
+  const Tile* tiles = p.tiles;
+  const int gi = blockIdx.x, j = blockIdx.y;
+  const Group gr = p.groups[gi];
+  if (j >= gr.len) return;
+  float* dst = p.G + ((int64_t)gr.b * p.Gdim + gr.start + j) * p.H;
+  for (int h = threadIdx.x; h < p.H; h += blockDim.x) {
+    float s = 0.0f;
+    for (int c = 0; c < gr.count; ++c) {
+      const int tid = p.idx[gr.first + c];
+      const int nsub = p.n_sub ? tiles[tid].htp / 32 : 1;
+      const float* src = p.P + (int64_t)(tid - p.tile_begin) * p.tile_stride + (int64_t)j * p.H + h;
+      for (int q = 0; q < nsub; ++q) s += src[q * p.sub_stride];
+    }
+    dst[h] += s;
+  }
+}
+
+hipError_t launch_group_reduce(const GroupReduceArgs& a, hipStream_t st) {
+  if (a.n_groups == 0) return hipSuccess;
+  dim3 grid(a.n_groups, a.max_len), block(256);
+  hipLaunchKernelGGL(group_reduce_kernel, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+__global__ void split_reduce_kernel(float* out, const float* P, int64_t n, int splits, int64_t stride,
+                                    int acc) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    float s = acc ? out[i] : 0.0f;
+    for (int q = 0; q < splits; ++q) s += P[q * stride + i];
+    out[i] = s;
+  }
+}
+
+hipError_t launch_split_reduce(float* out, const float* P, int64_t n, int splits, int64_t stride,
+                               bool accumulate, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(split_reduce_kernel, dim3(blocks), dim3(256), 0, st, out, P, n, splits, stride,
+                     accumulate ? 1 : 0);
+  return hipGetLastError();
+}
+
+__global__ void fill_kernel(float* p, int64_t n, float v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int blocks = (int)std::min<int64_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(fill_kernel, dim3(blocks), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
+__global__ void fill_bytes_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+hipError_t launch_fill_bytes(void* p, int64_t nbytes, hipStream_t st) {
+  int64_t n = nbytes / 4;
+  if (n <= 0) return hipSuccess;
+  int blocks = (int)std::min<int64_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(fill_bytes_kernel, dim3(blocks), dim3(256), 0, st, reinterpret_cast<uint32_t*>(p), n);
+  return hipGetLastError();
+}
+
+}  // namespace rnnt

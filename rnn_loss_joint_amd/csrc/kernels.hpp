@@ -1,0 +1,157 @@
+// Kernel argument records and launcher declarations (host <-> device glue).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace rnnt {
+
+// Fused joint + output layer (forward statistics or backward dh).
+struct JointArgs {
+  const Tile* tiles;
+  int tile_begin, tile_end;  // tiles of this launch, in plan order
+  int row_begin;             // global row of tiles[tile_begin]
+  int n_chunks;              // ROWS-row chunks covered by the launch
+  const int32_t* T_len;
+  const int32_t* U_len;
+  const int32_t* labels;  // [B, U1]
+  int T, U1, V, H, H_pad, V_pad, blank;
+  const float* a;  // [B*T, H_pad]  W^A h^A + b^Z
+  const float* l;  // [B*U1, H_pad] W^L h^L
+  const void* WO;  // [V, H]
+  const void* bO;  // [V]
+  // forward outputs, [B, U1, T]
+  float* lse_out;
+  float* phi_out;
+  float* psi_out;
+  int store;           // forward: also store scores and z (untiled mode)
+  void* logits_out;    // scores (forward store) or dh (backward), [rows, V_pad]
+  void* z_out;         // z, [rows, H_pad]
+  int buf_row_base;    // buffer row = global row - buf_row_base
+  // backward inputs
+  const float* lse;
+  const float* phi;
+  const float* psi;
+  const float* alpha;
+  const float* beta;
+  const float* lnP;
+  const float* dcosts;
+};
+
+struct DhInplaceArgs {
+  const Tile* tiles;
+  int tile_begin, tile_end, row_begin;
+  int64_t n_rows;
+  const int32_t* T_len;
+  const int32_t* U_len;
+  const int32_t* labels;
+  int T, U1, V, V_pad, blank;
+  void* logits;
+  int buf_row_base;
+  const float* lse;
+  const float* phi;
+  const float* psi;
+  const float* alpha;
+  const float* beta;
+  const float* lnP;
+  const float* dcosts;
+};
+
+int joint_ks_for(int H);
+hipError_t launch_joint(const JointArgs& a, bool bf16_mode, bool bwd, hipStream_t st);
+hipError_t launch_dh_inplace(const DhInplaceArgs& a, bool bf16_mode, hipStream_t st);
+
+// Forward-backward variables over each sample's lattice.
+struct LatticeArgs {
+  const int32_t* T_len;
+  const int32_t* U_len;
+  const float* phi;  // [B, U1, T]
+  const float* psi;
+  float* alpha;
+  float* beta;
+  float* lnP;   // [B] (may be null)
+  float* costs; // [B] (may be null)
+  int B, T, U1;
+};
+hipError_t launch_lattice(const LatticeArgs& a, int U1max, hipStream_t st);
+
+// ---------------------------------------------------------------- GEMMs
+// C[m, n] = sum_k A[m, k] * B[n, k] over a K range, 128 x 128 workgroup tiles.
+// Operand access: "kc" = element (m, k) at base + m*ld + k (k contiguous);
+// "mn" = element (m, k) at base + k*ld + m (m contiguous). kvalid (optional)
+// masks whole k rows of an mn operand: k is valid iff
+// (k % kv_T) < kv_len[k / kv_T] (+ kv_add), used to skip padded time/label
+// rows of h^A / h^L.
+struct Operand {
+  const void* base;
+  int64_t ld;
+  int rows;          // valid m (or n) extent
+  const int32_t* kv_len;
+  int kv_T, kv_add;  // see above
+};
+
+struct GemmArgs {
+  Operand A, B;
+  int M, N, K;
+  int k_per_split;   // K range per blockIdx.z
+  // epilogue
+  float* C;          // output (or partials base)
+  int64_t ldc;
+  int64_t split_stride;  // elements between split partials (0 = no split)
+  int c_cols;        // columns to write (cols in [N, c_cols) get 0)
+  const void* bias;  // optional bias over n
+  int bias_bf16;
+  // optional column sums of A over k (sum over k of A[m, k]) for n-tile 0
+  float* colsum;     // [splits, M] partials
+};
+
+enum GemmKind { GEMM_KC_KC = 0, GEMM_KC_MN = 1, GEMM_MN_MN = 2 };
+// compute: 0 = bf16 MFMA (operands bf16), 1 = f32 MFMA; src_bf16 flags give the
+// storage type of A and B.
+hipError_t launch_gemm(const GemmArgs& g, GemmKind kind, bool bf16_compute, bool a_bf16,
+                       bool b_bf16, int splits, hipStream_t st);
+
+// dz = dh . W^O with dtanh and the per-tile sums over u (gA) and t (gL).
+struct DzArgs {
+  const Tile* tiles;
+  int tile_begin, tile_end;
+  int strip_begin;       // strip0 of tiles[tile_begin]
+  int n_strips;
+  int wave_row_base;     // buffer row = global row - wave_row_base
+  const void* dh;        // [rows, V_pad]
+  const void* z;         // [rows, H_pad]
+  const void* WO;        // [V, H]
+  int V, V_pad, H, H_pad;
+  float* PA;             // [tiles_in_wave, tile_tp, H]
+  float* PL;             // [tiles_in_wave, tile_tp/32, tile_u, H]
+  int tile_tp, tile_u;
+};
+hipError_t launch_dz(const DzArgs& a, bool bf16_mode, hipStream_t st);
+
+// Deterministic sums of the per-tile partials into gA / gL.
+struct GroupReduceArgs {
+  const Tile* tiles;
+  const Group* groups;
+  int n_groups;
+  const int32_t* idx;    // tile ids (plan order)
+  int tile_begin;        // partial slot = tile id - tile_begin
+  const float* P;        // PA or PL
+  int64_t tile_stride;   // floats per tile slot
+  int n_sub;             // 1: sum the tile's htp/32 strips (PL); 0: one slot (PA)
+  int64_t sub_stride;    // floats between strips
+  float* G;              // gA [B*T, H] or gL [B*U1, H]
+  int Gdim;              // T (for gA) or U1 (for gL)
+  int H;
+  int max_len;
+};
+hipError_t launch_group_reduce(const GroupReduceArgs& a, hipStream_t st);
+
+// out[i] (+)= sum_s P[s*stride + i]
+hipError_t launch_split_reduce(float* out, const float* P, int64_t n, int splits, int64_t stride,
+                               bool accumulate, hipStream_t st);
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st);
+hipError_t launch_fill_bytes(void* p, int64_t nbytes, hipStream_t st);
+
+}  // namespace rnnt

@@ -1,0 +1,256 @@
+// Host-side tile plan and buffer layout. See plan.hpp.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <utility>
+
+namespace rnnt {
+
+namespace {
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+bool check_dims(const Dims& d, std::string& err, int& status) {
+  status = -1;  // RNNT_E_INVALID
+  if (d.B <= 0 || d.T <= 0 || d.U < 0 || d.V < 2 || d.HA <= 0 || d.HL <= 0 || d.H <= 0) {
+    err = "dimensions must satisfy B,T,HA,HL,H > 0, U >= 0, V >= 2";
+    return false;
+  }
+  if (d.blank < 0 || d.blank >= d.V) {
+    err = "blank must lie in [0, V)";
+    return false;
+  }
+  if (d.tile_t <= 0 || d.tile_u <= 0) {
+    err = "tile_t and tile_u must be positive";
+    return false;
+  }
+  if (d.tiles_per_wave < 0) {
+    err = "tiles_per_wave must be >= 0";
+    return false;
+  }
+  status = -4;  // RNNT_E_UNSUPPORTED
+  if (d.H % 8 || d.HA % 8 || d.HL % 8) {
+    err = "this build needs H, HA and HL to be multiples of 8";
+    return false;
+  }
+  if (d.H > 768) {
+    err = "this build supports H <= 768";
+    return false;
+  }
+  if (d.U + 1 > 1024) {
+    err = "this build supports U + 1 <= 1024";
+    return false;
+  }
+  if (d.V > 65536) {
+    err = "this build supports V <= 65536";
+    return false;
+  }
+  if ((int64_t)d.B * d.T * (d.U + 1) > ((int64_t)1 << 30)) {
+    err = "B*T*(U+1) exceeds 2^30 lattice cells";
+    return false;
+  }
+  status = 0;
+  return true;
+}
+
+bool check_lengths(const Dims& d, const int32_t* T_len, const int32_t* U_len, std::string& err) {
+  if (!T_len || !U_len) {
+    err = "length arrays must not be null";
+    return false;
+  }
+  for (int b = 0; b < d.B; ++b) {
+    if (T_len[b] < 1 || T_len[b] > d.T) {
+      err = "T_len[" + std::to_string(b) + "] must lie in [1, T]";
+      return false;
+    }
+    if (U_len[b] < 0 || U_len[b] > d.U) {
+      err = "U_len[" + std::to_string(b) + "] must lie in [0, U]";
+      return false;
+    }
+  }
+  return true;
+}
+
+void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H_pad, Plan& p) {
+  p = Plan{};
+  p.d = d;
+  p.U1 = d.U + 1;
+  p.H_pad = H_pad;
+  p.V_pad = (int)cdiv(d.V, 64) * 64;
+  p.KS = H_pad / 16;
+  p.tile_tp = (int)cdiv(d.tile_t, 32) * 32;
+
+  // per-sample tile grids
+  std::vector<int> nt(d.B), nu(d.B);
+  int max_tiles = 0;
+  for (int b = 0; b < d.B; ++b) {
+    nt[b] = (int)cdiv(T_len[b], d.tile_t);
+    nu[b] = (int)cdiv(U_len[b] + 1, d.tile_u);
+    max_tiles = std::max(max_tiles, nt[b] * nu[b]);
+  }
+  auto make_tile = [&](int b, int k) {
+    int it = k / nu[b], iu = k % nu[b];
+    TileH t{};
+    t.b = b;
+    t.t0 = it * d.tile_t;
+    t.u0 = iu * d.tile_u;
+    t.ht = std::min(d.tile_t, T_len[b] - t.t0);
+    t.wu = std::min(d.tile_u, U_len[b] + 1 - t.u0);
+    t.htp = (int)cdiv(t.ht, 32) * 32;
+    return t;
+  };
+  if (d.untiled) {
+    // one wave holding every tile, sample by sample
+    for (int b = 0; b < d.B; ++b)
+      for (int k = 0; k < nt[b] * nu[b]; ++k) p.tiles.push_back(make_tile(b, k));
+  } else {
+    // round robin over samples, so consecutive tiles belong to different samples
+    for (int k = 0; k < max_tiles; ++k)
+      for (int b = 0; b < d.B; ++b)
+        if (k < nt[b] * nu[b]) p.tiles.push_back(make_tile(b, k));
+  }
+  int64_t row = 0, strip = 0;
+  for (auto& t : p.tiles) {
+    t.row0 = (int32_t)row;
+    t.strip0 = (int32_t)strip;
+    row += (int64_t)t.wu * t.htp;
+    strip += t.htp / 32;
+  }
+  p.total_rows = row;
+
+  const int n = (int)p.tiles.size();
+  int tpw = d.tiles_per_wave;
+  if (tpw <= 0) {
+    // enough rows per wave to fill the GPU: at least B tiles and ~128K rows
+    int64_t area = (int64_t)p.tile_tp * d.tile_u;
+    tpw = (int)std::max<int64_t>(d.B, cdiv(131072, area));
+  }
+  if (d.untiled) tpw = std::max(n, 1);
+  p.tpw = tpw;
+
+  for (int w0 = 0; w0 < n; w0 += tpw) {
+    WaveInfo wv{};
+    wv.tile_begin = w0;
+    wv.tile_end = std::min(n, w0 + tpw);
+    const TileH& first = p.tiles[wv.tile_begin];
+    const TileH& last = p.tiles[wv.tile_end - 1];
+    wv.row_begin = first.row0;
+    wv.row_end = last.row0 + last.wu * last.htp;
+    wv.strip_begin = first.strip0;
+    wv.strip_end = last.strip0 + last.htp / 32;
+    // gA groups: tiles of this wave sharing (b, t0); gL groups: sharing (b, u0)
+    std::map<std::pair<int, int>, std::vector<int>> ga, gl;
+    for (int i = wv.tile_begin; i < wv.tile_end; ++i) {
+      ga[{p.tiles[i].b, p.tiles[i].t0}].push_back(i);
+      gl[{p.tiles[i].b, p.tiles[i].u0}].push_back(i);
+    }
+    auto emit = [&](const std::map<std::pair<int, int>, std::vector<int>>& m, bool is_a, int& mx) {
+      for (const auto& kv : m) {
+        GroupH g{};
+        g.b = kv.first.first;
+        g.start = kv.first.second;
+        const TileH& t = p.tiles[kv.second[0]];
+        g.len = is_a ? t.ht : t.wu;
+        g.first = (int)p.gidx.size();
+        g.count = (int)kv.second.size();
+        for (int id : kv.second) p.gidx.push_back(id);
+        mx = std::max(mx, g.len);
+        p.groups.push_back(g);
+      }
+    };
+    wv.gA_begin = (int)p.groups.size();
+    emit(ga, true, wv.maxA_len);
+    wv.gA_end = (int)p.groups.size();
+    wv.gL_begin = (int)p.groups.size();
+    emit(gl, false, wv.maxL_len);
+    wv.gL_end = (int)p.groups.size();
+    p.waves.push_back(wv);
+    p.max_wave_rows = std::max(p.max_wave_rows, wv.row_end - wv.row_begin);
+    p.max_wave_tiles = std::max(p.max_wave_tiles, wv.tile_end - wv.tile_begin);
+  }
+
+  // Tiled mode sizes the wave buffers by the tile bound, not by the largest
+  // wave actually planned, so the working set depends on the tile size and
+  // tiles_per_wave only (min'd with the tile count for small problems).
+  if (!d.untiled) {
+    int64_t bound_tiles = std::min<int64_t>(tpw, n);
+    p.max_wave_rows = (int)std::max<int64_t>(p.max_wave_rows, bound_tiles * p.tile_tp * d.tile_u);
+    p.max_wave_tiles = (int)std::max<int64_t>(p.max_wave_tiles, bound_tiles);
+  }
+  // split-K counts: about 1024 workgroups for dW^O, 512 for dW^A / dW^L
+  int64_t tiles_vh = cdiv(d.V, 128) * cdiv(d.H, 128);
+  p.s6 = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(1024, tiles_vh), p.max_wave_rows / 2048));
+  int64_t tiles_ha = cdiv(d.H, 128) * cdiv(d.HA, 128);
+  int64_t tiles_hl = cdiv(d.H, 128) * cdiv(d.HL, 128);
+  p.s7a = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(512, tiles_ha), cdiv((int64_t)d.B * d.T, 64)));
+  p.s7l = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(512, tiles_hl), cdiv((int64_t)d.B * p.U1, 64)));
+}
+
+Layout make_layout(const Plan& p) {
+  const Dims& d = p.d;
+  Layout L{};
+  const size_t ct = d.bf16 ? 2 : 4;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  L.off_Tlen = take(sizeof(int32_t) * d.B);
+  L.off_Ulen = take(sizeof(int32_t) * d.B);
+  L.off_tiles = take(sizeof(TileH) * p.tiles.size());
+  L.off_groups = take(sizeof(GroupH) * p.groups.size());
+  L.off_gidx = take(sizeof(int32_t) * p.gidx.size());
+  L.plan_bytes = o;
+  const size_t cells = (size_t)d.B * p.U1 * d.T;
+  L.off_a = take(sizeof(float) * (size_t)d.B * d.T * p.H_pad);
+  L.off_l = take(sizeof(float) * (size_t)d.B * p.U1 * p.H_pad);
+  L.off_lse = take(sizeof(float) * cells);
+  L.off_phi = take(sizeof(float) * cells);
+  L.off_psi = take(sizeof(float) * cells);
+  L.off_alpha = take(sizeof(float) * cells);
+  L.off_beta = take(sizeof(float) * cells);
+  L.off_lnP = take(sizeof(float) * d.B);
+  L.off_logits = L.off_z = 0;
+  if (d.untiled) {
+    L.off_logits = take(ct * (size_t)p.total_rows * p.V_pad);
+    L.off_z = take(ct * (size_t)p.total_rows * p.H_pad);
+  }
+  L.saved_bytes = o;
+
+  o = 0;
+  L.w_dh = L.w_z = 0;
+  if (!d.untiled) {
+    L.w_dh = take(ct * (size_t)p.max_wave_rows * p.V_pad);
+    L.w_z = take(ct * (size_t)p.max_wave_rows * p.H_pad);
+  }
+  L.w_gA = take(sizeof(float) * (size_t)d.B * d.T * d.H);
+  L.w_gL = take(sizeof(float) * (size_t)d.B * p.U1 * d.H);
+  L.w_PA = take(sizeof(float) * (size_t)p.max_wave_tiles * p.tile_tp * d.H);
+  L.w_PL = take(sizeof(float) * (size_t)p.max_wave_tiles * (p.tile_tp / 32) * d.tile_u * d.H);
+  L.w_PW = take(sizeof(float) * (size_t)p.s6 * d.V * d.H);
+  L.w_PB = take(sizeof(float) * (size_t)p.s6 * d.V);
+  L.w_PWA = take(sizeof(float) * (size_t)p.s7a * d.H * d.HA);
+  L.w_PBZ = take(sizeof(float) * (size_t)p.s7a * d.H);
+  L.w_PWL = take(sizeof(float) * (size_t)p.s7l * d.H * d.HL);
+  L.workspace_bytes = o;
+  return L;
+}
+
+void serialize_plan(const Plan& p, const Layout& L, const int32_t* T_len, const int32_t* U_len,
+                    std::vector<char>& out) {
+  out.assign(L.plan_bytes, 0);
+  const int B = p.d.B;
+  std::memcpy(out.data() + L.off_Tlen, T_len, sizeof(int32_t) * B);
+  std::memcpy(out.data() + L.off_Ulen, U_len, sizeof(int32_t) * B);
+  if (!p.tiles.empty()) std::memcpy(out.data() + L.off_tiles, p.tiles.data(), sizeof(TileH) * p.tiles.size());
+  if (!p.groups.empty()) std::memcpy(out.data() + L.off_groups, p.groups.data(), sizeof(GroupH) * p.groups.size());
+  if (!p.gidx.empty()) std::memcpy(out.data() + L.off_gidx, p.gidx.data(), sizeof(int32_t) * p.gidx.size());
+}
+
+}  // namespace rnnt

@@ -1,0 +1,73 @@
+// Host-side tile plan and buffer layout (plain C++, no HIP calls).
+//
+// The lattice of sample b (t < T_b, u <= U_b) is cut into tiles of at most
+// tile_t x tile_u cells ("Flash RNN-T", section "Compute it, use it, make
+// room": grid positions are grouped into tiles, and the working space of the
+// joint intermediates depends on the tile size, not the recording length).
+// Tiles are grouped into waves of at most tiles_per_wave tiles; only one
+// wave's scores and z exist at a time in the backward. Padded cells are never
+// part of any tile ("Neural transducer training ...", Introduction and
+// Conclusion: padding removal).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "common_host.hpp"
+
+namespace rnnt {
+
+struct Dims {
+  int B, T, U, V, HA, HL, H, blank;
+  bool bf16;
+  bool untiled;
+  int tile_t, tile_u, tiles_per_wave;
+};
+
+struct WaveInfo {
+  int tile_begin, tile_end;
+  int row_begin, row_end;      // global rows
+  int strip_begin, strip_end;  // global strips
+  int gA_begin, gA_end;        // group ranges
+  int gL_begin, gL_end;
+  int maxA_len, maxL_len;
+};
+
+struct Plan {
+  Dims d;
+  int U1, H_pad, V_pad, KS, tile_tp, tpw;
+  std::vector<TileH> tiles;
+  std::vector<WaveInfo> waves;
+  std::vector<GroupH> groups;
+  std::vector<int32_t> gidx;
+  int64_t total_rows = 0;
+  int max_wave_rows = 0, max_wave_tiles = 0;
+  int s6 = 1, s7a = 1, s7l = 1;  // split-K counts
+};
+
+// Byte offsets inside `saved` and `workspace` (all 256-byte aligned).
+struct Layout {
+  size_t plan_bytes;  // lengths + tiles + groups + gidx (one host->device copy)
+  size_t off_Tlen, off_Ulen, off_tiles, off_groups, off_gidx;
+  size_t off_a, off_l, off_lse, off_phi, off_psi, off_alpha, off_beta, off_lnP;
+  size_t off_logits, off_z;  // untiled only
+  size_t saved_bytes;
+  size_t w_dh, w_z, w_gA, w_gL, w_PA, w_PL, w_PW, w_PB, w_PWA, w_PBZ, w_PWL;
+  size_t workspace_bytes;
+};
+
+// Validates dims and lengths; on failure returns false and sets err.
+bool check_dims(const Dims& d, std::string& err, int& status);
+bool check_lengths(const Dims& d, const int32_t* T_len, const int32_t* U_len, std::string& err);
+// Builds the tile plan (deterministic in its inputs).
+void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H_pad, Plan& p);
+Layout make_layout(const Plan& p);
+// Serializes lengths, tiles, groups and gidx in layout order into out
+// (plan_bytes bytes, offsets relative to the start of `saved`).
+void serialize_plan(const Plan& p, const Layout& L, const int32_t* T_len, const int32_t* U_len,
+                    std::vector<char>& out);
+
+}  // namespace rnnt

@@ -1,0 +1,240 @@
+"""Parity of the HIP library with the fp64 oracle, through the C ABI.
+
+Tolerances (per sample cost; per gradient tensor relative to its max-abs):
+  fp32 mode: cost 1e-5 relative, gradients 1e-4 of max-abs
+  bf16 mode: cost 2e-3 relative, gradients 2e-2 of max-abs
+Padded gradient rows must be exactly 0. At the full sizes of the large
+workloads the oracle computes a few samples, selected on the GPU side by a
+one-hot upstream gradient (the gradients are linear in dcosts), and closed
+forms (W^O = 0) check every sample's cost.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from rnnt_inputs import make_inputs, poison_padding, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-4), "bf16": (2e-3, 2e-2)}
+GRADS = ("dhA", "dhL", "dWA", "dWL", "dbZ", "dWO", "dbO")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(rl, inp, mode="tiled", tile=(64, 32), tpw=0, dcosts=None):
+    import torch
+
+    prob = rl.Problem(inp, mode=mode, tile=tile, tiles_per_wave=tpw)
+    costs = prob.forward().clone()
+    dc = None if dcosts is None else torch.tensor(np.asarray(dcosts, np.float32), device=prob.device)
+    grads = prob.backward(dc)
+    torch.cuda.synchronize()
+    out = costs.cpu().numpy().astype(np.float64), {k: v.cpu().numpy().astype(np.float64) for k, v in grads.items()}
+    del prob
+    return out
+
+
+def check_costs(inp, got, ref, samples=None):
+    rc, _ = TOL[inp.dtype]
+    idx = range(len(ref)) if samples is None else samples
+    for b in idx:
+        err = abs(got[b] - ref[b]) / abs(ref[b])
+        assert err <= rc, f"sample {b}: cost {got[b]} vs {ref[b]} (rel {err:.2e})"
+
+
+def check_grads(inp, got, ref):
+    _, rg = TOL[inp.dtype]
+    for k in GRADS:
+        scale = np.max(np.abs(ref[k]))
+        err = np.max(np.abs(got[k] - ref[k]))
+        assert err <= rg * max(scale, 1e-30), f"{k}: max err {err:.3e} vs max-abs {scale:.3e}"
+    for b in range(len(inp.T_len)):
+        assert np.all(got["dhA"][b, inp.T_len[b]:] == 0), "padded dhA rows"
+        assert np.all(got["dhL"][b, inp.U_len[b] + 1:] == 0), "padded dhL rows"
+
+
+def full_check(rl, inp, **kw):
+    ref = oracle.loss_and_grads(inp)
+    costs, grads = run_gpu(rl, inp, **kw)
+    check_costs(inp, costs, ref.costs)
+    check_grads(inp, grads, ref.grads)
+    return costs, grads
+
+
+def sampled_check(rl, inp, samples, **kw):
+    """GPU at full size with a one-hot upstream gradient per sample."""
+    B = len(inp.T_len)
+    for b in samples:
+        e = np.zeros(B)
+        e[b] = 1.0
+        say(f"  sample {b}: T_b={inp.T_len[b]} U_b={inp.U_len[b]}")
+        costs, grads = run_gpu(rl, inp, dcosts=e, **kw)
+        ref = oracle.loss_and_grads(inp, dcosts=e, samples=[b])
+        check_costs(inp, costs, ref.costs, samples=[b])
+        check_grads(inp, grads, ref.grads)
+    return costs
+
+
+def lnC(n, k):
+    return math.lgamma(n + 1) - math.lgamma(k + 1) - math.lgamma(n - k + 1)
+
+
+# ----------------------------------------------------------------------------- lattice kernel alone
+
+def test_lattice_kernel_matches_oracle(gpu_lib):
+    import torch
+
+    rl = gpu_lib
+    inp = make_inputs(5, 70, 40, 33, 8, 8, 8, dtype="f32", seed=31, t_range=(1, 70), u_range=(0, 40))
+    say("lattice kernel: B=5 T=70 U=40 ragged")
+    r = oracle.loss_and_grads(inp, want_grads=False)
+    B, T, U1 = 5, 70, 41
+    phi = np.zeros((B, U1, T), np.float32)
+    psi = np.zeros((B, U1, T), np.float32)
+    for b, s in enumerate(r.samples):
+        Tb, Ub = inp.T_len[b], inp.U_len[b]
+        phi[b, :Ub + 1, :Tb] = s.phi.T
+        psi[b, :Ub + 1, :Tb] = np.where(np.isfinite(s.psi.T), s.psi.T, 0)
+    dev = torch.device("cuda:0")
+    tp = lambda a: torch.from_numpy(a).to(dev)
+    al = torch.full((B, U1, T), 7.0, device=dev)
+    be = torch.full((B, U1, T), 7.0, device=dev)
+    costs = torch.zeros(B, device=dev)
+    d = rl.make_desc(B, T, 40, 33, 8, 8, 8)
+    rl.rnnt_lattice(d, tp(inp.T_len), tp(inp.U_len), tp(phi), tp(psi), al, be, costs)
+    torch.cuda.synchronize()
+    al, be, costs = al.cpu().numpy(), be.cpu().numpy(), costs.cpu().numpy()
+    for b, s in enumerate(r.samples):
+        Tb, Ub = inp.T_len[b], inp.U_len[b]
+        assert abs(costs[b] - s.cost) <= 1e-5 * abs(s.cost)
+        ga, gb = al[b, :Ub + 1, :Tb].T, be[b, :Ub + 1, :Tb].T
+        scale = max(1.0, np.abs(s.alpha).max())
+        assert np.max(np.abs(ga - s.alpha)) <= 2e-6 * scale * (Tb + Ub)
+        assert np.max(np.abs(gb - s.beta)) <= 2e-6 * scale * (Tb + Ub)
+        # cells outside the lattice are untouched
+        assert np.all(al[b, Ub + 1:] == 7.0) and np.all(al[b, :, Tb:] == 7.0)
+
+
+# ----------------------------------------------------------------------------- fp32 mode
+
+@pytest.mark.parametrize("mode", ["tiled", "untiled"])
+def test_config1_fp32(gpu_lib, mode):
+    say(f"config 1 fp32 {mode}")
+    full_check(gpu_lib, workload_inputs(1), mode=mode)
+
+
+@pytest.mark.parametrize("mode,tile,tpw", [("tiled", (32, 16), 3), ("tiled", (64, 32), 0),
+                                           ("untiled", (32, 16), 0), ("tiled", (20, 7), 2)])
+def test_fp32_ragged_multitile(gpu_lib, mode, tile, tpw):
+    inp = make_inputs(3, 75, 41, 300, 48, 40, 64, dtype="f32", seed=41, t_range=(20, 75),
+                      u_range=(0, 41), bias_std=0.3)
+    say(f"fp32 ragged B=3 T=75 U=41 V=300 {mode} tile={tile} tpw={tpw}")
+    full_check(gpu_lib, inp, mode=mode, tile=tile, tpw=tpw)
+
+
+# ----------------------------------------------------------------------------- bf16 mode
+
+@pytest.mark.parametrize("mode", ["tiled", "untiled"])
+def test_bf16_reduced(gpu_lib, mode):
+    inp = make_inputs(4, 100, 30, 1000, 128, 96, 128, dtype="bf16", seed=51, t_range=(40, 100),
+                      u_range=(0, 30), bias_std=0.1)
+    say(f"bf16 reduced B=4 T=100 U=30 V=1000 {mode}")
+    full_check(gpu_lib, inp, mode=mode, tile=(32, 16), tpw=5)
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("mode", ["tiled", "untiled"])
+def test_config2_full(gpu_lib, mode):
+    say(f"config 2 full bf16 {mode}")
+    full_check(gpu_lib, workload_inputs(2), mode=mode)
+
+
+@pytest.mark.timeout(400)
+def test_config3_sampled_tiled_and_untiled(gpu_lib):
+    inp = workload_inputs(3)
+    say("config 3 full bf16 tiled 64x32, sampled oracle")
+    ct = sampled_check(gpu_lib, inp, [0, 17])
+    say("config 3 untiled vs tiled")
+    cu, gu = run_gpu(gpu_lib, inp, mode="untiled")
+    c2, g2 = run_gpu(gpu_lib, inp)
+    assert np.array_equal(cu, c2)  # forward math is identical in both modes
+    for k in GRADS:
+        assert np.max(np.abs(gu[k] - g2[k])) <= 1e-2 * np.max(np.abs(g2[k])), k
+
+
+@pytest.mark.timeout(600)
+def test_config4_tile_sweep(gpu_lib):
+    inp = workload_inputs(4)
+    results = {}
+    for tile in ((32, 16), (64, 32), (128, 64)):
+        say(f"config 4 bf16 tile {tile}")
+        results[tile] = run_gpu(gpu_lib, inp, tile=tile)
+    base_c, base_g = results[(64, 32)]
+    for tile, (c, g) in results.items():
+        assert np.array_equal(c, base_c), tile  # costs do not depend on the tile size
+        for k in GRADS:
+            assert np.max(np.abs(g[k] - base_g[k])) <= 1e-2 * np.max(np.abs(base_g[k])), (tile, k)
+    say("config 4 sampled oracle")
+    sampled_check(gpu_lib, inp, [3], tile=(32, 16))
+
+
+@pytest.mark.timeout(600)
+def test_config5_closed_form_and_sample(gpu_lib):
+    import dataclasses
+
+    inp = workload_inputs(5)
+    say("config 5 full, W^O = 0: closed-form cost for every sample")
+    inp0 = dataclasses.replace(inp, WO=np.zeros_like(inp.WO))
+    c0, _ = run_gpu(gpu_lib, inp0)
+    for b in range(len(inp0.T_len)):
+        Tb, Ub = int(inp0.T_len[b]), int(inp0.U_len[b])
+        want = (Tb + Ub) * math.log(1024) - lnC(Tb + Ub - 1, Ub)
+        assert abs(c0[b] - want) <= 1e-5 * want, (b, c0[b], want)
+    say("config 5 full, sampled oracle")
+    sampled_check(gpu_lib, inp, [11])
+
+
+# ----------------------------------------------------------------------------- structure
+
+def test_padding_poison_is_ignored(gpu_lib):
+    inp = make_inputs(3, 60, 20, 257, 64, 64, 64, dtype="bf16", seed=61, t_range=(10, 60), u_range=(0, 20))
+    say("padding poison bf16")
+    c0, g0 = run_gpu(gpu_lib, inp, tile=(32, 16))
+    c1, g1 = run_gpu(gpu_lib, poison_padding(inp), tile=(32, 16))
+    assert np.array_equal(c0, c1)
+    for k in GRADS:
+        assert np.array_equal(g0[k], g1[k]), k
+
+
+def test_deterministic_repeats(gpu_lib):
+    inp = workload_inputs(2)
+    say("determinism config 2")
+    a = run_gpu(gpu_lib, inp)
+    b = run_gpu(gpu_lib, inp)
+    assert np.array_equal(a[0], b[0])
+    for k in GRADS:
+        assert np.array_equal(a[1][k], b[1][k]), k
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_edge_cases(gpu_lib, dtype):
+    """U_b = 0, T_b = 1, a transcript label equal to the blank id, blank != 0,
+    one tile per wave, V not a multiple of 64."""
+    inp = make_inputs(5, 9, 4, 70, 16, 24, 32, dtype=dtype, seed=71, bias_std=0.5)
+    inp.T_len[:] = [1, 9, 3, 9, 1]
+    inp.U_len[:] = [0, 0, 4, 2, 3]
+    inp.blank = 69
+    inp.labels[:, 0] = 69
+    for b in range(5):
+        inp.labels[b, inp.U_len[b] + 1:] = 69
+    inp.labels[2, 2] = 69  # a label that is the blank id
+    say(f"edge cases {dtype}")
+    full_check(gpu_lib, inp, tile=(32, 2), tpw=1)
+    full_check(gpu_lib, inp, mode="untiled")
