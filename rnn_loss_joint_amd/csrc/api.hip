@@ -304,6 +304,7 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
     a.store = d.untiled ? 1 : 0;
     a.logits_out = sv.logits;
     a.z_out = sv.z;
+    a.z_ld = p.total_rows;
     a.buf_row_base = 0;
     {
       ProfScope ps_("joint_fwd", st);
@@ -350,6 +351,12 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
   float* PB = at<float>(workspace, L.w_PB);
   void* dh_buf = d.untiled ? sv.logits : at<char>(workspace, L.w_dh);
   void* z_buf = d.untiled ? sv.z : at<char>(workspace, L.w_z);
+  const int64_t z_ld = d.untiled ? p.total_rows : p.max_wave_rows;
+  void* WOT = at<char>(workspace, L.w_WOT);
+  {
+    ProfScope ps_("transpose_wo", st);
+    RNNT_HIP(rnnt::launch_transpose_wo(WOT, WO, d.V, d.H, p.V_pad, bf, st));
+  }
 
   {
     ProfScope ps_("fill", st);
@@ -408,6 +415,7 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       a.n_chunks = wrows / rows_per_chunk(bf);
       a.logits_out = dh_buf;
       a.z_out = z_buf;
+      a.z_ld = z_ld;
       a.buf_row_base = buf_base;
       a.dcosts = dcosts;
       {
@@ -426,7 +434,8 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       a.wave_row_base = buf_base;
       a.dh = dh_buf;
       a.z = z_buf;
-      a.WO = WO;
+      a.z_ld = z_ld;
+      a.WOT = WOT;
       a.V = d.V;
       a.V_pad = p.V_pad;
       a.H = d.H;
@@ -478,7 +487,7 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
     {
       rnnt::GemmArgs g{};
       g.A = rnnt::Operand{dh_buf, p.V_pad, d.V, nullptr, 1, 0};
-      g.B = rnnt::Operand{z_buf, p.H_pad, d.H, nullptr, 1, 0};
+      g.B = rnnt::Operand{z_buf, z_ld, d.H, nullptr, 1, 0};  // z^T: k (row) contiguous
       g.M = d.V;
       g.N = d.H;
       g.K = wrows;
@@ -492,7 +501,7 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       // rows of the dh/z buffers start at the wave's first row
       {
         ProfScope ps_("dWO_gemm", st);
-        RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_MN_MN, bf, bf, bf, p.s6, st));
+        RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_MN_KC, bf, bf, bf, p.s6, st));
       }
       {
         ProfScope ps_("split_reduce", st);

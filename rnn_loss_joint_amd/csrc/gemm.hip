@@ -27,52 +27,58 @@ __device__ inline bool kvalid(const Operand& o, int k) {
 }
 
 // k-contiguous operand: piece i of thread tid is row i*32 + tid/8, chunk tid%8.
+// A stage is loaded into a register set (load) and later written to LDS
+// (store), so two sets give a prefetch distance of two stages.
 template <class M, class S>
 struct KcLoader {
   using CT = typename M::CT;
   static constexpr int KPL = M::KPL;
+  struct Regs {
+    u32x4 v[4];
+  };
   const S* rowp[4];
-  u32x4 v[4];
   int c, K;
   __device__ void init(int tid, int K_) {
     c = tid & 7;
     K = K_;
   }
   __device__ void set_row(int i, const S* p) { rowp[i] = p; }
-  __device__ void load(int k0) {
+  __device__ void load(int k0, Regs& r) const {
     int k = k0 + c * KPL;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (rowp[i] && k < K) {
         if constexpr (sizeof(S) == sizeof(CT)) {
-          v[i] = ldg<u32x4>(rowp[i] + k);
+          r.v[i] = ldg<u32x4>(rowp[i] + k);
         } else {  // bf16 source, fp32 compute: 4 bf16 -> 4 floats
-          bf16x4 x = ldg<bf16x4>(rowp[i] + k);
-          f32x4 f = {(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-          v[i] = __builtin_bit_cast(u32x4, f);
+          u32x2 x = ldg<u32x2>(rowp[i] + k);
+          r.v[i] = u32x4{x[0] << 16, x[0] & 0xffff0000u, x[1] << 16, x[1] & 0xffff0000u};
         }
       } else {
-        v[i] = u32x4{0, 0, 0, 0};
+        r.v[i] = u32x4{0, 0, 0, 0};
       }
     }
   }
-  __device__ void store(char* buf, int tid) const {
+  __device__ void store(char* buf, int tid, const Regs& r) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(buf + lds_off(i * 32 + (tid >> 3), c)) = v[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(buf + lds_off(i * 32 + (tid >> 3), c)) = r.v[i];
   }
 };
 
-// m-contiguous operand: thread covers 4 k rows x ER consecutive m and writes
-// them transposed. bf16: ER = 8 (16 k-groups x 16 m-groups); fp32: ER = 4
-// (8 k-groups x 32 m-groups).
+// m-contiguous operand: a thread covers 4 k rows x ER consecutive m and
+// writes them transposed (bf16: ER = 8, one v_perm per output dword; fp32:
+// ER = 4, register moves). bf16: 16 k-groups x 16 m-groups; fp32: 8 x 32.
 template <class M, class S, bool COLSUM>
 struct MnLoader {
   using CT = typename M::CT;
-  static constexpr int ER = (sizeof(CT) == 2) ? 8 : 4;
+  static constexpr bool BF = sizeof(CT) == 2;
+  static constexpr int ER = BF ? 8 : 4;
   static constexpr int NRQ = TM / ER;
+  struct Regs {
+    u32x4 v[4];  // v[i] = k row i: bf16 x 8 m (BF) or f32 x 4 m
+  };
   Operand o;
   int K, m0, kq, rq;
-  CT val[4][ER];
   float cs[ER];
   __device__ void init(const Operand& op, int K_, int m0_, int tid) {
     o = op;
@@ -83,7 +89,7 @@ struct MnLoader {
 #pragma unroll
     for (int e = 0; e < ER; ++e) cs[e] = 0.0f;
   }
-  __device__ void load(int k0) {
+  __device__ void load(int k0, Regs& r) {
     const int m = m0 + rq * ER;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -91,40 +97,68 @@ struct MnLoader {
       bool ok = k < K && kvalid(o, k);
       const S* src = reinterpret_cast<const S*>(o.base) + (int64_t)k * o.ld + m;
       if (ok && m + ER <= o.rows) {
-        if constexpr (sizeof(S) == 2 && ER == 8) {
-          bf16x8 x = ldg<bf16x8>(src);
-#pragma unroll
-          for (int e = 0; e < ER; ++e) val[i][e] = (CT)x[e];
-        } else if constexpr (sizeof(S) == 2) {
-          bf16x4 x = ldg<bf16x4>(src);
-#pragma unroll
-          for (int e = 0; e < ER; ++e) val[i][e] = (CT)(float)x[e];
-        } else {
-          f32x4 x = ldg<f32x4>(src);
-#pragma unroll
-          for (int e = 0; e < ER; ++e) val[i][e] = to_ct<CT>(x[e]);
+        if constexpr (BF || sizeof(S) == 4) {
+          r.v[i] = ldg<u32x4>(src);  // 8 bf16 or 4 floats
+        } else {                     // bf16 source, fp32 compute
+          u32x2 x = ldg<u32x2>(src);
+          r.v[i] = u32x4{x[0] << 16, x[0] & 0xffff0000u, x[1] << 16, x[1] & 0xffff0000u};
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < ER; ++e)
-          val[i][e] = (ok && m + e < o.rows) ? to_ct<CT>(to_f32(src[e])) : to_ct<CT>(0.0f);
+      } else if (!ok || m >= o.rows) {
+        r.v[i] = u32x4{0, 0, 0, 0};
+      } else {  // partial m range at the edge
+        if constexpr (BF) {
+          uint32_t w[4] = {0, 0, 0, 0};
+          const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src);
+          for (int e = 0; e < ER; ++e)
+            if (m + e < o.rows) w[e >> 1] |= (uint32_t)s16[e] << (16 * (e & 1));
+          r.v[i] = u32x4{w[0], w[1], w[2], w[3]};
+        } else {
+          float f[4] = {0, 0, 0, 0};
+          for (int e = 0; e < ER; ++e)
+            if (m + e < o.rows) f[e] = to_f32(src[e]);
+          r.v[i] = __builtin_bit_cast(u32x4, f32x4{f[0], f[1], f[2], f[3]});
+        }
       }
-      if (COLSUM) {
+    }
+    if constexpr (COLSUM) {
 #pragma unroll
-        for (int e = 0; e < ER; ++e) cs[e] += to_f32(val[i][e]);
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (BF) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t x = r.v[i][w];
+            cs[2 * w] += __uint_as_float(x << 16);
+            cs[2 * w + 1] += __uint_as_float(x & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t x = r.v[i][w];  // scalar copy: a bit_cast of the vector element itself
+            cs[w] += __uint_as_float(x);   // was miscompiled to read one element for every w
+          }
+        }
       }
     }
   }
-  __device__ void store(char* buf, int) const {
+  __device__ void store(char* buf, int, const Regs& r) const {
+    if constexpr (BF) {
+      // row m gets k = 4kq..4kq+3: dwords (k0|k1<<16, k2|k3<<16) of its m
 #pragma unroll
-    for (int e = 0; e < ER; ++e) {
-      int row = rq * ER + e;
-      if constexpr (sizeof(CT) == 2) {
-        bf16x4 w = {val[0][e], val[1][e], val[2][e], val[3][e]};
-        *reinterpret_cast<bf16x4*>(buf + lds_off(row, kq >> 1) + (kq & 1) * 8) = w;
-      } else {
-        f32x4 w = {val[0][e], val[1][e], val[2][e], val[3][e]};
-        *reinterpret_cast<f32x4*>(buf + lds_off(row, kq)) = w;
+      for (int w = 0; w < 4; ++w) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+          u32x2 out = {__builtin_amdgcn_perm(r.v[1][w], r.v[0][w], sel),
+                       __builtin_amdgcn_perm(r.v[3][w], r.v[2][w], sel)};
+          const int row = rq * ER + 2 * w + h;
+          *reinterpret_cast<u32x2*>(buf + lds_off(row, kq >> 1) + (kq & 1) * 8) = out;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < ER; ++e) {
+        u32x4 out = {r.v[0][e], r.v[1][e], r.v[2][e], r.v[3][e]};
+        *reinterpret_cast<u32x4*>(buf + lds_off(rq * ER + e, kq)) = out;
       }
     }
   }
@@ -162,34 +196,51 @@ struct WaveTile {
   }
 };
 
-// Full k loop over [kb, ke) with double-buffered LDS stages.
+// Full k loop over [kb, ke): two LDS buffers, two register sets per operand.
+// Stage s+2 is requested from memory while stage s is multiplied and stage
+// s+1 (requested one stage earlier) is written to LDS.
 template <class M, class LA, class LB>
 __device__ void mainloop(WaveTile<M>& wt, LA& la, LB& lb, int kb, int ke, char* lds, int tid) {
   constexpr int KST = 8 * M::KPL;
+  constexpr int SB = TM * 128;  // bytes per operand stage
   const int lane = tid & 63, wave = tid >> 6, wr = wave >> 1, wc = wave & 1;
-  // stage s: A at lds + s*TM*128, B at lds + (2+s)*TM*128 (offsets, so the
-  // compiler keeps the LDS address space)
-  constexpr int SB = TM * 128;
   if (kb >= ke) return;
-  la.load(kb);
-  lb.load(kb);
-  la.store(lds, tid);
-  lb.store(lds + 2 * SB, tid);
+  const int n = (ke - kb + KST - 1) / KST;
+  typename LA::Regs a0, a1;
+  typename LB::Regs b0, b1;
+  la.load(kb, a0);
+  lb.load(kb, b0);
+  if (n > 1) {
+    la.load(kb + KST, a1);
+    lb.load(kb + KST, b1);
+  }
+  la.store(lds, tid, a0);
+  lb.store(lds + 2 * SB, tid, b0);
   __syncthreads();
-  int cur = 0;
-  for (int k0 = kb; k0 < ke; k0 += KST) {
-    const bool next = k0 + KST < ke;
-    if (next) {
-      la.load(k0 + KST);
-      lb.load(k0 + KST);
+  for (int s = 0; s < n; s += 2) {
+    // stage s in buffer 0, stage s+1 in set 1
+    if (s + 2 < n) {
+      la.load(kb + (s + 2) * KST, a0);
+      lb.load(kb + (s + 2) * KST, b0);
     }
-    wt.mma_stage(lds + cur * SB, lds + (2 + cur) * SB, wr, wc, lane);
-    if (next) {
-      la.store(lds + (cur ^ 1) * SB, tid);
-      lb.store(lds + (2 + (cur ^ 1)) * SB, tid);
+    wt.mma_stage(lds, lds + 2 * SB, wr, wc, lane);
+    if (s + 1 < n) {
+      la.store(lds + SB, tid, a1);
+      lb.store(lds + 3 * SB, tid, b1);
     }
     __syncthreads();
-    cur ^= 1;
+    if (s + 1 >= n) break;
+    // stage s+1 in buffer 1, stage s+2 in set 0
+    if (s + 3 < n) {
+      la.load(kb + (s + 3) * KST, a1);
+      lb.load(kb + (s + 3) * KST, b1);
+    }
+    wt.mma_stage(lds + SB, lds + 3 * SB, wr, wc, lane);
+    if (s + 2 < n) {
+      la.store(lds, tid, a0);
+      lb.store(lds + 2 * SB, tid, b0);
+    }
+    __syncthreads();
   }
 }
 
@@ -232,9 +283,20 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
   } else {
     MnLoader<M, SA, COLSUM> la;
     la.init(g.A, g.K, m0, tid);
-    MnLoader<M, SB, false> lb;
-    lb.init(g.B, g.K, n0, tid);
-    mainloop<M>(wt, la, lb, kb, ke, lds, tid);
+    if constexpr (KIND == GEMM_MN_MN) {
+      MnLoader<M, SB, false> lb;
+      lb.init(g.B, g.K, n0, tid);
+      mainloop<M>(wt, la, lb, kb, ke, lds, tid);
+    } else {
+      KcLoader<M, SB> lb;
+      lb.init(tid, g.K);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int n = n0 + i * 32 + (tid >> 3);
+        lb.set_row(i, n < g.B.rows ? reinterpret_cast<const SB*>(g.B.base) + (int64_t)n * g.B.ld : nullptr);
+      }
+      mainloop<M>(wt, la, lb, kb, ke, lds, tid);
+    }
     if constexpr (COLSUM) {
       if (do_cs) {
         // sum the per-thread column sums over the k groups
@@ -294,6 +356,10 @@ hipError_t launch_gemm(const GemmArgs& g, GemmKind kind, bool bf16_compute, bool
         if (cs) launch_gemm_t<MfmaBf16, GEMM_MN_MN, bf16, bf16, true>(g, splits, st);
         else launch_gemm_t<MfmaBf16, GEMM_MN_MN, bf16, bf16, false>(g, splits, st);
         break;
+      case GEMM_MN_KC:
+        if (cs) launch_gemm_t<MfmaBf16, GEMM_MN_KC, bf16, bf16, true>(g, splits, st);
+        else launch_gemm_t<MfmaBf16, GEMM_MN_KC, bf16, bf16, false>(g, splits, st);
+        break;
     }
   } else {
 #define RNNT_F32_CASES(SA, SB)                                                            \
@@ -303,6 +369,10 @@ hipError_t launch_gemm(const GemmArgs& g, GemmKind kind, bool bf16_compute, bool
     case GEMM_MN_MN:                                                                     \
       if (cs) launch_gemm_t<MfmaF32, GEMM_MN_MN, SA, SB, true>(g, splits, st);           \
       else launch_gemm_t<MfmaF32, GEMM_MN_MN, SA, SB, false>(g, splits, st);             \
+      break;                                                                             \
+    case GEMM_MN_KC:                                                                     \
+      if (cs) launch_gemm_t<MfmaF32, GEMM_MN_KC, SA, SB, true>(g, splits, st);           \
+      else launch_gemm_t<MfmaF32, GEMM_MN_KC, SA, SB, false>(g, splits, st);             \
       break;                                                                             \
   }
     if (!a_bf16 && !b_bf16) { RNNT_F32_CASES(float, float) }
@@ -353,7 +423,14 @@ __global__ void __launch_bounds__(256) dz_kernel(DzArgs p) {
 #pragma unroll
       for (int e = 0; e < NACC; ++e) gacc[a][j][e] = 0.0f;
 
-  Operand wo{p.WO, p.H, p.H, nullptr, 1, 0};
+  const CT* wot = reinterpret_cast<const CT*>(p.WOT);
+  KcLoader<M, CT> lb;
+  lb.init(tid, p.V_pad);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int h = h0 + i * 32 + (tid >> 3);
+    lb.set_row(i, h < p.H ? wot + (int64_t)h * p.V_pad : nullptr);
+  }
   const int ngroups = (tl.wu + 3) / 4;
   for (int ug = 0; ug < ngroups; ++ug) {
     KcLoader<M, CT> la;
@@ -364,8 +441,6 @@ __global__ void __launch_bounds__(256) dz_kernel(DzArgs p) {
       int ul = ug * 4 + row / 32;
       la.set_row(i, ul < tl.wu ? dh + (int64_t)(tile_row + ul * tl.htp + tl0 + row % 32) * p.V_pad : nullptr);
     }
-    MnLoader<M, CT, false> lb;
-    lb.init(wo, p.V, h0, tid);
     WaveTile<M> wt;
     wt.zero();
     mainloop<M>(wt, la, lb, 0, p.V_pad, lds, tid);
@@ -383,14 +458,30 @@ __global__ void __launch_bounds__(256) dz_kernel(DzArgs p) {
         const int h = h0 + wc * 64 + j * ROWS + M::col_of(lane);
         float lsum = 0.0f;
 #pragma unroll
-        for (int e = 0; e < NACC; ++e) {
-          float ds = 0.0f;
+        for (int e4 = 0; e4 < NACC; e4 += 4) {
+          // rows row_of(e4..e4+3) are consecutive: one 4-element load of z^T
+          float zz[4] = {0.0f, 0.0f, 0.0f, 0.0f};
           if (uok && h < p.H) {
-            float z = to_f32(zb[(zrow0 + M::row_of(e, lane)) * p.H_pad + h]);
-            ds = wt.acc[i][j][e] * (1.0f - z * z);
+            const CT* zp = zb + (int64_t)h * p.z_ld + zrow0 + M::row_of(e4, lane);
+            if constexpr (sizeof(CT) == 2) {
+              u32x2 w = ldg<u32x2>(zp);
+              const uint32_t w0 = w[0], w1 = w[1];
+              zz[0] = __uint_as_float(w0 << 16);
+              zz[1] = __uint_as_float(w0 & 0xffff0000u);
+              zz[2] = __uint_as_float(w1 << 16);
+              zz[3] = __uint_as_float(w1 & 0xffff0000u);
+            } else {
+              f32x4 w = ldg<f32x4>(zp);
+              zz[0] = w[0]; zz[1] = w[1]; zz[2] = w[2]; zz[3] = w[3];
+            }
           }
-          gacc[ts][j][e] += ds;
-          lsum += ds;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int e = e4 + q;
+            float ds = (uok && h < p.H) ? wt.acc[i][j][e] * (1.0f - zz[q] * zz[q]) : 0.0f;
+            gacc[ts][j][e] += ds;
+            lsum += ds;
+          }
         }
         wt.acc[i][j][0] = lsum;  // stash per-block t-sum for the gL reduction below
       }
@@ -492,6 +583,34 @@ hipError_t launch_split_reduce(float* out, const float* P, int64_t n, int splits
   int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
   hipLaunchKernelGGL(split_reduce_kernel, dim3(blocks), dim3(256), 0, st, out, P, n, splits, stride,
                      accumulate ? 1 : 0);
+  return hipGetLastError();
+}
+
+// W^O [V, H] -> W^O^T [H, V_pad] through a 32 x 32 LDS tile.
+template <class T>
+__global__ void __launch_bounds__(256) transpose_wo_kernel(T* dst, const T* src, int V, int H, int V_pad) {
+  __shared__ T tile[32][33];
+  const int v0 = blockIdx.x * 32, h0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int y = ty; y < 32; y += 8) {
+    int v = v0 + y, h = h0 + tx;
+    tile[y][tx] = (v < V && h < H) ? src[(int64_t)v * H + h] : T(0.0f);
+  }
+  __syncthreads();
+  for (int y = ty; y < 32; y += 8) {
+    int h = h0 + y, v = v0 + tx;
+    if (h < H && v < V_pad) dst[(int64_t)h * V_pad + v] = tile[tx][y];
+  }
+}
+
+hipError_t launch_transpose_wo(void* dst, const void* src, int V, int H, int V_pad, bool bf16, hipStream_t st) {
+  dim3 grid((V_pad + 31) / 32, (H + 31) / 32), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(transpose_wo_kernel<__bf16>, grid, block, 0, st, reinterpret_cast<__bf16*>(dst),
+                       reinterpret_cast<const __bf16*>(src), V, H, V_pad);
+  else
+    hipLaunchKernelGGL(transpose_wo_kernel<float>, grid, block, 0, st, reinterpret_cast<float*>(dst),
+                       reinterpret_cast<const float*>(src), V, H, V_pad);
   return hipGetLastError();
 }
 

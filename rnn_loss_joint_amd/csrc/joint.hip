@@ -150,9 +150,12 @@ joint_kernel(JointArgs p) {
   }
   const bool write_z = BWD || p.store;
   if (active && write_z) {
-    CT* zrow = reinterpret_cast<CT*>(p.z_out) + (size_t)(R0 - p.buf_row_base + r) * p.H_pad;
+    // z^T: lanes with consecutive rows write consecutive addresses of one h row
+    CT* zcol = reinterpret_cast<CT*>(p.z_out) + (R0 - p.buf_row_base + r);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) *reinterpret_cast<Frag*>(zrow + s * 16 + g * KPL) = Z[s];
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int e = 0; e < KPL; ++e) zcol[(int64_t)(s * 16 + g * KPL + e) * p.z_ld] = Z[s][e];
   }
 
   // ---- blank and label scores by dot products with the two W^O rows

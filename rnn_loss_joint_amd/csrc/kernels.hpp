@@ -28,7 +28,8 @@ struct JointArgs {
   float* psi_out;
   int store;           // forward: also store scores and z (untiled mode)
   void* logits_out;    // scores (forward store) or dh (backward), [rows, V_pad]
-  void* z_out;         // z, [rows, H_pad]
+  void* z_out;         // z transposed, [H_pad, z_ld] (element (row, h) at h*z_ld + row)
+  int64_t z_ld;
   int buf_row_base;    // buffer row = global row - buf_row_base
   // backward inputs
   const float* lse;
@@ -107,7 +108,7 @@ struct GemmArgs {
   float* colsum;     // [splits, M] partials
 };
 
-enum GemmKind { GEMM_KC_KC = 0, GEMM_KC_MN = 1, GEMM_MN_MN = 2 };
+enum GemmKind { GEMM_KC_KC = 0, GEMM_KC_MN = 1, GEMM_MN_MN = 2, GEMM_MN_KC = 3 };
 // compute: 0 = bf16 MFMA (operands bf16), 1 = f32 MFMA; src_bf16 flags give the
 // storage type of A and B.
 hipError_t launch_gemm(const GemmArgs& g, GemmKind kind, bool bf16_compute, bool a_bf16,
@@ -121,8 +122,9 @@ struct DzArgs {
   int n_strips;
   int wave_row_base;     // buffer row = global row - wave_row_base
   const void* dh;        // [rows, V_pad]
-  const void* z;         // [rows, H_pad]
-  const void* WO;        // [V, H]
+  const void* z;         // z transposed, [H_pad, z_ld]
+  int64_t z_ld;
+  const void* WOT;       // W^O transposed, [H, V_pad] (zero for v >= V)
   int V, V_pad, H, H_pad;
   float* PA;             // [tiles_in_wave, tile_tp, H]
   float* PL;             // [tiles_in_wave, tile_tp/32, tile_u, H]
@@ -152,6 +154,8 @@ hipError_t launch_group_reduce(const GroupReduceArgs& a, hipStream_t st);
 hipError_t launch_split_reduce(float* out, const float* P, int64_t n, int splits, int64_t stride,
                                bool accumulate, hipStream_t st);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st);
+// dst[h, v] = src[v, h] for v < V (0 for V <= v < V_pad), element size 2 or 4
+hipError_t launch_transpose_wo(void* dst, const void* src, int V, int H, int V_pad, bool bf16, hipStream_t st);
 hipError_t launch_fill_bytes(void* p, int64_t nbytes, hipStream_t st);
 
 }  // namespace rnnt

@@ -227,7 +227,7 @@ Layout make_layout(const Plan& p) {
   L.w_dh = L.w_z = 0;
   if (!d.untiled) {
     L.w_dh = take(ct * (size_t)p.max_wave_rows * p.V_pad);
-    L.w_z = take(ct * (size_t)p.max_wave_rows * p.H_pad);
+    L.w_z = take(ct * (size_t)p.max_wave_rows * p.H_pad);  // z^T [H_pad, max_wave_rows]
   }
   L.w_gA = take(sizeof(float) * (size_t)d.B * d.T * d.H);
   L.w_gL = take(sizeof(float) * (size_t)d.B * p.U1 * d.H);
@@ -238,6 +238,7 @@ Layout make_layout(const Plan& p) {
   L.w_PWA = take(sizeof(float) * (size_t)p.s7a * d.H * d.HA);
   L.w_PBZ = take(sizeof(float) * (size_t)p.s7a * d.H);
   L.w_PWL = take(sizeof(float) * (size_t)p.s7l * d.H * d.HL);
+  L.w_WOT = take(ct * (size_t)d.H * p.V_pad);
   L.workspace_bytes = o;
   return L;
 }
