@@ -120,6 +120,10 @@ struct MnLoader {
         }
       }
     }
+  }
+  // Column sums are taken here, one stage after the load was issued, so
+  // they do not force an early wait on the outstanding loads.
+  __device__ void store(char* buf, int, const Regs& r) {
     if constexpr (COLSUM) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -139,8 +143,6 @@ struct MnLoader {
         }
       }
     }
-  }
-  __device__ void store(char* buf, int, const Regs& r) const {
     if constexpr (BF) {
       // row m gets k = 4kq..4kq+3: dwords (k0|k1<<16, k2|k3<<16) of its m
 #pragma unroll

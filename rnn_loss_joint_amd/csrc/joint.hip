@@ -233,22 +233,30 @@ joint_kernel(JointArgs p) {
   for (int n = 0; n < NB; ++n) acc[n] = Acc{};
 
   const int VC = (V + BN - 1) / BN;
-  StageRegs<M> sr;
-  load_wo_stage<M>(sr, WO, V, H, 0, 0, tid);
-  store_wo_stage<M>(sr, stage_buf[0], tid);
+  const int NS = VC * SPV;  // stages in total
+  // Pipeline: stage q is in LDS buffer q&1, stage q+1 in register set (q+1)&1;
+  // stage q+2 is requested at the top of step q. SPV is even, so q&1 == qs&1.
+  static_assert(SPV % 2 == 0, "stages per V chunk must be even");
+  StageRegs<M> sr[2];
+  load_wo_stage<M>(sr[0], WO, V, H, 0, 0, tid);
+  if (NS > 1) load_wo_stage<M>(sr[1], WO, V, H, 0, 1, tid);
+  store_wo_stage<M>(sr[0], stage_buf[0], tid);
   __syncthreads();
-  int cur = 0;
   CT* dh_base = BWD ? reinterpret_cast<CT*>(p.logits_out) : nullptr;
   CT* lg_base = (!BWD && p.store) ? reinterpret_cast<CT*>(p.logits_out) : nullptr;
 
   for (int vc = 0; vc < VC; ++vc) {
 #pragma unroll
     for (int qs = 0; qs < SPV; ++qs) {
+      const int q = vc * SPV + qs;
       const bool last_q = (qs + 1 == SPV);
-      const bool has_next = !last_q || (vc + 1 < VC);
-      if (has_next) load_wo_stage<M>(sr, WO, V, H, last_q ? vc + 1 : vc, last_q ? 0 : qs + 1, tid);
+      if (q + 2 < NS) {
+        const int qs2 = (qs + 2) % SPV;
+        const int vc2 = vc + (qs + 2) / SPV;
+        load_wo_stage<M>(sr[qs & 1], WO, V, H, vc2, qs2, tid);
+      }
       if (active) {
-        const char* buf = stage_buf[cur];
+        const char* buf = stage_buf[qs & 1];
 #pragma unroll
         for (int ss = 0; ss < SPS; ++ss) {
 #pragma unroll
@@ -320,9 +328,8 @@ joint_kernel(JointArgs p) {
 #pragma unroll
         for (int n = 0; n < NB; ++n) acc[n] = Acc{};
       }
-      if (has_next) store_wo_stage<M>(sr, stage_buf[cur ^ 1], tid);
+      if (q + 1 < NS) store_wo_stage<M>(sr[(qs + 1) & 1], stage_buf[(qs + 1) & 1], tid);
       __syncthreads();
-      cur ^= 1;
     }
   }
 
@@ -435,7 +442,6 @@ static hipError_t launch_joint_h(const JointArgs& a, int KS, hipStream_t st) {
 #define RNNT_KS_CASE(ks) \
   case ks: hipLaunchKernelGGL((joint_kernel<M, ks, BWD>), grid, block, 0, st, a); break;
   switch (KS) {
-    RNNT_KS_CASE(4)
     RNNT_KS_CASE(8)
     RNNT_KS_CASE(16)
     RNNT_KS_CASE(24)
@@ -451,7 +457,7 @@ static hipError_t launch_joint_h(const JointArgs& a, int KS, hipStream_t st) {
 int joint_ks_for(int H) {
   int hp = (H + 63) / 64 * 64;
   int ks = hp / 16;
-  static const int ok[] = {4, 8, 16, 24, 32, 40, 48};
+  static const int ok[] = {8, 16, 24, 32, 40, 48};  // even stage count per V chunk
   for (int v : ok)
     if (v >= ks) return v;
   return -1;
