@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
+GEMM_KERNELS = ("joint_fwd", "joint_bwd", "scores_fwd", "scores_bwd", "dz", "dWO_gemm")
 
 
 def mfma_flops(inp):
@@ -35,8 +36,10 @@ def mfma_flops(inp):
     rows_l = int(np.sum(inp.U_len + 1))
     pre = 2.0 * H * (rows_a * HA + rows_l * HL)
     return {
-        "joint_fwd": 2.0 * H * V * Nc,   # scores for every valid cell
-        "joint_bwd": 2.0 * H * V * Nc,   # recomputed scores
+        "joint_fwd": 2.0 * H * V * Nc,   # scores for every valid cell (fp32 path)
+        "joint_bwd": 2.0 * H * V * Nc,   # recomputed scores (fp32 path)
+        "scores_fwd": 2.0 * H * V * Nc,  # scores for every valid cell (bf16 path)
+        "scores_bwd": 2.0 * H * V * Nc,  # recomputed scores (bf16 path)
         "dz": 2.0 * H * V * Nc,          # dz = dh W^O
         "dWO_gemm": 2.0 * H * V * Nc,    # dW^O = dh^T z
         "preproj_gemm": pre,             # a = W^A h^A, l = W^L h^L
@@ -144,7 +147,7 @@ def main():
         if name == "lattice" and tot > 0:
             k["gbs"] = 24.0 * inp.valid_cells * args.steps / (tot * 1e-3) / 1e9
         kernels[name] = k
-    mfma_names = [n for n in kernels if n in flops and n in ("joint_fwd", "joint_bwd", "dz", "dWO_gemm")]
+    mfma_names = [n for n in kernels if n in flops and n in GEMM_KERNELS]
     dom = max(mfma_names, key=lambda n: kernels[n]["ms_per_step"])
     dk = kernels[dom]
     ach = dk["tflops"]

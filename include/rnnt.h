@@ -94,7 +94,9 @@ rnnt_status rnnt_loss_query(const rnnt_desc* desc, const int32_t* T_len_host,
 /* Forward: per-sample costs[b] = -ln P(y_b | x_b) (fp32 [B], device).
  * Fills `saved` with the tile plan, the joint pre-activations, the per-cell
  * log-softmax denominators and two log-probs, alpha, beta and ln P (and, in
- * untiled mode, z and the scores). workspace may be NULL in the forward. */
+ * untiled mode, z and the scores). bf16 mode uses `workspace` (at least
+ * rnnt_loss_query's workspace_bytes) for one wave of z rows and per-tile
+ * statistics; fp32 mode does not use it (it may be NULL). */
 rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
                           const int32_t* labels, const int32_t* T_len_host,
                           const int32_t* U_len_host, const void* WA, const void* WL,

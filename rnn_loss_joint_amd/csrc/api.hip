@@ -291,8 +291,91 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
       RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_KC_KC, bf, bf, bf, 1, st));
     }
   }
-  // 2. fused joint + output layer + log-softmax statistics
-  {
+  // 2. joint + output layer + log-softmax statistics
+  if (bf) {
+    // bf16: per wave of tiles, z rows (and the blank / label scores), then
+    // 256 x 256 score tiles with per-tile (max, sum), then the merge
+    if (!workspace) return fail(RNNT_E_INVALID, "bf16 mode needs the workspace in the forward");
+    if (workspace_bytes < L.workspace_bytes)
+      return fail(RNNT_E_WORKSPACE, "workspace buffer smaller than rnnt_loss_query");
+    void* zbuf = d.untiled ? sv.z : at<char>(workspace, L.w_z);
+    auto* stats = at<rnnt::f32x2>(workspace, L.w_stats);
+    float* hb = at<float>(workspace, L.w_hb);
+    float* hy = at<float>(workspace, L.w_hy);
+    for (const rnnt::WaveInfo& wv : p.waves) {
+      const int wrows = wv.row_end - wv.row_begin;
+      const int base = d.untiled ? 0 : wv.row_begin;  // buffer row = global row - base
+      rnnt::ZArgs z{};
+      z.tiles = sv.tiles;
+      z.tile_begin = wv.tile_begin;
+      z.tile_end = wv.tile_end;
+      z.row_begin = wv.row_begin;
+      z.n_rows = wrows;
+      z.buf_row_base = base;
+      z.U_len = sv.Ulen;
+      z.labels = labels;
+      z.T = d.T;
+      z.U1 = p.U1;
+      z.H = d.H;
+      z.H_pad = p.H_pad;
+      z.blank = d.blank;
+      z.a = sv.a;
+      z.l = sv.l;
+      z.WO = WO;
+      z.bO = bO;
+      z.z = zbuf;
+      z.z_ld = p.H_pad;
+      z.hb = hb - (wv.row_begin - base);  // hb/hy indexed by wave-relative row
+      z.hy = hy - (wv.row_begin - base);
+      {
+        ProfScope ps_("zrow", st);
+        RNNT_HIP(rnnt::launch_zrow(z, st));
+      }
+      rnnt::ScoresArgs sc{};
+      sc.tiles = sv.tiles;
+      sc.tile_begin = wv.tile_begin;
+      sc.tile_end = wv.tile_end;
+      sc.row_begin = wv.row_begin;
+      sc.n_rows = wrows;
+      sc.buf_row_base = wv.row_begin;
+      sc.T = d.T;
+      sc.U1 = p.U1;
+      sc.V = d.V;
+      sc.H = d.H;
+      sc.V_pad = p.V_pad;
+      sc.blank = d.blank;
+      sc.WO = WO;
+      sc.bO = bO;
+      sc.z = at<char>(zbuf, (size_t)(wv.row_begin - base) * p.H_pad * 2);
+      sc.z_ld = p.H_pad;
+      sc.stats = stats;
+      sc.logits = d.untiled ? sv.logits : nullptr;
+      {
+        ProfScope ps_("scores_fwd", st);
+        RNNT_HIP(rnnt::launch_scores(sc, false, st));
+      }
+      rnnt::MergeArgs mg{};
+      mg.tiles = sv.tiles;
+      mg.tile_begin = wv.tile_begin;
+      mg.tile_end = wv.tile_end;
+      mg.n_rows = wrows;
+      mg.buf_row_base = wv.row_begin;
+      mg.nvt = p.nvt;
+      mg.U_len = sv.Ulen;
+      mg.T = d.T;
+      mg.U1 = p.U1;
+      mg.stats = stats;
+      mg.hb = hb;
+      mg.hy = hy;
+      mg.lse = sv.lse;
+      mg.phi = sv.phi;
+      mg.psi = sv.psi;
+      {
+        ProfScope ps_("lse_merge", st);
+        RNNT_HIP(rnnt::launch_lse_merge(mg, st));
+      }
+    }
+  } else {
     rnnt::JointArgs a = joint_args(p, sv, labels, WO, bO);
     a.tile_begin = 0;
     a.tile_end = (int)p.tiles.size();
@@ -407,6 +490,66 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
         ProfScope ps_("dh_inplace", st);
         RNNT_HIP(rnnt::launch_dh_inplace(a, bf, st));
       }
+    } else if (bf) {
+      // z rows for the wave, then dh from 256 x 256 score tiles
+      rnnt::ZArgs z{};
+      z.tiles = sv.tiles;
+      z.tile_begin = wv.tile_begin;
+      z.tile_end = wv.tile_end;
+      z.row_begin = wv.row_begin;
+      z.n_rows = wrows;
+      z.buf_row_base = buf_base;
+      z.U_len = sv.Ulen;
+      z.labels = labels;
+      z.T = d.T;
+      z.U1 = p.U1;
+      z.H = d.H;
+      z.H_pad = p.H_pad;
+      z.blank = d.blank;
+      z.a = sv.a;
+      z.l = sv.l;
+      z.WO = WO;
+      z.bO = bO;
+      z.z = z_buf;
+      z.z_ld = p.H_pad;
+      z.hb = at<float>(workspace, L.w_hb);
+      z.hy = at<float>(workspace, L.w_hy);
+      {
+        ProfScope ps_("zrow", st);
+        RNNT_HIP(rnnt::launch_zrow(z, st));
+      }
+      rnnt::ScoresArgs sc{};
+      sc.tiles = sv.tiles;
+      sc.tile_begin = wv.tile_begin;
+      sc.tile_end = wv.tile_end;
+      sc.row_begin = wv.row_begin;
+      sc.n_rows = wrows;
+      sc.buf_row_base = wv.row_begin;
+      sc.T_len = sv.Tlen;
+      sc.U_len = sv.Ulen;
+      sc.labels = labels;
+      sc.T = d.T;
+      sc.U1 = p.U1;
+      sc.V = d.V;
+      sc.H = d.H;
+      sc.V_pad = p.V_pad;
+      sc.blank = d.blank;
+      sc.WO = WO;
+      sc.bO = bO;
+      sc.z = z_buf;
+      sc.z_ld = p.H_pad;
+      sc.dh = dh_buf;
+      sc.lse = sv.lse;
+      sc.phi = sv.phi;
+      sc.psi = sv.psi;
+      sc.alpha = sv.alpha;
+      sc.beta = sv.beta;
+      sc.lnP = sv.lnP;
+      sc.dcosts = dcosts;
+      {
+        ProfScope ps_("scores_bwd", st);
+        RNNT_HIP(rnnt::launch_scores(sc, true, st));
+      }
     } else {
       rnnt::JointArgs a = joint_args(p, sv, labels, WO, bO);
       a.tile_begin = wv.tile_begin;
@@ -444,7 +587,11 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       a.PL = PL;
       a.tile_tp = p.tile_tp;
       a.tile_u = d.tile_u;
-      {
+      if (bf) {
+        a.z_ld = p.H_pad;  // bf16 path: z rows are row-major
+        ProfScope ps_("dz", st);
+        RNNT_HIP(rnnt::launch_dz2(a, st));
+      } else {
         ProfScope ps_("dz", st);
         RNNT_HIP(rnnt::launch_dz(a, bf, st));
       }
@@ -484,6 +631,32 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       }
     }
     // 7. dW^O and db^O
+    if (bf) {
+      rnnt::DwoArgs w{};
+      w.dh = dh_buf;
+      w.dh_ld = p.V_pad;
+      w.z = z_buf;
+      w.z_ld = p.H_pad;
+      w.V = d.V;
+      w.H = d.H;
+      w.K = wrows;
+      w.splits = p.s6;
+      w.k_per_split = ((wrows + p.s6 - 1) / p.s6 + 63) / 64 * 64;
+      w.PW = PW;
+      w.PB = PB;
+      {
+        ProfScope ps_("dWO_gemm", st);
+        RNNT_HIP(rnnt::launch_dwo(w, st));
+      }
+      {
+        ProfScope ps_("split_reduce", st);
+        RNNT_HIP(rnnt::launch_split_reduce(dWO, PW, (int64_t)d.V * d.H, p.s6, (int64_t)d.V * d.H, true, st));
+      }
+      {
+        ProfScope ps_("split_reduce", st);
+        RNNT_HIP(rnnt::launch_split_reduce(dbO, PB, d.V, p.s6, d.V, true, st));
+      }
+    } else
     {
       rnnt::GemmArgs g{};
       g.A = rnnt::Operand{dh_buf, p.V_pad, d.V, nullptr, 1, 0};

@@ -154,6 +154,76 @@ hipError_t launch_group_reduce(const GroupReduceArgs& a, hipStream_t st);
 hipError_t launch_split_reduce(float* out, const float* P, int64_t n, int splits, int64_t stride,
                                bool accumulate, hipStream_t st);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st);
+
+// ---------------------------------------------------------------- bf16 large-tile path
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+struct DwoArgs {  // dW^O = dh^T z (split-K partials), db^O from a column of ones
+  const void* dh;
+  int64_t dh_ld;
+  const void* z;
+  int64_t z_ld;
+  int V, H, K, k_per_split, splits;
+  float* PW;  // [splits, V, H]
+  float* PB;  // [splits, V]
+};
+hipError_t launch_dwo(const DwoArgs& a, hipStream_t st);
+hipError_t launch_dz2(const DzArgs& a, hipStream_t st);
+
+struct ZArgs {  // z rows and the blank / label scores for a range of rows
+  const Tile* tiles;
+  int tile_begin, tile_end, row_begin, n_rows, buf_row_base;
+  const int32_t* U_len;
+  const int32_t* labels;
+  int T, U1, H, H_pad, blank;
+  const float* a;
+  const float* l;
+  const void* WO;
+  const void* bO;
+  void* z;  // [rows, z_ld] bf16
+  int64_t z_ld;
+  float* hb;
+  float* hy;
+};
+hipError_t launch_zrow(const ZArgs& a, hipStream_t st);
+
+struct ScoresArgs {  // scores^T tiles: forward statistics or backward dh
+  const Tile* tiles;
+  int tile_begin, tile_end, row_begin, n_rows, buf_row_base;
+  const int32_t* T_len;
+  const int32_t* U_len;
+  const int32_t* labels;
+  int T, U1, V, H, V_pad, blank;
+  const void* WO;
+  const void* bO;
+  const void* z;
+  int64_t z_ld;
+  f32x2* stats;   // forward: [rows, V tiles] (max, sum)
+  void* logits;   // forward, untiled: scores [rows, V_pad] (global rows)
+  void* dh;       // backward: [rows, V_pad]
+  const float* lse;
+  const float* phi;
+  const float* psi;
+  const float* alpha;
+  const float* beta;
+  const float* lnP;
+  const float* dcosts;
+};
+hipError_t launch_scores(const ScoresArgs& a, bool bwd, hipStream_t st);
+
+struct MergeArgs {
+  const Tile* tiles;
+  int tile_begin, tile_end, n_rows, buf_row_base, nvt;
+  const int32_t* U_len;
+  int T, U1;
+  const f32x2* stats;
+  const float* hb;
+  const float* hy;
+  float* lse;
+  float* phi;
+  float* psi;
+};
+hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t st);
 // dst[h, v] = src[v, h] for v < V (0 for V <= v < V_pad), element size 2 or 4
 hipError_t launch_transpose_wo(void* dst, const void* src, int V, int H, int V_pad, bool bf16, hipStream_t st);
 hipError_t launch_fill_bytes(void* p, int64_t nbytes, hipStream_t st);

@@ -1,0 +1,703 @@
+// Large-tile bf16 MFMA core for gfx950 and the bf16 kernels built on it.
+//
+// Core: 256 threads = 4 waves in a 2 x 2 grid over a BM x BN output tile
+// (BM = 256, BN = 256 or 128), each wave 128 x BN/2, v_mfma_f32_32x32x16_bf16.
+// Operand tiles are moved global -> LDS by global_load_lds_dwordx4 (no VGPR
+// staging), NSTAGE stages in flight. A k-contiguous tile is stored
+// [row][64 k] with 16-byte chunks XOR-swizzled by the row; an m-contiguous
+// tile is stored [64 k][m] with 8-byte units XOR-swizzled by k and is read
+// with ds_read_b64_tr_b16, which hands each lane four consecutive k of one m,
+// so both orientations become MFMA fragments without register transposes.
+// Pieces outside the operand read a zero page (or a page of bf16 ones, used
+// to append a column of ones to an operand).
+#include <algorithm>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace rnnt {
+
+__device__ __attribute__((aligned(16))) uint32_t g_zero_page[4] = {0u, 0u, 0u, 0u};
+__device__ __attribute__((aligned(16))) uint32_t g_ones_page[4] = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
+                                                                  0x3F803F80u};
+
+namespace m3 {
+
+constexpr int BM = 256;
+constexpr int BK = 64;  // k (bf16 elements) per stage
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ inline void dma16(const void* g, const char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (lds_void*)(lds_wave_base), 16, 0, 0);
+}
+
+// k-contiguous fragment: row `row`, k-step ss of the stage, lane group g
+__device__ inline bf16x8 frag_kc(const char* buf, int row, int ss, int g) {
+  return *reinterpret_cast<const bf16x8*>(buf + lds_off(row, ss * 2 + g));
+}
+
+// m-contiguous fragment for m in [m_base, m_base+32), k-step ss; rowbytes =
+// bytes of one k row of the tile.
+__device__ inline bf16x8 frag_mn(const char* buf, int m_base, int ss, int lane, int rowbytes) {
+  const int G = lane >> 4, L = lane & 15;
+  const int m = m_base + 16 * (G & 1) + 4 * (L & 3);
+  bf16x8 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k = ss * 16 + 8 * (G >> 1) + 4 * h + (L >> 2);
+    const int unit = (m >> 2) ^ (4 * (k & 3));
+    bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + k * rowbytes + unit * 8));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[4 * h + j] = v[j];
+  }
+  return out;
+}
+
+// Operand description for the core.
+struct Opnd {
+  const bf16* base;
+  int64_t ld;      // elements between consecutive rows (kc) or k rows (mn)
+  int rows;        // valid extent of the non-k dimension
+  int K;           // valid k extent
+  int ones_row;    // mn only: this m index reads the ones page (-1 = none)
+};
+
+// Loader of a k-contiguous operand tile [ROWS][BK]; rows given per thread.
+template <int ROWS>
+struct KcTile {
+  static constexpr int INSTR = ROWS * 128 / 1024 / 4;  // dma instructions per wave per stage
+  static constexpr int BYTES = ROWS * 128;
+  const bf16* rowp[INSTR];
+  int K, c;
+  // row r of the tile is at rowptr(r) (nullptr = outside the operand)
+  template <class F>
+  __device__ void init(int wave, int lane, int K_, F rowptr) {
+    K = K_;
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+      const int row = (i * 4 + wave) * 8 + (lane >> 3);
+      rowp[i] = rowptr(row);
+    }
+    c = lane & 7;
+  }
+  __device__ void issue(const char* stage, int wave, int lane, int k0) const {
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+      const int row = (i * 4 + wave) * 8 + (lane >> 3);
+      const int lc = c ^ swz(row);
+      const int k = k0 + lc * 8;
+      const void* g = (rowp[i] && k < K) ? (const void*)(rowp[i] + k) : (const void*)g_zero_page;
+      dma16(g, stage + (i * 4 + wave) * 1024);
+    }
+  }
+};
+
+// Loader of an m-contiguous operand tile [BK][M] (M = 256 or 128).
+template <int M>
+struct MnTile {
+  static constexpr int SLOTS = M / 8;                  // 16-byte slots per k row
+  static constexpr int KPI = 64 / SLOTS;               // k rows per dma instruction
+  static constexpr int INSTR = BK / KPI / 4;           // instructions per wave per stage
+  static constexpr int BYTES = BK * M * 2;
+  static constexpr int ROWBYTES = M * 2;
+  Opnd o;
+  int m0;
+  __device__ void init(const Opnd& op, int m0_) {
+    o = op;
+    m0 = m0_;
+  }
+  __device__ void issue(const char* stage, int wave, int lane, int k0) const {
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+      const int kr = (i * 4 + wave) * KPI + lane / SLOTS;
+      const int ps = lane % SLOTS;
+      const int ls = ps ^ (2 * (kr & 3));
+      const int k = k0 + kr;
+      const int m = m0 + ls * 8;
+      const void* g = g_zero_page;
+      if (k < o.K) {
+        if (m < o.rows) g = o.base + (int64_t)k * o.ld + m;
+        else if (m == o.ones_row) g = g_ones_page;
+      }
+      dma16(g, stage + (i * 4 + wave) * 1024);
+    }
+  }
+};
+
+template <int BN>
+struct Acc {
+  static constexpr int WM = 4, WN = BN / 64;  // 32x32 blocks per wave
+  f32x16 c[WM][WN];
+  __device__ void zero() {
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) c[i][j] = f32x16{};
+  }
+};
+
+// Number of outstanding dma instructions allowed while the oldest stage must be complete.
+template <int N>
+__device__ inline void wait_vm() {
+  if constexpr (N >= 63) asm volatile("s_waitcnt vmcnt(63)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Main loop over k in [0, K_loop) (multiple of BK). LA/LB: tile loaders;
+// A_MN/B_MN select the fragment reader. Stage s lives at
+// lds + (s % NSTAGE) * STAGE_BYTES (A then B).
+template <int BN, bool A_MN, bool B_MN, int NSTAGE, class LA, class LB>
+__device__ void core(Acc<BN>& acc, const LA& la, const LB& lb, int K_loop, char* lds, int tid) {
+  constexpr int A_BYTES = LA::BYTES, B_BYTES = LB::BYTES;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int PER_STAGE = LA::INSTR + LB::INSTR;  // dma per thread per stage
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int r = lane & 31, g = lane >> 5;
+  const int nq = K_loop / BK;
+
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s) {
+    if (s < nq) {
+      la.issue(lds + s * STAGE, wave, lane, s * BK);
+      lb.issue(lds + s * STAGE + A_BYTES, wave, lane, s * BK);
+    }
+  }
+  for (int q = 0; q < nq; ++q) {
+    // stage q complete: at most the later stages' dma may still be in flight
+    const int later = min(NSTAGE - 2, nq - 1 - q);
+    if (later >= 2) wait_vm<2 * PER_STAGE>();
+    else if (later == 1) wait_vm<PER_STAGE>();
+    else wait_vm<0>();
+    __syncthreads();
+    if (q + NSTAGE - 1 < nq) {
+      const int s = (q + NSTAGE - 1) % NSTAGE;
+      la.issue(lds + s * STAGE, wave, lane, (q + NSTAGE - 1) * BK);
+      lb.issue(lds + s * STAGE + A_BYTES, wave, lane, (q + NSTAGE - 1) * BK);
+    }
+    const char* abuf = lds + (q % NSTAGE) * STAGE;
+    const char* bbuf = abuf + A_BYTES;
+    // fragments of k-step ss+1 are requested before the MFMAs of k-step ss
+    bf16x8 af[2][Acc<BN>::WM], bfr[2][Acc<BN>::WN];
+    auto load_frags = [&](int ss, bf16x8* a, bf16x8* b) {
+#pragma unroll
+      for (int i = 0; i < Acc<BN>::WM; ++i) {
+        const int m = wr * 128 + i * 32;
+        if constexpr (A_MN) a[i] = frag_mn(abuf, m, ss, lane, LA::ROWBYTES);
+        else a[i] = frag_kc(abuf, m + r, ss, g);
+      }
+#pragma unroll
+      for (int j = 0; j < Acc<BN>::WN; ++j) {
+        const int n = wc * (BN / 2) + j * 32;
+        if constexpr (B_MN) b[j] = frag_mn(bbuf, n, ss, lane, LB::ROWBYTES);
+        else b[j] = frag_kc(bbuf, n + r, ss, g);
+      }
+    };
+    load_frags(0, af[0], bfr[0]);
+#pragma unroll
+    for (int ss = 0; ss < BK / 16; ++ss) {
+      if (ss + 1 < BK / 16) load_frags(ss + 1, af[(ss + 1) & 1], bfr[(ss + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < Acc<BN>::WM; ++i)
+#pragma unroll
+        for (int j = 0; j < Acc<BN>::WN; ++j)
+          acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ss & 1][i], bfr[ss & 1][j], acc.c[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __syncthreads();  // LDS free for the caller's epilogue
+}
+
+// row / col of accumulator element e of block (i, j) for this lane
+__device__ inline int acc_row(int wr, int i, int e, int lane) { return wr * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
+
+}  // namespace m3
+
+// ============================================================================ dW^O, db^O
+// C[v, h] = sum over rows k of dh[k, v] * z[k, h]; column h = H of z reads the
+// ones page, so C[v, H] = sum_k dh[k, v] = db^O[v]. Split-K partials.
+// Workgroup ids are arranged so the tiles of one k split share an XCD (L2).
+__global__ void __launch_bounds__(256) dwo_kernel(DwoArgs p) {
+  using namespace m3;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * MnTile<256>::BYTES];
+  const int tid = threadIdx.x;
+  const int nv = (p.V + BM - 1) / BM, nh = (p.H + 1 + 255) / 256;
+  const int id = blockIdx.x;
+  const int xcd = id & 7, local = id >> 3;
+  const int per = nv * nh;
+  const int split = (local / per) * 8 + xcd;
+  if (split >= p.splits) return;
+  const int rem = local % per;
+  const int vt = rem / nh, ht = rem % nh;
+  const int kb = split * p.k_per_split;
+  const int ke = min(p.K, kb + p.k_per_split);
+
+  MnTile<256> la;
+  la.init(Opnd{reinterpret_cast<const bf16*>(p.dh) + (int64_t)kb * p.dh_ld, p.dh_ld, p.V, max(0, ke - kb), -1},
+          vt * 256);
+  MnTile<256> lb;
+  lb.init(Opnd{reinterpret_cast<const bf16*>(p.z) + (int64_t)kb * p.z_ld, p.z_ld, p.H, max(0, ke - kb), p.H},
+          ht * 256);
+  Acc<256> acc;
+  acc.zero();
+  const int kl = (max(0, ke - kb) + BK - 1) / BK * BK;
+  core<256, true, true, 2>(acc, la, lb, kl, lds, tid);
+
+  const int lane = tid & 63, wave = tid >> 6, wr = wave >> 1, wc = wave & 1;
+  float* C = p.PW + (int64_t)split * p.V * p.H;
+#pragma unroll
+  for (int j = 0; j < Acc<256>::WN; ++j) {
+    const int h = ht * 256 + wc * 128 + j * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < Acc<256>::WM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int v = vt * 256 + acc_row(wr, i, e, lane);
+        if (v < p.V) {
+          if (h < p.H) C[(int64_t)v * p.H + h] = acc.c[i][j][e];
+          else if (h == p.H) p.PB[(int64_t)split * p.V + v] = acc.c[i][j][e];
+        }
+      }
+  }
+}
+
+hipError_t launch_dwo(const DwoArgs& a, hipStream_t st) {
+  const int nv = (a.V + 255) / 256, nh = (a.H + 1 + 255) / 256;
+  const int groups = (a.splits + 7) / 8;
+  dim3 grid(groups * 8 * nv * nh), block(256);
+  hipLaunchKernelGGL(dwo_kernel, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+// ============================================================================ dz, dtanh, sums
+// Workgroup = one 32-row strip of a tile (32 consecutive t) x 128 columns of
+// H, walking the tile's u values eight at a time: M row i of a pass is
+// (u = u0 + 8*ug + i/32, t = strip t + i%32). dz = dh . W^O (W^O^T operand is
+// k-contiguous), ds = dz (1 - z^2) with z read from the row-major z buffer;
+// sums over u stay in registers across passes (gA partial, written once);
+// sums over the strip's t are written per u (gL partial).
+__global__ void __launch_bounds__(256) dz2_kernel(DzArgs p) {
+  using namespace m3;
+  __shared__ __attribute__((aligned(1024))) char lds[3 * (KcTile<256>::BYTES + KcTile<128>::BYTES)];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), wr = wave >> 1, wc = wave & 1;
+  const int nh = (p.H + 127) / 128;
+  const int id = blockIdx.x;
+  const int xcd = id & 7, local = id >> 3;
+  const int strip_rel = (local / nh) * 8 + xcd;
+  if (strip_rel >= p.n_strips) return;
+  const int ht = local % nh;
+  const int strip = p.strip_begin + strip_rel;
+  const int h0 = ht * 128;
+
+  int lo = p.tile_begin, hi = p.tile_end - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (p.tiles[mid].strip0 <= strip) lo = mid; else hi = mid - 1;
+  }
+  const Tile tl = p.tiles[lo];
+  const int slot = lo - p.tile_begin;
+  const int s_local = strip - tl.strip0;
+  const int tl0 = s_local * 32;
+  const int tile_row = tl.row0 - p.wave_row_base;
+  const bf16* dh = reinterpret_cast<const bf16*>(p.dh);
+  const bf16* zb = reinterpret_cast<const bf16*>(p.z);
+  const bf16* wot = reinterpret_cast<const bf16*>(p.WOT);
+
+  KcTile<128> lb;
+  lb.init(wave, lane, p.V_pad, [&](int row) -> const bf16* {
+    const int h = h0 + row;
+    return h < p.H ? wot + (int64_t)h * p.V_pad : nullptr;
+  });
+
+  // gA partial: per wave, 32 t (lane rows) x its 64 columns, summed over u
+  float gacc[Acc<128>::WN][16];
+#pragma unroll
+  for (int j = 0; j < Acc<128>::WN; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) gacc[j][e] = 0.0f;
+
+  const int ngroups = (tl.wu + 7) / 8;
+  for (int ug = 0; ug < ngroups; ++ug) {
+    KcTile<256> la;
+    la.init(wave, lane, p.V_pad, [&](int row) -> const bf16* {
+      const int ul = ug * 8 + row / 32;
+      return ul < tl.wu ? dh + (int64_t)(tile_row + ul * tl.htp + tl0 + row % 32) * p.V_pad : nullptr;
+    });
+    Acc<128> acc;
+    acc.zero();
+    core<128, false, false, 3>(acc, la, lb, (p.V_pad + BK - 1) / BK * BK, lds, tid);
+
+    // wave rows: 4 blocks of 32 rows = u_local ug*8 + wr*4 + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ul = ug * 8 + wr * 4 + i;
+      const bool uok = ul < tl.wu;
+      const int64_t zrow0 = (int64_t)(tile_row + ul * tl.htp + tl0);
+#pragma unroll
+      for (int j = 0; j < Acc<128>::WN; ++j) {
+        const int h = h0 + wc * 64 + j * 32 + (lane & 31);
+        float lsum = 0.0f;
+        const bool ok = uok && h < p.H;
+        const bf16* zc = ok ? zb + zrow0 * p.z_ld + h : zb;  // clamped: loads are unconditional
+        float zv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int trow = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          zv[e] = (float)zc[ok ? trow * p.z_ld : 0];
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float ds = ok ? acc.c[i][j][e] * (1.0f - zv[e] * zv[e]) : 0.0f;
+          gacc[j][e] += ds;
+          lsum += ds;
+        }
+        lsum += __shfl_xor(lsum, 32);
+        if (lane < 32 && uok && h < p.H)
+          p.PL[(((int64_t)slot * (p.tile_tp / 32) + s_local) * p.tile_u + ul) * p.H + h] = lsum;
+      }
+    }
+  }
+
+  // combine the two wave rows (same columns), then one write per (t, h)
+  float* red = reinterpret_cast<float*>(lds);
+  constexpr int PER = Acc<128>::WN * 16;
+  if (wr == 1) {
+#pragma unroll
+    for (int j = 0; j < Acc<128>::WN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[((wc * PER) + j * 16 + e) * 64 + lane] = gacc[j][e];
+  }
+  __syncthreads();
+  if (wr == 0) {
+#pragma unroll
+    for (int j = 0; j < Acc<128>::WN; ++j) {
+      const int h = h0 + wc * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float v = gacc[j][e] + red[((wc * PER) + j * 16 + e) * 64 + lane];
+        const int t = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (h < p.H) p.PA[((int64_t)slot * p.tile_tp + tl0 + t) * p.H + h] = v;
+      }
+    }
+  }
+}
+
+hipError_t launch_dz2(const DzArgs& a, hipStream_t st) {
+  if (a.n_strips == 0) return hipSuccess;
+  const int nh = (a.H + 127) / 128;
+  const int groups = (a.n_strips + 7) / 8;
+  dim3 grid(groups * 8 * nh), block(256);
+  hipLaunchKernelGGL(dz2_kernel, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+// ============================================================================ z and the two scores
+// One workgroup per 32-row chunk (32 consecutive t at one u of one tile):
+// z[row, k] = bf16(tanh(a[b,t,k] + l[b,u,k])) for k < H (0 up to H_pad and on
+// padding rows), and the blank / label scores of the row as dot products of
+// that bf16 z with the two W^O rows (plus the biases).
+__global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
+  const int tid = threadIdx.x;
+  const int R0 = p.row_begin + blockIdx.x * 32;
+  int lo = p.tile_begin, hi = p.tile_end - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (p.tiles[mid].row0 <= R0) lo = mid; else hi = mid - 1;
+  }
+  const Tile tl = p.tiles[lo];
+  const int local = R0 - tl.row0;
+  const int ul = local / tl.htp;
+  const int tloc = local - ul * tl.htp;
+  const int b = tl.b, u = tl.u0 + ul;
+  const int Ub = p.U_len[b];
+  const int r = tid >> 3, q = tid & 7;  // row within the chunk, k slice
+  const bool row_ok = tloc + r < tl.ht;
+  const int t = tl.t0 + tloc + r;
+  const int lab = u < Ub ? p.labels[(size_t)b * p.U1 + u + 1] : -1;
+  const bf16* WO = reinterpret_cast<const bf16*>(p.WO);
+  const bf16* bO = reinterpret_cast<const bf16*>(p.bO);
+  const float* arow = p.a + ((size_t)b * p.T + (row_ok ? t : 0)) * p.H_pad;
+  const float* lrow = p.l + ((size_t)b * p.U1 + u) * p.H_pad;
+  bf16* zrow = reinterpret_cast<bf16*>(p.z) + (int64_t)(R0 - p.buf_row_base + r) * p.z_ld;
+  const bf16* wb = WO + (size_t)p.blank * p.H;
+  const bf16* wy = WO + (size_t)(lab >= 0 ? lab : 0) * p.H;
+  float hb = 0.0f, hy = 0.0f;
+  for (int k = q * 8; k < p.z_ld; k += 64) {
+    bf16x8 z;
+    if (row_ok && k < p.H) {
+      f32x4 a0 = ldg<f32x4>(arow + k), a1 = ldg<f32x4>(arow + k + 4);
+      f32x4 l0 = ldg<f32x4>(lrow + k), l1 = ldg<f32x4>(lrow + k + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        z[e] = (bf16)tanh_fast(a0[e] + l0[e]);
+        z[e + 4] = (bf16)tanh_fast(a1[e] + l1[e]);
+      }
+      bf16x8 xb = ldg<bf16x8>(wb + k), xy = ldg<bf16x8>(wy + k);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hb = __builtin_fmaf((float)z[e], (float)xb[e], hb);
+        hy = __builtin_fmaf((float)z[e], (float)xy[e], hy);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[e] = (bf16)0.0f;
+    }
+    *reinterpret_cast<bf16x8*>(zrow + k) = z;
+  }
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) {
+    hb += __shfl_xor(hb, off);
+    hy += __shfl_xor(hy, off);
+  }
+  if (q == 0) {
+    const int rr = R0 - p.buf_row_base + r;
+    p.hb[rr] = hb + (float)bO[p.blank];
+    p.hy[rr] = lab >= 0 ? hy + (float)bO[lab] : 0.0f;
+  }
+}
+
+hipError_t launch_zrow(const ZArgs& a, hipStream_t st) {
+  if (a.n_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(zrow_kernel, dim3(a.n_rows / 32), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ============================================================================ scores^T tiles
+// C[v, c] = sum_k W^O[v, k] z[c, k] for a 256-score x 256-cell tile, so each
+// lane holds whole cells (columns) and the reductions over the vocabulary are
+// lane-local. The V tiles of one cell tile share an XCD.
+//   forward: per cell, (max, sum exp) over the tile's scores (+ b^O) ->
+//            partial statistics [row, V tile]; optionally the scores.
+//   backward: dh = g*occ*exp(h - lse) - [v=blank] g*bflow - [v=y] g*lflow,
+//            written [row, V_pad] in bf16.
+template <bool BWD>
+__global__ void __launch_bounds__(256) scores_kernel(ScoresArgs p) {
+  using namespace m3;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * KcTile<256>::BYTES];
+  __shared__ float cell[5][256];
+  __shared__ float bias_s[256];  // b^O of this V tile (0 past V)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), wr = wave >> 1, wc = wave & 1;
+  const int nvt = (p.V + 255) / 256;
+  const int id = blockIdx.x;
+  const int xcd = id & 7, local = id >> 3;
+  const int ct = (local / nvt) * 8 + xcd;
+  const int vt = local % nvt;
+  const int c0 = ct * 256;  // first row (buffer-relative) of the cell tile
+  if (c0 >= p.n_rows) return;
+  const bf16* WO = reinterpret_cast<const bf16*>(p.WO);
+  const bf16* bO = reinterpret_cast<const bf16*>(p.bO);
+  const bf16* zb = reinterpret_cast<const bf16*>(p.z);
+
+  {
+    const int v = vt * 256 + tid;
+    bias_s[tid] = v < p.V ? (float)bO[v] : 0.0f;
+  }
+  // per-cell coefficients (backward) / validity
+  if (BWD) {
+    const int rr = c0 + tid;  // buffer row
+    float ls = 0.0f, co = 0.0f, cb = 0.0f, cl = 0.0f, lab = -1.0f;
+    if (rr < p.n_rows) {
+      const int R = rr + p.buf_row_base;
+      int lo = p.tile_begin, hi = p.tile_end - 1;
+      while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (p.tiles[mid].row0 <= R) lo = mid; else hi = mid - 1;
+      }
+      const Tile tl = p.tiles[lo];
+      const int local_r = R - tl.row0;
+      const int ul = local_r / tl.htp, tloc = local_r - ul * tl.htp;
+      if (tloc < tl.ht) {
+        const int b = tl.b, u = tl.u0 + ul, t = tl.t0 + tloc;
+        const int Tb = p.T_len[b], Ub = p.U_len[b];
+        const size_t idx = ((size_t)b * p.U1 + u) * p.T + t;
+        const float lp = p.lnP[b];
+        const float gb = p.dcosts ? p.dcosts[b] : 1.0f;
+        const float A = p.alpha[idx], Bt = p.beta[idx];
+        ls = p.lse[idx];
+        const float bn = (t + 1 < Tb) ? p.beta[idx + 1] : (u == Ub ? 0.0f : kNegInf);
+        co = gb * fexp2((A + Bt - lp) * kLog2e);
+        cb = gb * fexp2((A + p.phi[idx] + bn - lp) * kLog2e);
+        if (u < Ub) {
+          cl = gb * fexp2((A + p.psi[idx] + p.beta[idx + p.T] - lp) * kLog2e);
+          lab = (float)p.labels[(size_t)b * p.U1 + u + 1];
+        }
+      }
+    }
+    cell[0][tid] = ls * kLog2e;
+    cell[1][tid] = co;
+    cell[2][tid] = cb;
+    cell[3][tid] = cl;
+    cell[4][tid] = lab;
+  }
+
+  KcTile<256> la;
+  la.init(wave, lane, p.H, [&](int row) -> const bf16* {
+    const int v = vt * 256 + row;
+    return v < p.V ? WO + (int64_t)v * p.H : nullptr;
+  });
+  KcTile<256> lb;
+  lb.init(wave, lane, p.H, [&](int row) -> const bf16* {
+    const int rr = c0 + row;
+    return rr < p.n_rows ? zb + (int64_t)rr * p.z_ld : nullptr;
+  });
+  Acc<256> acc;
+  acc.zero();
+  core<256, false, false, 2>(acc, la, lb, (p.H + BK - 1) / BK * BK, lds, tid);
+
+  // lane columns: cells wc*128 + j*32 + (lane & 31); rows: scores
+  if (!BWD) {
+    float mrow[4], srow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float m = -1e30f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int vr = acc_row(wr, i, e, lane);
+          const float x = acc.c[i][j][e] + bias_s[vr];
+          m = (vt * 256 + vr < p.V) ? __builtin_fmaxf(m, x) : m;
+        }
+      const float ml = m * kLog2e;
+      float sm = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int vr = acc_row(wr, i, e, lane);
+          const float ex = fexp2(__builtin_fmaf(acc.c[i][j][e] + bias_s[vr], kLog2e, -ml));
+          sm += (vt * 256 + vr < p.V) ? ex : 0.0f;
+        }
+      // combine with the other half-wave (same cells, other score rows)
+      const float m2 = __shfl_xor(m, 32), s2 = __shfl_xor(sm, 32);
+      const float mn = __builtin_fmaxf(m, m2);
+      sm = sm * fexp2((m - mn) * kLog2e) + s2 * fexp2((m2 - mn) * kLog2e);
+      mrow[j] = mn;
+      srow[j] = sm;
+    }
+    // combine the two wave rows through LDS
+    float* red = reinterpret_cast<float*>(lds);
+    if (wr == 1 && lane < 32) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        red[(wc * 4 + j) * 64 + lane] = mrow[j];
+        red[(wc * 4 + j) * 64 + 32 + lane] = srow[j];
+      }
+    }
+    __syncthreads();
+    if (wr == 0 && lane < 32) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float m2 = red[(wc * 4 + j) * 64 + lane], s2 = red[(wc * 4 + j) * 64 + 32 + lane];
+        const float mn = __builtin_fmaxf(mrow[j], m2);
+        const float sm = srow[j] * fexp2((mrow[j] - mn) * kLog2e) + s2 * fexp2((m2 - mn) * kLog2e);
+        const int rr = c0 + wc * 128 + j * 32 + lane;
+        if (rr < p.n_rows) p.stats[((int64_t)rr * nvt + vt)] = f32x2{mn, sm};
+      }
+    }
+    if (p.logits) {  // untiled: keep the scores (bias included), 4 consecutive v per store
+      bf16* lg = reinterpret_cast<bf16*>(p.logits);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = c0 + wc * 128 + j * 32 + (lane & 31);
+        if (rr >= p.n_rows) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e4 = 0; e4 < 16; e4 += 4) {
+            const int v = vt * 256 + acc_row(wr, i, e4, lane);
+            if (v >= p.V_pad) continue;
+            bf16x4 w;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              w[q] = (bf16)(v + q < p.V ? acc.c[i][j][e4 + q] + bias_s[v + q - vt * 256] : 0.0f);
+            *reinterpret_cast<bf16x4*>(lg + (int64_t)(rr + p.buf_row_base) * p.V_pad + v) = w;
+          }
+      }
+    }
+  } else {
+    bf16* dh = reinterpret_cast<bf16*>(p.dh);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cc = wc * 128 + j * 32 + (lane & 31);
+      const int rr = c0 + cc;
+      if (rr >= p.n_rows) continue;
+      const float lsl = cell[0][cc], co = cell[1][cc], cb = cell[2][cc], cl = cell[3][cc];
+      const int lab = (int)cell[4][cc];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e4 = 0; e4 < 16; e4 += 4) {
+          const int v = vt * 256 + acc_row(wr, i, e4, lane);
+          if (v >= p.V_pad) continue;
+          bf16x4 w;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int vv = v + q;
+            const float x = acc.c[i][j][e4 + q] + bias_s[vv - vt * 256];
+            float d = co * fexp2(__builtin_fmaf(x, kLog2e, -lsl));
+            d -= (vv == p.blank) ? cb : 0.0f;
+            d -= (vv == lab) ? cl : 0.0f;
+            w[q] = (bf16)(vv < p.V ? d : 0.0f);
+          }
+          *reinterpret_cast<bf16x4*>(dh + (int64_t)rr * p.V_pad + v) = w;
+        }
+    }
+  }
+}
+
+hipError_t launch_scores(const ScoresArgs& a, bool bwd, hipStream_t st) {
+  if (a.n_rows == 0) return hipSuccess;
+  const int nvt = (a.V + 255) / 256;
+  const int nct = (a.n_rows + 255) / 256;
+  const int groups = (nct + 7) / 8;
+  dim3 grid(groups * 8 * nvt), block(256);
+  if (bwd) hipLaunchKernelGGL(scores_kernel<true>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(scores_kernel<false>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+// lse = logsumexp over the V tiles' partial statistics; phi, psi from the
+// blank / label scores; written to the [b, u, t] arrays for valid cells.
+__global__ void __launch_bounds__(256) lse_merge_kernel(MergeArgs p) {
+  const int rr = blockIdx.x * 256 + threadIdx.x;
+  if (rr >= p.n_rows) return;
+  const int R = rr + p.buf_row_base;
+  int lo = p.tile_begin, hi = p.tile_end - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (p.tiles[mid].row0 <= R) lo = mid; else hi = mid - 1;
+  }
+  const Tile tl = p.tiles[lo];
+  const int local_r = R - tl.row0;
+  const int ul = local_r / tl.htp, tloc = local_r - ul * tl.htp;
+  if (tloc >= tl.ht) return;
+  const int b = tl.b, u = tl.u0 + ul, t = tl.t0 + tloc;
+  float M = -1e30f;
+  for (int v = 0; v < p.nvt; ++v) M = __builtin_fmaxf(M, p.stats[(int64_t)rr * p.nvt + v][0]);
+  float S = 0.0f;
+  for (int v = 0; v < p.nvt; ++v) {
+    const f32x2 st = p.stats[(int64_t)rr * p.nvt + v];
+    S += st[1] * fexp2((st[0] - M) * kLog2e);
+  }
+  const float lse = M + kLn2 * flog2(S);
+  const size_t idx = ((size_t)b * p.U1 + u) * p.T + t;
+  p.lse[idx] = lse;
+  p.phi[idx] = p.hb[rr] - lse;
+  p.psi[idx] = u < p.U_len[b] ? p.hy[rr] - lse : kNegInf;
+}
+
+hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t st) {
+  if (a.n_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(lse_merge_kernel, dim3((a.n_rows + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace rnnt

@@ -182,9 +182,16 @@ void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H
     p.max_wave_rows = (int)std::max<int64_t>(p.max_wave_rows, bound_tiles * p.tile_tp * d.tile_u);
     p.max_wave_tiles = (int)std::max<int64_t>(p.max_wave_tiles, bound_tiles);
   }
-  // split-K counts: about 1024 workgroups for dW^O, 512 for dW^A / dW^L
-  int64_t tiles_vh = cdiv(d.V, 128) * cdiv(d.H, 128);
-  p.s6 = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(1024, tiles_vh), p.max_wave_rows / 2048));
+  // split-K counts: dW^O ~1024 workgroups of 128 x 128 (fp32 path) or ~256
+  // of 256 x 256 (bf16 path); dW^A / dW^L ~512
+  p.nvt = (int)cdiv(d.V, 256);
+  if (d.bf16) {
+    int64_t tiles_vh = cdiv(d.V, 256) * cdiv(d.H + 1, 256);
+    p.s6 = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(256, tiles_vh), p.max_wave_rows / 4096));
+  } else {
+    int64_t tiles_vh = cdiv(d.V, 128) * cdiv(d.H, 128);
+    p.s6 = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(1024, tiles_vh), p.max_wave_rows / 2048));
+  }
   int64_t tiles_ha = cdiv(d.H, 128) * cdiv(d.HA, 128);
   int64_t tiles_hl = cdiv(d.H, 128) * cdiv(d.HL, 128);
   p.s7a = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(512, tiles_ha), cdiv((int64_t)d.B * d.T, 64)));
@@ -239,6 +246,12 @@ Layout make_layout(const Plan& p) {
   L.w_PBZ = take(sizeof(float) * (size_t)p.s7a * d.H);
   L.w_PWL = take(sizeof(float) * (size_t)p.s7l * d.H * d.HL);
   L.w_WOT = take(ct * (size_t)d.H * p.V_pad);
+  // bf16 forward buffers, one wave of rows (all rows in untiled mode)
+  const size_t frows = d.untiled ? (size_t)p.total_rows : (size_t)p.max_wave_rows;
+  L.w_zf = 0;  // the tiled forward's z rows reuse the backward's z buffer (w_z)
+  L.w_stats = d.bf16 ? take(8 * frows * p.nvt) : 0;
+  L.w_hb = d.bf16 ? take(4 * frows) : 0;
+  L.w_hy = d.bf16 ? take(4 * frows) : 0;
   L.workspace_bytes = o;
   return L;
 }

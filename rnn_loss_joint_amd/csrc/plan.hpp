@@ -46,6 +46,7 @@ struct Plan {
   int64_t total_rows = 0;
   int max_wave_rows = 0, max_wave_tiles = 0;
   int s6 = 1, s7a = 1, s7l = 1;  // split-K counts
+  int nvt = 1;                   // 256-score tiles of the vocabulary (bf16 path)
 };
 
 // Byte offsets inside `saved` and `workspace` (all 256-byte aligned).
@@ -56,6 +57,7 @@ struct Layout {
   size_t off_logits, off_z;  // untiled only; z is stored transposed [H_pad, total_rows]
   size_t saved_bytes;
   size_t w_dh, w_z, w_gA, w_gL, w_PA, w_PL, w_PW, w_PB, w_PWA, w_PBZ, w_PWL, w_WOT;
+  size_t w_zf, w_stats, w_hb, w_hy;  // bf16 forward: z rows, V-tile statistics, blank/label scores
   size_t workspace_bytes;
 };
 
