@@ -10,7 +10,12 @@
 // so both orientations become MFMA fragments without register transposes.
 // Pieces outside the operand read a zero page (or a page of bf16 ones, used
 // to append a column of ones to an operand).
+// Each kernel declares exactly one __shared__ array and carves every LDS
+// region out of it: with several LDS variables the compiler attaches alias
+// scopes and then makes every read of the stage buffers wait for all dma in
+// flight, which removes the overlap of loads and MFMAs.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -39,21 +44,52 @@ __device__ inline bf16x8 frag_kc(const char* buf, int row, int ss, int g) {
   return *reinterpret_cast<const bf16x8*>(buf + lds_off(row, ss * 2 + g));
 }
 
+// XOR applied to the 8-byte unit index of k row k of an m-contiguous tile.
+// A transposed read takes 4 units of each of 4 consecutive k rows per 16
+// lanes (32 lanes: 8 units); the pattern puts those on distinct banks both
+// per 16 lanes (128 bytes) and per 32 lanes (256 bytes).
+__device__ inline int mn_swz(int k) { return (k & 1) * 20 ^ (k & 2) * 4; }
+
+// ds_read_b64_tr_b16 issued from inline asm. Through the builtin the compiler
+// makes every such read wait for all global->LDS dma in flight; here the
+// caller waits on lgkmcnt itself (wait_frags) before the data is used.
+typedef __attribute__((address_space(3))) const char lds_cchar;
+__device__ inline u32x2 ds_read_tr16(const char* p) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"((uint32_t)(uintptr_t)(lds_cchar*)p));
+  return v;
+}
+
 // m-contiguous fragment for m in [m_base, m_base+32), k-step ss; rowbytes =
-// bytes of one k row of the tile.
+// bytes of one k row of the tile. The two reads are outstanding on return.
 __device__ inline bf16x8 frag_mn(const char* buf, int m_base, int ss, int lane, int rowbytes) {
   const int G = lane >> 4, L = lane & 15;
   const int m = m_base + 16 * (G & 1) + 4 * (L & 3);
-  bf16x8 out;
+  u32x4 out;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int k = ss * 16 + 8 * (G >> 1) + 4 * h + (L >> 2);
-    const int unit = (m >> 2) ^ (4 * (k & 3));
-    bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + k * rowbytes + unit * 8));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[4 * h + j] = v[j];
+    const int unit = (m >> 2) ^ mn_swz(k);
+    const u32x2 v = ds_read_tr16(buf + k * rowbytes + unit * 8);
+    out[2 * h] = v[0];
+    out[2 * h + 1] = v[1];
   }
-  return out;
+  return __builtin_bit_cast(bf16x8, out);
+}
+
+// Waits until at most N LDS operations are outstanding; the fragments pass
+// through the asm so that their uses cannot be scheduled above the wait.
+template <int N, int NA, int NB>
+__device__ inline void wait_frags(bf16x8 (&a)[NA], bf16x8 (&b)[NB]) {
+  static_assert(NA == 4 && (NB == 4 || NB == 2), "fragment counts");
+  if constexpr (NB == 4)
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
+                 : "n"(N));
+  else
+    asm volatile("s_waitcnt lgkmcnt(%6)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1])
+                 : "n"(N));
 }
 
 // Operand description for the core.
@@ -83,47 +119,48 @@ struct KcTile {
     }
     c = lane & 7;
   }
-  __device__ void issue(const char* stage, int wave, int lane, int k0) const {
-#pragma unroll
-    for (int i = 0; i < INSTR; ++i) {
-      const int row = (i * 4 + wave) * 8 + (lane >> 3);
-      const int lc = c ^ swz(row);
-      const int k = k0 + lc * 8;
-      const void* g = (rowp[i] && k < K) ? (const void*)(rowp[i] + k) : (const void*)g_zero_page;
-      dma16(g, stage + (i * 4 + wave) * 1024);
-    }
+  // dma instruction i of stage k0 (i < INSTR, compile-time after unrolling)
+  __device__ void issue_one(const char* stage, int wave, int lane, int k0, int i) const {
+    const int row = (i * 4 + wave) * 8 + (lane >> 3);
+    const int lc = c ^ swz(row);
+    const int k = k0 + lc * 8;
+    const void* g = (rowp[i] && k < K) ? (const void*)(rowp[i] + k) : (const void*)g_zero_page;
+    dma16(g, stage + (i * 4 + wave) * 1024);
   }
 };
 
 // Loader of an m-contiguous operand tile [BK][M] (M = 256 or 128).
 template <int M>
 struct MnTile {
+  static_assert(M >= 128, "mn_swz needs at least 32 units per k row");
   static constexpr int SLOTS = M / 8;                  // 16-byte slots per k row
   static constexpr int KPI = 64 / SLOTS;               // k rows per dma instruction
   static constexpr int INSTR = BK / KPI / 4;           // instructions per wave per stage
   static constexpr int BYTES = BK * M * 2;
   static constexpr int ROWBYTES = M * 2;
-  Opnd o;
-  int m0;
-  __device__ void init(const Opnd& op, int m0_) {
-    o = op;
-    m0 = m0_;
+  // Instruction i of a thread moves k row kr0 + 4 KPI i; kr0 & 3 and hence
+  // the swizzled column m are the same for every i, so one pointer (k row
+  // kr0, column m) plus a uniform row offset addresses them all.
+  const char* p0;      // data: &base[kr0][m]; otherwise the ones or zero page
+  const char* zero;
+  int64_t ldb;         // bytes per k row
+  int kr0, K;
+  bool data;
+  __device__ void init(const Opnd& op, int m0, int wave, int lane) {
+    kr0 = wave * KPI + lane / SLOTS;
+    const int ls = (lane % SLOTS) ^ (mn_swz(kr0) >> 1);
+    const int m = m0 + ls * 8;
+    ldb = op.ld * 2;
+    K = op.K;
+    zero = reinterpret_cast<const char*>(g_zero_page);
+    data = m < op.rows;
+    p0 = data ? reinterpret_cast<const char*>(op.base + (int64_t)kr0 * op.ld + m)
+              : (m == op.ones_row ? reinterpret_cast<const char*>(g_ones_page) : zero);
   }
-  __device__ void issue(const char* stage, int wave, int lane, int k0) const {
-#pragma unroll
-    for (int i = 0; i < INSTR; ++i) {
-      const int kr = (i * 4 + wave) * KPI + lane / SLOTS;
-      const int ps = lane % SLOTS;
-      const int ls = ps ^ (2 * (kr & 3));
-      const int k = k0 + kr;
-      const int m = m0 + ls * 8;
-      const void* g = g_zero_page;
-      if (k < o.K) {
-        if (m < o.rows) g = o.base + (int64_t)k * o.ld + m;
-        else if (m == o.ones_row) g = g_ones_page;
-      }
-      dma16(g, stage + (i * 4 + wave) * 1024);
-    }
+  __device__ void issue_one(const char* stage, int wave, int lane, int k0, int i) const {
+    const int kofs = k0 + i * 4 * KPI;  // uniform
+    const char* g = kr0 + kofs < K ? (data ? p0 + kofs * ldb : p0) : zero;
+    dma16(g, stage + (i * 4 + wave) * 1024);
   }
 };
 
@@ -139,6 +176,11 @@ struct Acc {
   }
 };
 
+// Workgroup barrier for LDS hand-over only: the wave's own LDS reads are
+// complete, outstanding global->LDS dma is left in flight (a __syncthreads
+// fence would wait for it).
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Number of outstanding dma instructions allowed while the oldest stage must be complete.
 template <int N>
 __device__ inline void wait_vm() {
@@ -147,70 +189,107 @@ __device__ inline void wait_vm() {
 }
 
 // Main loop over k in [0, K_loop) (multiple of BK). LA/LB: tile loaders;
-// A_MN/B_MN select the fragment reader. Stage s lives at
-// lds + (s % NSTAGE) * STAGE_BYTES (A then B).
-template <int BN, bool A_MN, bool B_MN, int NSTAGE, class LA, class LB>
+// MN selects the m-contiguous fragment reader for both operands. Stage s
+// lives at lds + (s % NSTAGE) * STAGE_BYTES (A then B).
+//
+// Software pipeline, per stage of four k-steps: every MFMA of k-step ss is
+// followed by a share of the fragment reads of k-step ss+1 (double-buffered
+// registers), so LDS reads and their address arithmetic run under the MFMAs.
+// The hand-over to the next stage (wait for its dma, barrier) sits before
+// k-step 3; k-step 3 then reads the next stage's first fragments and issues
+// the dma of stage q + NSTAGE into the slot just released.
+template <int BN, bool MN, int NSTAGE, class LA, class LB>
 __device__ void core(Acc<BN>& acc, const LA& la, const LB& lb, int K_loop, char* lds, int tid) {
+  constexpr int WM = Acc<BN>::WM, WN = Acc<BN>::WN;
+  constexpr int NMF = WM * WN;  // MFMAs per k-step
+  constexpr int NFR = WM + WN;  // fragments per k-step
   constexpr int A_BYTES = LA::BYTES, B_BYTES = LB::BYTES;
   constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int PER_STAGE = LA::INSTR + LB::INSTR;  // dma per thread per stage
+  constexpr int NDMA = LA::INSTR + LB::INSTR;  // dma per thread per stage
+  static_assert(BK / 16 == 4, "four k-steps per stage");
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
   const int r = lane & 31, g = lane >> 5;
   const int nq = K_loop / BK;
+  if (nq == 0) return;
 
-#pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s) {
-    if (s < nq) {
-      la.issue(lds + s * STAGE, wave, lane, s * BK);
-      lb.issue(lds + s * STAGE + A_BYTES, wave, lane, s * BK);
+#define RNNT_FI __attribute__((always_inline))
+  auto slot = [&](int s) RNNT_FI -> char* { return lds + (s % NSTAGE) * STAGE; };
+  // d-th dma of stage s; a stage at or past nq reads only the zero page
+  auto issue_dma = [&](int d, int s) RNNT_FI {
+    char* st = slot(s);
+    if (d < LA::INSTR) la.issue_one(st, wave, lane, s * BK, d);
+    else lb.issue_one(st + A_BYTES, wave, lane, s * BK, d - LA::INSTR);
+  };
+  auto read_frag = [&](int f, const char* st, int ss, bf16x8* a, bf16x8* b) RNNT_FI {
+    if (f < WM) {
+      const int m = wr * 128 + f * 32;
+      if constexpr (MN) a[f] = frag_mn(st, m, ss, lane, LA::ROWBYTES);
+      else a[f] = frag_kc(st, m + r, ss, g);
+    } else {
+      const int n = wc * (BN / 2) + (f - WM) * 32;
+      if constexpr (MN) b[f - WM] = frag_mn(st + A_BYTES, n, ss, lane, LB::ROWBYTES);
+      else b[f - WM] = frag_kc(st + A_BYTES, n + r, ss, g);
     }
-  }
+  };
+
+  bf16x8 af[2][WM], bfr[2][WN];
+  // one k-step: MFMAs on register buffer CB; the fragments of (rd_st, rd_ss)
+  // go to buffer CB^1, spread over the MFMA slots; with DMA, also the dma of
+  // stage dma_stage.
+  auto kstep = [&](auto CB, auto DMA, const char* rd_st, int rd_ss, int dma_stage) RNNT_FI {
+    constexpr int cb = decltype(CB)::value;
+    constexpr bool dma = decltype(DMA)::value;
+    if constexpr (MN) wait_frags<0>(af[cb], bfr[cb]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int x = 0; x < NMF; ++x) {
+      const int i = x / WN, j = x % WN;
+      acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j], acc.c[i][j], 0, 0, 0);
+#pragma unroll
+      for (int f = 0; f < NFR; ++f)
+        if (f * NMF / NFR == x) read_frag(f, rd_st, rd_ss, af[cb ^ 1], bfr[cb ^ 1]);
+      if constexpr (dma) {
+#pragma unroll
+        for (int d = 0; d < NDMA; ++d)
+          if (d * NMF / NDMA == x) issue_dma(d, dma_stage);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using NoDma = std::integral_constant<bool, false>;
+  using Dma = std::integral_constant<bool, true>;
+
+  // Prologue: stages 0 .. NSTAGE-2 in flight, stage 0 landed and its first
+  // fragments read, then stage NSTAGE-1 in flight. From here on every stage
+  // s issues exactly NDMA dma per thread (stages past the end read zeros),
+  // so "stage s landed" is always "at most NSTAGE-2 later stages in flight".
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s)
+#pragma unroll
+    for (int d = 0; d < NDMA; ++d) issue_dma(d, s);
+  wait_vm<(NSTAGE - 2) * NDMA>();
+  lds_barrier();
+#pragma unroll
+  for (int f = 0; f < NFR; ++f) read_frag(f, slot(0), 0, af[0], bfr[0]);
+#pragma unroll
+  for (int d = 0; d < NDMA; ++d) issue_dma(d, NSTAGE - 1);
+
   for (int q = 0; q < nq; ++q) {
-    // stage q complete: at most the later stages' dma may still be in flight
-    const int later = min(NSTAGE - 2, nq - 1 - q);
-    if (later >= 2) wait_vm<2 * PER_STAGE>();
-    else if (later == 1) wait_vm<PER_STAGE>();
-    else wait_vm<0>();
-    __syncthreads();
-    if (q + NSTAGE - 1 < nq) {
-      const int s = (q + NSTAGE - 1) % NSTAGE;
-      la.issue(lds + s * STAGE, wave, lane, (q + NSTAGE - 1) * BK);
-      lb.issue(lds + s * STAGE + A_BYTES, wave, lane, (q + NSTAGE - 1) * BK);
-    }
-    const char* abuf = lds + (q % NSTAGE) * STAGE;
-    const char* bbuf = abuf + A_BYTES;
-    // fragments of k-step ss+1 are requested before the MFMAs of k-step ss
-    bf16x8 af[2][Acc<BN>::WM], bfr[2][Acc<BN>::WN];
-    auto load_frags = [&](int ss, bf16x8* a, bf16x8* b) {
-#pragma unroll
-      for (int i = 0; i < Acc<BN>::WM; ++i) {
-        const int m = wr * 128 + i * 32;
-        if constexpr (A_MN) a[i] = frag_mn(abuf, m, ss, lane, LA::ROWBYTES);
-        else a[i] = frag_kc(abuf, m + r, ss, g);
-      }
-#pragma unroll
-      for (int j = 0; j < Acc<BN>::WN; ++j) {
-        const int n = wc * (BN / 2) + j * 32;
-        if constexpr (B_MN) b[j] = frag_mn(bbuf, n, ss, lane, LB::ROWBYTES);
-        else b[j] = frag_kc(bbuf, n + r, ss, g);
-      }
-    };
-    load_frags(0, af[0], bfr[0]);
-#pragma unroll
-    for (int ss = 0; ss < BK / 16; ++ss) {
-      if (ss + 1 < BK / 16) load_frags(ss + 1, af[(ss + 1) & 1], bfr[(ss + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < Acc<BN>::WM; ++i)
-#pragma unroll
-        for (int j = 0; j < Acc<BN>::WN; ++j)
-          acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ss & 1][i], bfr[ss & 1][j], acc.c[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    const char* cur = slot(q);
+    kstep(C0{}, NoDma{}, cur, 1, 0);
+    kstep(C1{}, NoDma{}, cur, 2, 0);
+    kstep(C0{}, NoDma{}, cur, 3, 0);
+    wait_vm<(NSTAGE - 2) * NDMA>();  // stage q+1 landed
+    lds_barrier();                     // every wave is done with slot q
+    kstep(C1{}, Dma{}, slot(q + 1), 0, q + NSTAGE);
   }
-  __syncthreads();  // LDS free for the caller's epilogue
+  wait_vm<0>();   // the zero-page dma past the end must land before LDS is reused
+  lds_barrier();  // LDS free for the caller's epilogue
+#undef RNNT_FI
 }
 
 // row / col of accumulator element e of block (i, j) for this lane
@@ -237,18 +316,19 @@ __global__ void __launch_bounds__(256) dwo_kernel(DwoArgs p) {
   const int kb = split * p.k_per_split;
   const int ke = min(p.K, kb + p.k_per_split);
 
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   MnTile<256> la;
   la.init(Opnd{reinterpret_cast<const bf16*>(p.dh) + (int64_t)kb * p.dh_ld, p.dh_ld, p.V, max(0, ke - kb), -1},
-          vt * 256);
+          vt * 256, wave, tid & 63);
   MnTile<256> lb;
   lb.init(Opnd{reinterpret_cast<const bf16*>(p.z) + (int64_t)kb * p.z_ld, p.z_ld, p.H, max(0, ke - kb), p.H},
-          ht * 256);
+          ht * 256, wave, tid & 63);
   Acc<256> acc;
   acc.zero();
   const int kl = (max(0, ke - kb) + BK - 1) / BK * BK;
-  core<256, true, true, 2>(acc, la, lb, kl, lds, tid);
+  core<256, true, 2>(acc, la, lb, kl, lds, tid);
 
-  const int lane = tid & 63, wave = tid >> 6, wr = wave >> 1, wc = wave & 1;
+  const int lane = tid & 63, wr = wave >> 1, wc = wave & 1;
   float* C = p.PW + (int64_t)split * p.V * p.H;
 #pragma unroll
   for (int j = 0; j < Acc<256>::WN; ++j) {
@@ -331,34 +411,36 @@ __global__ void __launch_bounds__(256) dz2_kernel(DzArgs p) {
     });
     Acc<128> acc;
     acc.zero();
-    core<128, false, false, 3>(acc, la, lb, (p.V_pad + BK - 1) / BK * BK, lds, tid);
+    core<128, false, 3>(acc, la, lb, (p.V_pad + BK - 1) / BK * BK, lds, tid);
 
-    // wave rows: 4 blocks of 32 rows = u_local ug*8 + wr*4 + i
+    // wave rows: 4 blocks of 32 rows = u_local ug*8 + wr*4 + i. Row
+    // 8(e>>2) + (e&3) of a block is wave-uniform, so each z load is a scalar
+    // row base plus one per-lane offset (4 (lane>>5) rows + column h).
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ul = ug * 8 + wr * 4 + i;
-      const bool uok = ul < tl.wu;
-      const int64_t zrow0 = (int64_t)(tile_row + ul * tl.htp + tl0);
+      if (ul >= tl.wu) continue;  // wave-uniform
+      const int zrow0 = tile_row + ul * tl.htp + tl0;
 #pragma unroll
       for (int j = 0; j < Acc<128>::WN; ++j) {
         const int h = h0 + wc * 64 + j * 32 + (lane & 31);
-        float lsum = 0.0f;
-        const bool ok = uok && h < p.H;
-        const bf16* zc = ok ? zb + zrow0 * p.z_ld + h : zb;  // clamped: loads are unconditional
+        const bool hok = h < p.H;
+        const int loff = 4 * (lane >> 5) * p.z_ld + (hok ? h : 0);
         float zv[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int trow = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          zv[e] = (float)zc[ok ? trow * p.z_ld : 0];
+          const bf16* zr = zb + (int64_t)(zrow0 + 8 * (e >> 2) + (e & 3)) * p.z_ld;
+          zv[e] = (float)zr[loff];
         }
+        float lsum = 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float ds = ok ? acc.c[i][j][e] * (1.0f - zv[e] * zv[e]) : 0.0f;
+          const float ds = hok ? acc.c[i][j][e] * (1.0f - zv[e] * zv[e]) : 0.0f;
           gacc[j][e] += ds;
           lsum += ds;
         }
         lsum += __shfl_xor(lsum, 32);
-        if (lane < 32 && uok && h < p.H)
+        if (lane < 32 && hok)
           p.PL[(((int64_t)slot * (p.tile_tp / 32) + s_local) * p.tile_u + ul) * p.H + h] = lsum;
       }
     }
@@ -479,9 +561,10 @@ hipError_t launch_zrow(const ZArgs& a, hipStream_t st) {
 template <bool BWD>
 __global__ void __launch_bounds__(256) scores_kernel(ScoresArgs p) {
   using namespace m3;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * KcTile<256>::BYTES];
-  __shared__ float cell[5][256];
-  __shared__ float bias_s[256];  // b^O of this V tile (0 past V)
+  constexpr int STAGES_BYTES = 2 * 2 * KcTile<256>::BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[STAGES_BYTES + 6 * 256 * 4];
+  float* cell = reinterpret_cast<float*>(lds + STAGES_BYTES);  // [5][256] per-cell coefficients
+  float* bias_l = cell + 5 * 256;  // b^O * log2(e) of this V tile; -1e30 past V
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), wr = wave >> 1, wc = wave & 1;
   const int nvt = (p.V + 255) / 256;
@@ -497,9 +580,9 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoresArgs p) {
 
   {
     const int v = vt * 256 + tid;
-    bias_s[tid] = v < p.V ? (float)bO[v] : 0.0f;
+    bias_l[tid] = v < p.V ? (float)bO[v] * kLog2e : -1e30f;
   }
-  // per-cell coefficients (backward) / validity
+  // per-cell coefficients (backward)
   if (BWD) {
     const int rr = c0 + tid;  // buffer row
     float ls = 0.0f, co = 0.0f, cb = 0.0f, cl = 0.0f, lab = -1.0f;
@@ -530,11 +613,11 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoresArgs p) {
         }
       }
     }
-    cell[0][tid] = ls * kLog2e;
-    cell[1][tid] = co;
-    cell[2][tid] = cb;
-    cell[3][tid] = cl;
-    cell[4][tid] = lab;
+    cell[0 * 256 + tid] = ls * kLog2e;
+    cell[1 * 256 + tid] = co;
+    cell[2 * 256 + tid] = cb;
+    cell[3 * 256 + tid] = cl;
+    cell[4 * 256 + tid] = lab;
   }
 
   KcTile<256> la;
@@ -549,40 +632,53 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoresArgs p) {
   });
   Acc<256> acc;
   acc.zero();
-  core<256, false, false, 2>(acc, la, lb, (p.H + BK - 1) / BK * BK, lds, tid);
+  core<256, false, 2>(acc, la, lb, (p.H + BK - 1) / BK * BK, lds, tid);
 
-  // lane columns: cells wc*128 + j*32 + (lane & 31); rows: scores
+  // Lane columns: cells wc*128 + j*32 + (lane & 31). Rows: scores
+  // acc_row(wr, i, e, lane); for fixed (i, e>>2) four consecutive rows, so the
+  // bias of a lane's 16 rows of block i is four 16-byte LDS reads. Rows past V
+  // carry a bias of -1e30 and drop out of the max and the sum.
+  auto bias_block = [&](int i, f32x4* bq) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      bq[g] = *reinterpret_cast<const f32x4*>(bias_l + wr * 128 + i * 32 + 8 * g + 4 * (lane >> 5));
+  };
   if (!BWD) {
+    // scaled scores y = (W^O z + b^O) log2(e); per cell max and sum of
+    // 2^(y - max), block by block (16 rows) with the running sum rescaled.
+    float my[4], sm[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { my[j] = -1e30f; sm[j] = 0.0f; }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 bq[4];
+      bias_block(i, bq);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float y[16];
+        float bm = my[j];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          y[e] = __builtin_fmaf(acc.c[i][j][e], kLog2e, bq[e >> 2][e & 3]);
+          bm = __builtin_fmaxf(bm, y[e]);
+        }
+        float bs = sm[j] * fexp2(my[j] - bm);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) bs += fexp2(y[e] - bm);
+        my[j] = bm;
+        sm[j] = bs;
+      }
+    }
     float mrow[4], srow[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float m = -1e30f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int vr = acc_row(wr, i, e, lane);
-          const float x = acc.c[i][j][e] + bias_s[vr];
-          m = (vt * 256 + vr < p.V) ? __builtin_fmaxf(m, x) : m;
-        }
-      const float ml = m * kLog2e;
-      float sm = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int vr = acc_row(wr, i, e, lane);
-          const float ex = fexp2(__builtin_fmaf(acc.c[i][j][e] + bias_s[vr], kLog2e, -ml));
-          sm += (vt * 256 + vr < p.V) ? ex : 0.0f;
-        }
       // combine with the other half-wave (same cells, other score rows)
-      const float m2 = __shfl_xor(m, 32), s2 = __shfl_xor(sm, 32);
-      const float mn = __builtin_fmaxf(m, m2);
-      sm = sm * fexp2((m - mn) * kLog2e) + s2 * fexp2((m2 - mn) * kLog2e);
+      const float m2 = __shfl_xor(my[j], 32), s2 = __shfl_xor(sm[j], 32);
+      const float mn = __builtin_fmaxf(my[j], m2);
+      srow[j] = sm[j] * fexp2(my[j] - mn) + s2 * fexp2(m2 - mn);
       mrow[j] = mn;
-      srow[j] = sm;
     }
-    // combine the two wave rows through LDS
+    // combine the two wave rows through LDS (stage buffers are free after the core)
     float* red = reinterpret_cast<float*>(lds);
     if (wr == 1 && lane < 32) {
 #pragma unroll
@@ -591,64 +687,77 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoresArgs p) {
         red[(wc * 4 + j) * 64 + 32 + lane] = srow[j];
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (wr == 0 && lane < 32) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float m2 = red[(wc * 4 + j) * 64 + lane], s2 = red[(wc * 4 + j) * 64 + 32 + lane];
         const float mn = __builtin_fmaxf(mrow[j], m2);
-        const float sm = srow[j] * fexp2((mrow[j] - mn) * kLog2e) + s2 * fexp2((m2 - mn) * kLog2e);
+        const float sv = srow[j] * fexp2(mrow[j] - mn) + s2 * fexp2(m2 - mn);
         const int rr = c0 + wc * 128 + j * 32 + lane;
-        if (rr < p.n_rows) p.stats[((int64_t)rr * nvt + vt)] = f32x2{mn, sm};
+        if (rr < p.n_rows) p.stats[((int64_t)rr * nvt + vt)] = f32x2{mn * kLn2, sv};
       }
     }
     if (p.logits) {  // untiled: keep the scores (bias included), 4 consecutive v per store
       bf16* lg = reinterpret_cast<bf16*>(p.logits);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rr = c0 + wc * 128 + j * 32 + (lane & 31);
-        if (rr >= p.n_rows) continue;
+      for (int i = 0; i < 4; ++i) {
+        f32x4 bq[4];
+        bias_block(i, bq);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) {
+          const int rr = c0 + wc * 128 + j * 32 + (lane & 31);
 #pragma unroll
-          for (int e4 = 0; e4 < 16; e4 += 4) {
-            const int v = vt * 256 + acc_row(wr, i, e4, lane);
-            if (v >= p.V_pad) continue;
+          for (int g = 0; g < 4; ++g) {
+            const int v = vt * 256 + acc_row(wr, i, 4 * g, lane);
             bf16x4 w;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              w[q] = (bf16)(v + q < p.V ? acc.c[i][j][e4 + q] + bias_s[v + q - vt * 256] : 0.0f);
-            *reinterpret_cast<bf16x4*>(lg + (int64_t)(rr + p.buf_row_base) * p.V_pad + v) = w;
+            for (int q = 0; q < 4; ++q) {
+              const float y = __builtin_fmaf(acc.c[i][j][4 * g + q], kLog2e, bq[g][q]) * kLn2;
+              w[q] = (bf16)(v + q < p.V ? y : 0.0f);
+            }
+            if (rr < p.n_rows && v < p.V_pad)
+              *reinterpret_cast<bf16x4*>(lg + (int64_t)(rr + p.buf_row_base) * p.V_pad + v) = w;
           }
+        }
       }
     }
   } else {
+    // dh = co 2^(y - lse log2 e) - cb [v = blank] - cl [v = label]
     bf16* dh = reinterpret_cast<bf16*>(p.dh);
+    float lsl[4], co[4], cb[4], cl[4];
+    int lab[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cc = wc * 128 + j * 32 + (lane & 31);
-      const int rr = c0 + cc;
-      if (rr >= p.n_rows) continue;
-      const float lsl = cell[0][cc], co = cell[1][cc], cb = cell[2][cc], cl = cell[3][cc];
-      const int lab = (int)cell[4][cc];
+      lsl[j] = cell[0 * 256 + cc];
+      co[j] = cell[1 * 256 + cc];
+      cb[j] = cell[2 * 256 + cc];
+      cl[j] = cell[3 * 256 + cc];
+      lab[j] = (int)cell[4 * 256 + cc];
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      f32x4 bq[4];
+      bias_block(i, bq);
 #pragma unroll
-        for (int e4 = 0; e4 < 16; e4 += 4) {
-          const int v = vt * 256 + acc_row(wr, i, e4, lane);
-          if (v >= p.V_pad) continue;
+      for (int j = 0; j < 4; ++j) {
+        const int rr = c0 + wc * 128 + j * 32 + (lane & 31);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int v = vt * 256 + acc_row(wr, i, 4 * g, lane);
           bf16x4 w;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int vv = v + q;
-            const float x = acc.c[i][j][e4 + q] + bias_s[vv - vt * 256];
-            float d = co * fexp2(__builtin_fmaf(x, kLog2e, -lsl));
-            d -= (vv == p.blank) ? cb : 0.0f;
-            d -= (vv == lab) ? cl : 0.0f;
-            w[q] = (bf16)(vv < p.V ? d : 0.0f);
+            float d = co[j] * fexp2(__builtin_fmaf(acc.c[i][j][4 * g + q], kLog2e, bq[g][q]) - lsl[j]);
+            d -= (vv == p.blank) ? cb[j] : 0.0f;
+            d -= (vv == lab[j]) ? cl[j] : 0.0f;
+            w[q] = (bf16)d;
           }
-          *reinterpret_cast<bf16x4*>(dh + (int64_t)rr * p.V_pad + v) = w;
+          if (rr < p.n_rows && v < p.V_pad) *reinterpret_cast<bf16x4*>(dh + (int64_t)rr * p.V_pad + v) = w;
         }
+      }
     }
   }
 }
