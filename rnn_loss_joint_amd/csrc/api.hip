@@ -46,6 +46,12 @@ rnnt_status fail(rnnt_status s, const std::string& msg) {
       return fail(RNNT_E_HIP, std::string(#call) + ": " + hipGetErrorString(e_));     \
   } while (0)
 
+#define RNNT_STATUS(call)              \
+  do {                                 \
+    rnnt_status s_ = (call);           \
+    if (s_ != RNNT_OK) return s_;      \
+  } while (0)
+
 rnnt_status to_dims(const rnnt_desc* desc, rnnt::Dims& d) {
   if (!desc) return fail(RNNT_E_INVALID, "desc is null");
   if (desc->dtype != RNNT_F32 && desc->dtype != RNNT_BF16) return fail(RNNT_E_INVALID, "unknown dtype");
@@ -103,6 +109,33 @@ rnnt_status upload(void* dst, const std::vector<char>& src, hipStream_t st) {
   RNNT_HIP(hipMemcpyAsync(dst, g_staging.host, src.size(), hipMemcpyHostToDevice, st));
   RNNT_HIP(hipEventRecord(g_staging.ev, st));
   g_staging.pending = true;
+  return RNNT_OK;
+}
+
+// ---------------------------------------------------------------- side stream
+// The bf16 backward runs dW^O (a split-K GEMM whose grid fills about three
+// quarters of the CUs) concurrently with the dz kernel, which reads the same
+// dh rows: fork from the caller's stream with an event, join back with
+// another. One default-priority stream per device, created on first use.
+struct Side {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+std::vector<Side> g_side;
+
+rnnt_status side_stream(Side*& out) {
+  int dev = 0;
+  RNNT_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  if ((int)g_side.size() <= dev) g_side.resize(dev + 1);
+  Side& sd = g_side[dev];
+  if (!sd.s) {
+    RNNT_HIP(hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking));
+    RNNT_HIP(hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming));
+    RNNT_HIP(hipEventCreateWithFlags(&sd.join, hipEventDisableTiming));
+  }
+  out = &sd;
   return RNNT_OK;
 }
 
@@ -309,8 +342,9 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
       z.tiles = sv.tiles;
       z.tile_begin = wv.tile_begin;
       z.tile_end = wv.tile_end;
-      z.row_begin = wv.row_begin;
-      z.n_rows = wrows;
+      z.strip_begin = wv.strip_begin;
+      z.n_strips = wv.strip_end - wv.strip_begin;
+      z.n_ug = (d.tile_u + 7) / 8;
       z.buf_row_base = base;
       z.U_len = sv.Ulen;
       z.labels = labels;
@@ -496,8 +530,9 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       z.tiles = sv.tiles;
       z.tile_begin = wv.tile_begin;
       z.tile_end = wv.tile_end;
-      z.row_begin = wv.row_begin;
-      z.n_rows = wrows;
+      z.strip_begin = wv.strip_begin;
+      z.n_strips = wv.strip_end - wv.strip_begin;
+      z.n_ug = (d.tile_u + 7) / 8;
       z.buf_row_base = buf_base;
       z.U_len = sv.Ulen;
       z.labels = labels;
@@ -512,8 +547,8 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       z.bO = bO;
       z.z = z_buf;
       z.z_ld = p.H_pad;
-      z.hb = at<float>(workspace, L.w_hb);
-      z.hy = at<float>(workspace, L.w_hy);
+      z.hb = nullptr;  // the backward needs z only
+      z.hy = nullptr;
       {
         ProfScope ps_("zrow", st);
         RNNT_HIP(rnnt::launch_zrow(z, st));
@@ -565,6 +600,38 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
         ProfScope ps_("joint_bwd", st);
         RNNT_HIP(rnnt::launch_joint(a, bf, true, st));
       }
+    }
+    // 7 (bf16). dW^O and db^O on the side stream, concurrent with 5 and 6
+    Side* side = nullptr;
+    if (bf) {
+      RNNT_STATUS(side_stream(side));
+      RNNT_HIP(hipEventRecord(side->fork, st));
+      RNNT_HIP(hipStreamWaitEvent(side->s, side->fork, 0));
+      rnnt::DwoArgs w{};
+      w.dh = dh_buf;
+      w.dh_ld = p.V_pad;
+      w.z = z_buf;
+      w.z_ld = p.H_pad;
+      w.V = d.V;
+      w.H = d.H;
+      w.K = wrows;
+      w.splits = p.s6;
+      w.k_per_split = ((wrows + p.s6 - 1) / p.s6 + 63) / 64 * 64;
+      w.PW = PW;
+      w.PB = PB;
+      {
+        ProfScope ps_("dWO_gemm", side->s);
+        RNNT_HIP(rnnt::launch_dwo(w, side->s));
+      }
+      {
+        ProfScope ps_("split_reduce", side->s);
+        RNNT_HIP(rnnt::launch_split_reduce(dWO, PW, (int64_t)d.V * d.H, p.s6, (int64_t)d.V * d.H, true, side->s));
+      }
+      {
+        ProfScope ps_("split_reduce", side->s);
+        RNNT_HIP(rnnt::launch_split_reduce(dbO, PB, d.V, p.s6, d.V, true, side->s));
+      }
+      RNNT_HIP(hipEventRecord(side->join, side->s));
     }
     // 5. dz, dtanh and per-tile sums
     {
@@ -630,34 +697,10 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
         RNNT_HIP(rnnt::launch_group_reduce(r, st));
       }
     }
-    // 7. dW^O and db^O
+    // 7. dW^O and db^O (fp32 path; the bf16 path joins the side stream)
     if (bf) {
-      rnnt::DwoArgs w{};
-      w.dh = dh_buf;
-      w.dh_ld = p.V_pad;
-      w.z = z_buf;
-      w.z_ld = p.H_pad;
-      w.V = d.V;
-      w.H = d.H;
-      w.K = wrows;
-      w.splits = p.s6;
-      w.k_per_split = ((wrows + p.s6 - 1) / p.s6 + 63) / 64 * 64;
-      w.PW = PW;
-      w.PB = PB;
-      {
-        ProfScope ps_("dWO_gemm", st);
-        RNNT_HIP(rnnt::launch_dwo(w, st));
-      }
-      {
-        ProfScope ps_("split_reduce", st);
-        RNNT_HIP(rnnt::launch_split_reduce(dWO, PW, (int64_t)d.V * d.H, p.s6, (int64_t)d.V * d.H, true, st));
-      }
-      {
-        ProfScope ps_("split_reduce", st);
-        RNNT_HIP(rnnt::launch_split_reduce(dbO, PB, d.V, p.s6, d.V, true, st));
-      }
-    } else
-    {
+      RNNT_HIP(hipStreamWaitEvent(st, side->join, 0));
+    } else {
       rnnt::GemmArgs g{};
       g.A = rnnt::Operand{dh_buf, p.V_pad, d.V, nullptr, 1, 0};
       g.B = rnnt::Operand{z_buf, z_ld, d.H, nullptr, 1, 0};  // z^T: k (row) contiguous

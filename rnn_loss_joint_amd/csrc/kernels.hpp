@@ -170,9 +170,9 @@ struct DwoArgs {  // dW^O = dh^T z (split-K partials), db^O from a column of one
 hipError_t launch_dwo(const DwoArgs& a, hipStream_t st);
 hipError_t launch_dz2(const DzArgs& a, hipStream_t st);
 
-struct ZArgs {  // z rows and the blank / label scores for a range of rows
+struct ZArgs {  // z rows and (hb != null) the blank / label scores of a wave's strips
   const Tile* tiles;
-  int tile_begin, tile_end, row_begin, n_rows, buf_row_base;
+  int tile_begin, tile_end, strip_begin, n_strips, n_ug, buf_row_base;
   const int32_t* U_len;
   const int32_t* labels;
   int T, U1, H, H_pad, blank;

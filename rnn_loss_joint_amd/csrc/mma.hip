@@ -480,73 +480,111 @@ hipError_t launch_dz2(const DzArgs& a, hipStream_t st) {
 }
 
 // ============================================================================ z and the two scores
-// One workgroup per 32-row chunk (32 consecutive t at one u of one tile):
-// z[row, k] = bf16(tanh(a[b,t,k] + l[b,u,k])) for k < H (0 up to H_pad and on
-// padding rows), and the blank / label scores of the row as dot products of
-// that bf16 z with the two W^O rows (plus the biases).
+// One workgroup per (32-t strip of a tile, group of 8 u values): thread
+// (tt, q) = (tid / 8, tid % 8) owns t = strip start + tt and the 8-wide k
+// chunks q, q+8, ...; each chunk of a[b, t] is loaded once and combined with
+// the group's 8 rows of l. Writes z[row, k] = bf16(tanh(a + l)) for k < H (0
+// up to z_ld and on padding rows t >= t0 + ht) and, with SCORES, the blank
+// and label scores of each row as dot products of that bf16 z with the two
+// W^O rows (plus the biases).
+template <bool SCORES>
 __global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
   const int tid = threadIdx.x;
-  const int R0 = p.row_begin + blockIdx.x * 32;
+  const int ug = blockIdx.x % p.n_ug;
+  const int strip = p.strip_begin + blockIdx.x / p.n_ug;
   int lo = p.tile_begin, hi = p.tile_end - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
-    if (p.tiles[mid].row0 <= R0) lo = mid; else hi = mid - 1;
+    if (p.tiles[mid].strip0 <= strip) lo = mid; else hi = mid - 1;
   }
   const Tile tl = p.tiles[lo];
-  const int local = R0 - tl.row0;
-  const int ul = local / tl.htp;
-  const int tloc = local - ul * tl.htp;
-  const int b = tl.b, u = tl.u0 + ul;
-  const int Ub = p.U_len[b];
-  const int r = tid >> 3, q = tid & 7;  // row within the chunk, k slice
-  const bool row_ok = tloc + r < tl.ht;
-  const int t = tl.t0 + tloc + r;
-  const int lab = u < Ub ? p.labels[(size_t)b * p.U1 + u + 1] : -1;
+  const int u_first = ug * 8;
+  if (u_first >= tl.wu) return;  // workgroup-uniform
+  const int nu = min(8, tl.wu - u_first);
+  const int tt = tid >> 3, q = tid & 7;
+  const int tloc = (strip - tl.strip0) * 32 + tt;
+  const bool row_ok = tloc < tl.ht;
+  const int b = tl.b;
+  const int u0 = tl.u0 + u_first;
+  const float* arow = p.a + ((size_t)b * p.T + tl.t0 + (row_ok ? tloc : 0)) * p.H_pad;
+  const float* lrow0 = p.l + ((size_t)b * p.U1 + u0) * p.H_pad;
+  const int64_t row0 = (int64_t)tl.row0 - p.buf_row_base + (int64_t)u_first * tl.htp + tloc;
+  bf16* zb = reinterpret_cast<bf16*>(p.z);
   const bf16* WO = reinterpret_cast<const bf16*>(p.WO);
   const bf16* bO = reinterpret_cast<const bf16*>(p.bO);
-  const float* arow = p.a + ((size_t)b * p.T + (row_ok ? t : 0)) * p.H_pad;
-  const float* lrow = p.l + ((size_t)b * p.U1 + u) * p.H_pad;
-  bf16* zrow = reinterpret_cast<bf16*>(p.z) + (int64_t)(R0 - p.buf_row_base + r) * p.z_ld;
-  const bf16* wb = WO + (size_t)p.blank * p.H;
-  const bf16* wy = WO + (size_t)(lab >= 0 ? lab : 0) * p.H;
-  float hb = 0.0f, hy = 0.0f;
-  for (int k = q * 8; k < p.z_ld; k += 64) {
-    bf16x8 z;
-    if (row_ok && k < p.H) {
-      f32x4 a0 = ldg<f32x4>(arow + k), a1 = ldg<f32x4>(arow + k + 4);
-      f32x4 l0 = ldg<f32x4>(lrow + k), l1 = ldg<f32x4>(lrow + k + 4);
+
+  float hb[8], hy[8];
+  int lab[8];
+  if constexpr (SCORES) {
+    const int Ub = p.U_len[b];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        z[e] = (bf16)tanh_fast(a0[e] + l0[e]);
-        z[e + 4] = (bf16)tanh_fast(a1[e] + l1[e]);
-      }
-      bf16x8 xb = ldg<bf16x8>(wb + k), xy = ldg<bf16x8>(wy + k);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        hb = __builtin_fmaf((float)z[e], (float)xb[e], hb);
-        hy = __builtin_fmaf((float)z[e], (float)xy[e], hy);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) z[e] = (bf16)0.0f;
+    for (int uu = 0; uu < 8; ++uu) {
+      hb[uu] = 0.0f;
+      hy[uu] = 0.0f;
+      lab[uu] = (uu < nu && u0 + uu < Ub) ? p.labels[(size_t)b * p.U1 + u0 + uu + 1] : -1;
     }
-    *reinterpret_cast<bf16x8*>(zrow + k) = z;
   }
+  const bf16* wb = WO + (size_t)p.blank * p.H;
+  for (int k = q * 8; k < p.z_ld; k += 64) {
+    const bool kok = row_ok && k < p.H;
+    f32x4 a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
+    bf16x8 xb;
+    if (kok) {
+      a0 = ldg<f32x4>(arow + k);
+      a1 = ldg<f32x4>(arow + k + 4);
+      if constexpr (SCORES) xb = ldg<bf16x8>(wb + k);
+    }
 #pragma unroll
-  for (int off = 1; off < 8; off <<= 1) {
-    hb += __shfl_xor(hb, off);
-    hy += __shfl_xor(hy, off);
+    for (int uu = 0; uu < 8; ++uu) {
+      if (uu >= nu) continue;  // workgroup-uniform
+      bf16x8 z;
+      if (kok) {
+        const float* lrow = lrow0 + (size_t)uu * p.H_pad;
+        const f32x4 l0 = ldg<f32x4>(lrow + k), l1 = ldg<f32x4>(lrow + k + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          z[e] = (bf16)tanh_fast(a0[e] + l0[e]);
+          z[e + 4] = (bf16)tanh_fast(a1[e] + l1[e]);
+        }
+        if constexpr (SCORES) {
+          const bf16x8 xy = ldg<bf16x8>(WO + (size_t)(lab[uu] >= 0 ? lab[uu] : 0) * p.H + k);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            hb[uu] = __builtin_fmaf((float)z[e], (float)xb[e], hb[uu]);
+            hy[uu] = __builtin_fmaf((float)z[e], (float)xy[e], hy[uu]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = (bf16)0.0f;
+      }
+      *reinterpret_cast<bf16x8*>(zb + (row0 + (int64_t)uu * tl.htp) * p.z_ld + k) = z;
+    }
   }
-  if (q == 0) {
-    const int rr = R0 - p.buf_row_base + r;
-    p.hb[rr] = hb + (float)bO[p.blank];
-    p.hy[rr] = lab >= 0 ? hy + (float)bO[lab] : 0.0f;
+  if constexpr (SCORES) {
+    const float bb = (float)bO[p.blank];
+#pragma unroll
+    for (int uu = 0; uu < 8; ++uu) {
+      float vb = hb[uu], vy = hy[uu];
+#pragma unroll
+      for (int off = 1; off < 8; off <<= 1) {
+        vb += __shfl_xor(vb, off);
+        vy += __shfl_xor(vy, off);
+      }
+      if (q == 0 && uu < nu) {
+        const int64_t rr = row0 + (int64_t)uu * tl.htp;
+        p.hb[rr] = vb + bb;
+        p.hy[rr] = lab[uu] >= 0 ? vy + (float)bO[lab[uu]] : 0.0f;
+      }
+    }
   }
 }
 
 hipError_t launch_zrow(const ZArgs& a, hipStream_t st) {
-  if (a.n_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(zrow_kernel, dim3(a.n_rows / 32), dim3(256), 0, st, a);
+  if (a.n_strips == 0) return hipSuccess;
+  dim3 grid(a.n_strips * a.n_ug), block(256);
+  if (a.hb) hipLaunchKernelGGL(zrow_kernel<true>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(zrow_kernel<false>, grid, block, 0, st, a);
   return hipGetLastError();
 }
 

@@ -182,12 +182,15 @@ void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H
     p.max_wave_rows = (int)std::max<int64_t>(p.max_wave_rows, bound_tiles * p.tile_tp * d.tile_u);
     p.max_wave_tiles = (int)std::max<int64_t>(p.max_wave_tiles, bound_tiles);
   }
-  // split-K counts: dW^O ~1024 workgroups of 128 x 128 (fp32 path) or ~256
-  // of 256 x 256 (bf16 path); dW^A / dW^L ~512
+  // split-K counts: dW^O ~1024 workgroups of 128 x 128 (fp32 path); in the
+  // bf16 path all output tiles of one split run on one XCD (32 CUs, the
+  // split's dh and z rows shared in its L2), as many whole splits per XCD as
+  // fit, one round (the dz kernel runs beside it); dW^A / dW^L ~512
   p.nvt = (int)cdiv(d.V, 256);
   if (d.bf16) {
     int64_t tiles_vh = cdiv(d.V, 256) * cdiv(d.H + 1, 256);
-    p.s6 = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(256, tiles_vh), p.max_wave_rows / 4096));
+    int64_t per_xcd = std::max<int64_t>(1, 32 / tiles_vh);
+    p.s6 = (int)std::max<int64_t>(1, std::min<int64_t>(8 * per_xcd, p.max_wave_rows / 4096));
   } else {
     int64_t tiles_vh = cdiv(d.V, 128) * cdiv(d.H, 128);
     p.s6 = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(1024, tiles_vh), p.max_wave_rows / 2048));
