@@ -52,6 +52,10 @@ rnnt_status fail(rnnt_status s, const std::string& msg) {
     if (s_ != RNNT_OK) return s_;      \
   } while (0)
 
+// The persistent score kernels need at least 8 stages of 64 k per item
+// (the previous item's epilogue runs in the first five).
+bool use_scores3(const rnnt::Plan& p) { return p.d.bf16 && !p.d.untiled && p.H_pad / 64 >= 8; }
+
 rnnt_status to_dims(const rnnt_desc* desc, rnnt::Dims& d) {
   if (!desc) return fail(RNNT_E_INVALID, "desc is null");
   if (desc->dtype != RNNT_F32 && desc->dtype != RNNT_BF16) return fail(RNNT_E_INVALID, "unknown dtype");
@@ -335,6 +339,12 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
     auto* stats = at<rnnt::f32x2>(workspace, L.w_stats);
     float* hb = at<float>(workspace, L.w_hb);
     float* hy = at<float>(workspace, L.w_hy);
+    const bool s3 = use_scores3(p);
+    if (s3) {
+      ProfScope ps_("score_tables", st);
+      RNNT_HIP(rnnt::launch_score_tables(WO, bO, at<char>(workspace, L.w_WOp), at<float>(workspace, L.w_bl), d.V,
+                                         d.H, p.H_pad, p.nvt, st));
+    }
     for (const rnnt::WaveInfo& wv : p.waves) {
       const int wrows = wv.row_end - wv.row_begin;
       const int base = d.untiled ? 0 : wv.row_begin;  // buffer row = global row - base
@@ -384,7 +394,23 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
       sc.z_ld = p.H_pad;
       sc.stats = stats;
       sc.logits = d.untiled ? sv.logits : nullptr;
-      {
+      if (s3) {
+        rnnt::Scores3Args a3{};
+        a3.n_rows = wrows;
+        a3.n_ct = (wrows + 127) / 128;
+        a3.V = d.V;
+        a3.H_pad = p.H_pad;
+        a3.V_pad = p.V_pad;
+        a3.nvt = p.nvt;
+        a3.blank = d.blank;
+        a3.WOp = at<char>(workspace, L.w_WOp);
+        a3.bl = at<float>(workspace, L.w_bl);
+        a3.z = sc.z;
+        a3.z_ld = p.H_pad;
+        a3.stats = stats;
+        ProfScope ps_("scores_fwd", st);
+        RNNT_HIP(rnnt::launch_scores3(a3, false, st));
+      } else {
         ProfScope ps_("scores_fwd", st);
         RNNT_HIP(rnnt::launch_scores(sc, false, st));
       }
@@ -473,6 +499,12 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
   {
     ProfScope ps_("transpose_wo", st);
     RNNT_HIP(rnnt::launch_transpose_wo(WOT, WO, d.V, d.H, p.V_pad, bf, st));
+  }
+  const bool s3 = use_scores3(p);
+  if (s3) {
+    ProfScope ps_("score_tables", st);
+    RNNT_HIP(rnnt::launch_score_tables(WO, bO, at<char>(workspace, L.w_WOp), at<float>(workspace, L.w_bl), d.V, d.H,
+                                       p.H_pad, p.nvt, st));
   }
 
   {
@@ -581,7 +613,51 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       sc.beta = sv.beta;
       sc.lnP = sv.lnP;
       sc.dcosts = dcosts;
-      {
+      if (s3) {
+        rnnt::Scores3Args a3{};
+        a3.tiles = sv.tiles;
+        a3.tile_begin = wv.tile_begin;
+        a3.tile_end = wv.tile_end;
+        a3.n_rows = wrows;
+        a3.n_ct = (wrows + 127) / 128;
+        a3.buf_row_base = wv.row_begin;
+        a3.T_len = sv.Tlen;
+        a3.U_len = sv.Ulen;
+        a3.labels = labels;
+        a3.T = d.T;
+        a3.U1 = p.U1;
+        a3.V = d.V;
+        a3.H_pad = p.H_pad;
+        a3.V_pad = p.V_pad;
+        a3.nvt = p.nvt;
+        a3.blank = d.blank;
+        a3.WOp = at<char>(workspace, L.w_WOp);
+        a3.bl = at<float>(workspace, L.w_bl);
+        a3.z = z_buf;
+        a3.z_ld = p.H_pad;
+        a3.dh = dh_buf;
+        a3.coefA = at<char>(workspace, L.w_coefA);
+        a3.coefB = at<char>(workspace, L.w_coefB);
+        a3.lse = sv.lse;
+        a3.phi = sv.phi;
+        a3.psi = sv.psi;
+        a3.alpha = sv.alpha;
+        a3.beta = sv.beta;
+        a3.lnP = sv.lnP;
+        a3.dcosts = dcosts;
+        {
+          ProfScope ps_("coef", st);
+          RNNT_HIP(rnnt::launch_coef(a3, st));
+        }
+        {
+          ProfScope ps_("scores_bwd", st);
+          RNNT_HIP(rnnt::launch_scores3(a3, true, st));
+        }
+        {
+          ProfScope ps_("dh_fix", st);
+          RNNT_HIP(rnnt::launch_dh_fix(a3, st));
+        }
+      } else {
         ProfScope ps_("scores_bwd", st);
         RNNT_HIP(rnnt::launch_scores(sc, true, st));
       }

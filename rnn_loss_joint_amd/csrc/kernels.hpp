@@ -211,6 +211,38 @@ struct ScoresArgs {  // scores^T tiles: forward statistics or backward dh
 };
 hipError_t launch_scores(const ScoresArgs& a, bool bwd, hipStream_t st);
 
+// Persistent 256-score x 128-cell tiles of the bf16 tiled path (one wave of
+// tiles): forward (max, sum) statistics or backward dh without the blank /
+// label terms; coef_kernel fills coefA / coefB, dh_fix subtracts the terms.
+struct Scores3Args {
+  const Tile* tiles;
+  int tile_begin, tile_end, n_rows, n_ct, buf_row_base;  // n_ct = ceil(n_rows / 128)
+  const int32_t* T_len;
+  const int32_t* U_len;
+  const int32_t* labels;
+  int T, U1, V, H_pad, V_pad, nvt, blank;
+  const void* WOp;   // [nvt*256][H_pad] bf16, zero-padded W^O
+  const float* bl;   // [nvt*256] b^O log2 e, -1e30 past V
+  const void* z;     // [n_ct*128][z_ld] bf16
+  int64_t z_ld;
+  f32x2* stats;      // forward: [n_ct*128][nvt]
+  void* dh;          // backward: [n_ct*128][V_pad] bf16
+  void* coefA;       // [n_ct*128] (lse log2 e, occupancy)
+  void* coefB;       // [n_ct*128] (cb, cl, label, 0)
+  const float* lse;
+  const float* phi;
+  const float* psi;
+  const float* alpha;
+  const float* beta;
+  const float* lnP;
+  const float* dcosts;
+};
+hipError_t launch_scores3(const Scores3Args& a, bool bwd, hipStream_t st);
+hipError_t launch_score_tables(const void* WO, const void* bO, void* WOp, float* bl, int V, int H, int H_pad,
+                               int nvt, hipStream_t st);
+hipError_t launch_coef(const Scores3Args& a, hipStream_t st);
+hipError_t launch_dh_fix(const Scores3Args& a, hipStream_t st);
+
 struct MergeArgs {
   const Tile* tiles;
   int tile_begin, tile_end, n_rows, buf_row_base, nvt;

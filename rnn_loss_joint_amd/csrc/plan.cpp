@@ -81,7 +81,8 @@ void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H
   p.d = d;
   p.U1 = d.U + 1;
   p.H_pad = H_pad;
-  p.V_pad = (int)cdiv(d.V, 64) * 64;
+  // bf16: whole 256-score tiles (the score kernels write every column of dh)
+  p.V_pad = d.bf16 ? (int)cdiv(d.V, 256) * 256 : (int)cdiv(d.V, 64) * 64;
   p.KS = H_pad / 16;
   p.tile_tp = (int)cdiv(d.tile_t, 32) * 32;
 
@@ -235,9 +236,11 @@ Layout make_layout(const Plan& p) {
 
   o = 0;
   L.w_dh = L.w_z = 0;
+  // wave buffers hold whole 128-row cell tiles (rows past the wave are scratch)
+  const size_t wrows = (size_t)cdiv(p.max_wave_rows, 128) * 128;
   if (!d.untiled) {
-    L.w_dh = take(ct * (size_t)p.max_wave_rows * p.V_pad);
-    L.w_z = take(ct * (size_t)p.max_wave_rows * p.H_pad);  // z^T [H_pad, max_wave_rows]
+    L.w_dh = take(ct * wrows * p.V_pad);
+    L.w_z = take(ct * wrows * p.H_pad);  // bf16: z rows; fp32: z^T [H_pad, max_wave_rows]
   }
   L.w_gA = take(sizeof(float) * (size_t)d.B * d.T * d.H);
   L.w_gL = take(sizeof(float) * (size_t)d.B * p.U1 * d.H);
@@ -250,11 +253,19 @@ Layout make_layout(const Plan& p) {
   L.w_PWL = take(sizeof(float) * (size_t)p.s7l * d.H * d.HL);
   L.w_WOT = take(ct * (size_t)d.H * p.V_pad);
   // bf16 forward buffers, one wave of rows (all rows in untiled mode)
-  const size_t frows = d.untiled ? (size_t)p.total_rows : (size_t)p.max_wave_rows;
+  const size_t frows = d.untiled ? (size_t)p.total_rows : wrows;
   L.w_zf = 0;  // the tiled forward's z rows reuse the backward's z buffer (w_z)
   L.w_stats = d.bf16 ? take(8 * frows * p.nvt) : 0;
   L.w_hb = d.bf16 ? take(4 * frows) : 0;
   L.w_hy = d.bf16 ? take(4 * frows) : 0;
+  // persistent score kernels (bf16, tiled): padded W^O, bias table, cell coefficients
+  L.w_WOp = L.w_bl = L.w_coefA = L.w_coefB = 0;
+  if (d.bf16 && !d.untiled) {
+    L.w_WOp = take(2 * (size_t)p.nvt * 256 * p.H_pad);
+    L.w_bl = take(4 * (size_t)p.nvt * 256);
+    L.w_coefA = take(8 * wrows);
+    L.w_coefB = take(16 * wrows);
+  }
   L.workspace_bytes = o;
   return L;
 }

@@ -1,0 +1,477 @@
+// Persistent score-tile kernels of the bf16 tiled path, and their helpers.
+//
+// The output projection h = W^O z + b^O ("Neural transducer training ...",
+// section "Transducer training", Eq. (4)) is computed transposed, 256 scores
+// (rows) x 128 lattice cells (columns) per work item, so each lane holds whole
+// cells and the reductions over the vocabulary stay lane-local:
+//   forward : per cell and 256-score slice, (max, sum 2^(y - max)) of the
+//             scaled scores y = (W^O z + b^O) log2 e (the log-softmax
+//             denominator of Eq. (5) in pieces, merged afterwards);
+//   backward: dh = occupancy * softmax (Eq. (10) without the blank / label
+//             terms, which a separate pass subtracts) written as bf16.
+//
+// One workgroup per CU (256 threads, 4 waves of 128 x 64 outputs) walks its
+// list of items; the A operand (a 256-row slice of a zero-padded copy of
+// W^O) and the B operand (128 rows of z) move global -> LDS by dma in three
+// 48 KB stages. The epilogue of item n runs inside the first five stages of
+// item n+1, a few VALU instructions after each MFMA, on the second of two
+// accumulator sets, so exp2 and the other vector work overlap the matrix
+// cores. Per-item bias and cell coefficients arrive by dma with the stages.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mfma_core.hpp"
+
+namespace rnnt {
+namespace s3 {
+
+constexpr int BN = 128;  // cells per item
+constexpr int BK = 64;
+constexpr int NST = 3;   // stages in flight
+constexpr int A_BYTES = 256 * BK * 2;
+constexpr int B_BYTES = BN * BK * 2;
+constexpr int STAGE = A_BYTES + B_BYTES;
+constexpr int NDA = A_BYTES / (256 * 16);  // 16-byte dma per thread per stage
+constexpr int NDB = B_BYTES / (256 * 16);
+constexpr int OFF_BIAS = NST * STAGE;              // [2][256] f32: b^O log2 e
+constexpr int OFF_COEF = OFF_BIAS + 2 * 256 * 4;   // [2][128][2] f32: (lse log2 e, occupancy)
+constexpr int OFF_RED = OFF_COEF + 2 * 256 * 4;    // [2 wc][2 j][2][32] f32
+constexpr int LDS_BYTES = OFF_RED + 2 * 2 * 2 * 32 * 4;
+constexpr int WM = 4, WN = 2;  // 32 x 32 blocks per wave
+constexpr int EPI_STAGES = 5;  // stages of item n+1 that carry the epilogue of item n
+static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ inline void dma_b128(const char* g, char* l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g, (lds_void*)l, 16, 0, 0);
+}
+__device__ inline void dma_b32(const char* g, char* l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g, (lds_void*)l, 4, 0, 0);
+}
+
+}  // namespace s3
+
+template <bool BWD>
+__global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
+  using namespace s3;
+  using m3::lds_barrier;
+  using m3::wait_vm;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int r = lane & 31, g = lane >> 5;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int nvt = p.nvt, nq = p.H_pad / BK;
+  // items (ct, vt): cell tiles ct = 8 ctl + xcd of this XCD, all V tiles of a
+  // cell tile on neighbouring slots (their z rows shared in L2)
+  const int nctl = (p.n_ct - xcd + 7) / 8;
+  const int n_items = max(0, (nctl * nvt - slot + 31) / 32);
+  if (n_items == 0) return;
+  constexpr int ND = NDA + NDB + (BWD ? 2 : 1);  // dma per thread per stage
+
+  // Per-thread dma source offsets (bytes). Instruction d moves rows
+  // 32 d + 8 wave + lane/8 (8 rows x 8 chunks of 16 bytes); the chunk swizzle
+  // of those rows depends only on d & 1, so two offsets per operand plus a
+  // uniform 32 d rows address every instruction.
+  uint32_t offA[2], offB[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = (i * 4 + wave) * 8 + (lane >> 3);
+    offA[i] = (uint32_t)(row * p.H_pad * 2 + (((lane & 7) ^ swz(row)) << 4));
+    offB[i] = (uint32_t)(row * (int)p.z_ld * 2 + (((lane & 7) ^ swz(row)) << 4));
+  }
+  const int64_t stepA = (int64_t)32 * p.H_pad * 2, stepB = (int64_t)32 * p.z_ld * 2;
+  // Fragment reads: row wr*128 + 32 f + r of A (wc*64 + 32 f + r of B), chunk
+  // (2 ss + g) ^ swz(row); swz(row) = s0 ^ 4 (f & 1) with s0 = swz(r), so the
+  // per-lane part is rb + (c0[ss] ^ 64 (f & 1)) and 4096 f is an immediate.
+  const int s0 = swz(r);
+  const uint32_t rbA = (uint32_t)((wr * 128 + r) * 128), rbB = (uint32_t)(A_BYTES + (wc * 64 + r) * 128);
+  const char* WOp = reinterpret_cast<const char*>(p.WOp);
+  const char* zb = reinterpret_cast<const char*>(p.z);
+  const char* blt = reinterpret_cast<const char*>(p.bl);
+  const char* cft = reinterpret_cast<const char*>(p.coefA);
+
+  auto item_of = [&](int n, int& ct, int& vt) {
+    n = min(n, n_items - 1);
+    const int idx = slot + 32 * n;
+    const int ctl = idx / nvt;
+    vt = idx - ctl * nvt;
+    ct = ctl * 8 + xcd;
+  };
+  struct Src {
+    const char *a, *b, *bias, *coef;
+    char* st;
+    int par;
+  };
+  auto stage_src = [&](int S) {
+    const int n = S / nq, q = S - (S / nq) * nq;
+    int ct, vt;
+    item_of(n, ct, vt);
+    Src s;
+    s.a = WOp + ((int64_t)vt * 256 * p.H_pad + q * BK) * 2;
+    s.b = zb + ((int64_t)ct * BN * p.z_ld + q * BK) * 2;
+    s.bias = blt + (int64_t)vt * 256 * 4;
+    s.coef = cft + (int64_t)ct * BN * 8;
+    s.st = lds + (S % NST) * STAGE;
+    s.par = min(n, n_items - 1) & 1;
+    return s;
+  };
+  auto issue_one = [&](const Src& s, int d) {
+    if (d < NDA) s3::dma_b128(s.a + (d >> 1) * 2 * stepA + offA[d & 1], s.st + (d * 4 + wave) * 1024);
+    else if (d < NDA + NDB)
+      s3::dma_b128(s.b + ((d - NDA) >> 1) * 2 * stepB + offB[(d - NDA) & 1], s.st + A_BYTES + ((d - NDA) * 4 + wave) * 1024);
+    else if (d == NDA + NDB) s3::dma_b32(s.bias + tid * 4, lds + OFF_BIAS + s.par * 1024 + wave * 256);
+    else s3::dma_b32(s.coef + tid * 4, lds + OFF_COEF + s.par * 1024 + wave * 256);
+  };
+  auto read_frag = [&](int f, const char* st, int ss, bf16x8* a, bf16x8* b) {
+    const uint32_t c0 = (uint32_t)((((2 * ss + g) ^ s0) << 4));
+    if (f < WM) {
+      const uint32_t o = rbA + (c0 ^ (uint32_t)(64 * (f & 1)));
+      a[f] = *reinterpret_cast<const bf16x8*>(st + o + 4096 * f);
+    } else {
+      const int fb = f - WM;
+      const uint32_t o = rbB + (c0 ^ (uint32_t)(64 * (fb & 1)));
+      b[fb] = *reinterpret_cast<const bf16x8*>(st + o + 4096 * fb);
+    }
+  };
+
+  f32x16 acc[2][WM][WN];
+  bf16x8 af[2][WM], bfr[2][WN];
+
+  // ---------------------------------------------------------------- epilogue state
+  // The item being finalized: its cell tile, V tile and parity (LDS buffers).
+  int e_ct = 0, e_vt = 0, e_par = 0;
+  bool e_live = false;
+  // forward: running (max, sum) per column block j; backward: (lse log2 e,
+  // occupancy) per column block
+  float em[2], es[2];
+  float y[16];
+  float ebm = 0.0f;
+  f32x4 bq[4];
+  float* stats2 = reinterpret_cast<float*>(p.stats);
+  bf16* dh = reinterpret_cast<bf16*>(p.dh);
+
+  // One chunk (issued after one MFMA) of epilogue task T on accumulator set E.
+  auto epi_chunk = [&](auto EE, auto TT, auto XX) __attribute__((always_inline)) {
+    constexpr int E = decltype(EE)::value;
+    constexpr int T = decltype(TT)::value;
+    constexpr int X = decltype(XX)::value;
+    const float* bias = reinterpret_cast<const float*>(lds + OFF_BIAS + e_par * 1024);
+    if constexpr (!BWD) {
+      if constexpr (T < 16) {
+        constexpr int b = T >> 1, i = b >> 1, j = b & 1;
+        if constexpr ((T & 1) == 0) {
+          // task A(b): scaled scores of block (i, j) and their max
+          if constexpr (X == 0) {
+            if constexpr (j == 0) {
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4)
+                bq[q4] = *reinterpret_cast<const f32x4*>(bias + wr * 128 + i * 32 + 8 * q4 + 4 * g);
+            }
+            if constexpr (b < 2) {
+              em[j] = -1e30f;
+              es[j] = 0.0f;
+            }
+            ebm = em[j];
+          }
+#pragma unroll
+          for (int e = 2 * X; e < 2 * X + 2; ++e) {
+            y[e] = __builtin_fmaf(acc[E][i][j][e], kLog2e, bq[e >> 2][e & 3]);
+            ebm = __builtin_fmaxf(ebm, y[e]);
+          }
+        } else {
+          // task B(b): fold 2^(y - max) into the running sum
+          if constexpr (X == 0) es[j] *= fexp2(em[j] - ebm);
+          es[j] += fexp2(y[2 * X] - ebm) + fexp2(y[2 * X + 1] - ebm);
+          if constexpr (X == 7) em[j] = ebm;
+        }
+      } else if constexpr (T == 16 && X == 0) {
+        // combine the two half-waves (same cells, other score rows); wave row 1 -> LDS
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float m2 = __shfl_xor(em[j], 32), s2 = __shfl_xor(es[j], 32);
+          const float mn = __builtin_fmaxf(em[j], m2);
+          es[j] = es[j] * fexp2(em[j] - mn) + s2 * fexp2(m2 - mn);
+          em[j] = mn;
+        }
+        float* red = reinterpret_cast<float*>(lds + OFF_RED);
+        if (wr == 1 && lane < 32) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            red[((wc * 2 + j) * 2 + 0) * 32 + lane] = em[j];
+            red[((wc * 2 + j) * 2 + 1) * 32 + lane] = es[j];
+          }
+        }
+      } else if constexpr (T == 19 && X == 0) {
+        // after the stage barrier: wave row 0 merges and stores (max ln 2, sum)
+        const float* red = reinterpret_cast<const float*>(lds + OFF_RED);
+        if (wr == 0 && lane < 32 && e_live) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float m2 = red[((wc * 2 + j) * 2 + 0) * 32 + lane];
+            const float s2 = red[((wc * 2 + j) * 2 + 1) * 32 + lane];
+            const float mn = __builtin_fmaxf(em[j], m2);
+            const float sv = es[j] * fexp2(em[j] - mn) + s2 * fexp2(m2 - mn);
+            const int64_t rr = (int64_t)e_ct * BN + wc * 64 + j * 32 + lane;
+            *reinterpret_cast<f32x2*>(stats2 + 2 * (rr * nvt + e_vt)) = f32x2{mn * kLn2, sv};
+          }
+        }
+      }
+    } else {
+      if constexpr (T == 0 && X == 0) {
+        const float* cf = reinterpret_cast<const float*>(lds + OFF_COEF + e_par * 1024);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const f32x2 c = *reinterpret_cast<const f32x2*>(cf + 2 * (wc * 64 + j * 32 + r));
+          em[j] = c[0];
+          es[j] = c[1];
+        }
+      } else if constexpr (T >= 1 && T < 17) {
+        // block b = (T-1)/2, half hh: elements 8 hh + X; dh = co 2^(y - lse log2 e)
+        constexpr int b = (T - 1) >> 1, hh = (T - 1) & 1, i = b >> 1, j = b & 1;
+        if constexpr (X == 0 && hh == 0 && j == 0) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            bq[q4] = *reinterpret_cast<const f32x4*>(bias + wr * 128 + i * 32 + 8 * q4 + 4 * g);
+        }
+        constexpr int e = 8 * hh + X;
+        y[e] = es[j] * fexp2(__builtin_fmaf(acc[E][i][j][e], kLog2e, bq[e >> 2][e & 3]) - em[j]);
+        if constexpr (X == 3 || X == 7) {
+          constexpr int e4 = e - 3;
+          bf16x4 w;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) w[q] = (bf16)y[e4 + q];
+          if (e_live) {
+            const int64_t rr = (int64_t)e_ct * BN + wc * 64 + j * 32 + r;
+            const int v = e_vt * 256 + wr * 128 + i * 32 + 8 * (e4 >> 2) + 4 * g;
+            *reinterpret_cast<bf16x4*>(dh + rr * p.V_pad + v) = w;
+          }
+        }
+      }
+    }
+  };
+
+  // One k-step: MFMAs on register buffer CB into accumulator set C (ZERO:
+  // first k-step of an item), fragments of (rd_st, rd_ss) into buffer CB^1,
+  // optionally the dma of stage dma_s, and epilogue task T on set C^1
+  // (T < 0: none).
+  auto kstep = [&](auto CB, auto CC, auto ZERO, auto TT, const char* rd_st, int rd_ss, bool dma,
+                   int dma_s) __attribute__((always_inline)) {
+    constexpr int cb = decltype(CB)::value;
+    constexpr int C = decltype(CC)::value;
+    constexpr bool zero = decltype(ZERO)::value;
+    constexpr int T = decltype(TT)::value;
+    Src ds{};
+    if (dma) ds = stage_src(dma_s);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int x = 0; x < WM * WN; ++x) {
+      const int i = x / WN, j = x % WN;
+      acc[C][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j],
+                                                             zero ? f32x16{} : acc[C][i][j], 0, 0, 0);
+      if (x < WM + WN) read_frag(x, rd_st, rd_ss, af[cb ^ 1], bfr[cb ^ 1]);
+      if (dma) {
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+          if (d * 8 / ND == x) issue_one(ds, d);
+      }
+      if constexpr (T >= 0) {
+        using Cx = std::integral_constant<int, C ^ 1>;
+        using Tx = std::integral_constant<int, T>;
+        if (x == 0) epi_chunk(Cx{}, Tx{}, std::integral_constant<int, 0>{});
+        if (x == 1) epi_chunk(Cx{}, Tx{}, std::integral_constant<int, 1>{});
+        if (x == 2) epi_chunk(Cx{}, Tx{}, std::integral_constant<int, 2>{});
+        if (x == 3) epi_chunk(Cx{}, Tx{}, std::integral_constant<int, 3>{});
+        if (x == 4) epi_chunk(Cx{}, Tx{}, std::integral_constant<int, 4>{});
+        if (x == 5) epi_chunk(Cx{}, Tx{}, std::integral_constant<int, 5>{});
+        if (x == 6) epi_chunk(Cx{}, Tx{}, std::integral_constant<int, 6>{});
+        if (x == 7) epi_chunk(Cx{}, Tx{}, std::integral_constant<int, 7>{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using F = std::integral_constant<bool, false>;
+  using Tr = std::integral_constant<bool, true>;
+  using NoT = std::integral_constant<int, -1>;
+
+  // prologue: stages 0 and 1 in flight, stage 0 landed, its first fragments,
+  // stage 2 in flight
+  {
+    const Src s0 = stage_src(0), s1 = stage_src(1);
+#pragma unroll
+    for (int d = 0; d < ND; ++d) issue_one(s0, d);
+#pragma unroll
+    for (int d = 0; d < ND; ++d) issue_one(s1, d);
+    wait_vm<ND>();
+    lds_barrier();
+#pragma unroll
+    for (int f = 0; f < WM + WN; ++f) read_frag(f, lds, 0, af[0], bfr[0]);
+    const Src s2 = stage_src(2);
+#pragma unroll
+    for (int d = 0; d < ND; ++d) issue_one(s2, d);
+  }
+
+  // stage S of the current item; the epilogue of the previous item runs in
+  // stages q < EPI_STAGES (task 4q + k-step)
+  auto stage = [&](auto CC, auto QQ, int S) __attribute__((always_inline)) {
+    constexpr int C = decltype(CC)::value;
+    constexpr int Q = decltype(QQ)::value;  // < 0: a stage without epilogue work
+    const char* cur = lds + (S % NST) * STAGE;
+    if constexpr (Q >= 0) {
+      using Z = std::integral_constant<bool, Q == 0>;
+      kstep(C0{}, CC, Z{}, std::integral_constant<int, 4 * Q + 0>{}, cur, 1, false, 0);
+      kstep(C1{}, CC, F{}, std::integral_constant<int, 4 * Q + 1>{}, cur, 2, false, 0);
+      kstep(C0{}, CC, F{}, std::integral_constant<int, 4 * Q + 2>{}, cur, 3, false, 0);
+      wait_vm<ND>();  // stage S+1 landed; stage S+2 may be in flight
+      lds_barrier();  // every wave is done with slot S
+      kstep(C1{}, CC, F{}, std::integral_constant<int, 4 * Q + 3>{}, lds + ((S + 1) % NST) * STAGE, 0, true, S + 3);
+    } else {
+      kstep(C0{}, CC, F{}, NoT{}, cur, 1, false, 0);
+      kstep(C1{}, CC, F{}, NoT{}, cur, 2, false, 0);
+      kstep(C0{}, CC, F{}, NoT{}, cur, 3, false, 0);
+      wait_vm<ND>();
+      lds_barrier();
+      kstep(C1{}, CC, F{}, NoT{}, lds + ((S + 1) % NST) * STAGE, 0, true, S + 3);
+    }
+  };
+  auto item = [&](auto CC, int n) __attribute__((always_inline)) {
+    const int S0 = n * nq;
+    stage(CC, std::integral_constant<int, 0>{}, S0 + 0);
+    stage(CC, std::integral_constant<int, 1>{}, S0 + 1);
+    stage(CC, std::integral_constant<int, 2>{}, S0 + 2);
+    stage(CC, std::integral_constant<int, 3>{}, S0 + 3);
+    stage(CC, std::integral_constant<int, 4>{}, S0 + 4);
+    for (int q = EPI_STAGES; q < nq; ++q) stage(CC, NoT{}, S0 + q);
+    // this item is the one finalized during the next
+    e_live = true;
+    item_of(n, e_ct, e_vt);
+    e_par = n & 1;
+  };
+
+  for (int n = 0; n < n_items; n += 2) {
+    item(C0{}, n);
+    if (n + 1 < n_items) item(C1{}, n + 1);
+  }
+  // the last item's epilogue, with no MFMAs to hide it under
+  auto drain = [&](auto EE) __attribute__((always_inline)) {
+#define RNNT_E3(T)                                                                                      \
+  epi_chunk(EE, std::integral_constant<int, T>{}, std::integral_constant<int, 0>{});                 \
+  epi_chunk(EE, std::integral_constant<int, T>{}, std::integral_constant<int, 1>{});                 \
+  epi_chunk(EE, std::integral_constant<int, T>{}, std::integral_constant<int, 2>{});                 \
+  epi_chunk(EE, std::integral_constant<int, T>{}, std::integral_constant<int, 3>{});                 \
+  epi_chunk(EE, std::integral_constant<int, T>{}, std::integral_constant<int, 4>{});                 \
+  epi_chunk(EE, std::integral_constant<int, T>{}, std::integral_constant<int, 5>{});                 \
+  epi_chunk(EE, std::integral_constant<int, T>{}, std::integral_constant<int, 6>{});                 \
+  epi_chunk(EE, std::integral_constant<int, T>{}, std::integral_constant<int, 7>{});
+    RNNT_E3(0) RNNT_E3(1) RNNT_E3(2) RNNT_E3(3) RNNT_E3(4) RNNT_E3(5) RNNT_E3(6) RNNT_E3(7)
+    RNNT_E3(8) RNNT_E3(9) RNNT_E3(10) RNNT_E3(11) RNNT_E3(12) RNNT_E3(13) RNNT_E3(14) RNNT_E3(15)
+    RNNT_E3(16) RNNT_E3(17) RNNT_E3(18)
+    lds_barrier();
+    RNNT_E3(19)
+#undef RNNT_E3
+  };
+  if (n_items & 1) drain(C0{});
+  else drain(C1{});
+  wait_vm<0>();  // dma past the end must land before the workgroup's LDS is released
+}
+
+hipError_t launch_scores3(const Scores3Args& a, bool bwd, hipStream_t st) {
+  if (a.n_ct == 0) return hipSuccess;
+  dim3 grid(256), block(256);
+  if (bwd) hipLaunchKernelGGL(scores3_kernel<true>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(scores3_kernel<false>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+// ============================================================================ helpers
+// Zero-padded copy of W^O: [nvt*256][H_pad], 0 for v >= V or k >= H.
+__global__ void pad_wo_kernel(const bf16* __restrict__ WO, bf16* __restrict__ WOp, int V, int H, int H_pad,
+                              int rows) {
+  const int64_t n = (int64_t)rows * H_pad;
+  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < n; x += (int64_t)gridDim.x * blockDim.x) {
+    const int v = (int)(x / H_pad), k = (int)(x - (int64_t)v * H_pad);
+    WOp[x] = (v < V && k < H) ? WO[(int64_t)v * H + k] : (bf16)0.0f;
+  }
+}
+// bl[v] = b^O[v] log2 e for v < V, -1e30 up to nvt*256 (those rows drop out of
+// the max and the sum)
+__global__ void bias_table_kernel(const bf16* __restrict__ bO, float* __restrict__ bl, int V, int rows) {
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (v < rows) bl[v] = v < V ? (float)bO[v] * kLog2e : -1e30f;
+}
+
+hipError_t launch_score_tables(const void* WO, const void* bO, void* WOp, float* bl, int V, int H, int H_pad,
+                               int nvt, hipStream_t st) {
+  const int rows = nvt * 256;
+  hipLaunchKernelGGL(pad_wo_kernel, dim3(512), dim3(256), 0, st, reinterpret_cast<const bf16*>(WO),
+                     reinterpret_cast<bf16*>(WOp), V, H, H_pad, rows);
+  hipLaunchKernelGGL(bias_table_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, reinterpret_cast<const bf16*>(bO),
+                     bl, V, rows);
+  return hipGetLastError();
+}
+
+// Per buffer row (cell) of a wave, the backward coefficients of Eq. (10):
+// coefA = (lse log2 e, g alpha beta / P), coefB = (g alpha phi beta' / P,
+// g alpha psi beta'' / P, label, 0); zeros (label -1) on padding rows.
+__global__ void coef_kernel(Scores3Args p) {
+  const int rr = blockIdx.x * blockDim.x + threadIdx.x;
+  if (rr >= p.n_ct * s3::BN) return;
+  float ls = 0.0f, co = 0.0f, cb = 0.0f, cl = 0.0f, lab = -1.0f;
+  if (rr < p.n_rows) {
+    const int R = rr + p.buf_row_base;
+    int lo = p.tile_begin, hi = p.tile_end - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (p.tiles[mid].row0 <= R) lo = mid; else hi = mid - 1;
+    }
+    const Tile tl = p.tiles[lo];
+    const int local_r = R - tl.row0;
+    const int ul = local_r / tl.htp, tloc = local_r - ul * tl.htp;
+    if (tloc < tl.ht) {
+      const int b = tl.b, u = tl.u0 + ul, t = tl.t0 + tloc;
+      const int Tb = p.T_len[b], Ub = p.U_len[b];
+      const size_t idx = ((size_t)b * p.U1 + u) * p.T + t;
+      const float lp = p.lnP[b];
+      const float gb = p.dcosts ? p.dcosts[b] : 1.0f;
+      const float A = p.alpha[idx], Bt = p.beta[idx];
+      ls = p.lse[idx];
+      const float bn = (t + 1 < Tb) ? p.beta[idx + 1] : (u == Ub ? 0.0f : kNegInf);
+      co = gb * fexp2((A + Bt - lp) * kLog2e);
+      cb = gb * fexp2((A + p.phi[idx] + bn - lp) * kLog2e);
+      if (u < Ub) {
+        cl = gb * fexp2((A + p.psi[idx] + p.beta[idx + p.T] - lp) * kLog2e);
+        lab = (float)p.labels[(size_t)b * p.U1 + u + 1];
+      }
+    }
+  }
+  reinterpret_cast<f32x2*>(p.coefA)[rr] = f32x2{ls * kLog2e, co};
+  reinterpret_cast<f32x4*>(p.coefB)[rr] = f32x4{cb, cl, lab, 0.0f};
+}
+
+// dh[row, blank] -= cb, dh[row, label] -= cl (in fp32, rounded once more to bf16)
+__global__ void dh_fix_kernel(Scores3Args p) {
+  const int rr = blockIdx.x * blockDim.x + threadIdx.x;
+  if (rr >= p.n_rows) return;
+  const f32x4 c = reinterpret_cast<const f32x4*>(p.coefB)[rr];
+  bf16* row = reinterpret_cast<bf16*>(p.dh) + (int64_t)rr * p.V_pad;
+  if (c[0] != 0.0f) row[p.blank] = (bf16)((float)row[p.blank] - c[0]);
+  const int lab = (int)c[2];
+  if (lab >= 0 && c[1] != 0.0f) row[lab] = (bf16)((float)row[lab] - c[1]);
+}
+
+hipError_t launch_coef(const Scores3Args& a, hipStream_t st) {
+  const int rows = a.n_ct * s3::BN;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(coef_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t launch_dh_fix(const Scores3Args& a, hipStream_t st) {
+  if (a.n_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(dh_fix_kernel, dim3((a.n_rows + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace rnnt

@@ -164,7 +164,10 @@ def test_config3_sampled_tiled_and_untiled(gpu_lib):
     say("config 3 untiled vs tiled")
     cu, gu = run_gpu(gpu_lib, inp, mode="untiled")
     c2, g2 = run_gpu(gpu_lib, inp)
-    assert np.array_equal(cu, c2)  # forward math is identical in both modes
+    # same equations; the tiled forward accumulates the per-V-tile (max, sum)
+    # block by block, the untiled one per 256-score tile, so only the
+    # summation order differs
+    assert np.allclose(cu, c2, rtol=1e-5, atol=0), np.max(np.abs(cu - c2) / np.abs(c2))
     for k in GRADS:
         assert np.max(np.abs(gu[k] - g2[k])) <= 1e-2 * np.max(np.abs(g2[k])), k
 
