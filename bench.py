@@ -24,7 +24,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
-GEMM_KERNELS = ("joint_fwd", "joint_bwd", "scores_fwd", "scores_bwd", "dz", "dWO_gemm")
+GEMM_KERNELS = ("joint_fwd", "joint_bwd", "scores_fwd", "scores_bwd", "dz", "dWO_gemm", "dz_dwo")
 
 
 def mfma_flops(inp):
@@ -40,7 +40,8 @@ def mfma_flops(inp):
         "joint_bwd": 2.0 * H * V * Nc,   # recomputed scores (fp32 path)
         "scores_fwd": 2.0 * H * V * Nc,  # scores for every valid cell (bf16 path)
         "scores_bwd": 2.0 * H * V * Nc,  # recomputed scores (bf16 path)
-        "dz": 2.0 * H * V * Nc,          # dz = dh W^O
+        "dz": 2.0 * H * V * Nc,          # dz = dh W^O (fp32 path)
+        "dz_dwo": 4.0 * H * V * Nc,      # dz = dh W^O and dW^O = dh^T z in one launch (bf16 path)
         "dWO_gemm": 2.0 * H * V * Nc,    # dW^O = dh^T z
         "preproj_gemm": pre,             # a = W^A h^A, l = W^L h^L
         "dh_enc_gemm": pre,              # dh^A, dh^L

@@ -116,33 +116,6 @@ rnnt_status upload(void* dst, const std::vector<char>& src, hipStream_t st) {
   return RNNT_OK;
 }
 
-// ---------------------------------------------------------------- side stream
-// The bf16 backward runs dW^O (a split-K GEMM whose grid fills about three
-// quarters of the CUs) concurrently with the dz kernel, which reads the same
-// dh rows: fork from the caller's stream with an event, join back with
-// another. One default-priority stream per device, created on first use.
-struct Side {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-std::mutex g_side_mu;
-std::vector<Side> g_side;
-
-rnnt_status side_stream(Side*& out) {
-  int dev = 0;
-  RNNT_HIP(hipGetDevice(&dev));
-  std::lock_guard<std::mutex> lk(g_side_mu);
-  if ((int)g_side.size() <= dev) g_side.resize(dev + 1);
-  Side& sd = g_side[dev];
-  if (!sd.s) {
-    RNNT_HIP(hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking));
-    RNNT_HIP(hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming));
-    RNNT_HIP(hipEventCreateWithFlags(&sd.join, hipEventDisableTiming));
-  }
-  out = &sd;
-  return RNNT_OK;
-}
-
 // ---------------------------------------------------------------- launch timing
 // When enabled, every launch site records a hipEvent pair on the launch
 // stream; rnnt_profile_stop() resolves them into per-kernel totals.
@@ -677,13 +650,9 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
         RNNT_HIP(rnnt::launch_joint(a, bf, true, st));
       }
     }
-    // 7 (bf16). dW^O and db^O on the side stream, concurrent with 5 and 6
-    Side* side = nullptr;
+    // bf16: dW^O / db^O split-K partials, launched together with dz (step 5)
+    rnnt::DwoArgs w{};
     if (bf) {
-      RNNT_STATUS(side_stream(side));
-      RNNT_HIP(hipEventRecord(side->fork, st));
-      RNNT_HIP(hipStreamWaitEvent(side->s, side->fork, 0));
-      rnnt::DwoArgs w{};
       w.dh = dh_buf;
       w.dh_ld = p.V_pad;
       w.z = z_buf;
@@ -695,19 +664,6 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       w.k_per_split = ((wrows + p.s6 - 1) / p.s6 + 63) / 64 * 64;
       w.PW = PW;
       w.PB = PB;
-      {
-        ProfScope ps_("dWO_gemm", side->s);
-        RNNT_HIP(rnnt::launch_dwo(w, side->s));
-      }
-      {
-        ProfScope ps_("split_reduce", side->s);
-        RNNT_HIP(rnnt::launch_split_reduce(dWO, PW, (int64_t)d.V * d.H, p.s6, (int64_t)d.V * d.H, true, side->s));
-      }
-      {
-        ProfScope ps_("split_reduce", side->s);
-        RNNT_HIP(rnnt::launch_split_reduce(dbO, PB, d.V, p.s6, d.V, true, side->s));
-      }
-      RNNT_HIP(hipEventRecord(side->join, side->s));
     }
     // 5. dz, dtanh and per-tile sums
     {
@@ -732,8 +688,8 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       a.tile_u = d.tile_u;
       if (bf) {
         a.z_ld = p.H_pad;  // bf16 path: z rows are row-major
-        ProfScope ps_("dz", st);
-        RNNT_HIP(rnnt::launch_dz2(a, st));
+        ProfScope ps_("dz_dwo", st);
+        RNNT_HIP(rnnt::launch_dz_dwo(a, w, st));
       } else {
         ProfScope ps_("dz", st);
         RNNT_HIP(rnnt::launch_dz(a, bf, st));
@@ -773,9 +729,16 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
         RNNT_HIP(rnnt::launch_group_reduce(r, st));
       }
     }
-    // 7. dW^O and db^O (fp32 path; the bf16 path joins the side stream)
+    // 7. dW^O and db^O (the bf16 partials came with dz)
     if (bf) {
-      RNNT_HIP(hipStreamWaitEvent(st, side->join, 0));
+      {
+        ProfScope ps_("split_reduce", st);
+        RNNT_HIP(rnnt::launch_split_reduce(dWO, PW, (int64_t)d.V * d.H, p.s6, (int64_t)d.V * d.H, true, st));
+      }
+      {
+        ProfScope ps_("split_reduce", st);
+        RNNT_HIP(rnnt::launch_split_reduce(dbO, PB, d.V, p.s6, d.V, true, st));
+      }
     } else {
       rnnt::GemmArgs g{};
       g.A = rnnt::Operand{dh_buf, p.V_pad, d.V, nullptr, 1, 0};

@@ -167,8 +167,6 @@ struct DwoArgs {  // dW^O = dh^T z (split-K partials), db^O from a column of one
   float* PW;  // [splits, V, H]
   float* PB;  // [splits, V]
 };
-hipError_t launch_dwo(const DwoArgs& a, hipStream_t st);
-hipError_t launch_dz2(const DzArgs& a, hipStream_t st);
 
 struct ZArgs {  // z rows and (hb != null) the blank / label scores of a wave's strips
   const Tile* tiles;
@@ -186,6 +184,7 @@ struct ZArgs {  // z rows and (hb != null) the blank / label scores of a wave's 
   float* hy;
 };
 hipError_t launch_zrow(const ZArgs& a, hipStream_t st);
+hipError_t launch_dz_dwo(const DzArgs& a, const DwoArgs& w, hipStream_t st);
 
 struct ScoresArgs {  // scores^T tiles: forward statistics or backward dh
   const Tile* tiles;

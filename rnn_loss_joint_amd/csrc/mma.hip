@@ -28,12 +28,11 @@ namespace rnnt {
 // C[v, h] = sum over rows k of dh[k, v] * z[k, h]; column h = H of z reads the
 // ones page, so C[v, H] = sum_k dh[k, v] = db^O[v]. Split-K partials.
 // Workgroup ids are arranged so the tiles of one k split share an XCD (L2).
-__global__ void __launch_bounds__(256) dwo_kernel(DwoArgs p) {
+constexpr int kDwoLds = 2 * 2 * m3::MnTile<256>::BYTES;
+__device__ __attribute__((always_inline)) inline void dwo_body(const DwoArgs& p, char* lds, int id) {
   using namespace m3;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * MnTile<256>::BYTES];
   const int tid = threadIdx.x;
   const int nv = (p.V + BM - 1) / BM, nh = (p.H + 1 + 255) / 256;
-  const int id = blockIdx.x;
   const int xcd = id & 7, local = id >> 3;
   const int per = nv * nh;
   const int split = (local / per) * 8 + xcd;
@@ -73,13 +72,6 @@ __global__ void __launch_bounds__(256) dwo_kernel(DwoArgs p) {
   }
 }
 
-hipError_t launch_dwo(const DwoArgs& a, hipStream_t st) {
-  const int nv = (a.V + 255) / 256, nh = (a.H + 1 + 255) / 256;
-  const int groups = (a.splits + 7) / 8;
-  dim3 grid(groups * 8 * nv * nh), block(256);
-  hipLaunchKernelGGL(dwo_kernel, grid, block, 0, st, a);
-  return hipGetLastError();
-}
 
 // ============================================================================ dz, dtanh, sums
 // Workgroup = one 32-row strip of a tile (32 consecutive t) x 128 columns of
@@ -88,13 +80,12 @@ hipError_t launch_dwo(const DwoArgs& a, hipStream_t st) {
 // k-contiguous), ds = dz (1 - z^2) with z read from the row-major z buffer;
 // sums over u stay in registers across passes (gA partial, written once);
 // sums over the strip's t are written per u (gL partial).
-__global__ void __launch_bounds__(256) dz2_kernel(DzArgs p) {
+constexpr int kDzLds = 3 * (m3::KcTile<256>::BYTES + m3::KcTile<128>::BYTES);
+__device__ __attribute__((always_inline)) inline void dz2_body(const DzArgs& p, char* lds, int id) {
   using namespace m3;
-  __shared__ __attribute__((aligned(1024))) char lds[3 * (KcTile<256>::BYTES + KcTile<128>::BYTES)];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), wr = wave >> 1, wc = wave & 1;
   const int nh = (p.H + 127) / 128;
-  const int id = blockIdx.x;
   const int xcd = id & 7, local = id >> 3;
   const int strip_rel = (local / nh) * 8 + xcd;
   if (strip_rel >= p.n_strips) return;
@@ -197,12 +188,25 @@ __global__ void __launch_bounds__(256) dz2_kernel(DzArgs p) {
   }
 }
 
-hipError_t launch_dz2(const DzArgs& a, hipStream_t st) {
-  if (a.n_strips == 0) return hipSuccess;
+// dz and dW^O of one wave in one launch: both read the same dh rows. The
+// dW^O workgroups come first (ids 0 .. n_dwo-1, whole k splits per XCD, one
+// round on part of the CUs); the dz workgroups fill the remaining CUs and
+// then all of them. n_dwo is a multiple of 8, so both keep their XCD maps.
+__global__ void __launch_bounds__(256) dz_dwo_kernel(DzArgs dz, DwoArgs dw, int n_dwo) {
+  static_assert(kDzLds >= kDwoLds, "one LDS array serves both roles");
+  __shared__ __attribute__((aligned(1024))) char lds[kDzLds];
+  const int id = blockIdx.x;
+  if (id < n_dwo) dwo_body(dw, lds, id);
+  else dz2_body(dz, lds, id - n_dwo);
+}
+
+hipError_t launch_dz_dwo(const DzArgs& a, const DwoArgs& w, hipStream_t st) {
+  const int nv = (w.V + 255) / 256, nhw = (w.H + 1 + 255) / 256;
+  const int n_dwo = w.K > 0 ? (w.splits + 7) / 8 * 8 * nv * nhw : 0;
   const int nh = (a.H + 127) / 128;
-  const int groups = (a.n_strips + 7) / 8;
-  dim3 grid(groups * 8 * nh), block(256);
-  hipLaunchKernelGGL(dz2_kernel, grid, block, 0, st, a);
+  const int n_dz = a.n_strips > 0 ? (a.n_strips + 7) / 8 * 8 * nh : 0;
+  if (n_dwo + n_dz == 0) return hipSuccess;
+  hipLaunchKernelGGL(dz_dwo_kernel, dim3(n_dwo + n_dz), dim3(256), 0, st, a, w, n_dwo);
   return hipGetLastError();
 }
 

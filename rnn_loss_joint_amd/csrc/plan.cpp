@@ -186,7 +186,8 @@ void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H
   // split-K counts: dW^O ~1024 workgroups of 128 x 128 (fp32 path); in the
   // bf16 path all output tiles of one split run on one XCD (32 CUs, the
   // split's dh and z rows shared in its L2), as many whole splits per XCD as
-  // fit, one round (the dz kernel runs beside it); dW^A / dW^L ~512
+  // fit, one round (the dz workgroups of the same launch fill the rest);
+  // dW^A / dW^L ~512
   p.nvt = (int)cdiv(d.V, 256);
   if (d.bf16) {
     int64_t tiles_vh = cdiv(d.V, 256) * cdiv(d.H + 1, 256);
