@@ -7,7 +7,8 @@ timing (hipEvent pairs on the launch stream over the timed steps); the
 roofline object reports the dominant kernel. The fp64 CPU oracle is timed on
 a bounded sample of the same workload as cpu_baseline.
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--config 5]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--workload 40s-b256-bf16]
+    python bench.py --calibrate-copy BYTES   # counter calibration only
 """
 from __future__ import annotations
 
@@ -25,6 +26,33 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 GEMM_KERNELS = ("joint_fwd", "joint_bwd", "scores_fwd", "scores_bwd", "dz", "dWO_gemm", "dz_dwo")
+# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled
+# by a 1 GiB device copy: x2.000 / x1.000) on the 40 s x 256 workload; the
+# figure applies only while the kernel's sources hash to `src` (else null).
+TRAFFIC = {
+    "dz_dwo": {"bytes": 4.077e9, "src": "3d425e8ed46cce40",
+               "files": ("rnn_loss_joint_amd/csrc/mma.hip", "rnn_loss_joint_amd/csrc/mfma_core.hpp",
+                         "rnn_loss_joint_amd/csrc/common.hpp", "rnn_loss_joint_amd/csrc/kernels.hpp"),
+               "profile": "profiles/hbm_traffic_40s_b256_bf16.md", "workload": "40s-b256-bf16"},
+}
+
+
+def measured_traffic(kernel, workload):
+    """Measured HBM bytes per launch if the kernel's sources are unchanged."""
+    import hashlib
+
+    t = TRAFFIC.get(kernel)
+    if t is None or t["workload"] != workload:
+        return None
+    h = hashlib.sha256()
+    for f in t["files"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return t["bytes"] if h.hexdigest()[:16] == t["src"] else None
+
+
+FLOP_FORMULA = {"dz_dwo": "4*H*V*valid_cells", "preproj_gemm": "2*H*(rows_a*HA + rows_l*HL)",
+                "dh_enc_gemm": "2*H*(rows_a*HA + rows_l*HL)", "dW_enc_gemm": "2*H*(rows_a*HA + rows_l*HL)"}
 
 
 def mfma_flops(inp):
@@ -87,11 +115,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--workload", default="40s-b256-bf16",
+                    help="tiny-f32 | small-bf16 | 20s-bf16 | vocab4096-bf16 | 40s-b256-bf16")
     ap.add_argument("--mode", default="tiled", choices=["tiled", "untiled"])
     ap.add_argument("--tile", default="64x32")
     ap.add_argument("--tiles-per-wave", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget; 0 = skip")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes three times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
@@ -106,11 +137,22 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        # a plain copy kernel of known size: FETCH_SIZE / WRITE_SIZE of one
+        # dispatch against these bytes give the counters' scale
+        n = args.calibrate_copy // 4
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": 4 * n}))
+        return
     rl.load()
-    w = WORKLOADS[args.config]
+    w = WORKLOADS[args.workload]
     tile = tuple(int(x) for x in args.tile.split("x"))
     print(f"# generating {w.name} inputs", file=sys.stderr, flush=True)
-    inp = workload_inputs(args.config)
+    inp = workload_inputs(args.workload)
     prob = rl.Problem(inp, mode=args.mode, tile=tile, tiles_per_wave=args.tiles_per_wave)
     stream = torch.cuda.current_stream()
 
@@ -153,8 +195,9 @@ def main():
     dk = kernels[dom]
     ach = dk["tflops"]
     roof = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
-            "frac": ach / PEAK_TFLOPS[dtype], "traffic": None,
-            "per_launch": f"2*H*V*valid_cells / launches = {flops[dom] / max(1, dk['launches']):.4g} FLOP"}
+            "frac": ach / PEAK_TFLOPS[dtype], "traffic": measured_traffic(dom, w.name),
+            "per_launch": (f"{FLOP_FORMULA.get(dom, '2*H*V*valid_cells')} / launches = "
+                           f"{flops[dom] / max(1, dk['launches']):.4g} FLOP")}
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -178,7 +221,7 @@ def main():
         "data": "synthetic",
         "peak_hbm_bytes": int(peak),
         "valid_cells_per_s": inp.valid_cells / (ms * 1e-3),
-        "config": {"workload": f"config {args.config} ({w.name})", "B": d["B"], "T": d["T"], "U": d["U"],
+        "config": {"workload": w.name, "B": d["B"], "T": d["T"], "U": d["U"],
                    "V": d["V"], "HA": d["HA"], "HL": d["HL"], "H": d["H"], "mode": args.mode,
                    "tile": list(tile), "tiles_per_wave": args.tiles_per_wave,
                    "padded_cells": inp.padded_cells, "valid_cells": inp.valid_cells,

@@ -1,19 +1,13 @@
-// Large-tile bf16 MFMA core for gfx950 and the bf16 kernels built on it.
-//
-// Core: 256 threads = 4 waves in a 2 x 2 grid over a BM x BN output tile
-// (BM = 256, BN = 256 or 128), each wave 128 x BN/2, v_mfma_f32_32x32x16_bf16.
-// Operand tiles are moved global -> LDS by global_load_lds_dwordx4 (no VGPR
-// staging), NSTAGE stages in flight. A k-contiguous tile is stored
-// [row][64 k] with 16-byte chunks XOR-swizzled by the row; an m-contiguous
-// tile is stored [64 k][m] with 8-byte units XOR-swizzled by k and is read
-// with ds_read_b64_tr_b16, which hands each lane four consecutive k of one m,
-// so both orientations become MFMA fragments without register transposes.
-// Pieces outside the operand read a zero page (or a page of bf16 ones, used
-// to append a column of ones to an operand).
-// Each kernel declares exactly one __shared__ array and carves every LDS
-// region out of it: with several LDS variables the compiler attaches alias
-// scopes and then makes every read of the stage buffers wait for all dma in
-// flight, which removes the overlap of loads and MFMAs.
+// bf16 kernels on the large-tile MFMA core (mfma_core.hpp):
+//   dz_dwo   dz = dh W^O with dtanh and the per-tile u / t sums, and the
+//            split-K partials of dW^O = dh^T z and db^O, in one launch per wave;
+//   zrow     z = tanh(a + l) rows of a wave (and, in the forward, the blank /
+//            label scores);
+//   scores   256-score x 256-cell tiles of W^O z + b^O: forward (max, sum)
+//            statistics (and the scores themselves in untiled mode) or
+//            backward dh; used where the persistent kernels of scores3.hip
+//            do not apply (untiled mode, H_pad < 512);
+//   lse_merge  logsumexp over the V tiles' statistics, phi and psi.
 #include <algorithm>
 #include <type_traits>
 

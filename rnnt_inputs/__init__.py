@@ -38,7 +38,7 @@ class Workload:
     HL: int
     H: int
     dtype: str  # "f32" or "bf16"
-    enc: str  # "normal0.5" (config-1 style) or "normal1"
+    enc: str  # "normal0.5" (the tiny workload) or "normal1"
     weights: str  # "normal0.5" or "xavier"
     labels: str  # "uniform" or "zipf1.1"
     t_range: tuple  # inclusive integer range for T_b
@@ -55,18 +55,18 @@ def _frac_range(lo_frac: float, n: int) -> tuple:
 # shaped like ~10 s, ~20 s and ~40 s utterances at 40 ms frames, plus a
 # 4096-token vocabulary case. Lengths are integer-uniform over the ranges.
 WORKLOADS = {
-    1: Workload("tiny-f32", 2, 6, 3, 5, 8, 8, 8, "f32", "normal0.5", "normal0.5",
+    "tiny-f32": Workload("tiny-f32", 2, 6, 3, 5, 8, 8, 8, "f32", "normal0.5", "normal0.5",
                 "uniform", (6, 6), (3, 3), seed=1, tiles=((64, 32),)),
-    2: Workload("small-bf16", 8, 250, 64, 1024, 512, 512, 640, "bf16", "normal1",
+    "small-bf16": Workload("small-bf16", 8, 250, 64, 1024, 512, 512, 640, "bf16", "normal1",
                 "xavier", "uniform", (150, 250), (32, 64), seed=2,
                 tiles=((64, 32),)),
-    3: Workload("20s-bf16", 32, 500, 120, 1024, 512, 512, 640, "bf16", "normal1",
+    "20s-bf16": Workload("20s-bf16", 32, 500, 120, 1024, 512, 512, 640, "bf16", "normal1",
                 "xavier", "uniform", _frac_range(0.6, 500), _frac_range(0.6, 120),
                 seed=3, tiles=((64, 32),)),
-    4: Workload("vocab4096-bf16", 16, 400, 150, 4096, 640, 640, 640, "bf16",
+    "vocab4096-bf16": Workload("vocab4096-bf16", 16, 400, 150, 4096, 640, 640, 640, "bf16",
                 "normal1", "xavier", "zipf1.1", _frac_range(0.6, 400),
                 _frac_range(0.6, 150), seed=4, tiles=((32, 16), (64, 32), (128, 64))),
-    5: Workload("40s-b256-bf16", 256, 1000, 200, 1024, 512, 512, 640, "bf16",
+    "40s-b256-bf16": Workload("40s-b256-bf16", 256, 1000, 200, 1024, 512, 512, 640, "bf16",
                 "normal1", "xavier", "uniform", _frac_range(0.5, 1000),
                 _frac_range(0.5, 200), seed=5, tiles=((64, 32),)),
 }
@@ -216,9 +216,9 @@ def make_inputs(B: int, T: int, U: int, V: int, HA: int, HL: int, H: int, *,
                   WO=cv(WO), bO=cv(bO))
 
 
-def workload_inputs(cfg: int, *, seed: int | None = None, dtype: str | None = None,
+def workload_inputs(cfg: str, *, seed: int | None = None, dtype: str | None = None,
                     B: int | None = None) -> Inputs:
-    """Inputs for one of the five named workloads (seed defaults to its number).
+    """Inputs for one of the five named workloads (seed defaults to the workload's own).
 
     B overrides the batch size (the first B samples' lengths then differ from
     the full-batch draw, since lengths are drawn per batch).

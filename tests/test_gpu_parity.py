@@ -125,9 +125,9 @@ def test_lattice_kernel_matches_oracle(gpu_lib):
 # ----------------------------------------------------------------------------- fp32 mode
 
 @pytest.mark.parametrize("mode", ["tiled", "untiled"])
-def test_config1_fp32(gpu_lib, mode):
-    say(f"config 1 fp32 {mode}")
-    full_check(gpu_lib, workload_inputs(1), mode=mode)
+def test_tiny_fp32(gpu_lib, mode):
+    say(f"tiny fp32 {mode}")
+    full_check(gpu_lib, workload_inputs("tiny-f32"), mode=mode)
 
 
 @pytest.mark.parametrize("mode,tile,tpw", [("tiled", (32, 16), 3), ("tiled", (64, 32), 0),
@@ -151,17 +151,17 @@ def test_bf16_reduced(gpu_lib, mode):
 
 @pytest.mark.timeout(400)
 @pytest.mark.parametrize("mode", ["tiled", "untiled"])
-def test_config2_full(gpu_lib, mode):
-    say(f"config 2 full bf16 {mode}")
-    full_check(gpu_lib, workload_inputs(2), mode=mode)
+def test_small_full(gpu_lib, mode):
+    say(f"small full bf16 {mode}")
+    full_check(gpu_lib, workload_inputs("small-bf16"), mode=mode)
 
 
 @pytest.mark.timeout(400)
-def test_config3_sampled_tiled_and_untiled(gpu_lib):
-    inp = workload_inputs(3)
-    say("config 3 full bf16 tiled 64x32, sampled oracle")
+def test_20s_sampled_tiled_and_untiled(gpu_lib):
+    inp = workload_inputs("20s-bf16")
+    say("20s full bf16 tiled 64x32, sampled oracle")
     ct = sampled_check(gpu_lib, inp, [0, 17])
-    say("config 3 untiled vs tiled")
+    say("20s untiled vs tiled")
     cu, gu = run_gpu(gpu_lib, inp, mode="untiled")
     c2, g2 = run_gpu(gpu_lib, inp)
     # same equations; the tiled forward accumulates the per-V-tile (max, sum)
@@ -173,34 +173,34 @@ def test_config3_sampled_tiled_and_untiled(gpu_lib):
 
 
 @pytest.mark.timeout(600)
-def test_config4_tile_sweep(gpu_lib):
-    inp = workload_inputs(4)
+def test_vocab4096_tile_sweep(gpu_lib):
+    inp = workload_inputs("vocab4096-bf16")
     results = {}
     for tile in ((32, 16), (64, 32), (128, 64)):
-        say(f"config 4 bf16 tile {tile}")
+        say(f"vocab4096 bf16 tile {tile}")
         results[tile] = run_gpu(gpu_lib, inp, tile=tile)
     base_c, base_g = results[(64, 32)]
     for tile, (c, g) in results.items():
         assert np.array_equal(c, base_c), tile  # costs do not depend on the tile size
         for k in GRADS:
             assert np.max(np.abs(g[k] - base_g[k])) <= 1e-2 * np.max(np.abs(base_g[k])), (tile, k)
-    say("config 4 sampled oracle")
+    say("vocab4096 sampled oracle")
     sampled_check(gpu_lib, inp, [3], tile=(32, 16))
 
 
 @pytest.mark.timeout(600)
-def test_config5_closed_form_and_sample(gpu_lib):
+def test_40s_b256_closed_form_and_sample(gpu_lib):
     import dataclasses
 
-    inp = workload_inputs(5)
-    say("config 5 full, W^O = 0: closed-form cost for every sample")
+    inp = workload_inputs("40s-b256-bf16")
+    say("40s-b256 full, W^O = 0: closed-form cost for every sample")
     inp0 = dataclasses.replace(inp, WO=np.zeros_like(inp.WO))
     c0, _ = run_gpu(gpu_lib, inp0)
     for b in range(len(inp0.T_len)):
         Tb, Ub = int(inp0.T_len[b]), int(inp0.U_len[b])
         want = (Tb + Ub) * math.log(1024) - lnC(Tb + Ub - 1, Ub)
         assert abs(c0[b] - want) <= 1e-5 * want, (b, c0[b], want)
-    say("config 5 full, sampled oracle")
+    say("40s-b256 full, sampled oracle")
     sampled_check(gpu_lib, inp, [11])
 
 
@@ -217,8 +217,8 @@ def test_padding_poison_is_ignored(gpu_lib):
 
 
 def test_deterministic_repeats(gpu_lib):
-    inp = workload_inputs(2)
-    say("determinism config 2")
+    inp = workload_inputs("small-bf16")
+    say("determinism small")
     a = run_gpu(gpu_lib, inp)
     b = run_gpu(gpu_lib, inp)
     assert np.array_equal(a[0], b[0])

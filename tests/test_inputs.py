@@ -6,16 +6,16 @@ from rnnt_inputs import WORKLOADS, make_inputs, poison_padding, round_bf16, work
 
 
 def test_deterministic_per_seed():
-    a = workload_inputs(2)
-    b = workload_inputs(2)
-    c = workload_inputs(2, seed=99)
+    a = workload_inputs("small-bf16")
+    b = workload_inputs("small-bf16")
+    c = workload_inputs("small-bf16", seed=99)
     for k in ("T_len", "U_len", "labels", "hA", "hL", "WA", "WL", "WO"):
         assert np.array_equal(getattr(a, k), getattr(b, k))
     assert not np.array_equal(a.hA, c.hA)
 
 
 def test_length_and_label_ranges():
-    for cfg in (2, 3, 4):
+    for cfg in ("small-bf16", "20s-bf16", "vocab4096-bf16"):
         w = WORKLOADS[cfg]
         inp = workload_inputs(cfg)
         assert inp.T_len.min() >= w.t_range[0] and inp.T_len.max() <= w.t_range[1]
@@ -25,12 +25,12 @@ def test_length_and_label_ranges():
             lab = inp.labels[b, 1:inp.U_len[b] + 1]
             assert lab.min() >= 1 and lab.max() <= w.V - 1
             assert np.all(inp.labels[b, inp.U_len[b] + 1:] == 0)
-    assert WORKLOADS[3].t_range == (300, 500) and WORKLOADS[3].u_range == (72, 120)
-    assert WORKLOADS[5].t_range == (500, 1000) and WORKLOADS[5].u_range == (100, 200)
+    assert WORKLOADS["20s-bf16"].t_range == (300, 500) and WORKLOADS["20s-bf16"].u_range == (72, 120)
+    assert WORKLOADS["40s-b256-bf16"].t_range == (500, 1000) and WORKLOADS["40s-b256-bf16"].u_range == (100, 200)
 
 
 def test_zipf_labels_are_skewed():
-    inp = workload_inputs(4)
+    inp = workload_inputs("vocab4096-bf16")
     lab = np.concatenate([inp.labels[b, 1:inp.U_len[b] + 1] for b in range(16)])
     # P(1) / P(2) = 2^1.1 for Zipf(1.1); id 1 is by far the most frequent
     c1, c2 = np.sum(lab == 1), np.sum(lab == 2)
@@ -48,7 +48,7 @@ def test_bf16_rounding_matches_torch():
 
 
 def test_bf16_values_are_representable():
-    inp = workload_inputs(2)
+    inp = workload_inputs("small-bf16")
     for k in ("hA", "hL", "WA", "WL", "WO"):
         v = getattr(inp, k)
         assert np.array_equal(v, round_bf16(v))

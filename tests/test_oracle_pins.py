@@ -48,8 +48,8 @@ def test_dp_equals_brute_force(Tb, Ub):
     assert abs(bf - r.costs[0]) <= 1e-12 * abs(bf)
 
 
-def test_config1_brute_force():
-    inp = workload_inputs(1)
+def test_tiny_brute_force():
+    inp = workload_inputs("tiny-f32")
     r = oracle.loss_and_grads(inp, want_grads=False)
     for b, s in enumerate(r.samples):
         assert abs(oracle.brute_force_cost(s.phi, s.psi) - r.costs[b]) <= 1e-12 * abs(r.costs[b])
@@ -71,8 +71,8 @@ def test_alpha_beta_identity_ragged():
         assert abs(s.beta[0, 0] - s.lnP) <= 1e-12 * max(1.0, abs(s.lnP))
 
 
-def test_alpha_beta_identity_config2_sample():
-    inp = workload_inputs(2, B=1)
+def test_alpha_beta_identity_small_sample():
+    inp = workload_inputs("small-bf16", B=1)
     inp = make_inputs(1, 40, 12, 64, 32, 32, 48, dtype="bf16", seed=2, t_range=(25, 40), u_range=(6, 12))
     r = oracle.loss_and_grads(inp, want_grads=False)
     s = r.samples[0]
@@ -87,9 +87,9 @@ def zero_output_weights(inp, bias=None):
     return inp
 
 
-def test_closed_form_uniform_config1_lattice():
+def test_closed_form_uniform_tiny_lattice():
     """W^O = 0, b^O = 0: every p = 1/V, cost = (T_b+U_b) ln V - ln C(T_b+U_b-1, U_b)."""
-    inp = zero_output_weights(workload_inputs(1))
+    inp = zero_output_weights(workload_inputs("tiny-f32"))
     r = oracle.loss_and_grads(inp, want_grads=False)
     for b in range(2):
         Tb, Ub = int(inp.T_len[b]), int(inp.U_len[b])
@@ -217,8 +217,8 @@ def fd_check(inp, names=("hA", "hL", "WA", "WL", "bZ", "WO", "bO"), g=None, eps=
         assert err <= tol * max(1.0, np.max(np.abs(grad))), (name, err)
 
 
-def test_fd_every_parameter_config1():
-    fd_check(workload_inputs(1))
+def test_fd_every_parameter_tiny():
+    fd_check(workload_inputs("tiny-f32"))
 
 
 def test_fd_ragged_batch_with_biases():
@@ -272,12 +272,12 @@ def autograd_check(inp, g=None, tol=1e-12):
         assert err <= tol * max(1.0, np.max(np.abs(ref))), (k, err)
 
 
-def test_autograd_config1():
-    autograd_check(workload_inputs(1))
+def test_autograd_tiny():
+    autograd_check(workload_inputs("tiny-f32"))
 
 
-def test_autograd_reduced_config2():
-    # config-2 structure (bf16 values, Xavier weights, ragged lengths) at a size autograd can walk
+def test_autograd_reduced_small():
+    # small-workload structure (bf16 values, Xavier weights, ragged lengths) at a size autograd can walk
     inp = make_inputs(2, 9, 5, 40, 12, 10, 16, dtype="bf16", seed=2, t_range=(5, 9), u_range=(2, 5),
                       bias_std=0.2)
     autograd_check(inp, tol=1e-11)
@@ -317,12 +317,12 @@ def pin_suite():
     """Run the fast pins; return the names of those that fail."""
     failed = []
     checks = {
-        "brute": lambda: test_config1_brute_force(),
+        "brute": lambda: test_tiny_brute_force(),
         "identity": lambda: test_alpha_beta_identity_ragged(),
-        "closed_uniform": lambda: test_closed_form_uniform_config1_lattice(),
+        "closed_uniform": lambda: test_closed_form_uniform_tiny_lattice(),
         "closed_bias": lambda: test_closed_form_bias_only(6, 3, 5),
         "flows": lambda: test_flow_invariants_and_row_sums(),
-        "autograd": lambda: (autograd_check(workload_inputs(1)), autograd_check(_square_biased())),
+        "autograd": lambda: (autograd_check(workload_inputs("tiny-f32")), autograd_check(_square_biased())),
     }
     for name, fn in checks.items():
         try:
@@ -333,7 +333,7 @@ def pin_suite():
 
 
 def _square_biased():
-    # config-1 dimensions (H = H_A = H_L) with non-zero biases and ragged lengths
+    # tiny-workload dimensions (H = H_A = H_L) with non-zero biases and ragged lengths
     return make_inputs(3, 6, 3, 5, 8, 8, 8, dtype="f32", seed=23, enc="normal0.5", weights="normal0.5",
                        t_range=(2, 6), u_range=(0, 3), bias_std=0.4)
 
@@ -394,6 +394,6 @@ def test_pins_catch_wrong_dtanh(monkeypatch):
 
 
 def test_pins_catch_transposed_encoder_weight(monkeypatch):
-    # config 1 has H = H_A = H_L = 8, so a transposed W^A is shape-valid
+    # the tiny workload has H = H_A = H_L = 8, so a transposed W^A is shape-valid
     monkeypatch.setattr(ro, "encoding_grad", lambda g, W: g @ W.T)
     assert "autograd" in pin_suite()
