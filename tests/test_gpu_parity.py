@@ -88,14 +88,23 @@ def lnC(n, k):
 
 # ----------------------------------------------------------------------------- lattice kernel alone
 
-def test_lattice_kernel_matches_oracle(gpu_lib):
+# (T, U, T range, U range): the kernel variant is chosen by U + 1 (rows of 64
+# lanes: 1, 2, 3, 4, then the two wide variants above 256 rows); the U ranges
+# make rows beyond the first lane group live so neighbours cross lane groups.
+LATTICE_CASES = [(70, 40, (1, 70), (0, 40)), (90, 100, (1, 90), (64, 100)),
+                 (60, 170, (1, 60), (128, 170)), (50, 255, (1, 50), (192, 255)),
+                 (40, 300, (1, 40), (250, 300)), (24, 700, (1, 24), (500, 700))]
+
+
+@pytest.mark.parametrize("T,U,tr,ur", LATTICE_CASES)
+def test_lattice_kernel_matches_oracle(gpu_lib, T, U, tr, ur):
     import torch
 
     rl = gpu_lib
-    inp = make_inputs(5, 70, 40, 33, 8, 8, 8, dtype="f32", seed=31, t_range=(1, 70), u_range=(0, 40))
-    say("lattice kernel: B=5 T=70 U=40 ragged")
+    B, U1 = 5, U + 1
+    inp = make_inputs(B, T, U, 33, 8, 8, 8, dtype="f32", seed=31 + U, t_range=tr, u_range=ur)
+    say(f"lattice kernel: B={B} T={T} U={U} ragged")
     r = oracle.loss_and_grads(inp, want_grads=False)
-    B, T, U1 = 5, 70, 41
     phi = np.zeros((B, U1, T), np.float32)
     psi = np.zeros((B, U1, T), np.float32)
     for b, s in enumerate(r.samples):
@@ -107,19 +116,20 @@ def test_lattice_kernel_matches_oracle(gpu_lib):
     al = torch.full((B, U1, T), 7.0, device=dev)
     be = torch.full((B, U1, T), 7.0, device=dev)
     costs = torch.zeros(B, device=dev)
-    d = rl.make_desc(B, T, 40, 33, 8, 8, 8)
+    d = rl.make_desc(B, T, U, 33, 8, 8, 8)
     rl.rnnt_lattice(d, tp(inp.T_len), tp(inp.U_len), tp(phi), tp(psi), al, be, costs)
     torch.cuda.synchronize()
     al, be, costs = al.cpu().numpy(), be.cpu().numpy(), costs.cpu().numpy()
     for b, s in enumerate(r.samples):
         Tb, Ub = inp.T_len[b], inp.U_len[b]
-        assert abs(costs[b] - s.cost) <= 1e-5 * abs(s.cost)
+        assert abs(costs[b] - s.cost) <= 1e-5 * abs(s.cost), f"sample {b}"
         ga, gb = al[b, :Ub + 1, :Tb].T, be[b, :Ub + 1, :Tb].T
         scale = max(1.0, np.abs(s.alpha).max())
-        assert np.max(np.abs(ga - s.alpha)) <= 2e-6 * scale * (Tb + Ub)
-        assert np.max(np.abs(gb - s.beta)) <= 2e-6 * scale * (Tb + Ub)
+        assert np.max(np.abs(ga - s.alpha)) <= 2e-6 * scale * (Tb + Ub), f"alpha, sample {b}"
+        assert np.max(np.abs(gb - s.beta)) <= 2e-6 * scale * (Tb + Ub), f"beta, sample {b}"
         # cells outside the lattice are untouched
         assert np.all(al[b, Ub + 1:] == 7.0) and np.all(al[b, :, Tb:] == 7.0)
+        assert np.all(be[b, Ub + 1:] == 7.0) and np.all(be[b, :, Tb:] == 7.0)
 
 
 # ----------------------------------------------------------------------------- fp32 mode
