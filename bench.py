@@ -110,6 +110,34 @@ def cpu_baseline(inp, budget_s: float):
     }
 
 
+def reference_gemm(torch, w, rows=524288):
+    """Vendor bf16 GEMM (torch.matmul -> hipBLASLt) on the three product shapes of one wave of
+    `rows` lattice cells: scores z W^O^T, dz = dh W^O, dW^O = dh^T z. Context for the fused kernels'
+    MFMA fractions; these plain products fuse nothing."""
+    R, H, V = rows, w.H, w.V
+    g = torch.Generator(device="cuda").manual_seed(0)
+    z = torch.randn(R, H, device="cuda", dtype=torch.bfloat16, generator=g)
+    wo = torch.randn(V, H, device="cuda", dtype=torch.bfloat16, generator=g)
+    dh = torch.randn(R, V, device="cuda", dtype=torch.bfloat16, generator=g)
+    wot, dht = wo.t().contiguous(), dh.t().contiguous()
+    out = {}
+    for name, f in (("scores z W^O^T", lambda: torch.matmul(z, wot)), ("dz dh W^O", lambda: torch.matmul(dh, wo)),
+                    ("dW^O dh^T z", lambda: torch.matmul(dht, z))):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 20
+        tf = 2.0 * R * H * V / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_TFLOPS["bf16"], 4)}
+    print(json.dumps({"reference_gemm": out, "rows": R, "H": H, "V": V}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,10 +151,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget; 0 = skip")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (counter calibration)")
+    ap.add_argument("--reference-gemm", action="store_true",
+                    help="only time the vendor GEMM (torch.matmul) on this workload's three product shapes")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the batch shards by sample; see DESIGN.md for the multi-GPU design)", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the library computes one GPU's share of a batch sharded by sample)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -147,6 +177,9 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": 4 * n}))
+        return
+    if args.reference_gemm:
+        reference_gemm(torch, WORKLOADS[args.workload])
         return
     rl.load()
     w = WORKLOADS[args.workload]

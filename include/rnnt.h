@@ -58,7 +58,7 @@ typedef enum {
   RNNT_E_INVALID = -1,     /* bad dims, lengths, pointers or tile settings   */
   RNNT_E_WORKSPACE = -2,   /* saved/workspace smaller than rnnt_loss_query   */
   RNNT_E_HIP = -3,         /* a HIP runtime call or kernel launch failed      */
-  RNNT_E_UNSUPPORTED = -4  /* valid request outside this build's limits       */
+  RNNT_E_UNSUPPORTED = -4  /* valid request outside the library's limits      */
 } rnnt_status;
 
 typedef enum { RNNT_F32 = 0, RNNT_BF16 = 1 } rnnt_dtype;
@@ -78,7 +78,7 @@ typedef struct {
   int32_t reserved;              /* must be 0                                  */
 } rnnt_desc;
 
-/* Limits of this build (RNNT_E_UNSUPPORTED beyond them): H, HA, HL multiples
+/* Limits of this library (RNNT_E_UNSUPPORTED beyond them): H, HA, HL multiples
  * of 8; H <= 768; U+1 <= 1024; V <= 65536; B*T*(U+1) <= 2^30. Any tile size
  * is accepted; a tile's t extent is padded to a multiple of 32 rows inside the
  * library, so tile_t values that are multiples of 32 waste nothing. */

@@ -229,7 +229,7 @@ const char* rnnt_status_string(rnnt_status s) {
     case RNNT_E_INVALID: return "invalid argument";
     case RNNT_E_WORKSPACE: return "saved or workspace buffer too small";
     case RNNT_E_HIP: return "HIP runtime error";
-    case RNNT_E_UNSUPPORTED: return "unsupported by this build";
+    case RNNT_E_UNSUPPORTED: return "outside the limits of this library";
   }
   return "unknown status";
 }
@@ -901,7 +901,7 @@ rnnt_status rnnt_lattice(const rnnt_desc* desc, const int32_t* T_len_dev, const 
                          void* stream) {
   if (!desc) return fail(RNNT_E_INVALID, "desc is null");
   if (desc->B <= 0 || desc->T <= 0 || desc->U < 0) return fail(RNNT_E_INVALID, "need B, T > 0 and U >= 0");
-  if (desc->U + 1 > 1024) return fail(RNNT_E_UNSUPPORTED, "this build supports U + 1 <= 1024");
+  if (desc->U + 1 > 1024) return fail(RNNT_E_UNSUPPORTED, "this library supports U + 1 <= 1024");
   if (!T_len_dev || !U_len_dev || !phi || !psi || !alpha || !beta || !costs)
     return fail(RNNT_E_INVALID, "null pointer");
   rnnt::LatticeArgs la{T_len_dev, U_len_dev, phi, psi, alpha, beta, nullptr, costs, desc->B, desc->T, desc->U + 1};

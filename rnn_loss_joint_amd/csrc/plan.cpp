@@ -35,19 +35,19 @@ bool check_dims(const Dims& d, std::string& err, int& status) {
   }
   status = -4;  // RNNT_E_UNSUPPORTED
   if (d.H % 8 || d.HA % 8 || d.HL % 8) {
-    err = "this build needs H, HA and HL to be multiples of 8";
+    err = "this library needs H, HA and HL to be multiples of 8";
     return false;
   }
   if (d.H > 768) {
-    err = "this build supports H <= 768";
+    err = "this library supports H <= 768";
     return false;
   }
   if (d.U + 1 > 1024) {
-    err = "this build supports U + 1 <= 1024";
+    err = "this library supports U + 1 <= 1024";
     return false;
   }
   if (d.V > 65536) {
-    err = "this build supports V <= 65536";
+    err = "this library supports V <= 65536";
     return false;
   }
   if ((int64_t)d.B * d.T * (d.U + 1) > ((int64_t)1 << 30)) {
