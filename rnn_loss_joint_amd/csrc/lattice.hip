@@ -136,29 +136,46 @@ __global__ void __launch_bounds__(64) lattice_kernel(LatticeArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Windowed variant for U_b + 1 <= 256 (lanes own rows u = lane + 64 i).
-// The cells of diagonal d sit at t = d - u in the u-major arrays, so a
-// diagonal is a strided gather; per window of 8 diagonals, though, each row
-// u needs 8 consecutive t of phi and psi. Those are loaded coalesced (8 lanes
-// per row, 32 bytes), staged column-major in LDS (element e of row u at
-// e*264 + u floats: both the loader's and the row owners' accesses hit
-// distinct banks), and the window's alpha / beta go to an LDS tile flushed
-// the same way. The next window's loads are in flight while one computes.
-// Row u, element e of a window holds X[u][s_u + e], s_u = base - u, with
-// base = d0 - 1 (alpha, diagonals d0 .. d0+7) or d_hi - 7 (beta, diagonals
-// d_hi .. d_hi-7); the masks make every out-of-lattice entry -inf.
-constexpr int LW = 8;          // diagonals per window
-constexpr int LSTR = 264;      // LDS stride of one element column (floats)
-constexpr int LROWS = 256;
+// Multi-wave variant for U_b + 1 <= 64 NW: wave w of the workgroup owns rows
+// u = 64 w + lane, one per lane. The cells of diagonal d sit at t = d - u in
+// the u-major arrays, so a diagonal is a strided gather; over a window of SW
+// diagonals, though, each row needs SW consecutive t of phi and psi. A wave
+// loads them coalesced (16 lanes per row, 64 bytes), transposes them through
+// LDS (element e of row slot r at e * SSTR + r: the loader's and the row
+// owners' accesses both hit distinct banks) and writes its window of alpha /
+// beta back the same way. The next window's loads are in flight while a
+// window computes.
+//
+// The waves form a pipeline along u: alpha at row 64 w needs row 64 w - 1 of
+// the previous diagonal, which wave w - 1 owns, so wave w runs one window
+// behind wave w - 1 (beta: wave w runs one window behind wave w + 1, whose
+// row 64 (w + 1) it needs). The boundary row's values of a window go to an
+// LDS ring of the reading wave, indexed by position in the sweep (alpha:
+// d - 1, beta: D - 1 - d, so window k holds positions SW k .. SW k + SW - 1);
+// one barrier per window separates writer and reader. Step s of the
+// workgroup is window s - w of wave w (alpha) or s - (NW - 1 - w) (beta).
+//
+// Window k covers alpha diagonals d0 .. d0 + SW - 1 (d0 = 1 + SW k) or beta
+// diagonals d_hi .. d_hi - SW + 1 (d_hi = D - 1 - SW k). Row slot r, element
+// e of a window holds X[row][base - row + e] with base = d0 - 1 (alpha) or
+// d_hi - SW + 1 (beta); the psi slot of row u holds row u - 1 for alpha (the
+// label transition into u) and row u for beta. Out-of-lattice entries are
+// -inf.
+constexpr int SW = 16;       // diagonals per window
+constexpr int SSTR = 68;     // LDS stride of one element column (floats)
+constexpr int SRING = 64;    // boundary ring entries per wave (> 2 SW)
+constexpr int SWAVE_LDS = 3 * SW * SSTR;  // phi, psi, output tile
 
-template <int NI>
-__global__ void __launch_bounds__(64) lattice_win_kernel(LatticeArgs p) {
-  __shared__ float lds[(4 * LW + LW) * LSTR];  // phi/psi x 2 buffers, output tile
-  float* const stg = lds;                       // [buf][arr][e][u]: ((buf*2+arr)*LW + e)*LSTR + u
-  float* const out = lds + 4 * LW * LSTR;       // [e][u]
+// workgroup barrier that orders LDS only: the global loads in flight for the
+// next window stay in flight across it
+__device__ inline void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int NW, bool is_beta>
+__device__ __attribute__((always_inline)) inline void lattice_sys_body(const LatticeArgs& p, float* lds) {
   const int b = blockIdx.x;
-  const bool is_beta = blockIdx.y == 1;
-  const int lane = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int u = 64 * wave + lane;
   const int Tb = p.T_len[b], Ub = p.U_len[b];
   const int T = p.T;
   const size_t base0 = (size_t)b * p.U1 * T;
@@ -166,40 +183,55 @@ __global__ void __launch_bounds__(64) lattice_win_kernel(LatticeArgs p) {
   const float* psi = p.psi + base0;
   float* res = (is_beta ? p.beta : p.alpha) + base0;
   const int D = Tb - 1 + Ub;
-  constexpr int NJ = NI * 8;  // load instructions per array per window (8 rows each)
-  const int lr = lane >> 3, le = lane & 7;  // loader: row within an 8-row group, element
+  const int nwin = (D + SW - 1) / SW;
+  const int nsteps = nwin > 0 ? nwin + NW - 1 : 0;
+  const int lag = is_beta ? NW - 1 - wave : wave;
+  const int psi_shift = is_beta ? 0 : 1;
+  const bool live = 64 * wave <= Ub;  // a wave past U_b holds only -inf rows
 
-  // raw values of window `base` for this lane's loader slots. The loads are
-  // unconditional (masked entries read element 0 of the sample) and their
-  // results are not touched until stage() one window later, so the whole
-  // batch is in flight together; stage() applies the masks (-inf).
-  float sphi[NJ], spsi[NJ];
-  auto okp = [&](int u, int t) { return u <= Ub && t >= 0 && t <= Tb - 2; };
-  auto oks = [&](int u, int t) { return u < Ub && t >= 0 && t <= Tb - 1; };
-  auto load = [&](int base) {
+  float* const sphi_l = lds + wave * SWAVE_LDS;  // [e][slot]
+  float* const spsi_l = sphi_l + SW * SSTR;
+  float* const out = spsi_l + SW * SSTR;
+  float* const ring = lds + NW * SWAVE_LDS;       // [wave][SRING]: value the wave reads
+  float* const my_ring = ring + wave * SRING;
+
+  // loader lanes: slot r = 4 j + lr (j = 0 .. 15), element le. Element e of
+  // row r sits at r T + base - r + e = r (T - 1) + base + e; every index is
+  // clamped into the sample's [U1][T] block, so entries outside the lattice
+  // read arbitrary values of the sample. They are made finite at staging
+  // (fminf maps NaN and +inf to FLT_MAX) and never reach a lattice cell: the
+  // cell mask below keeps every out-of-lattice alpha / beta at -inf, and a
+  // valid cell's phi / psi operands are in the lattice or are added to such a
+  // -inf neighbour.
+  const int lr = lane >> 4, le = lane & 15;
+  const int lane_ix = lr * (T - 1) + le;
+  const int last_ix = p.U1 * T - 1;
+  float rphi[16], rpsi[16];
+  auto window_base = [&](int k) { return is_beta ? D - 1 - SW * k - (SW - 1) : SW * k; };
+  auto load = [&](int k) {
+    const int row0 = (64 * wave) * (T - 1) + window_base(k) + lane_ix;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int u = 8 * j + lr, t = base - u + le;
-      const int ix = u * T + t;
-      sphi[j] = phi[okp(u, t) ? ix : 0];
-      spsi[j] = psi[oks(u, t) ? ix : 0];
+    for (int j = 0; j < 16; ++j) {
+      const int ip = row0 + 4 * j * (T - 1), is = ip - psi_shift * (T - 1);
+      rphi[j] = phi[(unsigned)min(max(ip, 0), last_ix)];
+      rpsi[j] = psi[(unsigned)min(max(is, 0), last_ix)];
     }
   };
-  auto stage = [&](int buf, int base) {
+  auto stage = [&]() {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int u = 8 * j + lr, t = base - u + le;
-      stg[((buf * 2 + 0) * LW + le) * LSTR + u] = okp(u, t) ? sphi[j] : kNegInf;
-      stg[((buf * 2 + 1) * LW + le) * LSTR + u] = oks(u, t) ? spsi[j] : kNegInf;
+    for (int j = 0; j < 16; ++j) {
+      sphi_l[le * SSTR + 4 * j + lr] = fminf(rphi[j], __FLT_MAX__);
+      spsi_l[le * SSTR + 4 * j + lr] = fminf(rpsi[j], __FLT_MAX__);
     }
   };
-  // write the window's results: row u, element e -> res[u][s_u + e + shift]
-  auto flush = [&](int base, int shift) {
+  // results of window k: slot r, element e -> res[row][base - row + e + shift]
+  auto flush = [&](int k) {
+    const int base = window_base(k) + (is_beta ? 0 : 1);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int u = 8 * j + lr, t = base - u + le + shift;
-      const float v = out[le * LSTR + 8 * j + lr];
-      if (u <= Ub && t >= 0 && t < Tb) res[u * T + t] = v;
+    for (int j = 0; j < 16; ++j) {
+      const int r = 64 * wave + 4 * j + lr, t = base - r + le;
+      const float v = out[le * SSTR + 4 * j + lr];
+      if ((r <= Ub) & ((unsigned)t < (unsigned)Tb)) res[(unsigned)(r * T + t)] = v;
     }
   };
   // neighbour rows through DPP wave shifts: lane l receives lane l-1's
@@ -210,113 +242,113 @@ __global__ void __launch_bounds__(64) lattice_win_kernel(LatticeArgs p) {
   auto from_next_lane = [](float v, float old) {
     return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), 0x130, 0xf, 0xf, false));
   };
-  // one lane's value, moved as bits (the readlane builtin takes an int)
-  auto lane_value = [](float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
 
-  float cur[NI];
+  for (int i = threadIdx.x; i < NW * SRING; i += 64 * NW) ring[i] = kNegInf;
+  float cur;
+  float lnP = kNegInf;
   if (!is_beta) {
-    // diagonal 0: alpha(0, 0) = 0
-#pragma unroll
-    for (int i = 0; i < NI; ++i) cur[i] = (lane + 64 * i == 0) ? 0.0f : kNegInf;
-    if (lane == 0) res[0] = 0.0f;
-    float lnP = kNegInf;
-    int k = 0;
-    load(0);  // window d0 = 1: base = d0 - 1 = 0
-    stage(0, 0);
-    if (1 + LW <= D) load(LW);
-    for (int d0 = 1; d0 <= D; d0 += LW, ++k) {
-      const float* sp = stg + ((k & 1) * 2 + 0) * LW * LSTR;
-      const float* ss = stg + ((k & 1) * 2 + 1) * LW * LSTR;
-#pragma unroll
-      for (int w = 0; w < LW; ++w) {
-        const int d = d0 + w;
-        float nxt[NI];
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const int u = lane + 64 * i;
-          const float wrap = i > 0 ? lane_value(cur[i > 0 ? i - 1 : 0], 63) : kNegInf;
-          const float left = from_prev_lane(cur[i], wrap);
-          const float from_t = cur[i] + sp[w * LSTR + u];
-          const float from_u = left + (u > 0 ? ss[w * LSTR + u - 1] : kNegInf);
-          nxt[i] = log_add_exp(from_t, from_u);
-        }
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const int u = lane + 64 * i, t = d - u;
-          const bool ok = u <= Ub && t >= 0 && t < Tb;
-          cur[i] = ok ? nxt[i] : kNegInf;
-          out[w * LSTR + u] = cur[i];
-          if (d == D && u == Ub) lnP = cur[i];
-        }
-      }
-      // stage the next window (its loads were in flight), then write this one
-      if (d0 + LW <= D) {
-        stage((k + 1) & 1, d0 + LW - 1);
-        if (d0 + 2 * LW <= D) load(d0 + 2 * LW - 1);
-      }
-      flush(d0 - 1, 1);
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      if (lane + 64 * i == Ub) {
-        if (D == 0) lnP = cur[i];
-        const float v = lnP + phi[(size_t)Ub * T + Tb - 1];
-        if (p.lnP) p.lnP[b] = v;
-        if (p.costs) p.costs[b] = -v;
-      }
-    }
+    cur = u == 0 ? 0.0f : kNegInf;  // diagonal 0
+    if (u == 0) res[0] = 0.0f;
   } else {
-    // diagonal D: beta(T_b-1, U_b) = phi(T_b-1, U_b)
-    const float fin = phi[(size_t)Ub * T + Tb - 1];
+    const float fin = phi[(unsigned)(Ub * T + Tb - 1)];  // diagonal D
+    cur = u == Ub ? fin : kNegInf;
+    if (u == Ub) res[(unsigned)(Ub * T + Tb - 1)] = fin;
+  }
+  if (live && nwin > 0) {
+    load(0);
+    stage();
+    if (nwin > 1) load(1);
+  }
+  lds_sync();
+  // beta: the boundary value at diagonal D (position -1) for the wave below
+  if (is_beta && wave > 0 && lane == 0) ring[(wave - 1) * SRING + SRING - 1] = cur;
+
+  for (int s = 0; s < nsteps; ++s) {
+    const int k = s - lag;
+    if (live && k >= 0 && k < nwin) {
+      // window operands into registers first: element e = w (alpha) or
+      // SW - 1 - w (beta); the neighbour row's value one position earlier
+      float vp[SW], vs[SW], vn[SW];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) cur[i] = (lane + 64 * i == Ub) ? fin : kNegInf;
-    if (lane == 0) res[(size_t)Ub * T + Tb - 1] = fin;
-    int k = 0;
-    if (D - 1 >= 0) load(D - 1 - (LW - 1));
-    if (D - 1 >= 0) stage(0, D - 1 - (LW - 1));
-    if (D - 1 - LW >= 0) load(D - 1 - LW - (LW - 1));
-    for (int dh = D - 1; dh >= 0; dh -= LW, ++k) {
-      const float* sp = stg + ((k & 1) * 2 + 0) * LW * LSTR;
-      const float* ss = stg + ((k & 1) * 2 + 1) * LW * LSTR;
-#pragma unroll
-      for (int w = 0; w < LW; ++w) {
-        const int d = dh - w, e = LW - 1 - w;
-        float nxt[NI];
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const int u = lane + 64 * i;
-          const float wrap = i + 1 < NI ? lane_value(cur[i + 1 < NI ? i + 1 : i], 0) : kNegInf;
-          const float right = from_next_lane(cur[i], wrap);
-          const float by_blank = cur[i] + sp[e * LSTR + u];
-          const float by_label = right + ss[e * LSTR + u];
-          nxt[i] = log_add_exp(by_blank, by_label);
-        }
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const int u = lane + 64 * i, t = d - u;
-          const bool ok = u <= Ub && t >= 0 && t < Tb;
-          cur[i] = ok ? nxt[i] : kNegInf;
-          out[e * LSTR + u] = cur[i];
-        }
+      for (int w = 0; w < SW; ++w) {
+        const int e = is_beta ? SW - 1 - w : w;
+        vp[w] = sphi_l[e * SSTR + lane];
+        vs[w] = spsi_l[e * SSTR + lane];
       }
-      if (dh - LW >= 0) {
-        stage((k + 1) & 1, dh - LW - (LW - 1));
-        if (dh - 2 * LW >= 0) load(dh - 2 * LW - (LW - 1));
+      const int slot = (SW * k) & (SRING - 1);
+      vn[0] = my_ring[(slot - 1) & (SRING - 1)];
+#pragma unroll
+      for (int q = 0; q < SW / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(my_ring + slot + 4 * q);
+        if (4 * q + 1 < SW) vn[4 * q + 1] = v.x;
+        if (4 * q + 2 < SW) vn[4 * q + 2] = v.y;
+        if (4 * q + 3 < SW) vn[4 * q + 3] = v.z;
+        if (4 * q + 4 < SW) vn[4 * q + 4] = v.w;
       }
-      flush(dh - (LW - 1), 0);
+      // position w of the window is diagonal d0 + w (alpha) or d_hi - w
+      // (beta); the cell's t = d - u runs up (alpha) or down (beta) with w
+      const int t0 = is_beta ? D - 1 - SW * k - u : 1 + SW * k - u;
+      const bool row_ok = u <= Ub;
+      float res_w[SW];
+#pragma unroll
+      for (int w = 0; w < SW; ++w) {
+        const float nb = is_beta ? from_next_lane(cur, vn[w]) : from_prev_lane(cur, vn[w]);
+        const float nxt = log_add_exp(cur + vp[w], nb + vs[w]);
+        const int t = is_beta ? t0 - w : t0 + w;
+        cur = (row_ok & ((unsigned)t < (unsigned)Tb)) ? nxt : kNegInf;
+        res_w[w] = cur;
+      }
+      if (!is_beta && k == nwin - 1) {
+        // diagonal D is position D - 1 - SW k of the last window
+#pragma unroll
+        for (int w = 0; w < SW; ++w)
+          if (w == D - 1 - SW * k && u == Ub) lnP = res_w[w];
+      }
+#pragma unroll
+      for (int w = 0; w < SW; ++w) out[(is_beta ? SW - 1 - w : w) * SSTR + lane] = res_w[w];
+      // the edge lane's values go to the neighbour wave's ring
+      const int nbw = is_beta ? wave - 1 : wave + 1;
+      if (nbw >= 0 && nbw < NW && lane == (is_beta ? 0 : 63)) {
+        float* dst = ring + nbw * SRING + slot;
+#pragma unroll
+        for (int q = 0; q < SW / 4; ++q)
+          *reinterpret_cast<float4*>(dst + 4 * q) =
+              make_float4(res_w[4 * q], res_w[4 * q + 1], res_w[4 * q + 2], res_w[4 * q + 3]);
+      }
+      // stage the next window (its loads were in flight), start the one
+      // after, then write this window's results
+      if (k + 1 < nwin) {
+        stage();
+        if (k + 2 < nwin) load(k + 2);
+      }
+      flush(k);
     }
+    lds_sync();
+  }
+  if (!is_beta && u == Ub) {
+    if (D == 0) lnP = cur;
+    const float v = lnP + phi[(unsigned)(Ub * T + Tb - 1)];
+    if (p.lnP) p.lnP[b] = v;
+    if (p.costs) p.costs[b] = -v;
   }
 }
 
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) lattice_sys_kernel(LatticeArgs p) {
+  __shared__ __attribute__((aligned(16))) float lds[NW * SWAVE_LDS + NW * SRING];
+  if (blockIdx.y == 0) lattice_sys_body<NW, false>(p, lds);
+  else lattice_sys_body<NW, true>(p, lds);
+}
+
 hipError_t launch_lattice(const LatticeArgs& a, int U1max, hipStream_t st) {
-  dim3 grid(a.B, 2), block(64);
   if (a.B == 0) return hipSuccess;
-  if (U1max <= 64) hipLaunchKernelGGL((lattice_win_kernel<1>), grid, block, 0, st, a);
-  else if (U1max <= 128) hipLaunchKernelGGL((lattice_win_kernel<2>), grid, block, 0, st, a);
-  else if (U1max <= 192) hipLaunchKernelGGL((lattice_win_kernel<3>), grid, block, 0, st, a);
-  else if (U1max <= 256) hipLaunchKernelGGL((lattice_win_kernel<4>), grid, block, 0, st, a);
-  else if (U1max <= 512) hipLaunchKernelGGL((lattice_kernel<8, 8>), grid, block, 0, st, a);
-  else if (U1max <= 1024) hipLaunchKernelGGL((lattice_kernel<16, 4>), grid, block, 0, st, a);
+  const dim3 grid(a.B, 2);
+  if (U1max <= 64) hipLaunchKernelGGL((lattice_sys_kernel<1>), grid, dim3(64), 0, st, a);
+  else if (U1max <= 128) hipLaunchKernelGGL((lattice_sys_kernel<2>), grid, dim3(128), 0, st, a);
+  else if (U1max <= 192) hipLaunchKernelGGL((lattice_sys_kernel<3>), grid, dim3(192), 0, st, a);
+  else if (U1max <= 256) hipLaunchKernelGGL((lattice_sys_kernel<4>), grid, dim3(256), 0, st, a);
+  else if (U1max <= 512) hipLaunchKernelGGL((lattice_sys_kernel<8>), grid, dim3(512), 0, st, a);
+  else if (U1max <= 1024) hipLaunchKernelGGL((lattice_kernel<16, 4>), grid, dim3(64), 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
