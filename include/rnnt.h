@@ -125,10 +125,14 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
  * Eqs. (8)-(9)) on caller-given two log-probs, for testing and for callers
  * that produce phi/psi themselves. T_len_dev / U_len_dev are DEVICE int32
  * arrays [B] (same ranges as above, not checked here). phi, psi, alpha, beta
- * are fp32 [B, U+1, T] on the device (t fastest); psi at u = U_len[b] is
- * never read. costs[b] = -(alpha(T_b-1,U_b) + phi(T_b-1,U_b)). Cells outside
- * a sample's lattice are not written. desc supplies B, T, U (other fields
- * are ignored). */
+ * are fp32 device arrays in the diagonal-major lattice layout: with
+ * ND = T + U and US = U + 1 rounded up to a multiple of 32, cell (t, u) of
+ * sample b is element (b * ND + t + u) * US + u (B * ND * US elements per
+ * array). Elements that are not cells of a sample's lattice may hold any
+ * value, NaN and infinities included, and do not affect the results; psi
+ * at u = U_len[b] likewise. costs[b] = -(alpha(T_b-1,U_b) + phi(T_b-1,U_b)).
+ * Only the lattice cells of alpha and beta are written. desc supplies B, T,
+ * U (other fields are ignored). */
 rnnt_status rnnt_lattice(const rnnt_desc* desc, const int32_t* T_len_dev,
                          const int32_t* U_len_dev, const float* phi, const float* psi,
                          float* alpha, float* beta, float* costs, void* stream);

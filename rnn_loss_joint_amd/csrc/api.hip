@@ -405,7 +405,7 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
       mg.psi = sv.psi;
       {
         ProfScope ps_("lse_merge", st);
-        RNNT_HIP(rnnt::launch_lse_merge(mg, st));
+        RNNT_HIP(rnnt::launch_lse_merge(mg, d.tile_t, d.tile_u, st));
       }
     }
   } else {
@@ -620,7 +620,7 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
         a3.dcosts = dcosts;
         {
           ProfScope ps_("coef", st);
-          RNNT_HIP(rnnt::launch_coef(a3, st));
+          RNNT_HIP(rnnt::launch_coef(a3, d.tile_t, d.tile_u, st));
         }
         {
           ProfScope ps_("scores_bwd", st);

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common_host.hpp"
+
 namespace rnnt {
 
 typedef __bf16 bf16;

@@ -192,19 +192,19 @@ joint_kernel(JointArgs p) {
   if (BWD) {
     if (g == 0) {
       if (row_ok) {
-        size_t idx = ((size_t)b * U1 + u) * T + t_r;
+        size_t idx = (size_t)lat_ix(b, t_r, u, T, U1);
         float lp = p.lnP[b];
         float gb = p.dcosts ? p.dcosts[b] : 1.0f;
         float A = p.alpha[idx];
         float Bt = p.beta[idx];
         float ph = p.phi[idx];
         my_lse = p.lse[idx];
-        float bn = (t_r + 1 < Tb) ? p.beta[idx + 1] : (u == Ub ? 0.0f : kNegInf);
+        float bn = (t_r + 1 < Tb) ? p.beta[idx + lat_us(U1)] : (u == Ub ? 0.0f : kNegInf);
         my_occ = gb * fexp2((A + Bt - lp) * kLog2e);
         my_cb = gb * fexp2((A + ph + bn - lp) * kLog2e);
         if (u < Ub) {
           float ps = p.psi[idx];
-          float ln = p.beta[idx + T];
+          float ln = p.beta[idx + lat_us(U1) + 1];
           my_cl = gb * fexp2((A + ps + ln - lp) * kLog2e);
         }
       }
@@ -354,7 +354,7 @@ joint_kernel(JointArgs p) {
     __syncthreads();
     if (row_ok && g == 0) {
       float ls = row_lds[wave][0][r];
-      size_t idx = ((size_t)b * U1 + u) * T + t_r;
+      size_t idx = (size_t)lat_ix(b, t_r, u, T, U1);
       p.lse_out[idx] = ls;
       p.phi_out[idx] = hb - ls;
       p.psi_out[idx] = (u < Ub) ? hy - ls : kNegInf;
@@ -397,16 +397,16 @@ __global__ void __launch_bounds__(256) dh_inplace_kernel(DhInplaceArgs p) {
     float ls = 0, co = 0, cb = 0, cl = 0;
     float lab = -1;
     if (valid) {
-      size_t idx = ((size_t)b * U1 + u) * T + t;
+      size_t idx = (size_t)lat_ix(b, t, u, T, U1);
       float lp = p.lnP[b];
       float gb = p.dcosts ? p.dcosts[b] : 1.0f;
       float A = p.alpha[idx], Bt = p.beta[idx], ph = p.phi[idx];
       ls = p.lse[idx];
-      float bn = (t + 1 < Tb) ? p.beta[idx + 1] : (u == Ub ? 0.0f : kNegInf);
+      float bn = (t + 1 < Tb) ? p.beta[idx + lat_us(U1)] : (u == Ub ? 0.0f : kNegInf);
       co = gb * fexp2((A + Bt - lp) * kLog2e);
       cb = gb * fexp2((A + ph + bn - lp) * kLog2e);
       if (u < Ub) {
-        cl = gb * fexp2((A + p.psi[idx] + p.beta[idx + T] - lp) * kLog2e);
+        cl = gb * fexp2((A + p.psi[idx] + p.beta[idx + lat_us(U1) + 1] - lp) * kLog2e);
         lab = (float)p.labels[(size_t)b * U1 + u + 1];
       }
     }

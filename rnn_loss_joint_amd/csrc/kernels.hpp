@@ -22,7 +22,7 @@ struct JointArgs {
   const float* l;  // [B*U1, H_pad] W^L h^L
   const void* WO;  // [V, H]
   const void* bO;  // [V]
-  // forward outputs, [B, U1, T]
+  // forward outputs, lattice layout (lat_ix)
   float* lse_out;
   float* phi_out;
   float* psi_out;
@@ -68,7 +68,7 @@ hipError_t launch_dh_inplace(const DhInplaceArgs& a, bool bf16_mode, hipStream_t
 struct LatticeArgs {
   const int32_t* T_len;
   const int32_t* U_len;
-  const float* phi;  // [B, U1, T]
+  const float* phi;  // lattice layout (lat_ix)
   const float* psi;
   float* alpha;
   float* beta;
@@ -239,7 +239,8 @@ struct Scores3Args {
 hipError_t launch_scores3(const Scores3Args& a, bool bwd, hipStream_t st);
 hipError_t launch_score_tables(const void* WO, const void* bO, void* WOp, float* bl, int V, int H, int H_pad,
                                int nvt, hipStream_t st);
-hipError_t launch_coef(const Scores3Args& a, hipStream_t st);
+// grid over the wave's tiles x 32 x 32 blocks (+1 for the padding rows)
+hipError_t launch_coef(const Scores3Args& a, int tile_t, int tile_u, hipStream_t st);
 hipError_t launch_dh_fix(const Scores3Args& a, hipStream_t st);
 
 struct MergeArgs {
@@ -254,7 +255,8 @@ struct MergeArgs {
   float* phi;
   float* psi;
 };
-hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t st);
+// grid over the wave's tiles x 32 x 32 blocks: tile_t x tile_u bound every tile
+hipError_t launch_lse_merge(const MergeArgs& a, int tile_t, int tile_u, hipStream_t st);
 // dst[h, v] = src[v, h] for v < V (0 for V <= v < V_pad), element size 2 or 4
 hipError_t launch_transpose_wo(void* dst, const void* src, int V, int H, int V_pad, bool bf16, hipStream_t st);
 hipError_t launch_fill_bytes(void* p, int64_t nbytes, hipStream_t st);

@@ -362,16 +362,16 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoresArgs p) {
       if (tloc < tl.ht) {
         const int b = tl.b, u = tl.u0 + ul, t = tl.t0 + tloc;
         const int Tb = p.T_len[b], Ub = p.U_len[b];
-        const size_t idx = ((size_t)b * p.U1 + u) * p.T + t;
+        const size_t idx = (size_t)lat_ix(b, t, u, p.T, p.U1);
         const float lp = p.lnP[b];
         const float gb = p.dcosts ? p.dcosts[b] : 1.0f;
         const float A = p.alpha[idx], Bt = p.beta[idx];
         ls = p.lse[idx];
-        const float bn = (t + 1 < Tb) ? p.beta[idx + 1] : (u == Ub ? 0.0f : kNegInf);
+        const float bn = (t + 1 < Tb) ? p.beta[idx + lat_us(p.U1)] : (u == Ub ? 0.0f : kNegInf);
         co = gb * fexp2((A + Bt - lp) * kLog2e);
         cb = gb * fexp2((A + p.phi[idx] + bn - lp) * kLog2e);
         if (u < Ub) {
-          cl = gb * fexp2((A + p.psi[idx] + p.beta[idx + p.T] - lp) * kLog2e);
+          cl = gb * fexp2((A + p.psi[idx] + p.beta[idx + lat_us(p.U1) + 1] - lp) * kLog2e);
           lab = (float)p.labels[(size_t)b * p.U1 + u + 1];
         }
       }
@@ -537,38 +537,52 @@ hipError_t launch_scores(const ScoresArgs& a, bool bwd, hipStream_t st) {
 }
 
 // lse = logsumexp over the V tiles' partial statistics; phi, psi from the
-// blank / label scores; written to the [b, u, t] arrays for valid cells.
+// blank / label scores, for the valid cells. One workgroup per 32 t x 32 u
+// block of a tile: the block's rows are read in row order (t fastest) and
+// the results, transposed through LDS, are written along the block's
+// anti-diagonals, which are contiguous in the lattice layout.
+constexpr int kMB = 32, kMS = 34;  // block edge, LDS row stride (conflict-free both ways)
 __global__ void __launch_bounds__(256) lse_merge_kernel(MergeArgs p) {
-  const int rr = blockIdx.x * 256 + threadIdx.x;
-  if (rr >= p.n_rows) return;
-  const int R = rr + p.buf_row_base;
-  int lo = p.tile_begin, hi = p.tile_end - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (p.tiles[mid].row0 <= R) lo = mid; else hi = mid - 1;
+  __shared__ float sm[3][kMB * kMS];  // lse, phi, psi at [u][t]
+  const Tile tl = p.tiles[p.tile_begin + blockIdx.x];
+  const int tb = blockIdx.y * kMB, ub = blockIdx.z * kMB;
+  if (tb >= tl.ht || ub >= tl.wu) return;
+  const int nt = min(kMB, tl.ht - tb), nu = min(kMB, tl.wu - ub);
+  const int b = tl.b, Ub = p.U_len[b];
+#pragma unroll
+  for (int i = threadIdx.x; i < kMB * kMB; i += 256) {
+    const int ul = i / kMB, tt = i % kMB;
+    if (ul >= nu || tt >= nt) continue;
+    const int rr = tl.row0 + (ub + ul) * tl.htp + tb + tt - p.buf_row_base;
+    float M = -1e30f;
+    for (int v = 0; v < p.nvt; ++v) M = __builtin_fmaxf(M, p.stats[(int64_t)rr * p.nvt + v][0]);
+    float S = 0.0f;
+    for (int v = 0; v < p.nvt; ++v) {
+      const f32x2 st = p.stats[(int64_t)rr * p.nvt + v];
+      S += st[1] * fexp2((st[0] - M) * kLog2e);
+    }
+    const float lse = M + kLn2 * flog2(S);
+    sm[0][ul * kMS + tt] = lse;
+    sm[1][ul * kMS + tt] = p.hb[rr] - lse;
+    sm[2][ul * kMS + tt] = tl.u0 + ub + ul < Ub ? p.hy[rr] - lse : kNegInf;
   }
-  const Tile tl = p.tiles[lo];
-  const int local_r = R - tl.row0;
-  const int ul = local_r / tl.htp, tloc = local_r - ul * tl.htp;
-  if (tloc >= tl.ht) return;
-  const int b = tl.b, u = tl.u0 + ul, t = tl.t0 + tloc;
-  float M = -1e30f;
-  for (int v = 0; v < p.nvt; ++v) M = __builtin_fmaxf(M, p.stats[(int64_t)rr * p.nvt + v][0]);
-  float S = 0.0f;
-  for (int v = 0; v < p.nvt; ++v) {
-    const f32x2 st = p.stats[(int64_t)rr * p.nvt + v];
-    S += st[1] * fexp2((st[0] - M) * kLog2e);
+  __syncthreads();
+#pragma unroll
+  for (int i = threadIdx.x; i < (2 * kMB - 1) * kMB; i += 256) {
+    const int dl = i / kMB, ul = i % kMB, tt = dl - ul;
+    if (ul >= nu || tt < 0 || tt >= nt) continue;
+    const size_t idx = (size_t)lat_ix(b, tl.t0 + tb + tt, tl.u0 + ub + ul, p.T, p.U1);
+    p.lse[idx] = sm[0][ul * kMS + tt];
+    p.phi[idx] = sm[1][ul * kMS + tt];
+    p.psi[idx] = sm[2][ul * kMS + tt];
   }
-  const float lse = M + kLn2 * flog2(S);
-  const size_t idx = ((size_t)b * p.U1 + u) * p.T + t;
-  p.lse[idx] = lse;
-  p.phi[idx] = p.hb[rr] - lse;
-  p.psi[idx] = u < p.U_len[b] ? p.hy[rr] - lse : kNegInf;
 }
 
-hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t st) {
-  if (a.n_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(lse_merge_kernel, dim3((a.n_rows + 255) / 256), dim3(256), 0, st, a);
+hipError_t launch_lse_merge(const MergeArgs& a, int tile_t, int tile_u, hipStream_t st) {
+  const int ntiles = a.tile_end - a.tile_begin;
+  if (ntiles <= 0) return hipSuccess;
+  const dim3 grid(ntiles, (tile_t + kMB - 1) / kMB, (tile_u + kMB - 1) / kMB);
+  hipLaunchKernelGGL(lse_merge_kernel, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -219,7 +219,7 @@ Layout make_layout(const Plan& p) {
   L.off_groups = take(sizeof(GroupH) * p.groups.size());
   L.off_gidx = take(sizeof(int32_t) * p.gidx.size());
   L.plan_bytes = o;
-  const size_t cells = (size_t)d.B * p.U1 * d.T;
+  const size_t cells = (size_t)lat_cells(d.B, d.T, p.U1);
   L.off_a = take(sizeof(float) * (size_t)d.B * d.T * p.H_pad);
   L.off_l = take(sizeof(float) * (size_t)d.B * p.U1 * p.H_pad);
   L.off_lse = take(sizeof(float) * cells);

@@ -416,39 +416,87 @@ hipError_t launch_score_tables(const void* WO, const void* bO, void* WOp, float*
 // Per buffer row (cell) of a wave, the backward coefficients of Eq. (10):
 // coefA = (lse log2 e, g alpha beta / P), coefB = (g alpha phi beta' / P,
 // g alpha psi beta'' / P, label, 0); zeros (label -1) on padding rows.
-__global__ void coef_kernel(Scores3Args p) {
-  const int rr = blockIdx.x * blockDim.x + threadIdx.x;
-  if (rr >= p.n_ct * s3::BN) return;
-  float ls = 0.0f, co = 0.0f, cb = 0.0f, cl = 0.0f, lab = -1.0f;
-  if (rr < p.n_rows) {
-    const int R = rr + p.buf_row_base;
-    int lo = p.tile_begin, hi = p.tile_end - 1;
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (p.tiles[mid].row0 <= R) lo = mid; else hi = mid - 1;
+// One workgroup per 32 t x 32 u block of a tile: the lattice values are read
+// along the block's anti-diagonals (contiguous in the lattice layout) into
+// LDS, beta with one more t and u for the neighbours, and the coefficients
+// are written in row order. The workgroup past the last tile clears the
+// rows between the wave's last row and the 128-row padding.
+constexpr int kCB = 32, kCS = 34;  // block edge, LDS row stride (conflict-free both ways)
+__global__ void __launch_bounds__(256) coef_kernel(Scores3Args p) {
+  __shared__ float sm[4][kCB * kCS];        // alpha, phi, psi, lse at [u][t]
+  __shared__ float sb[(kCB + 1) * kCS];     // beta at [u][t], u, t <= 32
+  f32x2* coefA = reinterpret_cast<f32x2*>(p.coefA);
+  f32x4* coefB = reinterpret_cast<f32x4*>(p.coefB);
+  if ((int)blockIdx.x == p.tile_end - p.tile_begin) {
+    if (blockIdx.y == 0 && blockIdx.z == 0)
+      for (int rr = p.n_rows + threadIdx.x; rr < p.n_ct * s3::BN; rr += 256) {
+        coefA[rr] = f32x2{0.0f, 0.0f};
+        coefB[rr] = f32x4{0.0f, 0.0f, -1.0f, 0.0f};
+      }
+    return;
+  }
+  const Tile tl = p.tiles[p.tile_begin + blockIdx.x];
+  const int tb = blockIdx.y * kCB, ub = blockIdx.z * kCB;
+  if (tb >= tl.ht || ub >= tl.wu) return;
+  const int nt = min(kCB, tl.ht - tb), nu = min(kCB, tl.wu - ub);
+  const int b = tl.b, Tb = p.T_len[b], Ub = p.U_len[b];
+  const int t0 = tl.t0 + tb, u0 = tl.u0 + ub;
+  // lattice -> LDS along anti-diagonals of the (33 x 33) region; all loads
+  // of the thread are issued before any is stored (masked slots read entry 0)
+  constexpr int kSlots = (2 * kCB + 1) * (kCB + 1), kIt = (kSlots + 255) / 256;
+  float va[kIt], vb[kIt], vp[kIt], vs[kIt], vl[kIt];
+#pragma unroll
+  for (int q = 0; q < kIt; ++q) {
+    const int i = threadIdx.x + 256 * q;
+    const int dl = i / (kCB + 1), ul = i % (kCB + 1), tt = dl - ul;
+    const bool okb = i < kSlots && tt >= 0 && tt <= kCB && t0 + tt < Tb && u0 + ul <= Ub;
+    const bool oka = okb && tt < nt && ul < nu;
+    const size_t idx = okb ? (size_t)lat_ix(b, t0 + tt, u0 + ul, p.T, p.U1) : 0;
+    const size_t ia = oka ? idx : 0;
+    vb[q] = p.beta[idx];
+    va[q] = p.alpha[ia];
+    vp[q] = p.phi[ia];
+    vs[q] = p.psi[ia];
+    vl[q] = p.lse[ia];
+  }
+#pragma unroll
+  for (int q = 0; q < kIt; ++q) {
+    const int i = threadIdx.x + 256 * q;
+    const int dl = i / (kCB + 1), ul = i % (kCB + 1), tt = dl - ul;
+    const bool okb = i < kSlots && tt >= 0 && tt <= kCB && t0 + tt < Tb && u0 + ul <= Ub;
+    if (!okb) continue;
+    sb[ul * kCS + tt] = vb[q];
+    if (tt < nt && ul < nu) {
+      sm[0][ul * kCS + tt] = va[q];
+      sm[1][ul * kCS + tt] = vp[q];
+      sm[2][ul * kCS + tt] = vs[q];
+      sm[3][ul * kCS + tt] = vl[q];
     }
-    const Tile tl = p.tiles[lo];
-    const int local_r = R - tl.row0;
-    const int ul = local_r / tl.htp, tloc = local_r - ul * tl.htp;
-    if (tloc < tl.ht) {
-      const int b = tl.b, u = tl.u0 + ul, t = tl.t0 + tloc;
-      const int Tb = p.T_len[b], Ub = p.U_len[b];
-      const size_t idx = ((size_t)b * p.U1 + u) * p.T + t;
-      const float lp = p.lnP[b];
-      const float gb = p.dcosts ? p.dcosts[b] : 1.0f;
-      const float A = p.alpha[idx], Bt = p.beta[idx];
-      ls = p.lse[idx];
-      const float bn = (t + 1 < Tb) ? p.beta[idx + 1] : (u == Ub ? 0.0f : kNegInf);
+  }
+  __syncthreads();
+  const float lp = p.lnP[b];
+  const float gb = p.dcosts ? p.dcosts[b] : 1.0f;
+#pragma unroll
+  for (int i = threadIdx.x; i < kCB * kCB; i += 256) {
+    const int ul = i / kCB, tt = i % kCB;
+    if (ul >= nu) continue;
+    const int rr = tl.row0 + (ub + ul) * tl.htp + tb + tt - p.buf_row_base;
+    float ls = 0.0f, co = 0.0f, cb = 0.0f, cl = 0.0f, lab = -1.0f;
+    if (tt < nt) {  // rows past ht (up to htp) are padding
+      const int t = t0 + tt, u = u0 + ul;
+      const float A = sm[0][ul * kCS + tt], Bt = sb[ul * kCS + tt];
+      ls = sm[3][ul * kCS + tt];
+      const float bn = (t + 1 < Tb) ? sb[ul * kCS + tt + 1] : (u == Ub ? 0.0f : kNegInf);
       co = gb * fexp2((A + Bt - lp) * kLog2e);
-      cb = gb * fexp2((A + p.phi[idx] + bn - lp) * kLog2e);
+      cb = gb * fexp2((A + sm[1][ul * kCS + tt] + bn - lp) * kLog2e);
       if (u < Ub) {
-        cl = gb * fexp2((A + p.psi[idx] + p.beta[idx + p.T] - lp) * kLog2e);
+        cl = gb * fexp2((A + sm[2][ul * kCS + tt] + sb[(ul + 1) * kCS + tt] - lp) * kLog2e);
         lab = (float)p.labels[(size_t)b * p.U1 + u + 1];
       }
     }
+    coefA[rr] = f32x2{ls * kLog2e, co};
+    coefB[rr] = f32x4{cb, cl, lab, 0.0f};
   }
-  reinterpret_cast<f32x2*>(p.coefA)[rr] = f32x2{ls * kLog2e, co};
-  reinterpret_cast<f32x4*>(p.coefB)[rr] = f32x4{cb, cl, lab, 0.0f};
 }
 
 // dh[row, blank] -= cb, dh[row, label] -= cl (in fp32, rounded once more to bf16)
@@ -462,10 +510,10 @@ __global__ void dh_fix_kernel(Scores3Args p) {
   if (lab >= 0 && c[1] != 0.0f) row[lab] = (bf16)((float)row[lab] - c[1]);
 }
 
-hipError_t launch_coef(const Scores3Args& a, hipStream_t st) {
-  const int rows = a.n_ct * s3::BN;
-  if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(coef_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, a);
+hipError_t launch_coef(const Scores3Args& a, int tile_t, int tile_u, hipStream_t st) {
+  if (a.n_ct == 0) return hipSuccess;
+  const dim3 grid(a.tile_end - a.tile_begin + 1, (tile_t + kCB - 1) / kCB, (tile_u + kCB - 1) / kCB);
+  hipLaunchKernelGGL(coef_kernel, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 hipError_t launch_dh_fix(const Scores3Args& a, hipStream_t st) {

@@ -96,40 +96,56 @@ LATTICE_CASES = [(70, 40, (1, 70), (0, 40)), (90, 100, (1, 90), (64, 100)),
                  (40, 300, (1, 40), (250, 300)), (24, 700, (1, 24), (500, 700))]
 
 
+def lattice_layout(B, T, U1):
+    """Index arrays (b, t, u) -> entry of the documented diagonal-major layout:
+    (b * ND + t + u) * US + u with ND = T + U1 - 1 and US = U1 rounded up to 32."""
+    ND, US = T + U1 - 1, (U1 + 31) // 32 * 32
+    return ND, US
+
+
 @pytest.mark.parametrize("T,U,tr,ur", LATTICE_CASES)
 def test_lattice_kernel_matches_oracle(gpu_lib, T, U, tr, ur):
     import torch
 
     rl = gpu_lib
     B, U1 = 5, U + 1
+    ND, US = lattice_layout(B, T, U1)
     inp = make_inputs(B, T, U, 33, 8, 8, 8, dtype="f32", seed=31 + U, t_range=tr, u_range=ur)
     say(f"lattice kernel: B={B} T={T} U={U} ragged")
     r = oracle.loss_and_grads(inp, want_grads=False)
-    phi = np.zeros((B, U1, T), np.float32)
-    psi = np.zeros((B, U1, T), np.float32)
+    # entries outside every lattice hold poison the kernel must not let through
+    rng = np.random.default_rng(U)
+    poison = np.array([np.nan, np.inf, -np.inf, 1e30, -1e30, 7.0], np.float32)
+    phi = rng.choice(poison, size=B * ND * US).astype(np.float32)
+    psi = rng.choice(poison, size=B * ND * US).astype(np.float32)
+    cells = []
     for b, s in enumerate(r.samples):
         Tb, Ub = inp.T_len[b], inp.U_len[b]
-        phi[b, :Ub + 1, :Tb] = s.phi.T
-        psi[b, :Ub + 1, :Tb] = np.where(np.isfinite(s.psi.T), s.psi.T, 0)
+        t, u = np.meshgrid(np.arange(Tb), np.arange(Ub + 1), indexing="ij")
+        ix = (b * ND + t + u) * US + u
+        cells.append(ix)
+        phi[ix] = s.phi
+        psi[ix[:, :Ub]] = s.psi[:, :Ub]
     dev = torch.device("cuda:0")
     tp = lambda a: torch.from_numpy(a).to(dev)
-    al = torch.full((B, U1, T), 7.0, device=dev)
-    be = torch.full((B, U1, T), 7.0, device=dev)
+    al = torch.full((B * ND * US,), 7.0, device=dev)
+    be = torch.full((B * ND * US,), 7.0, device=dev)
     costs = torch.zeros(B, device=dev)
     d = rl.make_desc(B, T, U, 33, 8, 8, 8)
     rl.rnnt_lattice(d, tp(inp.T_len), tp(inp.U_len), tp(phi), tp(psi), al, be, costs)
     torch.cuda.synchronize()
     al, be, costs = al.cpu().numpy(), be.cpu().numpy(), costs.cpu().numpy()
+    touched = np.zeros(B * ND * US, bool)
     for b, s in enumerate(r.samples):
         Tb, Ub = inp.T_len[b], inp.U_len[b]
+        ix = cells[b]
+        touched[ix] = True
         assert abs(costs[b] - s.cost) <= 1e-5 * abs(s.cost), f"sample {b}"
-        ga, gb = al[b, :Ub + 1, :Tb].T, be[b, :Ub + 1, :Tb].T
         scale = max(1.0, np.abs(s.alpha).max())
-        assert np.max(np.abs(ga - s.alpha)) <= 2e-6 * scale * (Tb + Ub), f"alpha, sample {b}"
-        assert np.max(np.abs(gb - s.beta)) <= 2e-6 * scale * (Tb + Ub), f"beta, sample {b}"
-        # cells outside the lattice are untouched
-        assert np.all(al[b, Ub + 1:] == 7.0) and np.all(al[b, :, Tb:] == 7.0)
-        assert np.all(be[b, Ub + 1:] == 7.0) and np.all(be[b, :, Tb:] == 7.0)
+        assert np.max(np.abs(al[ix] - s.alpha)) <= 2e-6 * scale * (Tb + Ub), f"alpha, sample {b}"
+        assert np.max(np.abs(be[ix] - s.beta)) <= 2e-6 * scale * (Tb + Ub), f"beta, sample {b}"
+    # entries outside the lattices are untouched
+    assert np.all(al[~touched] == 7.0) and np.all(be[~touched] == 7.0)
 
 
 # ----------------------------------------------------------------------------- fp32 mode
