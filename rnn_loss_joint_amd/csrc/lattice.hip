@@ -24,8 +24,7 @@
 // indexed by position in the sweep (alpha: d - 1, beta: D - 1 - d, so window
 // k holds positions SW k .. SW k + SW - 1); one barrier per window separates
 // writer and reader. Step s of the workgroup is window s - w of wave w
-// (alpha) or s - (NW - 1 - w) (beta). The loads of a wave's next window are
-// in flight while it computes the current one.
+// (alpha) or s - (NW - 1 - w) (beta).
 //
 // Inside the kernel the variables are kept in base 2 (x log2 e), so a
 // log-add-exp is max(a, b) + log2(1 + 2^-|a - b|): the scale is applied once
@@ -35,11 +34,14 @@
 // Memory goes through buffer instructions on a resource spanning the
 // sample's block of ND x US entries, with the diagonal's offset in the
 // scalar offset: a read outside the block returns 0 and a store outside it
-// is dropped. Operands of cells outside the lattice are arbitrary values of
-// the block (uninitialised workspace in the loss path); each operand is made
-// finite or -inf when used (NaN and +inf become 1e30), and the per-cell mask
-// keeps every out-of-lattice alpha / beta at -inf, so those operands only
-// ever meet a -inf neighbour or a masked cell. Masked cells are not stored.
+// is dropped. A cell outside the lattice gets that out-of-range offset for
+// its operand reads and its store, so its bytes are neither read nor
+// written, and the per-cell mask keeps its alpha / beta at -inf. A cell in
+// the lattice can still have an operand outside it (phi(-1, u) for alpha at
+// t = 0, for instance), an arbitrary value of the block (uninitialised
+// workspace in the loss path): each operand is made finite or -inf when used
+// (NaN and +inf become 1e30) and such an operand only ever meets a -inf
+// neighbour. The loads of a window are issued two windows ahead.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -115,12 +117,26 @@ __device__ __attribute__((always_inline)) inline void lattice_body(const Lattice
   const unsigned vo_p = 4u * (unsigned)u;
   const unsigned vo_s = is_beta ? vo_p : vo_p - 4u;
   auto opnd_diag = [&](int k, int w) { return is_beta ? max(D - 1 - SW * k - w, 0) : SW * k + w; };
+  // Position w of window k is diagonal d_first + w (alpha) or d_first - w
+  // (beta), t = d - u; the cell is in the lattice for w_lo <= w < w_lo + cnt.
+  struct Span { int d_first, w_lo; unsigned cnt; };
+  auto span = [&](int k) {
+    const int d_first = is_beta ? D - 1 - SW * k : 1 + SW * k;
+    const int t0 = d_first - u;
+    const int w_lo = is_beta ? max(t0 - (Tb - 1), 0) : max(-t0, 0);
+    const int w_hi = is_beta ? min(t0, SW - 1) : min(Tb - 1 - t0, SW - 1);
+    return Span{d_first, w_lo, u <= Ub ? (unsigned)max(w_hi + 1 - w_lo, 0) : 0u};
+  };
+  // only a cell in the lattice uses its operands: the others read 0 (an
+  // out-of-range offset), which spares their bytes
   auto load = [&](int k, float* rp, float* rs) {
+    const Span sp = span(k);
 #pragma unroll
     for (int w = 0; w < SW; ++w) {
       const unsigned so = (unsigned)opnd_diag(k, w) * dstride;
-      rp[w] = buf_ld(rphi, vo_p, so);
-      rs[w] = buf_ld(rpsi, vo_s, so);
+      const bool ok = (unsigned)(w - sp.w_lo) < sp.cnt;
+      rp[w] = buf_ld(rphi, ok ? vo_p : kOffNone, so);
+      rs[w] = buf_ld(rpsi, ok ? vo_s : kOffNone, so);
     }
   };
 
@@ -139,12 +155,14 @@ __device__ __attribute__((always_inline)) inline void lattice_body(const Lattice
   // beta: the boundary value at diagonal D (position -1) for the wave below
   if (is_beta && wave > 0 && lane == 0) ring[(wave - 1) * SRING + SRING - 1] = cur;
 
-  // one step: window k (if this wave has it) from the operands in rp / rs,
-  // with the next window's loads issued into np / ns first
+  // Step s: issue the loads of window s + 2 - lag into np / ns, then compute
+  // window k = s - lag (if this wave has it) from rp / rs, which its loads
+  // filled two steps earlier. Register set j holds the windows loaded at
+  // steps s with s + 2 = j (mod 3), so the sets rotate with s alone.
   auto step = [&](int s, float* rp, float* rs, float* np, float* ns) {
     const int k = s - lag;
+    if (live && k + 2 >= 0 && k + 2 < nwin) load(k + 2, np, ns);
     if (live && k >= 0 && k < nwin) {
-      if (k + 1 < nwin) load(k + 1, np, ns);
       // the neighbour row's value one position earlier
       float vn[SW];
       const int slot = (SW * k) & (SRING - 1);
@@ -157,13 +175,9 @@ __device__ __attribute__((always_inline)) inline void lattice_body(const Lattice
         vn[4 * q + 3] = v.z;
         if (4 * q + 4 < SW) vn[4 * q + 4] = v.w;
       }
-      // position w is diagonal d0 + w (alpha) or d_hi - w (beta), t = d - u;
-      // the cell is in the lattice for w_lo <= w < w_lo + cnt
-      const int d_first = is_beta ? D - 1 - SW * k : 1 + SW * k;
-      const int t0 = d_first - u;
-      const int w_lo = is_beta ? max(t0 - (Tb - 1), 0) : max(-t0, 0);
-      const int w_hi = is_beta ? min(t0, SW - 1) : min(Tb - 1 - t0, SW - 1);
-      const unsigned cnt = u <= Ub ? (unsigned)max(w_hi + 1 - w_lo, 0) : 0u;
+      const Span sp = span(k);
+      const int d_first = sp.d_first, w_lo = sp.w_lo;
+      const unsigned cnt = sp.cnt;
       float res_w[SW];
 #pragma unroll
       for (int w = 0; w < SW; ++w) {
@@ -191,16 +205,15 @@ __device__ __attribute__((always_inline)) inline void lattice_body(const Lattice
               make_float4(res_w[4 * q], res_w[4 * q + 1], res_w[4 * q + 2], res_w[4 * q + 3]);
       }
     }
-    lds_sync();
+    if (s >= 0) lds_sync();
   };
 
-  float ra_p[SW], ra_s[SW], rb_p[SW], rb_s[SW];
-  if (live && nwin > 0) load(0, ra_p, ra_s);
-  // windows alternate between the two register sets
-  for (int s = 0; s < nsteps; s += 2) {
-    step(s, (lag & 1) ? rb_p : ra_p, (lag & 1) ? rb_s : ra_s, (lag & 1) ? ra_p : rb_p, (lag & 1) ? ra_s : rb_s);
-    if (s + 1 < nsteps)
-      step(s + 1, (lag & 1) ? ra_p : rb_p, (lag & 1) ? ra_s : rb_s, (lag & 1) ? rb_p : ra_p, (lag & 1) ? rb_s : ra_s);
+  // steps -2 and -1 only issue the first two windows' loads
+  float r0p[SW], r0s[SW], r1p[SW], r1s[SW], r2p[SW], r2s[SW];
+  for (int s = -2; s < nsteps; s += 3) {
+    step(s, r1p, r1s, r0p, r0s);
+    if (s + 1 < nsteps) step(s + 1, r2p, r2s, r1p, r1s);
+    if (s + 2 < nsteps) step(s + 2, r0p, r0s, r2p, r2s);
   }
   if (!is_beta && u == Ub) {
     const float v = (D == 0 ? 0.0f : lnP2 * kLn2) + phi[(size_t)D * US + Ub];
