@@ -13,7 +13,9 @@ namespace rnnt {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -94,9 +96,9 @@ __device__ inline float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 // tanh from one exp2 and one reciprocal: tanh|x| = (1-e)/(1+e), e = exp(-2|x|).
 // Absolute error ~1e-7, far below bf16 rounding of the result.
 __device__ inline float tanh_fast(float x) {
-  float e = fexp2(-2.0f * kLog2e * __builtin_fabsf(x));
-  float t = (1.0f - e) * frcp(1.0f + e);
-  return __builtin_copysignf(t, x);
+  // tanh x = 2 / (1 + e^-2x) - 1; for x -> -inf, e^-2x overflows to +inf and
+  // the reciprocal to 0, giving -1
+  return __builtin_fmaf(2.0f, frcp(1.0f + fexp2(-2.0f * kLog2e * x)), -1.0f);
 }
 
 template <class CT> __device__ inline float joint_act(float x);

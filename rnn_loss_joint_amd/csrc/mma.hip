@@ -251,37 +251,41 @@ __global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
   }
   const bf16* wb = WO + (size_t)p.blank * p.H;
   for (int k = q * 8; k < p.z_ld; k += 64) {
+    // every load of the chunk first (masked ones read a valid row / column
+    // and are zeroed below), so the chunk waits on memory once
     const bool kok = row_ok && k < p.H;
-    f32x4 a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
-    bf16x8 xb;
-    if (kok) {
-      a0 = ldg<f32x4>(arow + k);
-      a1 = ldg<f32x4>(arow + k + 4);
-      if constexpr (SCORES) xb = ldg<bf16x8>(wb + k);
+    const int kk = kok ? k : 0;
+    const f32x4 a0 = ldg<f32x4>(arow + kk), a1 = ldg<f32x4>(arow + kk + 4);
+    f32x4 l0[8], l1[8];
+#pragma unroll
+    for (int uu = 0; uu < 8; ++uu) {
+      const float* lrow = lrow0 + (size_t)min(uu, nu - 1) * p.H_pad;
+      l0[uu] = ldg<f32x4>(lrow + kk);
+      l1[uu] = ldg<f32x4>(lrow + kk + 4);
+    }
+    bf16x8 xb, xy[8];
+    if constexpr (SCORES) {
+      xb = ldg<bf16x8>(wb + kk);
+#pragma unroll
+      for (int uu = 0; uu < 8; ++uu) xy[uu] = ldg<bf16x8>(WO + (size_t)(lab[uu] >= 0 ? lab[uu] : 0) * p.H + kk);
     }
 #pragma unroll
     for (int uu = 0; uu < 8; ++uu) {
       if (uu >= nu) continue;  // workgroup-uniform
-      bf16x8 z;
-      if (kok) {
-        const float* lrow = lrow0 + (size_t)uu * p.H_pad;
-        const f32x4 l0 = ldg<f32x4>(lrow + k), l1 = ldg<f32x4>(lrow + k + 4);
+      f32x8 zf;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          z[e] = (bf16)tanh_fast(a0[e] + l0[e]);
-          z[e + 4] = (bf16)tanh_fast(a1[e] + l1[e]);
+      for (int e = 0; e < 4; ++e) zf[e] = tanh_fast(a0[e] + l0[uu][e]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zf[e + 4] = tanh_fast(a1[e] + l1[uu][e]);
+      bf16x8 z = __builtin_convertvector(zf, bf16x8);  // adjacent pairs: one packed convert each
+      if (!kok) z = bf16x8{};
+      if constexpr (SCORES) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {  // bf16 pair dot products, fp32 accumulation
+          const bf16x2 zz = {z[e], z[e + 1]};
+          hb[uu] = __builtin_amdgcn_fdot2_f32_bf16(zz, bf16x2{xb[e], xb[e + 1]}, hb[uu], false);
+          hy[uu] = __builtin_amdgcn_fdot2_f32_bf16(zz, bf16x2{xy[uu][e], xy[uu][e + 1]}, hy[uu], false);
         }
-        if constexpr (SCORES) {
-          const bf16x8 xy = ldg<bf16x8>(WO + (size_t)(lab[uu] >= 0 ? lab[uu] : 0) * p.H + k);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            hb[uu] = __builtin_fmaf((float)z[e], (float)xb[e], hb[uu]);
-            hy[uu] = __builtin_fmaf((float)z[e], (float)xy[e], hy[uu]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = (bf16)0.0f;
       }
       *reinterpret_cast<bf16x8*>(zb + (row0 + (int64_t)uu * tl.htp) * p.z_ld + k) = z;
     }
