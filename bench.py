@@ -147,8 +147,10 @@ def main():
     ap.add_argument("--workload", default="40s-b256-bf16",
                     help="tiny-f32 | small-bf16 | 20s-bf16 | vocab4096-bf16 | 40s-b256-bf16")
     ap.add_argument("--mode", default="tiled", choices=["tiled", "untiled"])
-    ap.add_argument("--tile", default="64x32")
+    ap.add_argument("--tile", default="64x32", help="TxU, or 'sample' for whole-sample tiles (T x (U+1))")
     ap.add_argument("--tiles-per-wave", type=int, default=0)
+    ap.add_argument("--budget", type=float, default=0, metavar="BYTES",
+                    help="pick tiles_per_wave as the largest whose saved + workspace bytes fit (tiled mode)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget; 0 = skip")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (counter calibration)")
@@ -184,9 +186,13 @@ def main():
         return
     rl.load()
     w = WORKLOADS[args.workload]
-    tile = tuple(int(x) for x in args.tile.split("x"))
+    tile = (w.T, w.U + 1) if args.tile == "sample" else tuple(int(x) for x in args.tile.split("x"))
     print(f"# generating {w.name} inputs", file=sys.stderr, flush=True)
     inp = workload_inputs(args.workload)
+    if args.budget > 0:
+        d = rl.make_desc(w.B, w.T, w.U, w.V, w.HA, w.HL, w.H, dtype=w.dtype, tile=tile)
+        args.tiles_per_wave = rl.rnnt_waves_for_budget(d, inp.T_len, inp.U_len, int(args.budget))
+        print(f"# budget {args.budget:.3g} B -> {args.tiles_per_wave} tiles per wave", file=sys.stderr, flush=True)
     prob = rl.Problem(inp, mode=args.mode, tile=tile, tiles_per_wave=args.tiles_per_wave)
     stream = torch.cuda.current_stream()
 

@@ -79,7 +79,9 @@ typedef struct {
 } rnnt_desc;
 
 /* Limits of this library (RNNT_E_UNSUPPORTED beyond them): H, HA, HL multiples
- * of 8; H <= 768; U+1 <= 1024; V <= 65536; B*T*(U+1) <= 2^30. Any tile size
+ * of 8; H <= 768; U+1 <= 1024; V <= 65536; B*(T+U)*US <= 2^30 and
+ * (T+U)*US <= 2^29 with US = U+1 rounded up to a multiple of 32 (the entries of
+ * the lattice arrays, see rnnt_lattice). Any tile size
  * is accepted; a tile's t extent is padded to a multiple of 32 rows inside the
  * library, so tile_t values that are multiples of 32 waste nothing. */
 
@@ -90,6 +92,20 @@ typedef struct {
 rnnt_status rnnt_loss_query(const rnnt_desc* desc, const int32_t* T_len_host,
                             const int32_t* U_len_host, size_t* saved_bytes,
                             size_t* workspace_bytes);
+
+/* Wave size from a memory budget (tiled mode): the largest tiles_per_wave
+ * for which saved + workspace bytes (as rnnt_loss_query reports them for this
+ * descriptor with that tiles_per_wave) fit in budget_bytes; desc's own
+ * tiles_per_wave is ignored. Host-only. With tile_t >= T and tile_u >= U+1 a
+ * tile is a whole sample, so the result is the number of samples computed
+ * together: the sample-wise computation with batch splitting of "Neural
+ * transducer training ...", section "Sample-wise method" (Alg. 1), whose
+ * memory hardly grows with the batch size. RNNT_E_WORKSPACE if one tile per
+ * wave already exceeds the budget; RNNT_E_INVALID in untiled mode or for a
+ * null pointer; descriptor and length errors as rnnt_loss_query. */
+rnnt_status rnnt_waves_for_budget(const rnnt_desc* desc, const int32_t* T_len_host,
+                                  const int32_t* U_len_host, size_t budget_bytes,
+                                  int32_t* tiles_per_wave);
 
 /* Forward: per-sample costs[b] = -ln P(y_b | x_b) (fp32 [B], device).
  * Fills `saved` with the tile plan, the joint pre-activations, the per-cell

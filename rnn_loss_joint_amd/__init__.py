@@ -38,7 +38,7 @@ class RnntDesc(ctypes.Structure):
         "tiles_per_wave", "reserved")]
 
 
-EXPORTS = ("rnnt_loss_query", "rnnt_loss_fwd", "rnnt_loss_bwd", "rnnt_lattice", "rnnt_profile_start",
+EXPORTS = ("rnnt_loss_query", "rnnt_waves_for_budget", "rnnt_loss_fwd", "rnnt_loss_bwd", "rnnt_lattice", "rnnt_profile_start",
            "rnnt_profile_stop", "rnnt_profile_get", "rnnt_status_string", "rnnt_last_error")
 
 
@@ -57,7 +57,8 @@ def load(path: str = LIB_PATH):
     lib.rnnt_loss_bwd.argtypes = [DP, P, P, P, I32P, I32P, P, P, P, P, P, P, P, SZ, P, SZ,
                                   P, P, P, P, P, P, P, P]
     lib.rnnt_lattice.argtypes = [DP, P, P, P, P, P, P, P, P]
-    for f in ("rnnt_loss_query", "rnnt_loss_fwd", "rnnt_loss_bwd", "rnnt_lattice"):
+    lib.rnnt_waves_for_budget.argtypes = [DP, I32P, I32P, SZ, I32P]
+    for f in ("rnnt_loss_query", "rnnt_waves_for_budget", "rnnt_loss_fwd", "rnnt_loss_bwd", "rnnt_lattice"):
         getattr(lib, f).restype = ctypes.c_int
     lib.rnnt_profile_start.argtypes = []
     lib.rnnt_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_int32)]
@@ -118,6 +119,16 @@ def rnnt_loss_query(desc: RnntDesc, T_len, U_len):
     s, w = ctypes.c_size_t(0), ctypes.c_size_t(0)
     _check(lib.rnnt_loss_query(ctypes.byref(desc), tp, up, ctypes.byref(s), ctypes.byref(w)))
     return s.value, w.value
+
+
+def rnnt_waves_for_budget(desc: RnntDesc, T_len, U_len, budget_bytes: int) -> int:
+    """Largest tiles_per_wave whose saved + workspace bytes fit budget_bytes (tiled mode)."""
+    lib = load()
+    T_len, tp = _lens(T_len)
+    U_len, up = _lens(U_len)
+    n = ctypes.c_int32(0)
+    _check(lib.rnnt_waves_for_budget(ctypes.byref(desc), tp, up, int(budget_bytes), ctypes.byref(n)))
+    return n.value
 
 
 def rnnt_loss_fwd(desc, hA, hL, labels, T_len, U_len, WA, WL, bZ, WO, bO, costs, saved, workspace=None,

@@ -247,6 +247,39 @@ rnnt_status rnnt_loss_query(const rnnt_desc* desc, const int32_t* T_len_host, co
   return RNNT_OK;
 }
 
+rnnt_status rnnt_waves_for_budget(const rnnt_desc* desc, const int32_t* T_len_host, const int32_t* U_len_host,
+                                  size_t budget_bytes, int32_t* tiles_per_wave) {
+  if (!desc || !tiles_per_wave) return fail(RNNT_E_INVALID, "null descriptor or output pointer");
+  if (desc->mode != RNNT_TILED) return fail(RNNT_E_INVALID, "waves are chosen in tiled mode only");
+  rnnt_desc d = *desc;
+  auto bytes = [&](int tpw, size_t& total, int& n_tiles) -> rnnt_status {
+    d.tiles_per_wave = tpw;
+    rnnt::Plan p;
+    rnnt::Layout L;
+    const rnnt_status s = prepare(&d, T_len_host, U_len_host, p, L);
+    if (s != RNNT_OK) return s;
+    total = L.saved_bytes + L.workspace_bytes;
+    n_tiles = (int)p.tiles.size();
+    return RNNT_OK;
+  };
+  size_t total = 0;
+  int n_tiles = 0;
+  rnnt_status s = bytes(1, total, n_tiles);
+  if (s != RNNT_OK) return s;
+  if (total > budget_bytes) return fail(RNNT_E_WORKSPACE, "one tile per wave already exceeds the budget");
+  // the working set grows with tiles_per_wave up to the tile count
+  int lo = 1, hi = std::max(n_tiles, 1);
+  while (lo < hi) {
+    const int mid = lo + (hi - lo + 1) / 2;
+    int n = 0;
+    s = bytes(mid, total, n);
+    if (s != RNNT_OK) return s;
+    if (total <= budget_bytes) lo = mid; else hi = mid - 1;
+  }
+  *tiles_per_wave = lo;
+  return RNNT_OK;
+}
+
 rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL, const int32_t* labels,
                           const int32_t* T_len_host, const int32_t* U_len_host, const void* WA,
                           const void* WL, const void* bZ, const void* WO, const void* bO, float* costs,

@@ -154,3 +154,50 @@ def test_tiled_working_set_scales_with_tile_not_lattice():
     st, _ = rl.rnnt_loss_query(dt, np.full(B, T), np.full(B, U))
     cells = B * T * (U + 1)
     assert su - st >= cells * (V + H) * 2  # untiled keeps scores and z for every cell
+
+
+# ----------------------------------------------------------------------------- wave size from a budget
+
+def _total(d, T_len, U_len):
+    s, w = rl.rnnt_loss_query(d, T_len, U_len)
+    return s + w
+
+
+@pytest.mark.parametrize("tile", [(64, 32), (500, 121)])
+def test_waves_for_budget_is_the_largest_fit(tile):
+    B, T, U, V, HA, HL, H = 32, 500, 120, 1024, 512, 512, 640
+    rng = np.random.default_rng(3)
+    T_len, U_len = rng.integers(300, T + 1, B), rng.integers(72, U + 1, B)
+    d = rl.make_desc(B, T, U, V, HA, HL, H, tile=tile)
+    lo = _total(rl.make_desc(B, T, U, V, HA, HL, H, tile=tile, tiles_per_wave=1), T_len, U_len)
+    prev = 0
+    for budget in (lo, int(lo * 1.3), int(lo * 2), int(lo * 4), 1 << 40):
+        n = rl.rnnt_waves_for_budget(d, T_len, U_len, budget)
+        assert n >= max(prev, 1)  # monotone in the budget
+        prev = n
+        at = rl.make_desc(B, T, U, V, HA, HL, H, tile=tile, tiles_per_wave=n)
+        assert _total(at, T_len, U_len) <= budget
+        above = rl.make_desc(B, T, U, V, HA, HL, H, tile=tile, tiles_per_wave=n + 1)
+        n_tiles_reached = _total(above, T_len, U_len) == _total(at, T_len, U_len)
+        assert n_tiles_reached or _total(above, T_len, U_len) > budget
+    with pytest.raises(rl.RnntError) as e:
+        rl.rnnt_waves_for_budget(d, T_len, U_len, lo - 1)
+    assert e.value.status == rl.RNNT_E_WORKSPACE
+    with pytest.raises(rl.RnntError) as e:
+        rl.rnnt_waves_for_budget(rl.make_desc(B, T, U, V, HA, HL, H, mode="untiled"), T_len, U_len, 1 << 40)
+    assert e.value.status == rl.RNNT_E_INVALID
+
+
+def test_sample_wise_working_set_independent_of_batch():
+    """Whole-sample tiles, a fixed number of samples per wave: saved is a fixed
+    amount per sample (the lattice scalars and the a / l rows), and the
+    workspace minus the gA / gL accumulators does not grow with the batch."""
+    T, U, V, HA, HL, H = 500, 120, 1024, 512, 512, 640
+    saved_per_sample, ws_rest = set(), []
+    for B in (8, 32, 128):
+        d = rl.make_desc(B, T, U, V, HA, HL, H, tile=(T, U + 1), tiles_per_wave=4)
+        s, w = rl.rnnt_loss_query(d, np.full(B, T), np.full(B, U))
+        saved_per_sample.add(round(s / B, -3))
+        ws_rest.append(w - 4 * H * (T + U + 1) * B)
+    assert len(saved_per_sample) == 1, saved_per_sample  # plan records aside
+    assert ws_rest[0] <= ws_rest[1] and abs(ws_rest[2] - ws_rest[1]) <= 64 * 1024, ws_rest

@@ -183,6 +183,25 @@ def test_small_full(gpu_lib, mode):
 
 
 @pytest.mark.timeout(400)
+def test_sample_wise_waves_from_budget(gpu_lib):
+    """Whole-sample tiles ([N] section "Sample-wise method") with the wave size
+    chosen from a memory budget: a few samples per wave."""
+    rl = gpu_lib
+    inp = workload_inputs("small-bf16")
+    B, T, HA = inp.hA.shape
+    U = inp.hL.shape[1] - 1
+    V, H = inp.WO.shape
+    tile = (T, U + 1)
+    one = rl.make_desc(B, T, U, V, HA, inp.hL.shape[2], H, tile=tile, tiles_per_wave=1)
+    s1, w1 = rl.rnnt_loss_query(one, inp.T_len, inp.U_len)
+    d = rl.make_desc(B, T, U, V, HA, inp.hL.shape[2], H, tile=tile)
+    n = rl.rnnt_waves_for_budget(d, inp.T_len, inp.U_len, int((s1 + w1) * 1.6))
+    assert 1 < n < B
+    say(f"sample-wise tiles {tile}, {n} samples per wave")
+    full_check(rl, inp, tile=tile, tpw=n)
+
+
+@pytest.mark.timeout(400)
 def test_20s_sampled_tiled_and_untiled(gpu_lib):
     inp = workload_inputs("20s-bf16")
     say("20s full bf16 tiled 64x32, sampled oracle")
