@@ -139,6 +139,97 @@ def reference_gemm(torch, w, rows=524288):
     print(json.dumps({"reference_gemm": out, "rows": R, "H": H, "V": V}))
 
 
+def unfused_baseline(torch, rl, inp, steps, warmup):
+    """Comparator for the fused, tiled path: an unfused batched RNN-T loss over the materialised
+    [B, T, U+1, V] scores, as a warp-transducer style implementation computes it ("Neural transducer
+    training ...", section "Transducer training", f^W_1..4 as separate passes): torch GEMMs,
+    log_softmax and elementwise ops over the padded batch, this library's lattice kernel for alpha /
+    beta. Benchmark only. Returns (ms per fwd+bwd, peak bytes, costs, dWO, dhA)."""
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    B, T, HA = inp.hA.shape
+    U1, HL = inp.hL.shape[1], inp.hL.shape[2]
+    U = U1 - 1
+    V, H = inp.WO.shape
+    blank = int(inp.blank)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(bf)
+    hA, hL, WA, WL, bZ, WO, bO = map(up, (inp.hA, inp.hL, inp.WA, inp.WL, inp.bZ, inp.WO, inp.bO))
+    # right operands of every product contiguous (transposed views in batched bf16 products are avoided)
+    WAt, WLt, WOt = WA.t().contiguous(), WL.t().contiguous(), WO.t().contiguous()
+    WAf, WLf = WA.float(), WL.float()
+    lab = torch.from_numpy(np.ascontiguousarray(inp.labels[:, 1:], dtype=np.int64)).to(dev)  # [B, U]
+    Tl = torch.from_numpy(np.ascontiguousarray(inp.T_len, dtype=np.int32)).to(dev)
+    Ul = torch.from_numpy(np.ascontiguousarray(inp.U_len, dtype=np.int32)).to(dev)
+    # the lattice kernel's diagonal-major layout
+    ND, US = T + U1 - 1, (U1 + 31) // 32 * 32
+    bi, ti, ui = torch.arange(B, device=dev), torch.arange(T, device=dev), torch.arange(U1, device=dev)
+    diag = ((bi[:, None, None] * ND + ti[None, :, None] + ui[None, None, :]) * US + ui[None, None, :]).reshape(-1)
+    desc = rl.make_desc(B, T, U, V, HA, HL, H)
+    lab_idx = lab[:, None, :, None].expand(B, T, U, 1)
+    neg = float("-inf")
+
+    def fwd_bwd():
+        a = torch.matmul(hA, WAt).float() + bZ.float()                     # [B, T, H]
+        l = torch.matmul(hL, WLt).float()                                  # [B, U+1, H]
+        z = torch.tanh(a[:, :, None, :] + l[:, None, :, :]).to(bf)         # [B, T, U+1, H]
+        h = torch.matmul(z, WOt) + bO                                      # [B, T, U+1, V]
+        logp = torch.log_softmax(h.float(), dim=-1)
+        del h
+        phi = logp[..., blank].contiguous()
+        psi = torch.zeros_like(phi)
+        psi[:, :, :U] = logp[:, :, :U, :].gather(-1, lab_idx)[..., 0]
+        phid = torch.zeros(B * ND * US, device=dev)
+        psid = torch.zeros_like(phid)
+        phid[diag] = phi.reshape(-1)
+        psid[diag] = psi.reshape(-1)
+        ald = torch.full_like(phid, neg)
+        bed = torch.full_like(phid, neg)
+        costs = torch.zeros(B, device=dev)
+        rl.rnnt_lattice(desc, Tl, Ul, phid, psid, ald, bed, costs)
+        alpha, beta = ald[diag].view(B, T, U1), bed[diag].view(B, T, U1)   # -inf outside each lattice
+        lnP = -costs[:, None, None]
+        bt1 = torch.full_like(beta, neg)
+        bt1[:, :-1] = beta[:, 1:]
+        bt1[bi, Tl.long() - 1, Ul.long()] = 0.0                            # the terminal blank
+        bu1 = torch.full_like(beta, neg)
+        bu1[:, :, :-1] = beta[:, :, 1:]
+        occ = torch.exp(alpha + beta - lnP)
+        bflow = torch.exp(alpha + phi + bt1 - lnP)
+        lflow = torch.exp(alpha + psi + bu1 - lnP)
+        dh = torch.exp(logp) * occ[..., None]                              # d cost / d scores
+        del logp
+        dh[..., blank] -= bflow
+        dh[:, :, :U, :].scatter_add_(-1, lab_idx, -lflow[:, :, :U, None])
+        dh = dh.to(bf)
+        dz = torch.matmul(dh, WO).float()                                  # [B, T, U+1, H]
+        zf = z.float()
+        ds = dz * (1.0 - zf * zf)
+        del dz, zf
+        gA, gL = ds.sum(2), ds.sum(1)
+        del ds
+        dhf = dh.reshape(-1, V)
+        dWO = torch.matmul(dhf.t().contiguous(), z.reshape(-1, H)).float()
+        dbO = dhf.float().sum(0)
+        dhA, dhL = torch.matmul(gA, WAf), torch.matmul(gL, WLf)
+        dWA = torch.matmul(gA.reshape(-1, H).t().contiguous(), hA.reshape(-1, HA).float())
+        dWL = torch.matmul(gL.reshape(-1, H).t().contiguous(), hL.reshape(-1, HL).float())
+        dbZ = gA.sum((0, 1))
+        return costs, dWO, dhA, dbO, dhL, dWA, dWL, dbZ
+
+    for _ in range(warmup):
+        out = fwd_bwd()
+    del out
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        out = fwd_bwd()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, torch.cuda.max_memory_allocated(), out[0], out[1], out[2]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +247,9 @@ def main():
                     help="only run a plain device copy of BYTES bytes three times (counter calibration)")
     ap.add_argument("--reference-gemm", action="store_true",
                     help="only time the vendor GEMM (torch.matmul) on this workload's three product shapes")
+    ap.add_argument("--unfused-baseline", action="store_true",
+                    help="also time an unfused batched loss over materialised [B,T,U+1,V] scores (comparator; "
+                         "prints its own JSON line after checking it against this library)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -270,7 +364,36 @@ def main():
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
+    if args.unfused_baseline:
+        unfused_line(torch, rl, inp, prob, w.name, ms, peak, args)
+        return
     print(json.dumps(out))
+
+
+def unfused_line(torch, rl, inp, prob, name, ms, peak, args):
+    """Time the unfused comparator after checking it against this library's results."""
+    costs_f = prob.forward().clone()
+    grads = prob.backward()
+    torch.cuda.synchronize()
+    ref = {"costs": costs_f.cpu().numpy().astype(np.float64),
+           "dWO": grads["dWO"].cpu().numpy().astype(np.float64), "dhA": grads["dhA"].cpu().numpy().astype(np.float64)}
+    del prob, grads, costs_f
+    torch.cuda.empty_cache()
+    print("# unfused comparator", file=sys.stderr, flush=True)
+    ms_u, peak_u, cu, dWO_u, dhA_u = unfused_baseline(torch, rl, inp, args.steps, max(1, args.warmup))
+    got = {"costs": cu.cpu().numpy().astype(np.float64), "dWO": dWO_u.cpu().numpy().astype(np.float64),
+           "dhA": dhA_u.cpu().numpy().astype(np.float64)}
+    agree = {"costs_max_rel": float(np.max(np.abs(got["costs"] - ref["costs"]) / np.abs(ref["costs"])))}
+    for k in ("dWO", "dhA"):
+        agree[f"{k}_err_of_max_abs"] = float(np.max(np.abs(got[k] - ref[k])) / np.max(np.abs(ref[k])))
+    ok = agree["costs_max_rel"] <= 2e-3 and agree["dWO_err_of_max_abs"] <= 2e-2 and agree["dhA_err_of_max_abs"] <= 2e-2
+    print(json.dumps({"comparator": "unfused batched loss over materialised [B,T,U+1,V] scores", "workload": name,
+                      "steps": args.steps, "fused": {"ms_per_step": ms, "peak_hbm_bytes": int(peak)},
+                      "unfused": {"ms_per_step": ms_u, "peak_hbm_bytes": int(peak_u)},
+                      "unfused_over_fused_time": ms_u / ms, "unfused_over_fused_peak": peak_u / peak,
+                      "agreement": agree, "agrees": bool(ok)}))
+    if not ok:
+        sys.exit(3)
 
 
 if __name__ == "__main__":
