@@ -36,9 +36,14 @@ constexpr int OFF_BIAS = NST * STAGE;              // [2][256] f32: b^O log2 e
 constexpr int OFF_COEF = OFF_BIAS + 2 * 256 * 4;   // [2][128][2] f32: (lse log2 e, occupancy)
 constexpr int OFF_RED = OFF_COEF + 2 * 256 * 4;    // [2 wc][2 j][2][32] f32
 constexpr int LDS_BYTES = OFF_RED + 2 * 2 * 2 * 32 * 4;
+// backward: per wave, one finished 32 x 32 block of dh (bf16) [cell][score],
+// rows of 80 bytes (64 used), so dh goes out as whole 64-byte row pieces
+constexpr int DHS_ROW = 80, DHS_WAVE = 32 * DHS_ROW;
+constexpr int OFF_DHS = LDS_BYTES;
+constexpr int LDS_BYTES_BWD = OFF_DHS + 4 * DHS_WAVE;
 constexpr int WM = 4, WN = 2;  // 32 x 32 blocks per wave
 constexpr int EPI_STAGES = 5;  // stages of item n+1 that carry the epilogue of item n
-static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+static_assert(LDS_BYTES_BWD <= 160 * 1024, "LDS budget");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -56,7 +61,7 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
   using namespace s3;
   using m3::lds_barrier;
   using m3::wait_vm;
-  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[BWD ? LDS_BYTES_BWD : LDS_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
@@ -151,6 +156,8 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
   f32x4 bq[4];
   float* stats2 = reinterpret_cast<float*>(p.stats);
   bf16* dh = reinterpret_cast<bf16*>(p.dh);
+  char* const dhs = lds + OFF_DHS + wave * DHS_WAVE;  // backward block staging
+  bf16x8 fl[2];
 
   // One chunk (issued after one MFMA) of epilogue task T on accumulator set E.
   auto epi_chunk = [&](auto EE, auto TT, auto XX) __attribute__((always_inline)) {
@@ -219,6 +226,21 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
         }
       }
     } else {
+      // task T = 2 b + 3 (b = 0 .. 7), chunks 0 - 3: block b, finished in task
+      // T - 1, leaves the staging buffer (cells 16 h + lane / 4, scores
+      // 8 (lane % 4) .. +7 of the block) before block b + 1 is first written
+      // there in chunk 3; the wave's LDS accesses complete in order
+      if constexpr (T >= 3 && T <= 17 && (T & 1) == 1 && X < 4) {
+        constexpr int pb = (T - 3) >> 1, pi = pb >> 1, pj = pb & 1;
+        if constexpr (X < 2) {
+          fl[X] = *reinterpret_cast<const bf16x8*>(dhs + (16 * X + (lane >> 2)) * DHS_ROW + (lane & 3) * 16);
+        } else if (e_live) {
+          constexpr int h = X - 2;
+          const int64_t rr = (int64_t)e_ct * BN + wc * 64 + pj * 32 + 16 * h + (lane >> 2);
+          const int v = e_vt * 256 + wr * 128 + pi * 32 + 8 * (lane & 3);
+          *reinterpret_cast<bf16x8*>(dh + rr * p.V_pad + v) = fl[h];
+        }
+      }
       if constexpr (T == 0 && X == 0) {
         const float* cf = reinterpret_cast<const float*>(lds + OFF_COEF + e_par * 1024);
 #pragma unroll
@@ -238,15 +260,12 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
         constexpr int e = 8 * hh + X;
         y[e] = es[j] * fexp2(__builtin_fmaf(acc[E][i][j][e], kLog2e, bq[e >> 2][e & 3]) - em[j]);
         if constexpr (X == 3 || X == 7) {
+          // scores 8 (e4 / 4) + 4 g .. +3 of the block for cell r, into the staging buffer
           constexpr int e4 = e - 3;
           bf16x4 w;
 #pragma unroll
           for (int q = 0; q < 4; ++q) w[q] = (bf16)y[e4 + q];
-          if (e_live) {
-            const int64_t rr = (int64_t)e_ct * BN + wc * 64 + j * 32 + r;
-            const int v = e_vt * 256 + wr * 128 + i * 32 + 8 * (e4 >> 2) + 4 * g;
-            *reinterpret_cast<bf16x4*>(dh + rr * p.V_pad + v) = w;
-          }
+          *reinterpret_cast<bf16x4*>(dhs + r * DHS_ROW + (8 * (e4 >> 2) + 4 * g) * 2) = w;
         }
       }
     }
