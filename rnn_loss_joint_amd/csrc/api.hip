@@ -802,10 +802,25 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
     }
   }
 
-  // 8. encodings and joint weights (fp32 MFMA)
+  // 8. encodings and joint weights. bf16 mode: gA and gL (complete only after
+  // the last wave) are rounded to bf16 once and the four products run on bf16
+  // MFMA with fp32 accumulation; fp32 mode: fp32 MFMA.
+  const void* gA_op = gA;
+  const void* gL_op = gL;
+  if (bf) {
+    char* gb = at<char>(workspace, L.w_gb);
+    {
+      ProfScope ps_("to_bf16", st);
+      RNNT_HIP(rnnt::launch_to_bf16(gA, gb, (int64_t)d.B * d.T * d.H, st));
+      RNNT_HIP(rnnt::launch_to_bf16(gL, gb + 2 * (size_t)d.B * d.T * d.H, (int64_t)d.B * p.U1 * d.H, st));
+    }
+    gA_op = gb;
+    gL_op = gb + 2 * (size_t)d.B * d.T * d.H;
+  }
+  const int kst = bf ? 64 : 32;  // split-K granule of the GEMM engine
   {
     rnnt::GemmArgs g{};
-    g.A = rnnt::Operand{gA, d.H, d.B * d.T, nullptr, 1, 0};
+    g.A = rnnt::Operand{gA_op, d.H, d.B * d.T, nullptr, 1, 0};
     g.B = rnnt::Operand{WA, d.HA, d.HA, nullptr, 1, 0};
     g.M = d.B * d.T;
     g.N = d.HA;
@@ -816,9 +831,9 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
     g.c_cols = d.HA;
     {
       ProfScope ps_("dh_enc_gemm", st);
-      RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_KC_MN, false, false, bf, 1, st));
+      RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_KC_MN, bf, bf, bf, 1, st));
     }
-    g.A = rnnt::Operand{gL, d.H, d.B * p.U1, nullptr, 1, 0};
+    g.A = rnnt::Operand{gL_op, d.H, d.B * p.U1, nullptr, 1, 0};
     g.B = rnnt::Operand{WL, d.HL, d.HL, nullptr, 1, 0};
     g.M = d.B * p.U1;
     g.N = d.HL;
@@ -827,7 +842,7 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
     g.c_cols = d.HL;
     {
       ProfScope ps_("dh_enc_gemm", st);
-      RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_KC_MN, false, false, bf, 1, st));
+      RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_KC_MN, bf, bf, bf, 1, st));
     }
   }
   {
@@ -835,12 +850,12 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
     float* PBZ = at<float>(workspace, L.w_PBZ);
     float* PWL = at<float>(workspace, L.w_PWL);
     rnnt::GemmArgs g{};
-    g.A = rnnt::Operand{gA, d.H, d.H, nullptr, 1, 0};
+    g.A = rnnt::Operand{gA_op, d.H, d.H, nullptr, 1, 0};
     g.B = rnnt::Operand{hA, d.HA, d.HA, sv.Tlen, d.T, 0};
     g.M = d.H;
     g.N = d.HA;
     g.K = d.B * d.T;
-    g.k_per_split = (int)(((g.K + p.s7a - 1) / p.s7a + 31) / 32 * 32);
+    g.k_per_split = (int)(((g.K + p.s7a - 1) / p.s7a + kst - 1) / kst * kst);
     g.C = PWA;
     g.ldc = d.HA;
     g.split_stride = (int64_t)d.H * d.HA;
@@ -848,7 +863,7 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
     g.colsum = PBZ;
     {
       ProfScope ps_("dW_enc_gemm", st);
-      RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_MN_MN, false, false, bf, p.s7a, st));
+      RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_MN_MN, bf, bf, bf, p.s7a, st));
     }
     {
       ProfScope ps_("split_reduce", st);
@@ -858,11 +873,11 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       ProfScope ps_("split_reduce", st);
       RNNT_HIP(rnnt::launch_split_reduce(dbZ, PBZ, d.H, p.s7a, d.H, false, st));
     }
-    g.A = rnnt::Operand{gL, d.H, d.H, nullptr, 1, 0};
+    g.A = rnnt::Operand{gL_op, d.H, d.H, nullptr, 1, 0};
     g.B = rnnt::Operand{hL, d.HL, d.HL, sv.Ulen, p.U1, 1};
     g.N = d.HL;
     g.K = d.B * p.U1;
-    g.k_per_split = (int)(((g.K + p.s7l - 1) / p.s7l + 31) / 32 * 32);
+    g.k_per_split = (int)(((g.K + p.s7l - 1) / p.s7l + kst - 1) / kst * kst);
     g.C = PWL;
     g.ldc = d.HL;
     g.split_stride = (int64_t)d.H * d.HL;
@@ -870,7 +885,7 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
     g.colsum = nullptr;
     {
       ProfScope ps_("dW_enc_gemm", st);
-      RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_MN_MN, false, false, bf, p.s7l, st));
+      RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_MN_MN, bf, bf, bf, p.s7l, st));
     }
     {
       ProfScope ps_("split_reduce", st);

@@ -570,6 +570,21 @@ hipError_t launch_group_reduce(const GroupReduceArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+__global__ void to_bf16_kernel(const f32x4* __restrict__ src, bf16x4* __restrict__ dst, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = __builtin_convertvector(src[i], bf16x4);
+}
+
+hipError_t launch_to_bf16(const float* src, void* dst, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (n % 4) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 8192);
+  hipLaunchKernelGGL(to_bf16_kernel, dim3(blocks), dim3(256), 0, st, reinterpret_cast<const f32x4*>(src),
+                     reinterpret_cast<bf16x4*>(dst), n4);
+  return hipGetLastError();
+}
+
 __global__ void split_reduce_kernel(float* out, const float* P, int64_t n, int splits, int64_t stride,
                                     int acc) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {

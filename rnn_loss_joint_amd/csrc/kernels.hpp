@@ -151,6 +151,8 @@ struct GroupReduceArgs {
 hipError_t launch_group_reduce(const GroupReduceArgs& a, hipStream_t st);
 
 // out[i] (+)= sum_s P[s*stride + i]
+// dst[i] = bf16(src[i]) (round to nearest even), n a multiple of 4
+hipError_t launch_to_bf16(const float* src, void* dst, int64_t n, hipStream_t st);
 hipError_t launch_split_reduce(float* out, const float* P, int64_t n, int splits, int64_t stride,
                                bool accumulate, hipStream_t st);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st);

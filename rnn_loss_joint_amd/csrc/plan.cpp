@@ -271,6 +271,14 @@ Layout make_layout(const Plan& p) {
     L.w_coefA = take(8 * wrows);
     L.w_coefB = take(16 * wrows);
   }
+  // bf16: gA and gL rounded to bf16 for the encoder-side products, in the
+  // wave buffers (dh then z, contiguous, dead after the last wave) when they fit
+  L.w_gb = 0;
+  if (d.bf16) {
+    const size_t gb = 2 * ((size_t)d.B * d.T + (size_t)d.B * p.U1) * d.H;
+    const size_t wave_bytes = d.untiled ? 0 : ct * wrows * (size_t)(p.V_pad + p.H_pad);
+    L.w_gb = gb <= wave_bytes ? L.w_dh : take(gb);
+  }
   L.workspace_bytes = o;
   return L;
 }

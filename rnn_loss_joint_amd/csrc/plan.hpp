@@ -59,6 +59,7 @@ struct Layout {
   size_t w_dh, w_z, w_gA, w_gL, w_PA, w_PL, w_PW, w_PB, w_PWA, w_PBZ, w_PWL, w_WOT;
   size_t w_zf, w_stats, w_hb, w_hy;  // bf16 forward: z rows, V-tile statistics, blank/label scores
   size_t w_WOp, w_bl, w_coefA, w_coefB;  // bf16 tiled: persistent score kernels
+  size_t w_gb;  // bf16: rounded gA, gL for the encoder-side products (may alias w_dh)
   size_t workspace_bytes;
 };
 
