@@ -120,27 +120,35 @@ __device__ __attribute__((always_inline)) inline void dz2_body(const DzArgs& p, 
 
     // wave rows: 4 blocks of 32 rows = u_local ug*8 + wr*4 + i. Row
     // 8(e>>2) + (e&3) of a block is wave-uniform, so each z load is a scalar
-    // row base plus one per-lane offset (4 (lane>>5) rows + column h).
+    // row base plus one per-lane offset (4 (lane>>5) rows + column h). All z
+    // of the pass are loaded before any is used (one wait on memory per pass;
+    // u rows past the tile read its first row and go unused).
+    bf16x2 zv[4][Acc<128>::WN][8];  // packed pairs (elements 2q, 2q+1): 64 registers
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int zrow0 = tile_row + min(ug * 8 + wr * 4 + i, tl.wu - 1) * tl.htp + tl0;
+#pragma unroll
+      for (int j = 0; j < Acc<128>::WN; ++j) {
+        const int h = h0 + wc * 64 + j * 32 + (lane & 31);
+        const int loff = 4 * (lane >> 5) * p.z_ld + (h < p.H ? h : 0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          zv[i][j][e >> 1][e & 1] = (zb + (int64_t)(zrow0 + 8 * (e >> 2) + (e & 3)) * p.z_ld)[loff];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ul = ug * 8 + wr * 4 + i;
       if (ul >= tl.wu) continue;  // wave-uniform
-      const int zrow0 = tile_row + ul * tl.htp + tl0;
 #pragma unroll
       for (int j = 0; j < Acc<128>::WN; ++j) {
         const int h = h0 + wc * 64 + j * 32 + (lane & 31);
         const bool hok = h < p.H;
-        const int loff = 4 * (lane >> 5) * p.z_ld + (hok ? h : 0);
-        float zv[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const bf16* zr = zb + (int64_t)(zrow0 + 8 * (e >> 2) + (e & 3)) * p.z_ld;
-          zv[e] = (float)zr[loff];
-        }
         float lsum = 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float ds = hok ? acc.c[i][j][e] * (1.0f - zv[e] * zv[e]) : 0.0f;
+          const float zf = (float)zv[i][j][e >> 1][e & 1];
+          const float ds = hok ? acc.c[i][j][e] * (1.0f - zf * zf) : 0.0f;
           gacc[j][e] += ds;
           lsum += ds;
         }
