@@ -160,10 +160,11 @@ def unfused_baseline(torch, rl, inp, steps, warmup):
     lab = torch.from_numpy(np.ascontiguousarray(inp.labels[:, 1:], dtype=np.int64)).to(dev)  # [B, U]
     Tl = torch.from_numpy(np.ascontiguousarray(inp.T_len, dtype=np.int32)).to(dev)
     Ul = torch.from_numpy(np.ascontiguousarray(inp.U_len, dtype=np.int32)).to(dev)
-    # the lattice kernel's diagonal-major layout
-    ND, US = T + U1 - 1, (U1 + 31) // 32 * 32
+    # the lattice arrays' layout: groups of four anti-diagonals per row
+    NQ, US = (T + U1 - 1 + 3) // 4, (U1 + 31) // 32 * 32
     bi, ti, ui = torch.arange(B, device=dev), torch.arange(T, device=dev), torch.arange(U1, device=dev)
-    diag = ((bi[:, None, None] * ND + ti[None, :, None] + ui[None, None, :]) * US + ui[None, None, :]).reshape(-1)
+    dg = ti[None, :, None] + ui[None, None, :]
+    diag = (((bi[:, None, None] * NQ + dg // 4) * US + ui[None, None, :]) * 4 + dg % 4).reshape(-1)
     desc = rl.make_desc(B, T, U, V, HA, HL, H)
     lab_idx = lab[:, None, :, None].expand(B, T, U, 1)
     neg = float("-inf")
@@ -178,7 +179,7 @@ def unfused_baseline(torch, rl, inp, steps, warmup):
         phi = logp[..., blank].contiguous()
         psi = torch.zeros_like(phi)
         psi[:, :, :U] = logp[:, :, :U, :].gather(-1, lab_idx)[..., 0]
-        phid = torch.zeros(B * ND * US, device=dev)
+        phid = torch.zeros(B * NQ * US * 4, device=dev)
         psid = torch.zeros_like(phid)
         phid[diag] = phi.reshape(-1)
         psid[diag] = psi.reshape(-1)

@@ -79,9 +79,9 @@ typedef struct {
 } rnnt_desc;
 
 /* Limits of this library (RNNT_E_UNSUPPORTED beyond them): H, HA, HL multiples
- * of 8; H <= 768; U+1 <= 1024; V <= 65536; B*(T+U)*US <= 2^30 and
- * (T+U)*US <= 2^29 with US = U+1 rounded up to a multiple of 32 (the entries of
- * the lattice arrays, see rnnt_lattice). Any tile size
+ * of 8; H <= 768; U+1 <= 1024; V <= 65536; B*4*NQ*US <= 2^30 and
+ * 4*NQ*US <= 2^29 with NQ = ceil((T+U)/4) and US = U+1 rounded up to a
+ * multiple of 32 (the entries of the lattice arrays, see rnnt_lattice). Any tile size
  * is accepted; a tile's t extent is padded to a multiple of 32 rows inside the
  * library, so tile_t values that are multiples of 32 waste nothing. */
 
@@ -141,14 +141,17 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
  * Eqs. (8)-(9)) on caller-given two log-probs, for testing and for callers
  * that produce phi/psi themselves. T_len_dev / U_len_dev are DEVICE int32
  * arrays [B] (same ranges as above, not checked here). phi, psi, alpha, beta
- * are fp32 device arrays in the diagonal-major lattice layout: with
- * ND = T + U and US = U + 1 rounded up to a multiple of 32, cell (t, u) of
- * sample b is element (b * ND + t + u) * US + u (B * ND * US elements per
- * array). Elements that are not cells of a sample's lattice may hold any
+ * are fp32 device arrays, 16-byte aligned, in the lattice layout of groups of
+ * four anti-diagonals: with NQ = ceil((T + U) / 4) and US = U + 1 rounded up
+ * to a multiple of 32, cell (t, u) of sample b, on diagonal d = t + u, is
+ * element ((b * NQ + d / 4) * US + u) * 4 + d % 4 (B * NQ * US * 4 elements
+ * per array; the four diagonals of one group and row are one aligned 16-byte
+ * piece). Elements that are not cells of a sample's lattice may hold any
  * value, NaN and infinities included, and do not affect the results; psi
  * at u = U_len[b] likewise. costs[b] = -(alpha(T_b-1,U_b) + phi(T_b-1,U_b)).
  * Only the lattice cells of alpha and beta are written. desc supplies B, T,
- * U (other fields are ignored). */
+ * U (other fields are ignored). RNNT_E_INVALID for a null or misaligned
+ * pointer, RNNT_E_UNSUPPORTED beyond the limits above. */
 rnnt_status rnnt_lattice(const rnnt_desc* desc, const int32_t* T_len_dev,
                          const int32_t* U_len_dev, const float* phi, const float* psi,
                          float* alpha, float* beta, float* costs, void* stream);

@@ -952,6 +952,12 @@ rnnt_status rnnt_lattice(const rnnt_desc* desc, const int32_t* T_len_dev, const 
   if (desc->U + 1 > 1024) return fail(RNNT_E_UNSUPPORTED, "this library supports U + 1 <= 1024");
   if (!T_len_dev || !U_len_dev || !phi || !psi || !alpha || !beta || !costs)
     return fail(RNNT_E_INVALID, "null pointer");
+  for (const void* q : {(const void*)phi, (const void*)psi, (const void*)alpha, (const void*)beta})
+    if (reinterpret_cast<uintptr_t>(q) % 16 != 0)
+      return fail(RNNT_E_INVALID, "phi, psi, alpha and beta must be 16-byte aligned");
+  if (rnnt::lat_cells(desc->B, desc->T, desc->U + 1) > ((int64_t)1 << 30) ||
+      rnnt::lat_sample(desc->T, desc->U + 1) > ((int64_t)1 << 29))
+    return fail(RNNT_E_UNSUPPORTED, "the lattice arrays exceed B*4*NQ*US <= 2^30 or 4*NQ*US <= 2^29 entries");
   rnnt::LatticeArgs la{T_len_dev, U_len_dev, phi, psi, alpha, beta, nullptr, costs, desc->B, desc->T, desc->U + 1};
   RNNT_HIP(rnnt::launch_lattice(la, desc->U + 1, reinterpret_cast<hipStream_t>(stream)));
   return RNNT_OK;

@@ -15,18 +15,21 @@ struct GroupH {
   int32_t b, start, len, first, count, pad0, pad1, pad2;
 };
 
-// Lattice arrays (lse, phi, psi, alpha, beta) are stored diagonal-major per
-// sample: cell (t, u) of sample b is entry (b * ND + t + u) * US + u, with
-// ND = T + U1 - 1 diagonals and the diagonal stride US = U1 rounded up to 32
-// entries (128 bytes). A diagonal is then one contiguous, aligned vector
-// over u, which is what the forward-backward sweep reads and writes; the
-// neighbours (t + 1, u) and (t, u + 1) sit US and US + 1 entries further.
+// Lattice arrays (lse, phi, psi, alpha, beta) are stored per sample in
+// groups of four anti-diagonals: cell (t, u) of sample b, on diagonal
+// d = t + u, is entry ((b * NQ + d / 4) * US + u) * 4 + d % 4, with
+// NQ = ceil((T + U1 - 1) / 4) groups and US = U1 rounded up to 32 rows. The
+// four diagonals 4q .. 4q + 3 of row u form one aligned 16-byte piece and
+// the pieces of consecutive rows are adjacent, so the forward-backward sweep
+// (one row per lane, diagonal after diagonal) moves four diagonals of a row
+// with one 16-byte access, and a group of a diagonal's rows is contiguous.
 // (constexpr: usable from host and device code)
 constexpr int lat_us(int U1) { return (U1 + 31) & ~31; }
-constexpr int lat_nd(int T, int U1) { return T + U1 - 1; }
-constexpr int64_t lat_cells(int B, int T, int U1) { return (int64_t)B * lat_nd(T, U1) * lat_us(U1); }
+constexpr int lat_nq(int T, int U1) { return (T + U1 - 1 + 3) / 4; }
+constexpr int64_t lat_sample(int T, int U1) { return (int64_t)lat_nq(T, U1) * lat_us(U1) * 4; }
+constexpr int64_t lat_cells(int B, int T, int U1) { return (int64_t)B * lat_sample(T, U1); }
 constexpr int64_t lat_ix(int b, int t, int u, int T, int U1) {
-  return ((int64_t)b * lat_nd(T, U1) + t + u) * lat_us(U1) + u;
+  return (((int64_t)b * lat_nq(T, U1) + ((t + u) >> 2)) * lat_us(U1) + u) * 4 + ((t + u) & 3);
 }
 
 }  // namespace rnnt

@@ -199,12 +199,12 @@ joint_kernel(JointArgs p) {
         float Bt = p.beta[idx];
         float ph = p.phi[idx];
         my_lse = p.lse[idx];
-        float bn = (t_r + 1 < Tb) ? p.beta[idx + lat_us(U1)] : (u == Ub ? 0.0f : kNegInf);
+        float bn = (t_r + 1 < Tb) ? p.beta[lat_ix(b, t_r + 1, u, T, U1)] : (u == Ub ? 0.0f : kNegInf);
         my_occ = gb * fexp2((A + Bt - lp) * kLog2e);
         my_cb = gb * fexp2((A + ph + bn - lp) * kLog2e);
         if (u < Ub) {
           float ps = p.psi[idx];
-          float ln = p.beta[idx + lat_us(U1) + 1];
+          float ln = p.beta[lat_ix(b, t_r, u + 1, T, U1)];
           my_cl = gb * fexp2((A + ps + ln - lp) * kLog2e);
         }
       }
@@ -402,11 +402,11 @@ __global__ void __launch_bounds__(256) dh_inplace_kernel(DhInplaceArgs p) {
       float gb = p.dcosts ? p.dcosts[b] : 1.0f;
       float A = p.alpha[idx], Bt = p.beta[idx], ph = p.phi[idx];
       ls = p.lse[idx];
-      float bn = (t + 1 < Tb) ? p.beta[idx + lat_us(U1)] : (u == Ub ? 0.0f : kNegInf);
+      float bn = (t + 1 < Tb) ? p.beta[lat_ix(b, t + 1, u, T, U1)] : (u == Ub ? 0.0f : kNegInf);
       co = gb * fexp2((A + Bt - lp) * kLog2e);
       cb = gb * fexp2((A + ph + bn - lp) * kLog2e);
       if (u < Ub) {
-        cl = gb * fexp2((A + p.psi[idx] + p.beta[idx + lat_us(U1) + 1] - lp) * kLog2e);
+        cl = gb * fexp2((A + p.psi[idx] + p.beta[lat_ix(b, t, u + 1, T, U1)] - lp) * kLog2e);
         lab = (float)p.labels[(size_t)b * U1 + u + 1];
       }
     }

@@ -9,49 +9,58 @@
 //
 // Every cell of anti-diagonal d = t + u depends only on diagonal d - 1
 // (alpha) or d + 1 (beta), so the sweep runs over diagonals with one lattice
-// row u per lane. The arrays are diagonal-major (lat_ix): diagonal d of a
-// sample is one contiguous vector over u, so a wave reads its 64 rows of
-// phi / psi and writes its 64 results per diagonal as aligned 256-byte
-// vectors.
+// row u per lane. The arrays hold four consecutive diagonals of a row as one
+// aligned 16-byte piece (lat_ix), so a lane reads its operands and writes its
+// results for four diagonals with one 16-byte buffer access, and a wave's
+// 64 pieces are one contiguous kilobyte.
 //
 // A workgroup of NW waves serves one (sample, direction); wave w owns rows
-// u = 64 w + lane. The waves form a pipeline along u: alpha at row 64 w needs
-// row 64 w - 1 of the previous diagonal, which wave w - 1 owns, so wave w
-// runs one window of SW diagonals behind wave w - 1 (beta: one window behind
+// u = 64 w + lane. The sweep is cut into windows whose loads and stores are
+// the groups of SW diagonals from a multiple of SW (alpha computes diagonals
+// SW k + 1 .. SW k + SW in window k, upwards from the values on diagonal 0;
+// beta computes SW j + SW - 1 down to SW j, downwards from the window holding
+// D = T_b - 1 + U_b). The waves form a pipeline along u: alpha
+// at row 64 w needs row 64 w - 1 of the previous diagonal, which wave w - 1
+// owns, so wave w runs one window behind wave w - 1 (beta: one window behind
 // wave w + 1, whose row 64 (w + 1) it needs). Inside a wave the neighbour
-// row comes from the adjacent lane by a DPP shift; across waves, the
-// boundary row's values of a window go to an LDS ring of the reading wave,
-// indexed by position in the sweep (alpha: d - 1, beta: D - 1 - d, so window
-// k holds positions SW k .. SW k + SW - 1); one barrier per window separates
-// writer and reader. Step s of the workgroup is window s - w of wave w
-// (alpha) or s - (NW - 1 - w) (beta).
+// row comes from the adjacent lane by a DPP shift; across waves, the edge
+// row's values go to an LDS ring of the reading wave (slot d - 1 mod 128 for
+// alpha's diagonal d, slot d mod 128 for beta's), aligned so that a window's
+// values are four 16-byte entries; one barrier per window separates writer
+// and reader. Step s of the workgroup is window s - w of wave w (alpha) or
+// s - (NW - 1 - w) (beta). Alpha's window k stores diagonals SW k ..
+// SW k + SW - 1, the first of which the previous window computed.
 //
-// Inside the kernel the variables are kept in base 2 (x log2 e), so a
-// log-add-exp is max(a, b) + log2(1 + 2^-|a - b|): the scale is applied once
-// per operand and once per stored result, not on the sweep's dependency
-// chain.
+// Beta starts from a virtual cell, value 0 at (T_b, U_b), which it carries
+// unchanged through the diagonals above D. Inside the kernel the variables are kept in
+// base 2 (x log2 e), so a log-add-exp is max(a, b) + log2(1 + 2^-|a - b|):
+// the scale is applied once per operand and once per stored result, not on
+// the sweep's dependency chain.
 //
 // Memory goes through buffer instructions on a resource spanning the
-// sample's block of ND x US entries, with the diagonal's offset in the
-// scalar offset: a read outside the block returns 0 and a store outside it
-// is dropped. A cell outside the lattice gets that out-of-range offset for
-// its operand reads and its store, so its bytes are neither read nor
-// written, and the per-cell mask keeps its alpha / beta at -inf. A cell in
-// the lattice can still have an operand outside it (phi(-1, u) for alpha at
-// t = 0, for instance), an arbitrary value of the block (uninitialised
-// workspace in the loss path): each operand is made finite or -inf when used
-// (NaN and +inf become 1e30) and such an operand only ever meets a -inf
-// neighbour. The loads of a window are issued two windows ahead.
+// sample's block, with the group's offset in the scalar offset: a read
+// outside the block returns 0 and a store outside it is dropped. A lane
+// whose row has no cell among a group's diagonals uses an out-of-range
+// offset, so those bytes are neither read nor written; a group that holds
+// both cells and non-cells of a row is stored entry by entry, so that only
+// lattice cells are written. Operand values of non-cells inside a loaded
+// group, and operands outside the lattice that a cell at the lattice's edge
+// reads (phi(-1, u) for alpha at t = 0, for instance), may be anything, NaN
+// included: each operand is made finite or -inf when used (NaN and +inf
+// become 1e30) and such an operand only ever meets a -inf neighbour. Every
+// step issues the same number of loads and stores, so the compiler's wait
+// counts do not fall back to the shortest path; the loads of a window are
+// issued PF windows ahead.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace rnnt {
 
-constexpr int SRING = 64;                   // boundary ring entries per wave
+constexpr int SRING = 128;                  // boundary ring entries per wave (diagonal mod 128)
 constexpr unsigned kOffNone = 0xffffffffu;  // out-of-range buffer offset
 
 // workgroup barrier that orders LDS only: the global loads in flight for the
-// next window stay in flight across it
+// next windows stay in flight across it
 __device__ inline void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // raw buffer resource over `bytes` bytes at p (gfx9 word 3: 32-bit data)
@@ -59,17 +68,26 @@ __device__ inline __amdgpu_buffer_rsrc_t sample_rsrc(const float* p, unsigned by
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, (int)bytes, 0x00020000);
 }
 
-// one dword through the buffer resource at voff + soff (the builtins move
-// raw bits)
-__device__ inline float buf_ld(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+// The raw buffer builtins move integer bits: floats go through bit casts.
+typedef unsigned lat_u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline void buf_ld4(float* dst, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  const lat_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  dst[0] = __uint_as_float(v.x);
+  dst[1] = __uint_as_float(v.y);
+  dst[2] = __uint_as_float(v.z);
+  dst[3] = __uint_as_float(v.w);
+}
+__device__ inline void buf_st4(const float* v, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  const lat_u32x4 w = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, 0);
 }
 __device__ inline void buf_st(float v, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
 }
 
-// operand in base 2, finite or -inf
-__device__ inline float operand2(float raw) { return fminf(raw * kLog2e, 1e30f); }
+// x + raw log2 e with the operand made finite or -inf first (NaN and +inf
+// become 1e30), so that a -inf x stays -inf
+__device__ inline float add_operand2(float x, float raw) { return __builtin_fmaf(fminf(raw, 1e30f), kLog2e, x); }
 
 // base-2 log-add-exp; a = b = -inf gives NaN, which only occurs on cells the
 // caller masks
@@ -86,147 +104,198 @@ __device__ inline float from_next_lane(float v, float old) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), 0x130, 0xf, 0xf, false));
 }
 
-template <int NW, int SW, bool is_beta>
+template <int NW, int SW, int PF, bool is_beta>
 __device__ __attribute__((always_inline)) inline void lattice_body(const LatticeArgs& p, float* ring) {
-  static_assert(SW % 4 == 0 && 2 * SW < SRING, "ring slots of a window must not wrap onto unread ones");
+  static_assert(SW % 4 == 0 && 3 * SW <= SRING, "a window's ring slots must not wrap onto unread ones");
+  constexpr int NG = SW / 4;  // groups of four diagonals per window
   const int b = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int u = 64 * wave + lane;
   const int Tb = p.T_len[b], Ub = p.U_len[b];
-  const int US = lat_us(p.U1), ND = lat_nd(p.T, p.U1);
-  const size_t base0 = (size_t)b * ND * US;
-  const unsigned blk = (unsigned)(ND * US) * 4u;
+  const int US = lat_us(p.U1);
+  const size_t base0 = (size_t)b * lat_sample(p.T, p.U1);
+  const unsigned blk = (unsigned)lat_sample(p.T, p.U1) * 4u;
   const float* phi = p.phi + base0;
   const auto rphi = sample_rsrc(phi, blk);
   const auto rpsi = sample_rsrc(p.psi + base0, blk);
   const auto rres = sample_rsrc((is_beta ? p.beta : p.alpha) + base0, blk);
-  const unsigned dstride = (unsigned)US * 4u;  // bytes per diagonal
+  const unsigned gstride = (unsigned)US * 16u;  // bytes per group of four diagonals
   const int D = Tb - 1 + Ub;
-  const int nwin = (D + SW - 1) / SW;
-  const int nsteps = nwin > 0 ? nwin + NW - 1 : 0;
+  const int K = D / SW + 1;  // windows
+  const int nsteps = K + NW - 1;
   const int lag = is_beta ? NW - 1 - wave : wave;
-  const bool live = 64 * wave <= Ub;  // a wave past U_b holds only -inf rows
   float* const my_ring = ring + wave * SRING;
 
-  // Operands of window position w. Alpha at diagonal d = 1 + SW k + w reads
-  // phi(t-1, u) and psi(t, u-1), both on diagonal d - 1 = SW k + w (psi one
-  // row lower: lane offset u - 1; lane 0's read falls outside the block or
-  // on an unused entry). Beta at d = D - 1 - SW k - w reads phi(t, u) and
-  // psi(t, u) on diagonal d (clamped at 0: those positions are masked).
-  const unsigned vo_p = 4u * (unsigned)u;
-  const unsigned vo_s = is_beta ? vo_p : vo_p - 4u;
-  auto opnd_diag = [&](int k, int w) { return is_beta ? max(D - 1 - SW * k - w, 0) : SW * k + w; };
-  // Position w of window k is diagonal d_first + w (alpha) or d_first - w
-  // (beta), t = d - u; the cell is in the lattice for w_lo <= w < w_lo + cnt.
-  struct Span { int d_first, w_lo; unsigned cnt; };
-  auto span = [&](int k) {
-    const int d_first = is_beta ? D - 1 - SW * k : 1 + SW * k;
-    const int t0 = d_first - u;
-    const int w_lo = is_beta ? max(t0 - (Tb - 1), 0) : max(-t0, 0);
-    const int w_hi = is_beta ? min(t0, SW - 1) : min(Tb - 1 - t0, SW - 1);
-    return Span{d_first, w_lo, u <= Ub ? (unsigned)max(w_hi + 1 - w_lo, 0) : 0u};
-  };
-  // only a cell in the lattice uses its operands: the others read 0 (an
-  // out-of-range offset), which spares their bytes
+  for (int i = threadIdx.x; i < NW * SRING; i += 64 * NW) ring[i] = kNegInf;
+  // alpha: the values on diagonal 0; beta: the virtual start 0 at (T_b, U_b)
+  float cur = u == (is_beta ? Ub : 0) ? 0.0f : kNegInf;  // base 2
+  lds_sync();
+  // beta: the start value of row 64 w at diagonal D + 1, for the wave below
+  if (is_beta && wave > 0 && lane == 0) ring[(wave - 1) * SRING + ((D + 1) & (SRING - 1))] = cur;
+
+  if (64 * wave > Ub) {
+    // a wave past U_b holds only -inf rows: it takes part in the barriers
+    for (int s = -PF; s < nsteps; s += PF + 1)
+      for (int i = 0; i <= PF; ++i)
+        if (s + i >= 0) lds_sync();
+    return;
+  }
+
+  // Window k covers diagonals wlo(k) .. wlo(k) + SW - 1; the sweep visits
+  // them upwards (alpha) or downwards (beta). Group g of the window holds
+  // diagonals wlo + 4 g .. wlo + 4 g + 3.
+  auto wlo = [&](int k) { return SW * (is_beta ? K - 1 - k : k); };
+  const unsigned vo = 16u * (unsigned)u;
+  // alpha's psi operand is psi(t, u - 1): row u - 1's piece (none for u = 0)
+  const unsigned vo_s = is_beta ? vo : (u == 0 ? kOffNone : vo - 16u);
+
+  // Operands of window k, groups of diagonals wlo .. wlo + SW - 1. Alpha at
+  // diagonal d reads phi(t-1, u), psi(t, u-1) on diagonal d - 1, so alpha's
+  // window k computes diagonals wlo + 1 .. wlo + SW; beta at d reads
+  // phi(t, u), psi(t, u) on diagonal d and computes wlo + SW - 1 .. wlo. A
+  // group is read only if it serves a cell of this row (the row's cells lie
+  // on diagonals u .. u + Tb - 1).
   auto load = [&](int k, float* rp, float* rs) {
-    const Span sp = span(k);
+    const bool in = k >= 0 && k < K;
+    const int w0 = max(wlo(k), 0);
 #pragma unroll
-    for (int w = 0; w < SW; ++w) {
-      const unsigned so = (unsigned)opnd_diag(k, w) * dstride;
-      const bool ok = (unsigned)(w - sp.w_lo) < sp.cnt;
-      rp[w] = buf_ld(rphi, ok ? vo_p : kOffNone, so);
-      rs[w] = buf_ld(rpsi, ok ? vo_s : kOffNone, so);
+    for (int g = 0; g < NG; ++g) {
+      const int lo = w0 + 4 * g + (is_beta ? 0 : 1);  // first diagonal served
+      const bool need = in && u <= Ub && lo + 3 >= u && lo <= u + Tb - 1;
+      const unsigned off = 0u - (unsigned)!need;  // all-ones: no bytes read
+      const unsigned so = (unsigned)((w0 >> 2) + g) * gstride;
+      buf_ld4(rp + 4 * g, rphi, vo | off, so);
+      buf_ld4(rs + 4 * g, rpsi, vo_s | off, so);
     }
   };
 
-  for (int i = threadIdx.x; i < NW * SRING; i += 64 * NW) ring[i] = kNegInf;
-  float cur;  // base 2
-  float lnP2 = kNegInf;
-  if (!is_beta) {
-    cur = u == 0 ? 0.0f : kNegInf;  // diagonal 0
-    if (u == 0) buf_st(0.0f, rres, 0, 0);
-  } else {
-    const float fin = phi[(size_t)D * US + Ub];  // diagonal D
-    cur = u == Ub ? fin * kLog2e : kNegInf;
-    if (u == Ub) buf_st(fin, rres, vo_p, (unsigned)D * dstride);
-  }
-  lds_sync();
-  // beta: the boundary value at diagonal D (position -1) for the wave below
-  if (is_beta && wave > 0 && lane == 0) ring[(wave - 1) * SRING + SRING - 1] = cur;
+  // alpha: the result on diagonal wlo(k), computed by the previous window
+  // (at first the values on diagonal 0) and stored with window k's groups
+  float prev = cur;
+  float lnP2 = cur;  // alpha(T_b-1, U_b) in base 2 (diagonal 0 when D = 0)
 
-  // Step s: issue the loads of window s + 2 - lag into np / ns, then compute
+  // Step s: issue the loads of window s + PF - lag into np / ns, compute
   // window k = s - lag (if this wave has it) from rp / rs, which its loads
-  // filled two steps earlier. Register set j holds the windows loaded at
-  // steps s with s + 2 = j (mod 3), so the sets rotate with s alone.
-  auto step = [&](int s, float* rp, float* rs, float* np, float* ns) {
+  // filled PF steps earlier, then store it. Register set j holds the windows
+  // loaded at steps s with s + PF = j (mod PF + 1), so the sets rotate with s
+  // alone.
+  auto step = [&](int s, const float* rp, const float* rs, float* np, float* ns) {
     const int k = s - lag;
-    if (live && k + 2 >= 0 && k + 2 < nwin) load(k + 2, np, ns);
-    if (live && k >= 0 && k < nwin) {
-      // the neighbour row's value one position earlier
-      float vn[SW];
-      const int slot = (SW * k) & (SRING - 1);
-      vn[0] = my_ring[(slot - 1) & (SRING - 1)];
+    load(k + PF, np, ns);
+    float res[SW];
+#pragma unroll
+    for (int w = 0; w < SW; ++w) res[w] = 0.0f;
+    const int w0 = wlo(k);
+    const bool active = k >= 0 && k < K;
+    // position w of the sweep is diagonal d = dstart + w (alpha) or
+    // dstart - w (beta); the row's cell there is t = d - u, in the lattice
+    // for w_lo <= w < w_lo + cnt (kept as two integers rather than a lane
+    // mask per position, which would take two scalar registers each)
+    const int dstart = is_beta ? w0 + SW - 1 : w0 + 1;
+    const int t0 = dstart - u;
+    const int w_lo = is_beta ? max(t0 - (Tb - 1), 0) : max(-t0, 0);
+    const int w_hi = is_beta ? min(t0, SW - 1) : min(Tb - 1 - t0, SW - 1);
+    const unsigned cnt = active && u <= Ub ? (unsigned)max(w_hi + 1 - w_lo, 0) : 0u;
+    if (active) {
+      const int keep = is_beta ? dstart - D : 0;  // beta: positions above D pass the start value on
+      // the neighbour row's value one position earlier: ring slot d - 1
+      // (alpha) or d + 1 (beta)
+      const int slot = w0 & (SRING - 1);
+      float blkv[SW], vn[SW];
 #pragma unroll
       for (int q = 0; q < SW / 4; ++q) {
         const float4 v = *reinterpret_cast<const float4*>(my_ring + slot + 4 * q);
-        vn[4 * q + 1] = v.x;
-        vn[4 * q + 2] = v.y;
-        vn[4 * q + 3] = v.z;
-        if (4 * q + 4 < SW) vn[4 * q + 4] = v.w;
+        blkv[4 * q] = v.x;
+        blkv[4 * q + 1] = v.y;
+        blkv[4 * q + 2] = v.z;
+        blkv[4 * q + 3] = v.w;
       }
-      const Span sp = span(k);
-      const int d_first = sp.d_first, w_lo = sp.w_lo;
-      const unsigned cnt = sp.cnt;
-      float res_w[SW];
+      vn[0] = my_ring[(is_beta ? slot + SW : slot - 1) & (SRING - 1)];
+#pragma unroll
+      for (int w = 1; w < SW; ++w) vn[w] = is_beta ? blkv[SW - w] : blkv[w - 1];
 #pragma unroll
       for (int w = 0; w < SW; ++w) {
+        const float op_p = rp[is_beta ? SW - 1 - w : w];
+        const float op_s = rs[is_beta ? SW - 1 - w : w];
         const float nb = is_beta ? from_next_lane(cur, vn[w]) : from_prev_lane(cur, vn[w]);
-        const float nxt = lae2(cur + operand2(rp[w]), nb + operand2(rs[w]));
+        const float nxt = lae2(add_operand2(cur, op_p), add_operand2(nb, op_s));
         const bool ok = (unsigned)(w - w_lo) < cnt;
-        cur = ok ? nxt : kNegInf;
-        res_w[w] = cur;
-        const int d = is_beta ? d_first - w : d_first + w;
-        buf_st(cur * kLn2, rres, ok ? vo_p : kOffNone, (unsigned)max(d, 0) * dstride);
+        cur = ok ? nxt : (w < keep ? cur : kNegInf);
+        res[w] = cur;
+        if (!is_beta && w == D - dstart && u == Ub) lnP2 = cur;
       }
-      if (!is_beta && k == nwin - 1) {
-        // diagonal D is position D - 1 - SW k of the last window
-#pragma unroll
-        for (int w = 0; w < SW; ++w)
-          if (w == D - 1 - SW * k && u == Ub) lnP2 = res_w[w];
-      }
-      // the edge lane's values go to the neighbour wave's ring
+      // the edge lane's values go to the neighbour wave's ring, by diagonal
       const int nbw = is_beta ? wave - 1 : wave + 1;
       if (nbw >= 0 && nbw < NW && lane == (is_beta ? 0 : 63)) {
         float* dst = ring + nbw * SRING + slot;
 #pragma unroll
-        for (int q = 0; q < SW / 4; ++q)
-          *reinterpret_cast<float4*>(dst + 4 * q) =
-              make_float4(res_w[4 * q], res_w[4 * q + 1], res_w[4 * q + 2], res_w[4 * q + 3]);
+        for (int q = 0; q < SW / 4; ++q) {
+          const int a = 4 * q;
+          *reinterpret_cast<float4*>(dst + a) =
+              is_beta ? make_float4(res[SW - 1 - a], res[SW - 2 - a], res[SW - 3 - a], res[SW - 4 - a])
+                      : make_float4(res[a], res[a + 1], res[a + 2], res[a + 3]);
+        }
       }
     }
+    // stores: group g holds diagonals w0 + 4 g + e, sweep position
+    // SW - 1 - 4 g - e (beta) or 4 g + e - 1 (alpha; position -1 is the
+    // previous window's last result)
+    const bool prev_ok = active && u <= Ub && (unsigned)(w0 - u) < (unsigned)Tb;
+    const int wb = max(w0, 0);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float v[4];
+      bool o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int w = is_beta ? SW - 1 - 4 * g - e : 4 * g + e - 1;
+        v[e] = (w < 0 ? prev : res[w]) * kLn2;
+        o[e] = w < 0 ? prev_ok : (unsigned)(w - w_lo) < cnt;
+      }
+      const unsigned so = (unsigned)((wb >> 2) + g) * gstride;
+      // a group holding both cells and non-cells of some lane's row (only at
+      // row starts and ends) is stored entry by entry, every other group with
+      // one 16-byte store per lane (the choice is made per group: a choice
+      // per window for all its groups made the beta results vary from run to
+      // run)
+      const bool full = o[0] && o[1] && o[2] && o[3];
+      const bool part = (o[0] || o[1] || o[2] || o[3]) && !full;
+      if (__builtin_amdgcn_ballot_w64(part) != 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) buf_st(v[e], rres, o[e] ? vo + 4u * e : kOffNone, so);
+      } else {
+        buf_st4(v, rres, full ? vo : kOffNone, so);
+      }
+    }
+    if (!is_beta && active) prev = res[SW - 1];
     if (s >= 0) lds_sync();
   };
 
-  // steps -2 and -1 only issue the first two windows' loads
-  float r0p[SW], r0s[SW], r1p[SW], r1s[SW], r2p[SW], r2s[SW];
-  for (int s = -2; s < nsteps; s += 3) {
-    step(s, r1p, r1s, r0p, r0s);
-    if (s + 1 < nsteps) step(s + 1, r2p, r2s, r1p, r1s);
-    if (s + 2 < nsteps) step(s + 2, r0p, r0s, r2p, r2s);
+  // Steps -PF .. -1 only issue the first PF windows' loads. The loop runs
+  // whole groups of PF + 1 steps (up to PF past the last window, which
+  // compute and store nothing), so the loop body has no conditional step;
+  // step s + j of a group loads into set j and computes from set j + 1.
+  float rp[PF + 1][SW], rs[PF + 1][SW];
+  for (int s = -PF; s < nsteps; s += PF + 1) {
+#pragma unroll
+    for (int j = 0; j <= PF; ++j) step(s + j, rp[(j + 1) % (PF + 1)], rs[(j + 1) % (PF + 1)], rp[j], rs[j]);
   }
   if (!is_beta && u == Ub) {
-    const float v = (D == 0 ? 0.0f : lnP2 * kLn2) + phi[(size_t)D * US + Ub];
+    const float v = lnP2 * kLn2 + phi[lat_ix(0, Tb - 1, Ub, p.T, p.U1)];
     if (p.lnP) p.lnP[b] = v;
     if (p.costs) p.costs[b] = -v;
   }
 }
 
+// PF: windows of loads in flight ahead of the one computed (each costs
+// 2 SW registers; 3 windows measured no faster than 2)
 template <int NW, int SW>
 __global__ void __launch_bounds__(64 * NW) lattice_kernel(LatticeArgs p) {
+  constexpr int PF = 2;
   __shared__ __attribute__((aligned(16))) float ring[NW * SRING];
-  if (blockIdx.y == 0) lattice_body<NW, SW, false>(p, ring);
-  else lattice_body<NW, SW, true>(p, ring);
+  if (blockIdx.y == 0) lattice_body<NW, SW, PF, false>(p, ring);
+  else lattice_body<NW, SW, PF, true>(p, ring);
 }
 
 hipError_t launch_lattice(const LatticeArgs& a, int U1max, hipStream_t st) {

@@ -183,11 +183,11 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoresArgs p) {
         const float gb = p.dcosts ? p.dcosts[b] : 1.0f;
         const float A = p.alpha[idx], Bt = p.beta[idx];
         ls = p.lse[idx];
-        const float bn = (t + 1 < Tb) ? p.beta[idx + lat_us(p.U1)] : (u == Ub ? 0.0f : kNegInf);
+        const float bn = (t + 1 < Tb) ? p.beta[lat_ix(b, t + 1, u, p.T, p.U1)] : (u == Ub ? 0.0f : kNegInf);
         co = gb * fexp2((A + Bt - lp) * kLog2e);
         cb = gb * fexp2((A + p.phi[idx] + bn - lp) * kLog2e);
         if (u < Ub) {
-          cl = gb * fexp2((A + p.psi[idx] + p.beta[idx + lat_us(p.U1) + 1] - lp) * kLog2e);
+          cl = gb * fexp2((A + p.psi[idx] + p.beta[lat_ix(b, t, u + 1, p.T, p.U1)] - lp) * kLog2e);
           lab = (float)p.labels[(size_t)b * p.U1 + u + 1];
         }
       }
@@ -355,8 +355,10 @@ hipError_t launch_scores(const ScoresArgs& a, bool bwd, hipStream_t st) {
 // lse = logsumexp over the V tiles' partial statistics; phi, psi from the
 // blank / label scores, for the valid cells. One workgroup per 32 t x 32 u
 // block of a tile: the block's rows are read in row order (t fastest) and
-// the results, transposed through LDS, are written along the block's
-// anti-diagonals, which are contiguous in the lattice layout.
+// the results, transposed through LDS, are written group of four diagonals
+// by group in (row, diagonal) order, so that each wave writes the 16-byte
+// pieces of 16 consecutive rows (256 contiguous bytes of the lattice
+// layout).
 constexpr int kMB = 32, kMS = 34;  // block edge, LDS row stride (conflict-free both ways)
 __global__ void __launch_bounds__(256) lse_merge_kernel(MergeArgs p) {
   __shared__ float sm[3][kMB * kMS];  // lse, phi, psi at [u][t]
@@ -383,11 +385,15 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(MergeArgs p) {
     sm[2][ul * kMS + tt] = tl.u0 + ub + ul < Ub ? p.hy[rr] - lse : kNegInf;
   }
   __syncthreads();
+  // the block's diagonals T0 + U0 .. T0 + U0 + 62 lie in 17 groups from q0 on
+  const int T0 = tl.t0 + tb, U0 = tl.u0 + ub, q0 = (T0 + U0) >> 2;
+  constexpr int kGroups = (2 * kMB - 1 + 3) / 4 + 1;
 #pragma unroll
-  for (int i = threadIdx.x; i < (2 * kMB - 1) * kMB; i += 256) {
-    const int dl = i / kMB, ul = i % kMB, tt = dl - ul;
+  for (int i = threadIdx.x; i < kGroups * kMB * 4; i += 256) {
+    const int e = i & 3, ul = (i >> 2) % kMB, gq = (i >> 2) / kMB;
+    const int tt = 4 * (q0 + gq) + e - T0 - U0 - ul;  // t - T0 of the cell on that diagonal
     if (ul >= nu || tt < 0 || tt >= nt) continue;
-    const size_t idx = (size_t)lat_ix(b, tl.t0 + tb + tt, tl.u0 + ub + ul, p.T, p.U1);
+    const size_t idx = (size_t)lat_ix(b, T0 + tt, U0 + ul, p.T, p.U1);
     p.lse[idx] = sm[0][ul * kMS + tt];
     p.phi[idx] = sm[1][ul * kMS + tt];
     p.psi[idx] = sm[2][ul * kMS + tt];

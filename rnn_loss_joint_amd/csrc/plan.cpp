@@ -50,12 +50,11 @@ bool check_dims(const Dims& d, std::string& err, int& status) {
     err = "this library supports V <= 65536";
     return false;
   }
-  // the diagonal-major lattice arrays: B (T+U) US entries in all, and each
-  // sample's block addressable with 32-bit byte offsets
-  if (lat_cells(d.B, d.T, d.U + 1) > ((int64_t)1 << 30) ||
-      (int64_t)lat_nd(d.T, d.U + 1) * lat_us(d.U + 1) > ((int64_t)1 << 29)) {
-    err = "the lattice arrays exceed B*(T+U)*US <= 2^30 entries or (T+U)*US <= 2^29 per sample "
-          "(US = U+1 rounded up to 32)";
+  // the lattice arrays: B * 4 NQ * US entries in all, and each sample's block
+  // addressable with 32-bit byte offsets
+  if (lat_cells(d.B, d.T, d.U + 1) > ((int64_t)1 << 30) || lat_sample(d.T, d.U + 1) > ((int64_t)1 << 29)) {
+    err = "the lattice arrays exceed B*4*NQ*US <= 2^30 entries or 4*NQ*US <= 2^29 per sample "
+          "(NQ = ceil((T+U)/4), US = U+1 rounded up to 32)";
     return false;
   }
   status = 0;

@@ -436,9 +436,9 @@ hipError_t launch_score_tables(const void* WO, const void* bO, void* WOp, float*
 // coefA = (lse log2 e, g alpha beta / P), coefB = (g alpha phi beta' / P,
 // g alpha psi beta'' / P, label, 0); zeros (label -1) on padding rows.
 // One workgroup per 32 t x 32 u block of a tile: the lattice values are read
-// along the block's anti-diagonals (contiguous in the lattice layout) into
-// LDS, beta with one more t and u for the neighbours, and the coefficients
-// are written in row order. The workgroup past the last tile clears the
+// group of four diagonals by group in (row, diagonal) order (each wave reads
+// the 16-byte pieces of consecutive rows) into LDS, beta with one more t and
+// u for the neighbours, and the coefficients are written in row order. The workgroup past the last tile clears the
 // rows between the wave's last row and the 128-row padding.
 constexpr int kCB = 32, kCS = 34;  // block edge, LDS row stride (conflict-free both ways)
 __global__ void __launch_bounds__(256) coef_kernel(Scores3Args p) {
@@ -460,14 +460,23 @@ __global__ void __launch_bounds__(256) coef_kernel(Scores3Args p) {
   const int nt = min(kCB, tl.ht - tb), nu = min(kCB, tl.wu - ub);
   const int b = tl.b, Tb = p.T_len[b], Ub = p.U_len[b];
   const int t0 = tl.t0 + tb, u0 = tl.u0 + ub;
-  // lattice -> LDS along anti-diagonals of the (33 x 33) region; all loads
-  // of the thread are issued before any is stored (masked slots read entry 0)
-  constexpr int kSlots = (2 * kCB + 1) * (kCB + 1), kIt = (kSlots + 255) / 256;
+  // lattice -> LDS for the (33 x 33) region, whose diagonals t0 + u0 ..
+  // t0 + u0 + 64 lie in 17 groups from q0 on; all loads of the thread are
+  // issued before any is stored (masked slots read entry 0)
+  constexpr int kRows = kCB + 1, kGroups = (2 * kCB + 3) / 4 + 1;
+  constexpr int kSlots = kGroups * kRows * 4, kIt = (kSlots + 255) / 256;
+  const int q0 = (t0 + u0) >> 2;
+  auto slot_of = [&](int i, int& ul, int& tt) {
+    const int e = i & 3, gq = (i >> 2) / kRows;
+    ul = (i >> 2) - gq * kRows;
+    tt = 4 * (q0 + gq) + e - t0 - u0 - ul;
+  };
   float va[kIt], vb[kIt], vp[kIt], vs[kIt], vl[kIt];
 #pragma unroll
   for (int q = 0; q < kIt; ++q) {
     const int i = threadIdx.x + 256 * q;
-    const int dl = i / (kCB + 1), ul = i % (kCB + 1), tt = dl - ul;
+    int ul, tt;
+    slot_of(i, ul, tt);
     const bool okb = i < kSlots && tt >= 0 && tt <= kCB && t0 + tt < Tb && u0 + ul <= Ub;
     const bool oka = okb && tt < nt && ul < nu;
     const size_t idx = okb ? (size_t)lat_ix(b, t0 + tt, u0 + ul, p.T, p.U1) : 0;
@@ -481,7 +490,8 @@ __global__ void __launch_bounds__(256) coef_kernel(Scores3Args p) {
 #pragma unroll
   for (int q = 0; q < kIt; ++q) {
     const int i = threadIdx.x + 256 * q;
-    const int dl = i / (kCB + 1), ul = i % (kCB + 1), tt = dl - ul;
+    int ul, tt;
+    slot_of(i, ul, tt);
     const bool okb = i < kSlots && tt >= 0 && tt <= kCB && t0 + tt < Tb && u0 + ul <= Ub;
     if (!okb) continue;
     sb[ul * kCS + tt] = vb[q];

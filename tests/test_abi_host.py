@@ -124,6 +124,16 @@ def test_lattice_entry_rejects_null_and_large_U():
     with pytest.raises(rl.RnntError) as e:
         rl.rnnt_lattice(d, x, x, x, x, x, x, x, stream=0)
     assert e.value.status == rl.RNNT_E_UNSUPPORTED
+    # the lattice arrays move as 16-byte pieces: a misaligned one is rejected before any launch
+    d = rl.make_desc(2, 8, 2, 16, 8, 8, 8)
+    with pytest.raises(rl.RnntError) as e:
+        rl.rnnt_lattice(d, x, x, x, FakeTensor(16, 4), x, x, x, stream=0)
+    assert e.value.status == rl.RNNT_E_INVALID
+    # (T + U) * US per sample beyond 2^29 entries
+    d = rl.make_desc(1, 600000, 1000, 16, 8, 8, 8)
+    with pytest.raises(rl.RnntError) as e:
+        rl.rnnt_lattice(d, x, x, x, x, x, x, x, stream=0)
+    assert e.value.status == rl.RNNT_E_UNSUPPORTED
 
 
 def test_tile_working_set_independent_of_lattice_size():

@@ -97,10 +97,16 @@ LATTICE_CASES = [(70, 40, (1, 70), (0, 40)), (90, 100, (1, 90), (64, 100)),
 
 
 def lattice_layout(B, T, U1):
-    """Index arrays (b, t, u) -> entry of the documented diagonal-major layout:
-    (b * ND + t + u) * US + u with ND = T + U1 - 1 and US = U1 rounded up to 32."""
-    ND, US = T + U1 - 1, (U1 + 31) // 32 * 32
-    return ND, US
+    """Entries of the documented lattice layout and its index function: cell (t, u) of sample b,
+    on diagonal d = t + u, is entry ((b * NQ + d // 4) * US + u) * 4 + d % 4 with
+    NQ = ceil((T + U1 - 1) / 4) groups of four diagonals and US = U1 rounded up to 32."""
+    NQ, US = (T + U1 - 1 + 3) // 4, (U1 + 31) // 32 * 32
+
+    def ix(b, t, u):
+        d = t + u
+        return ((b * NQ + d // 4) * US + u) * 4 + d % 4
+
+    return B * NQ * US * 4, ix
 
 
 @pytest.mark.parametrize("T,U,tr,ur", LATTICE_CASES)
@@ -109,33 +115,33 @@ def test_lattice_kernel_matches_oracle(gpu_lib, T, U, tr, ur):
 
     rl = gpu_lib
     B, U1 = 5, U + 1
-    ND, US = lattice_layout(B, T, U1)
+    n, ix_of = lattice_layout(B, T, U1)
     inp = make_inputs(B, T, U, 33, 8, 8, 8, dtype="f32", seed=31 + U, t_range=tr, u_range=ur)
     say(f"lattice kernel: B={B} T={T} U={U} ragged")
     r = oracle.loss_and_grads(inp, want_grads=False)
     # entries outside every lattice hold poison the kernel must not let through
     rng = np.random.default_rng(U)
     poison = np.array([np.nan, np.inf, -np.inf, 1e30, -1e30, 7.0], np.float32)
-    phi = rng.choice(poison, size=B * ND * US).astype(np.float32)
-    psi = rng.choice(poison, size=B * ND * US).astype(np.float32)
+    phi = rng.choice(poison, size=n).astype(np.float32)
+    psi = rng.choice(poison, size=n).astype(np.float32)
     cells = []
     for b, s in enumerate(r.samples):
         Tb, Ub = inp.T_len[b], inp.U_len[b]
         t, u = np.meshgrid(np.arange(Tb), np.arange(Ub + 1), indexing="ij")
-        ix = (b * ND + t + u) * US + u
+        ix = ix_of(b, t, u)
         cells.append(ix)
         phi[ix] = s.phi
         psi[ix[:, :Ub]] = s.psi[:, :Ub]
     dev = torch.device("cuda:0")
     tp = lambda a: torch.from_numpy(a).to(dev)
-    al = torch.full((B * ND * US,), 7.0, device=dev)
-    be = torch.full((B * ND * US,), 7.0, device=dev)
+    al = torch.full((n,), 7.0, device=dev)
+    be = torch.full((n,), 7.0, device=dev)
     costs = torch.zeros(B, device=dev)
     d = rl.make_desc(B, T, U, 33, 8, 8, 8)
     rl.rnnt_lattice(d, tp(inp.T_len), tp(inp.U_len), tp(phi), tp(psi), al, be, costs)
     torch.cuda.synchronize()
     al, be, costs = al.cpu().numpy(), be.cpu().numpy(), costs.cpu().numpy()
-    touched = np.zeros(B * ND * US, bool)
+    touched = np.zeros(n, bool)
     for b, s in enumerate(r.samples):
         Tb, Ub = inp.T_len[b], inp.U_len[b]
         ix = cells[b]
@@ -146,6 +152,49 @@ def test_lattice_kernel_matches_oracle(gpu_lib, T, U, tr, ur):
         assert np.max(np.abs(be[ix] - s.beta)) <= 2e-6 * scale * (Tb + Ub), f"beta, sample {b}"
     # entries outside the lattices are untouched
     assert np.all(al[~touched] == 7.0) and np.all(be[~touched] == 7.0)
+
+
+def test_lattice_large_bitwise_reproducible(gpu_lib):
+    """At the 40 s workload's lattice shape (B=256, T=1000, U=200, ragged), two sweeps over the
+    same phi / psi give bit-identical alpha, beta and costs, and every lattice cell is written
+    (finite). Guards the sweep's cross-wave hand-over and load waits, which a wrong schedule
+    breaks only under full-GPU concurrency."""
+    import torch
+
+    rl = gpu_lib
+    B, T, U = 256, 1000, 200
+    U1 = U + 1
+    n, ix_of = lattice_layout(B, T, U1)
+    rng = np.random.default_rng(2026)
+    T_len = rng.integers(500, T + 1, B).astype(np.int32)
+    U_len = rng.integers(100, U + 1, B).astype(np.int32)
+    say(f"lattice B={B} T={T} U={U}: two sweeps, bitwise")
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(11)
+    phi = torch.empty(n, device=dev).uniform_(-4.5, -2.5, generator=g)
+    psi = torch.empty(n, device=dev).uniform_(-4.5, -2.5, generator=g)
+    Tl, Ul = torch.from_numpy(T_len).to(dev), torch.from_numpy(U_len).to(dev)
+    d = rl.make_desc(B, T, U, 33, 8, 8, 8)
+    runs = []
+    for _ in range(2):
+        al = torch.full((n,), float("nan"), device=dev)
+        be = torch.full((n,), float("nan"), device=dev)
+        costs = torch.zeros(B, device=dev)
+        rl.rnnt_lattice(d, Tl, Ul, phi, psi, al, be, costs)
+        torch.cuda.synchronize()
+        runs.append((al.view(torch.int32), be.view(torch.int32), costs.view(torch.int32)))
+    for x, y in zip(runs[0], runs[1]):
+        assert torch.equal(x, y)
+    # every lattice cell written: (b, t, u) with t < T_b, u <= U_b
+    bi = torch.arange(B, device=dev)[:, None, None]
+    ti = torch.arange(T, device=dev)[None, :, None]
+    ui = torch.arange(U1, device=dev)[None, None, :]
+    cell = (ti < Tl.long()[:, None, None]) & (ui <= Ul.long()[:, None, None])
+    ix = ix_of(bi, ti, ui).expand(B, T, U1)[cell]
+    al, be = runs[0][0].view(torch.float32), runs[0][1].view(torch.float32)
+    assert int(ix.numel()) == int((T_len.astype(np.int64) * (U_len + 1)).sum())
+    assert bool(torch.isfinite(al[ix]).all()) and bool(torch.isfinite(be[ix]).all())
+    assert bool(torch.isfinite(runs[0][2].view(torch.float32)).all())
 
 
 # ----------------------------------------------------------------------------- fp32 mode
