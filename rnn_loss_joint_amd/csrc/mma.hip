@@ -20,12 +20,19 @@ namespace rnnt {
 // One workgroup per (32-t strip of a tile, group of 8 u values): thread
 // (tt, q) = (tid / 8, tid % 8) owns t = strip start + tt and the 8-wide k
 // chunks q, q+8, ...; each chunk of a[b, t] is loaded once and combined with
-// the group's 8 rows of l. Writes z[row, k] = bf16(tanh(a + l)) for k < H (0
-// up to z_ld and on padding rows t >= t0 + ht) and, with SCORES, the blank
-// and label scores of each row as dot products of that bf16 z with the two
-// W^O rows (plus the biases).
+// the group's 8 rows of l. Those 8 rows (and, with SCORES, the blank and
+// label rows of W^O) are shared by all 32 t of the workgroup, so they are
+// staged in LDS once instead of being loaded by every thread (which kept the
+// vector memory address unit ~75 % busy). Writes z[row, k] = bf16(tanh(a + l))
+// for k < H (0 up to z_ld and on padding rows t >= t0 + ht) and, with
+// SCORES, the blank and label scores of each row as dot products of that
+// bf16 z with the two W^O rows (plus the biases).
+constexpr int kZHmax = 768;  // H_pad bound (the library's H <= 768)
 template <bool SCORES>
 __global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
+  __shared__ __attribute__((aligned(16))) char smem[8 * kZHmax * 4 + (SCORES ? 9 * kZHmax * 2 : 0)];
+  float* const ls = reinterpret_cast<float*>(smem);                 // [8][H_pad] l rows
+  bf16* const ws = reinterpret_cast<bf16*>(smem + 8 * kZHmax * 4);  // [9][H_pad] blank, label rows
   const int tid = threadIdx.x;
   const int ug = blockIdx.x % p.n_ug;
   const int strip = p.strip_begin + blockIdx.x / p.n_ug;
@@ -43,8 +50,9 @@ __global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
   const bool row_ok = tloc < tl.ht;
   const int b = tl.b;
   const int u0 = tl.u0 + u_first;
-  const float* arow = p.a + ((size_t)b * p.T + tl.t0 + (row_ok ? tloc : 0)) * p.H_pad;
-  const float* lrow0 = p.l + ((size_t)b * p.U1 + u0) * p.H_pad;
+  const int Hp = p.H_pad;
+  const float* arow = p.a + ((size_t)b * p.T + tl.t0 + (row_ok ? tloc : 0)) * Hp;
+  const float* lrow0 = p.l + ((size_t)b * p.U1 + u0) * Hp;
   const int64_t row0 = (int64_t)tl.row0 - p.buf_row_base + (int64_t)u_first * tl.htp + tloc;
   bf16* zb = reinterpret_cast<bf16*>(p.z);
   const bf16* WO = reinterpret_cast<const bf16*>(p.WO);
@@ -61,42 +69,54 @@ __global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
       lab[uu] = (uu < nu && u0 + uu < Ub) ? p.labels[(size_t)b * p.U1 + u0 + uu + 1] : -1;
     }
   }
-  const bf16* wb = WO + (size_t)p.blank * p.H;
+  // stage the group's l rows (rows past the tile repeat its last one) and the
+  // W^O rows (0 past H)
+  const int n4 = Hp / 4;
+  for (int i = tid; i < 8 * n4; i += 256) {
+    const int uu = i / n4, c = i - uu * n4;
+    reinterpret_cast<f32x4*>(ls)[i] = ldg<f32x4>(lrow0 + (size_t)min(uu, nu - 1) * Hp + 4 * c);
+  }
+  if constexpr (SCORES) {
+    const int n8 = Hp / 8;
+    for (int i = tid; i < 9 * n8; i += 256) {
+      const int r = i / n8, k = 8 * (i - r * n8);
+      const int v = r == 0 ? p.blank : max(lab[r - 1], 0);
+      reinterpret_cast<bf16x8*>(ws)[i] = k < p.H ? ldg<bf16x8>(WO + (size_t)v * p.H + k) : bf16x8{};
+    }
+  }
+  __syncthreads();
+  // a of the next chunk is loaded while the current one is computed
+  auto a_at = [&](int k) { return row_ok && k < p.H ? k : 0; };
+  f32x4 na0 = ldg<f32x4>(arow + a_at(q * 8)), na1 = ldg<f32x4>(arow + a_at(q * 8) + 4);
   for (int k = q * 8; k < p.z_ld; k += 64) {
-    // every load of the chunk first (masked ones read a valid row / column
-    // and are zeroed below), so the chunk waits on memory once
     const bool kok = row_ok && k < p.H;
     const int kk = kok ? k : 0;
-    const f32x4 a0 = ldg<f32x4>(arow + kk), a1 = ldg<f32x4>(arow + kk + 4);
-    f32x4 l0[8], l1[8];
-#pragma unroll
-    for (int uu = 0; uu < 8; ++uu) {
-      const float* lrow = lrow0 + (size_t)min(uu, nu - 1) * p.H_pad;
-      l0[uu] = ldg<f32x4>(lrow + kk);
-      l1[uu] = ldg<f32x4>(lrow + kk + 4);
+    const f32x4 a0 = na0, a1 = na1;
+    if (k + 64 < p.z_ld) {
+      na0 = ldg<f32x4>(arow + a_at(k + 64));
+      na1 = ldg<f32x4>(arow + a_at(k + 64) + 4);
     }
-    bf16x8 xb, xy[8];
-    if constexpr (SCORES) {
-      xb = ldg<bf16x8>(wb + kk);
-#pragma unroll
-      for (int uu = 0; uu < 8; ++uu) xy[uu] = ldg<bf16x8>(WO + (size_t)(lab[uu] >= 0 ? lab[uu] : 0) * p.H + kk);
-    }
+    bf16x8 xb;
+    if constexpr (SCORES) xb = *reinterpret_cast<const bf16x8*>(ws + kk);
 #pragma unroll
     for (int uu = 0; uu < 8; ++uu) {
       if (uu >= nu) continue;  // workgroup-uniform
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls + uu * Hp + kk);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + uu * Hp + kk + 4);
       f32x8 zf;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) zf[e] = tanh_fast(a0[e] + l0[uu][e]);
+      for (int e = 0; e < 4; ++e) zf[e] = tanh_fast(a0[e] + l0[e]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) zf[e + 4] = tanh_fast(a1[e] + l1[uu][e]);
+      for (int e = 0; e < 4; ++e) zf[e + 4] = tanh_fast(a1[e] + l1[e]);
       bf16x8 z = __builtin_convertvector(zf, bf16x8);  // adjacent pairs: one packed convert each
       if (!kok) z = bf16x8{};
       if constexpr (SCORES) {
+        const bf16x8 xy = *reinterpret_cast<const bf16x8*>(ws + (uu + 1) * Hp + kk);
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {  // bf16 pair dot products, fp32 accumulation
           const bf16x2 zz = {z[e], z[e + 1]};
           hb[uu] = __builtin_amdgcn_fdot2_f32_bf16(zz, bf16x2{xb[e], xb[e + 1]}, hb[uu], false);
-          hy[uu] = __builtin_amdgcn_fdot2_f32_bf16(zz, bf16x2{xy[uu][e], xy[uu][e + 1]}, hy[uu], false);
+          hy[uu] = __builtin_amdgcn_fdot2_f32_bf16(zz, bf16x2{xy[e], xy[e + 1]}, hy[uu], false);
         }
       }
       *reinterpret_cast<bf16x8*>(zb + (row0 + (int64_t)uu * tl.htp) * p.z_ld + k) = z;
@@ -123,6 +143,7 @@ __global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
 
 hipError_t launch_zrow(const ZArgs& a, hipStream_t st) {
   if (a.n_strips == 0) return hipSuccess;
+  if (a.H_pad > kZHmax || a.H_pad % 8 != 0 || a.z_ld > a.H_pad) return hipErrorInvalidValue;  // LDS staging bound
   dim3 grid(a.n_strips * a.n_ug), block(256);
   if (a.hb) hipLaunchKernelGGL(zrow_kernel<true>, grid, block, 0, st, a);
   else hipLaunchKernelGGL(zrow_kernel<false>, grid, block, 0, st, a);

@@ -258,6 +258,12 @@ def test_20s_sampled_tiled_and_untiled(gpu_lib):
     say("20s untiled vs tiled")
     cu, gu = run_gpu(gpu_lib, inp, mode="untiled")
     c2, g2 = run_gpu(gpu_lib, inp)
+    say("20s tiled twice: bitwise")
+    c3, g3 = run_gpu(gpu_lib, inp)
+    # ordered reductions only (no float atomics): a second run gives the same bits
+    assert np.array_equal(c2, c3)
+    for k in GRADS:
+        assert np.array_equal(g2[k], g3[k]), k
     # same equations; the tiled forward accumulates the per-V-tile (max, sum)
     # block by block, the untiled one per 256-score tile, so only the
     # summation order differs
