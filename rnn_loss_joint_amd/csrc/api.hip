@@ -318,6 +318,9 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
     g.c_cols = p.H_pad;
     g.bias = bZ;
     g.bias_bf16 = bf;
+    // bf16 mode: a and l are read only by the z-row kernel, which wants the
+    // tanh argument already scaled for its base-2 exponential
+    g.out_scale = bf ? rnnt::kTanhArgScale : 0.0f;
     {
       ProfScope ps_("preproj_gemm", st);
       RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_KC_KC, bf, bf, bf, 1, st));

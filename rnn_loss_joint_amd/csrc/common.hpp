@@ -95,6 +95,10 @@ __device__ inline float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // tanh from one exp2 and one reciprocal: tanh|x| = (1-e)/(1+e), e = exp(-2|x|).
 // Absolute error ~1e-7, far below bf16 rounding of the result.
+// z = tanh(x) from s = x * kTanhArgScale (the pre-projections of the bf16
+// path are stored scaled): 2 / (1 + 2^s) - 1
+constexpr float kTanhArgScale = -2.0f * 1.4426950408889634f;
+__device__ inline float tanh_from_scaled(float s) { return __builtin_fmaf(2.0f, frcp(1.0f + fexp2(s)), -1.0f); }
 __device__ inline float tanh_fast(float x) {
   // tanh x = 2 / (1 + e^-2x) - 1; for x -> -inf, e^-2x overflows to +inf and
   // the reciprocal to 0, giving -1

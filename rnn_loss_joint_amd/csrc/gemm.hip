@@ -321,6 +321,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
   // epilogue: C[m, n] = acc (+ bias[n]); columns in [N, c_cols) get 0
   constexpr int W = WaveTile<M>::W;
   float* C = g.C + (int64_t)split * g.split_stride;
+  const float osc = g.out_scale != 0.0f ? g.out_scale : 1.0f;
 #pragma unroll
   for (int j = 0; j < W; ++j) {
     int n = n0 + wc * 64 + j * M::ROWS + M::col_of(lane);
@@ -333,7 +334,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < M::NACC; ++e) {
         int m = m0 + wr * 64 + i * M::ROWS + M::row_of(e, lane);
-        if (m < g.M) C[(int64_t)m * g.ldc + n] = (n < g.N) ? wt.acc[i][j][e] + bias : 0.0f;
+        if (m < g.M) C[(int64_t)m * g.ldc + n] = (n < g.N) ? (wt.acc[i][j][e] + bias) * osc : 0.0f;
       }
     }
   }

@@ -104,6 +104,7 @@ struct GemmArgs {
   int c_cols;        // columns to write (cols in [N, c_cols) get 0)
   const void* bias;  // optional bias over n
   int bias_bf16;
+  float out_scale;   // C = (acc + bias) * out_scale; 0 means 1
   // optional column sums of A over k (sum over k of A[m, k]) for n-tile 0
   float* colsum;     // [splits, M] partials
 };

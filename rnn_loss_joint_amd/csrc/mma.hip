@@ -20,7 +20,7 @@ namespace rnnt {
 // One workgroup per (32-t strip of a tile, group of 8 u values): thread
 // (tt, q) = (tid / 8, tid % 8) owns t = strip start + tt and the 8-wide k
 // chunks q, q+8, ...; each chunk of a[b, t] is loaded once and combined with
-// the group's 8 rows of l. Those 8 rows (and, with SCORES, the blank and
+// the group's 8 rows of l (a and l arrive scaled by kTanhArgScale). Those 8 rows (and, with SCORES, the blank and
 // label rows of W^O) are shared by all 32 t of the workgroup, so they are
 // staged in LDS once instead of being loaded by every thread (which kept the
 // vector memory address unit ~75 % busy). Writes z[row, k] = bf16(tanh(a + l))
@@ -105,9 +105,9 @@ __global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
       const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + uu * Hp + kk + 4);
       f32x8 zf;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) zf[e] = tanh_fast(a0[e] + l0[e]);
+      for (int e = 0; e < 4; ++e) zf[e] = tanh_from_scaled(a0[e] + l0[e]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) zf[e + 4] = tanh_fast(a1[e] + l1[e]);
+      for (int e = 0; e < 4; ++e) zf[e + 4] = tanh_from_scaled(a1[e] + l1[e]);
       bf16x8 z = __builtin_convertvector(zf, bf16x8);  // adjacent pairs: one packed convert each
       if (!kok) z = bf16x8{};
       if constexpr (SCORES) {
