@@ -546,26 +546,32 @@ hipError_t launch_dz(const DzArgs& a, bool bf16_mode, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------- reductions
+// One workgroup per (group, row j of the group): dst row += the partial rows
+// of the group's tiles, in plan order (deterministic). 16-byte accesses: H is
+// a multiple of 8 and every partial row starts 16-byte aligned.
 __global__ void __launch_bounds__(256) group_reduce_kernel(GroupReduceArgs p) {
   const Tile* tiles = p.tiles;
   const int gi = blockIdx.x, j = blockIdx.y;
   const Group gr = p.groups[gi];
   if (j >= gr.len) return;
-  float* dst = p.G + ((int64_t)gr.b * p.Gdim + gr.start + j) * p.H;
-  for (int h = threadIdx.x; h < p.H; h += blockDim.x) {
-    float s = 0.0f;
+  f32x4* dst = reinterpret_cast<f32x4*>(p.G + ((int64_t)gr.b * p.Gdim + gr.start + j) * p.H);
+  for (int h4 = threadIdx.x; h4 < p.H / 4; h4 += blockDim.x) {
+    f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int c = 0; c < gr.count; ++c) {
       const int tid = p.idx[gr.first + c];
       const int nsub = p.n_sub ? tiles[tid].htp / 32 : 1;
-      const float* src = p.P + (int64_t)(tid - p.tile_begin) * p.tile_stride + (int64_t)j * p.H + h;
-      for (int q = 0; q < nsub; ++q) s += src[q * p.sub_stride];
+      const float* src = p.P + (int64_t)(tid - p.tile_begin) * p.tile_stride + (int64_t)j * p.H + 4 * h4;
+      for (int q = 0; q < nsub; ++q) s += *reinterpret_cast<const f32x4*>(src + q * p.sub_stride);
     }
-    dst[h] += s;
+    dst[h4] += s;
   }
 }
 
 hipError_t launch_group_reduce(const GroupReduceArgs& a, hipStream_t st) {
   if (a.n_groups == 0) return hipSuccess;
+  if (a.H % 4 || a.tile_stride % 4 || a.sub_stride % 4 || reinterpret_cast<uintptr_t>(a.P) % 16 ||
+      reinterpret_cast<uintptr_t>(a.G) % 16)
+    return hipErrorInvalidValue;  // the kernel moves 16-byte pieces
   dim3 grid(a.n_groups, a.max_len), block(256);
   hipLaunchKernelGGL(group_reduce_kernel, grid, block, 0, st, a);
   return hipGetLastError();
@@ -586,10 +592,12 @@ hipError_t launch_to_bf16(const float* src, void* dst, int64_t n, hipStream_t st
   return hipGetLastError();
 }
 
-__global__ void split_reduce_kernel(float* out, const float* P, int64_t n, int splits, int64_t stride,
-                                    int acc) {
+// out[i] (+)= sum over q of P[q stride + i], q in order; T = float or f32x4
+// (n and stride then count 16-byte pieces)
+template <class T>
+__global__ void split_reduce_kernel(T* out, const T* P, int64_t n, int splits, int64_t stride, int acc) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    float s = acc ? out[i] : 0.0f;
+    T s = acc ? out[i] : T{};
     for (int q = 0; q < splits; ++q) s += P[q * stride + i];
     out[i] = s;
   }
@@ -598,9 +606,16 @@ __global__ void split_reduce_kernel(float* out, const float* P, int64_t n, int s
 hipError_t launch_split_reduce(float* out, const float* P, int64_t n, int splits, int64_t stride,
                                bool accumulate, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
-  hipLaunchKernelGGL(split_reduce_kernel, dim3(blocks), dim3(256), 0, st, out, P, n, splits, stride,
-                     accumulate ? 1 : 0);
+  if (n % 4 == 0 && stride % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0 &&
+      reinterpret_cast<uintptr_t>(P) % 16 == 0) {
+    const int blocks = (int)std::min<int64_t>((n / 4 + 255) / 256, 4096);
+    hipLaunchKernelGGL(split_reduce_kernel<f32x4>, dim3(blocks), dim3(256), 0, st, reinterpret_cast<f32x4*>(out),
+                       reinterpret_cast<const f32x4*>(P), n / 4, splits, stride / 4, accumulate ? 1 : 0);
+  } else {
+    const int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(split_reduce_kernel<float>, dim3(blocks), dim3(256), 0, st, out, P, n, splits, stride,
+                       accumulate ? 1 : 0);
+  }
   return hipGetLastError();
 }
 
