@@ -341,6 +341,10 @@ def main():
 
     d = inp.dims
     value = inp.padded_cells / (ms * 1e-3)
+    # device inputs: h^A, h^L, W^A, W^L, b^Z, W^O, b^O in the mode dtype, labels int32
+    esz = 2 if dtype == "bf16" else 4
+    input_bytes = (esz * (d["B"] * d["T"] * d["HA"] + d["B"] * (d["U"] + 1) * d["HL"] + d["H"] * (d["HA"] + d["HL"] + 1)
+                          + d["V"] * (d["H"] + 1)) + 4 * d["B"] * (d["U"] + 1))
     out = {
         "metric": "RNN-T fwd+bwd lattice cells/s (B*T*(U+1)) at V=1024; peak HBM bytes",
         "value": value,
@@ -355,6 +359,8 @@ def main():
         "dtype": dtype,
         "data": "synthetic",
         "peak_hbm_bytes": int(peak),
+        "input_bytes": int(input_bytes),
+        "peak_hbm_minus_inputs_bytes": int(peak - input_bytes),
         "valid_cells_per_s": inp.valid_cells / (ms * 1e-3),
         "config": {"workload": w.name, "B": d["B"], "T": d["T"], "U": d["U"],
                    "V": d["V"], "HA": d["HA"], "HL": d["HL"], "H": d["H"], "mode": args.mode,
