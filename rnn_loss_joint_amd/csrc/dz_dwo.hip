@@ -12,64 +12,14 @@
 namespace rnnt {
 
 // ============================================================================ dW^O, db^O
-// C[v, h] = sum over rows k of dh[k, v] * z[k, h], split-K partials. The h
-// range is covered by 256-wide tiles and, for a remainder of at most 128
-// columns, one 128-wide tile. db^O[v] = sum_k dh[k, v] is taken on the dh
-// fragments of the h-tile-0 workgroups (bf16 dot products with ones beside
-// the MFMAs) rather than as an extra column of z, which would add a whole
-// 256-wide tile for one column at H = 640. Workgroup ids are arranged so the
-// tiles of one k split share an XCD (L2).
+// C[v, h] = sum over rows k of dh[k, v] * z[k, h]; column h = H of z reads the
+// ones page, so C[v, H] = sum_k dh[k, v] = db^O[v]. Split-K partials.
+// Workgroup ids are arranged so the tiles of one k split share an XCD (L2).
 constexpr int kDwoLds = 2 * 2 * m3::MnTile<256>::BYTES;
-
-// h tiles: H / 256 wide ones, then one more for the remainder (wide if it is
-// over 128 columns, else narrow)
-__host__ __device__ inline int dwo_h_tiles(int H) { return (H + 255) / 256; }
-__host__ __device__ inline bool dwo_narrow(int H, int ht) { return ht == H / 256 && H % 256 != 0 && H % 256 <= 128; }
-
-template <int BN>
-__device__ __attribute__((always_inline)) inline void dwo_tile(const DwoArgs& p, char* lds, int split, int vt,
-                                                               int ht, int kb, int ke) {
+__device__ __attribute__((always_inline)) inline void dwo_body(const DwoArgs& p, char* lds, int id) {
   using namespace m3;
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  MnTile<256> la;
-  la.init(Opnd{reinterpret_cast<const bf16*>(p.dh) + (int64_t)kb * p.dh_ld, p.dh_ld, p.V, max(0, ke - kb), -1},
-          vt * 256, wave, tid & 63);
-  MnTile<BN> lb;
-  lb.init(Opnd{reinterpret_cast<const bf16*>(p.z) + (int64_t)kb * p.z_ld, p.z_ld, p.H, max(0, ke - kb), -1},
-          ht * 256, wave, tid & 63);
-  Acc<BN> acc;
-  acc.zero();
-  float asum[Acc<BN>::WM] = {};
-  const int kl = (max(0, ke - kb) + BK - 1) / BK * BK;
-  core<BN, true, (BN == 256 ? 2 : 3), true>(acc, la, lb, kl, lds, tid, asum);
-
-  const int lane = tid & 63, wr = wave >> 1, wc = wave & 1;
-  float* C = p.PW + (int64_t)split * p.V * p.H;
-#pragma unroll
-  for (int j = 0; j < Acc<BN>::WN; ++j) {
-    const int h = ht * 256 + wc * (BN / 2) + j * 32 + (lane & 31);
-#pragma unroll
-    for (int i = 0; i < Acc<BN>::WM; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int v = vt * 256 + acc_row(wr, i, e, lane);
-        if (v < p.V && h < p.H) C[(int64_t)v * p.H + h] = acc.c[i][j][e];
-      }
-  }
-  // db^O: A fragment i of wave row wr holds v = vt 256 + wr 128 + 32 i + lane % 32
-  if (ht == 0) {
-#pragma unroll
-    for (int i = 0; i < Acc<BN>::WM; ++i) {
-      const float s = asum[i] + __shfl_xor(asum[i], 32);
-      const int v = vt * 256 + wr * 128 + i * 32 + lane;
-      if (wc == 0 && lane < 32 && v < p.V) p.PB[(int64_t)split * p.V + v] = s;
-    }
-  }
-}
-
-__device__ __attribute__((always_inline)) inline void dwo_body(const DwoArgs& p, char* lds, int id) {
-  const int nv = (p.V + m3::BM - 1) / m3::BM, nh = dwo_h_tiles(p.H);
+  const int nv = (p.V + BM - 1) / BM, nh = (p.H + 1 + 255) / 256;
   const int xcd = id & 7, local = id >> 3;
   const int per = nv * nh;
   const int split = (local / per) * 8 + xcd;
@@ -78,8 +28,35 @@ __device__ __attribute__((always_inline)) inline void dwo_body(const DwoArgs& p,
   const int vt = rem / nh, ht = rem % nh;
   const int kb = split * p.k_per_split;
   const int ke = min(p.K, kb + p.k_per_split);
-  if (dwo_narrow(p.H, ht)) dwo_tile<128>(p, lds, split, vt, ht, kb, ke);
-  else dwo_tile<256>(p, lds, split, vt, ht, kb, ke);
+
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  MnTile<256> la;
+  la.init(Opnd{reinterpret_cast<const bf16*>(p.dh) + (int64_t)kb * p.dh_ld, p.dh_ld, p.V, max(0, ke - kb), -1},
+          vt * 256, wave, tid & 63);
+  MnTile<256> lb;
+  lb.init(Opnd{reinterpret_cast<const bf16*>(p.z) + (int64_t)kb * p.z_ld, p.z_ld, p.H, max(0, ke - kb), p.H},
+          ht * 256, wave, tid & 63);
+  Acc<256> acc;
+  acc.zero();
+  const int kl = (max(0, ke - kb) + BK - 1) / BK * BK;
+  core<256, true, 2>(acc, la, lb, kl, lds, tid);
+
+  const int lane = tid & 63, wr = wave >> 1, wc = wave & 1;
+  float* C = p.PW + (int64_t)split * p.V * p.H;
+#pragma unroll
+  for (int j = 0; j < Acc<256>::WN; ++j) {
+    const int h = ht * 256 + wc * 128 + j * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < Acc<256>::WM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int v = vt * 256 + acc_row(wr, i, e, lane);
+        if (v < p.V) {
+          if (h < p.H) C[(int64_t)v * p.H + h] = acc.c[i][j][e];
+          else if (h == p.H) p.PB[(int64_t)split * p.V + v] = acc.c[i][j][e];
+        }
+      }
+  }
 }
 
 
@@ -219,7 +196,7 @@ __global__ void __launch_bounds__(256) dz_dwo_kernel(DzArgs dz, DwoArgs dw, int 
 }
 
 hipError_t launch_dz_dwo(const DzArgs& a, const DwoArgs& w, hipStream_t st) {
-  const int nv = (w.V + 255) / 256, nhw = dwo_h_tiles(w.H);
+  const int nv = (w.V + 255) / 256, nhw = (w.H + 1 + 255) / 256;
   const int n_dwo = w.K > 0 ? (w.splits + 7) / 8 * 8 * nv * nhw : 0;
   const int nh = (a.H + 127) / 128;
   const int n_dz = a.n_strips > 0 ? (a.n_strips + 7) / 8 * 8 * nh : 0;

@@ -194,13 +194,8 @@ __device__ inline void wait_vm() {
 // The hand-over to the next stage (wait for its dma, barrier) sits before
 // k-step 3; k-step 3 then reads the next stage's first fragments and issues
 // the dma of stage q + NSTAGE into the slot just released.
-//
-// SUMA: also sum each A row over k into asum[f] (A fragment f of this wave,
-// row m_base + lane % 32; lanes l and l + 32 hold the two k halves of a row),
-// by bf16 dot products with ones beside the MFMAs.
-template <int BN, bool MN, int NSTAGE, bool SUMA = false, class LA, class LB>
-__device__ void core(Acc<BN>& acc, const LA& la, const LB& lb, int K_loop, char* lds, int tid,
-                     float* asum = nullptr) {
+template <int BN, bool MN, int NSTAGE, class LA, class LB>
+__device__ void core(Acc<BN>& acc, const LA& la, const LB& lb, int K_loop, char* lds, int tid) {
   constexpr int WM = Acc<BN>::WM, WN = Acc<BN>::WN;
   constexpr int NMF = WM * WN;  // MFMAs per k-step
   constexpr int NFR = WM + WN;  // fragments per k-step
@@ -248,18 +243,6 @@ __device__ void core(Acc<BN>& acc, const LA& la, const LB& lb, int K_loop, char*
     for (int x = 0; x < NMF; ++x) {
       const int i = x / WN, j = x % WN;
       acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j], acc.c[i][j], 0, 0, 0);
-      if constexpr (SUMA) {
-        if (j == 0) {
-          const bf16x2 one2{(bf16)1.0f, (bf16)1.0f};
-          const bf16x8 a8 = af[cb][i];
-          float s = asum[i];
-          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a8, a8, 0, 1), one2, s, false);
-          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a8, a8, 2, 3), one2, s, false);
-          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a8, a8, 4, 5), one2, s, false);
-          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a8, a8, 6, 7), one2, s, false);
-          asum[i] = s;
-        }
-      }
 #pragma unroll
       for (int f = 0; f < NFR; ++f)
         if (f * NMF / NFR == x) read_frag(f, rd_st, rd_ss, af[cb ^ 1], bfr[cb ^ 1]);

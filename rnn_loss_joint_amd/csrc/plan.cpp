@@ -193,7 +193,7 @@ void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H
   // dW^A / dW^L ~512
   p.nvt = (int)cdiv(d.V, 256);
   if (d.bf16) {
-    int64_t tiles_vh = cdiv(d.V, 256) * cdiv(d.H, 256);
+    int64_t tiles_vh = cdiv(d.V, 256) * cdiv(d.H + 1, 256);
     int64_t per_xcd = std::max<int64_t>(1, 32 / tiles_vh);
     p.s6 = (int)std::max<int64_t>(1, std::min<int64_t>(8 * per_xcd, p.max_wave_rows / 4096));
   } else {

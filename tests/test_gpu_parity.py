@@ -224,6 +224,16 @@ def test_bf16_reduced(gpu_lib, mode):
     full_check(gpu_lib, inp, mode=mode, tile=(32, 16), tpw=5)
 
 
+@pytest.mark.parametrize("H", [320, 448])
+def test_bf16_dwo_column_tiles(gpu_lib, H):
+    """dW^O / db^O output tilings: H = 320 leaves a 64-column remainder (512 x 128 tiles over
+    V = 700, the last one partial in V), H = 448 a 192-column one (a partial 256 x 256 tile)."""
+    inp = make_inputs(3, 70, 24, 700, 64, 96, H, dtype="bf16", seed=81 + H, t_range=(20, 70),
+                      u_range=(0, 24), bias_std=0.1)
+    say(f"bf16 dW^O tiles B=3 T=70 U=24 V=700 H={H}")
+    full_check(gpu_lib, inp, mode="tiled", tile=(32, 16), tpw=4)
+
+
 @pytest.mark.timeout(400)
 @pytest.mark.parametrize("mode", ["tiled", "untiled"])
 def test_small_full(gpu_lib, mode):
