@@ -316,6 +316,39 @@ def test_40s_b256_closed_form_and_sample(gpu_lib):
 
 # ----------------------------------------------------------------------------- structure
 
+@pytest.mark.timeout(400)
+def test_device_memory_is_the_callers_buffers_and_tile_bounded(gpu_lib):
+    """Tiled mode on a 40 s-like family (B=32, tile 64x32, 64 tiles per wave, T x U from 250 x 50 to
+    1000 x 200): a fwd+bwd takes no device memory beyond the caller's buffers (free device memory is
+    unchanged across the calls), and the workspace minus the O(B (T+U+1) H) gradient accumulators is the
+    same for every lattice size, so the V- and H-proportional working set is set by the tile."""
+    import torch
+
+    rl = gpu_lib
+    B, V, HA, HL, H = 32, 1024, 512, 512, 640
+    rest = set()
+    for T, U in ((250, 50), (500, 100), (1000, 200)):
+        inp = make_inputs(B, T, U, V, HA, HL, H, dtype="bf16", seed=90 + T, t_range=(T // 2, T),
+                          u_range=(U // 2, U))
+        say(f"device memory B={B} T={T} U={U}")
+        prob = rl.Problem(inp, mode="tiled", tile=(64, 32), tiles_per_wave=64)
+        prob.forward()
+        prob.backward()  # first calls: code objects and runtime state are set up here
+        torch.cuda.synchronize()
+        free0 = torch.cuda.mem_get_info()[0]
+        costs = prob.forward().clone()
+        prob.backward()
+        torch.cuda.synchronize()
+        free1 = torch.cuda.mem_get_info()[0]
+        # the clone above is the only new allocation (served by torch's cache or one new block)
+        assert free0 - free1 <= 2 * 1024 * 1024, (free0, free1)
+        assert bool(torch.isfinite(costs).all())
+        rest.add(prob.ws_bytes - 4 * H * B * (T + U + 1))
+        del prob
+        torch.cuda.empty_cache()
+    assert max(rest) - min(rest) <= 4096, rest
+
+
 def test_padding_poison_is_ignored(gpu_lib):
     inp = make_inputs(3, 60, 20, 257, 64, 64, 64, dtype="bf16", seed=61, t_range=(10, 60), u_range=(0, 20))
     say("padding poison bf16")
