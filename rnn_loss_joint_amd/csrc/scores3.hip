@@ -313,7 +313,6 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
   using F = std::integral_constant<bool, false>;
-  using Tr = std::integral_constant<bool, true>;
   using NoT = std::integral_constant<int, -1>;
 
   // prologue: stages 0 and 1 in flight, stage 0 landed, its first fragments,
