@@ -224,6 +224,19 @@ def test_bf16_reduced(gpu_lib, mode):
     full_check(gpu_lib, inp, mode=mode, tile=(32, 16), tpw=5)
 
 
+def test_bf16_weighted_dcosts(gpu_lib):
+    """Per-sample upstream gradients of mixed sign and size (a weighted, partly negated sum): every
+    gradient term carries the sample's g_b, including the blank / label terms of dh."""
+    inp = make_inputs(5, 60, 18, 400, 64, 48, 96, dtype="bf16", seed=57, t_range=(10, 60), u_range=(0, 18),
+                      bias_std=0.1)
+    dc = np.array([0.5, -1.25, 2.0, 0.0, 1.0 / 3.0])
+    say("bf16 weighted dcosts B=5 T=60 U=18 V=400")
+    ref = oracle.loss_and_grads(inp, dcosts=dc)
+    costs, grads = run_gpu(gpu_lib, inp, tile=(32, 8), tpw=3, dcosts=dc)
+    check_costs(inp, costs, ref.costs)
+    check_grads(inp, grads, ref.grads)
+
+
 @pytest.mark.parametrize("H", [320, 448])
 def test_bf16_dwo_column_tiles(gpu_lib, H):
     """dW^O / db^O output tilings: H = 320 leaves a 64-column remainder (512 x 128 tiles over
