@@ -28,7 +28,7 @@ namespace rnnt {
 // SCORES, the blank and label scores of each row as dot products of that
 // bf16 z with the two W^O rows (plus the biases).
 constexpr int kZHmax = 768;  // H_pad bound (the library's H <= 768)
-template <bool SCORES>
+template <bool SCORES, int NCH>
 __global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[8 * kZHmax * 4 + (SCORES ? 9 * kZHmax * 2 : 0)];
   float* const ls = reinterpret_cast<float*>(smem);                 // [8][H_pad] l rows
@@ -85,17 +85,27 @@ __global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
     }
   }
   __syncthreads();
-  // a of the next chunk is loaded while the current one is computed
+  // The thread's NCH 8-column chunks k = q*8 + 64 c (z_ld = 64 NCH) of a are
+  // loaded half at a time, before any of that half's stores: with no load
+  // among the stores and a fixed count of both, the compiler's waits cover
+  // only the loads, and the stores are not drained chunk by chunk.
+  constexpr int ZPH = NCH / 2;
   auto a_at = [&](int k) { return row_ok && k < p.H ? k : 0; };
-  f32x4 na0 = ldg<f32x4>(arow + a_at(q * 8)), na1 = ldg<f32x4>(arow + a_at(q * 8) + 4);
-  for (int k = q * 8; k < p.z_ld; k += 64) {
+#pragma unroll
+  for (int c0 = 0; c0 < NCH; c0 += ZPH) {
+    f32x4 av[ZPH][2];
+#pragma unroll
+    for (int c = 0; c < ZPH; ++c) {
+      const int k = a_at(q * 8 + 64 * (c0 + c));
+      av[c][0] = ldg<f32x4>(arow + k);
+      av[c][1] = ldg<f32x4>(arow + k + 4);
+    }
+#pragma unroll
+    for (int c = 0; c < ZPH; ++c) {
+    const int k = q * 8 + 64 * (c0 + c);
     const bool kok = row_ok && k < p.H;
     const int kk = kok ? k : 0;
-    const f32x4 a0 = na0, a1 = na1;
-    if (k + 64 < p.z_ld) {
-      na0 = ldg<f32x4>(arow + a_at(k + 64));
-      na1 = ldg<f32x4>(arow + a_at(k + 64) + 4);
-    }
+    const f32x4 a0 = av[c][0], a1 = av[c][1];
     bf16x8 xb;
     if constexpr (SCORES) xb = *reinterpret_cast<const bf16x8*>(ws + kk);
 #pragma unroll
@@ -121,6 +131,7 @@ __global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
       }
       *reinterpret_cast<bf16x8*>(zb + (row0 + (int64_t)uu * tl.htp) * p.z_ld + k) = z;
     }
+    }
   }
   if constexpr (SCORES) {
     const float bb = (float)bO[p.blank];
@@ -145,8 +156,16 @@ hipError_t launch_zrow(const ZArgs& a, hipStream_t st) {
   if (a.n_strips == 0) return hipSuccess;
   if (a.H_pad > kZHmax || a.H_pad % 8 != 0 || a.z_ld > a.H_pad) return hipErrorInvalidValue;  // LDS staging bound
   dim3 grid(a.n_strips * a.n_ug), block(256);
-  if (a.hb) hipLaunchKernelGGL(zrow_kernel<true>, grid, block, 0, st, a);
-  else hipLaunchKernelGGL(zrow_kernel<false>, grid, block, 0, st, a);
+  switch (a.z_ld) {
+#define RNNT_ZROW(N)                                                                   \
+  case 64 * N:                                                                         \
+    if (a.hb) hipLaunchKernelGGL((zrow_kernel<true, N>), grid, block, 0, st, a);       \
+    else hipLaunchKernelGGL((zrow_kernel<false, N>), grid, block, 0, st, a);           \
+    break;
+    RNNT_ZROW(2) RNNT_ZROW(4) RNNT_ZROW(6) RNNT_ZROW(8) RNNT_ZROW(10) RNNT_ZROW(12)
+#undef RNNT_ZROW
+    default: return hipErrorInvalidValue;  // z rows are 128-column multiples up to kZHmax
+  }
   return hipGetLastError();
 }
 
