@@ -69,7 +69,9 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int nvt = p.nvt, nq = p.H_pad / BK;
   // items (ct, vt): cell tiles ct = 8 ctl + xcd of this XCD, all V tiles of a
-  // cell tile on neighbouring slots (their z rows shared in L2)
+  // cell tile on neighbouring slots (their z rows shared in L2); cell tiles
+  // are taken from the end of the wave's rows backwards, so the z rows the
+  // z-row kernel wrote last (still in the last-level cache) are read first
   const int nctl = (p.n_ct - xcd + 7) / 8;
   const int n_items = max(0, (nctl * nvt - slot + 31) / 32);
   if (n_items == 0) return;
@@ -100,9 +102,9 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
   auto item_of = [&](int n, int& ct, int& vt) {
     n = min(n, n_items - 1);
     const int idx = slot + 32 * n;
-    const int ctl = idx / nvt;
-    vt = idx - ctl * nvt;
-    ct = ctl * 8 + xcd;
+    const int c0 = idx / nvt;
+    vt = idx - c0 * nvt;
+    ct = (nctl - 1 - c0) * 8 + xcd;
   };
   struct Src {
     const char *a, *b, *bias, *coef;
