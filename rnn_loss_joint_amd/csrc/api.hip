@@ -304,8 +304,39 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
   if (s != RNNT_OK) return s;
   Saved sv = saved_view(saved, L);
 
-  // 1. joint pre-activations
-  {
+  // 1. joint pre-activations (bf16: large-tile row GEMM, scaled for the z-row
+  // kernel's base-2 exponential, the only reader of a and l in this mode)
+  if (bf) {
+    rnnt::RowGemmArgs r{};
+    r.A = hA;
+    r.lda = d.HA;
+    r.B = WA;
+    r.ldb = d.HA;
+    r.bias = bZ;
+    r.scale = rnnt::kTanhArgScale;
+    r.C = sv.a;
+    r.ldc = p.H_pad;
+    r.M = d.B * d.T;
+    r.N = d.H;
+    r.K = d.HA;
+    r.c_cols = p.H_pad;
+    {
+      ProfScope ps_("preproj_gemm", st);
+      RNNT_HIP(rnnt::launch_rowgemm(r, st));
+    }
+    r.A = hL;
+    r.lda = d.HL;
+    r.B = WL;
+    r.ldb = d.HL;
+    r.bias = nullptr;
+    r.C = sv.l;
+    r.M = d.B * p.U1;
+    r.K = d.HL;
+    {
+      ProfScope ps_("preproj_gemm", st);
+      RNNT_HIP(rnnt::launch_rowgemm(r, st));
+    }
+  } else {
     rnnt::GemmArgs g{};
     g.A = rnnt::Operand{hA, d.HA, d.B * d.T, nullptr, 1, 0};
     g.B = rnnt::Operand{WA, d.HA, d.H, nullptr, 1, 0};

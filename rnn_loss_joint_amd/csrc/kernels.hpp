@@ -187,6 +187,22 @@ struct ZArgs {  // z rows and (hb != null) the blank / label scores of a wave's 
   float* hy;
 };
 hipError_t launch_zrow(const ZArgs& a, hipStream_t st);
+
+// C[m, n] = (sum_k A[m, k] B[n, k] + bias[n]) * scale for n < N, 0 for
+// N <= n < c_cols; A [M, lda] and B [N, ldb] bf16 with k contiguous, bias
+// bf16 or null; fp32 C [M, ldc]. The bf16 joint pre-projections.
+struct RowGemmArgs {
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  const void* bias;
+  float scale;
+  float* C;
+  int64_t ldc;
+  int M, N, K, c_cols;
+};
+hipError_t launch_rowgemm(const RowGemmArgs& a, hipStream_t st);
 hipError_t launch_dz_dwo(const DzArgs& a, const DwoArgs& w, hipStream_t st);
 
 struct ScoresArgs {  // scores^T tiles: forward statistics or backward dh

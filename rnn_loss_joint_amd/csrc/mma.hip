@@ -169,6 +169,60 @@ hipError_t launch_zrow(const ZArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ============================================================================ row GEMM
+// The joint pre-projections a = (W^A h^A + b^Z) s and l = (W^L h^L) s ("Neural
+// transducer training ...", section "Transducer training", Eqs. (3)-(4), the
+// separable joint), s = kTanhArgScale: 256 rows x 128 columns per workgroup
+// on the large-tile core (both operands k-contiguous, streamed by dma).
+__global__ void __launch_bounds__(256) rowgemm_kernel(RowGemmArgs p) {
+  using namespace m3;
+  __shared__ __attribute__((aligned(1024))) char lds[3 * (KcTile<256>::BYTES + KcTile<128>::BYTES)];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), wr = wave >> 1, wc = wave & 1;
+  const int n0 = blockIdx.x * 128, m0 = blockIdx.y * 256;
+  const bf16* A = reinterpret_cast<const bf16*>(p.A);
+  const bf16* B = reinterpret_cast<const bf16*>(p.B);
+  KcTile<256> la;
+  la.init(wave, lane, p.K, [&](int row) -> const bf16* {
+    const int m = m0 + row;
+    return m < p.M ? A + (int64_t)m * p.lda : nullptr;
+  });
+  KcTile<128> lb;
+  lb.init(wave, lane, p.K, [&](int row) -> const bf16* {
+    const int n = n0 + row;
+    return n < p.N ? B + (int64_t)n * p.ldb : nullptr;
+  });
+  Acc<128> acc;
+  acc.zero();
+  core<128, false, 3>(acc, la, lb, (p.K + BK - 1) / BK * BK, lds, tid);
+
+  const bf16* bias = reinterpret_cast<const bf16*>(p.bias);
+#pragma unroll
+  for (int j = 0; j < Acc<128>::WN; ++j) {
+    const int n = n0 + wc * 64 + j * 32 + (lane & 31);
+    if (n >= p.c_cols) continue;
+    const bool nok = n < p.N;
+    const float bn = (nok && bias) ? (float)bias[n] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < Acc<128>::WM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + acc_row(wr, i, e, lane);
+        if (m < p.M) p.C[(int64_t)m * p.ldc + n] = nok ? (acc.c[i][j][e] + bn) * p.scale : 0.0f;
+      }
+  }
+}
+
+hipError_t launch_rowgemm(const RowGemmArgs& a, hipStream_t st) {
+  if (a.M <= 0 || a.c_cols <= 0) return hipSuccess;
+  if (a.K % 8 || a.lda % 8 || a.ldb % 8 || reinterpret_cast<uintptr_t>(a.A) % 16 ||
+      reinterpret_cast<uintptr_t>(a.B) % 16 || (a.M + 255) / 256 > 65535)
+    return hipErrorInvalidValue;  // 16-byte operand pieces; grid y bound
+  dim3 grid((a.c_cols + 127) / 128, (a.M + 255) / 256), block(256);
+  hipLaunchKernelGGL(rowgemm_kernel, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
 // ============================================================================ scores^T tiles
 // C[v, c] = sum_k W^O[v, k] z[c, k] for a 256-score x 256-cell tile, so each
 // lane holds whole cells (columns) and the reductions over the vocabulary are
