@@ -852,7 +852,45 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
     gL_op = gb + 2 * (size_t)d.B * d.T * d.H;
   }
   const int kst = bf ? 64 : 32;  // split-K granule of the GEMM engine
-  {
+  if (bf) {
+    // dh^A = gA W^A, dh^L = gL W^L on the large-tile row GEMM, with the
+    // weights transposed so that both operands run along H
+    char* WAT = at<char>(workspace, L.w_WAT);
+    char* WLT = at<char>(workspace, L.w_WLT);
+    {
+      ProfScope ps_("transpose_wo", st);
+      RNNT_HIP(rnnt::launch_transpose_wo(WAT, WA, d.H, d.HA, d.H, true, st));
+      RNNT_HIP(rnnt::launch_transpose_wo(WLT, WL, d.H, d.HL, d.H, true, st));
+    }
+    rnnt::RowGemmArgs r{};
+    r.A = gA_op;
+    r.lda = d.H;
+    r.B = WAT;
+    r.ldb = d.H;
+    r.bias = nullptr;
+    r.scale = 1.0f;
+    r.C = dhA;
+    r.ldc = d.HA;
+    r.M = d.B * d.T;
+    r.N = d.HA;
+    r.K = d.H;
+    r.c_cols = d.HA;
+    {
+      ProfScope ps_("dh_enc_gemm", st);
+      RNNT_HIP(rnnt::launch_rowgemm(r, st));
+    }
+    r.A = gL_op;
+    r.B = WLT;
+    r.C = dhL;
+    r.ldc = d.HL;
+    r.M = d.B * p.U1;
+    r.N = d.HL;
+    r.c_cols = d.HL;
+    {
+      ProfScope ps_("dh_enc_gemm", st);
+      RNNT_HIP(rnnt::launch_rowgemm(r, st));
+    }
+  } else {
     rnnt::GemmArgs g{};
     g.A = rnnt::Operand{gA_op, d.H, d.B * d.T, nullptr, 1, 0};
     g.B = rnnt::Operand{WA, d.HA, d.HA, nullptr, 1, 0};

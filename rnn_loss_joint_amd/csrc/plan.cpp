@@ -278,6 +278,8 @@ Layout make_layout(const Plan& p) {
     const size_t wave_bytes = d.untiled ? 0 : ct * wrows * (size_t)(p.V_pad + p.H_pad);
     L.w_gb = gb <= wave_bytes ? L.w_dh : take(gb);
   }
+  L.w_WAT = d.bf16 ? take(2 * (size_t)d.HA * d.H) : 0;
+  L.w_WLT = d.bf16 ? take(2 * (size_t)d.HL * d.H) : 0;
   L.workspace_bytes = o;
   return L;
 }

@@ -60,6 +60,7 @@ struct Layout {
   size_t w_zf, w_stats, w_hb, w_hy;  // bf16 forward: z rows, V-tile statistics, blank/label scores
   size_t w_WOp, w_bl, w_coefA, w_coefB;  // bf16 tiled: persistent score kernels
   size_t w_gb;  // bf16: rounded gA, gL for the encoder-side products (may alias w_dh)
+  size_t w_WAT, w_WLT;  // bf16: W^A^T [HA, H], W^L^T [HL, H] for dh^A, dh^L
   size_t workspace_bytes;
 };
 
