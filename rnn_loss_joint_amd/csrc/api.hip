@@ -917,6 +917,60 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       RNNT_HIP(rnnt::launch_gemm(g, rnnt::GEMM_KC_MN, bf, bf, bf, 1, st));
     }
   }
+  if (bf) {
+    // dW^A = gA^T h^A (db^Z from the ones column) and dW^L = gL^T h^L on the
+    // dW^O role of the dz_dwo kernel (256 x 256 tiles, split-K over the rows,
+    // whole splits per XCD), on copies of h^A, h^L with the padding rows zeroed
+    float* PWA = at<float>(workspace, L.w_PWA);
+    float* PBZ = at<float>(workspace, L.w_PBZ);
+    float* PWL = at<float>(workspace, L.w_PWL);
+    char* hsA = at<char>(workspace, L.w_hs);
+    char* hsL = hsA + 2 * (size_t)d.B * d.T * d.HA;
+    {
+      ProfScope ps_("mask_rows", st);
+      RNNT_HIP(rnnt::launch_mask_rows(hsA, hA, (int64_t)d.B * d.T, d.HA, d.T, sv.Tlen, 0, st));
+      RNNT_HIP(rnnt::launch_mask_rows(hsL, hL, (int64_t)d.B * p.U1, d.HL, p.U1, sv.Ulen, 1, st));
+    }
+    // out_b null: the ones column's sums (PB) are scratch
+    auto dw = [&](const void* gop, const void* hs, int Hin, int64_t rows, int s_max, float* PW, float* PB,
+                  float* out_W, float* out_b) -> rnnt_status {
+      const int tiles = ((d.H + 255) / 256) * ((Hin + 1 + 255) / 256);
+      const int splits = std::max(1, std::min(s_max, 8 * std::max(1, 32 / tiles)));
+      rnnt::DwoArgs w{};
+      w.dh = gop;
+      w.dh_ld = d.H;
+      w.z = hs;
+      w.z_ld = Hin;
+      w.V = d.H;
+      w.H = Hin;
+      w.K = (int)rows;
+      w.splits = splits;
+      w.k_per_split = (int)(((rows + splits - 1) / splits + 63) / 64 * 64);
+      w.PW = PW;
+      w.PB = PB;
+      rnnt::DzArgs none{};
+      {
+        ProfScope ps_("dW_enc_gemm", st);
+        RNNT_HIP(rnnt::launch_dz_dwo(none, w, st));
+      }
+      {
+        ProfScope ps_("split_reduce", st);
+        RNNT_HIP(rnnt::launch_split_reduce(out_W, PW, (int64_t)d.H * Hin, splits, (int64_t)d.H * Hin, false, st));
+      }
+      if (out_b) {
+        ProfScope ps_("split_reduce", st);
+        RNNT_HIP(rnnt::launch_split_reduce(out_b, PB, d.H, splits, d.H, false, st));
+      }
+      return RNNT_OK;
+    };
+    // PWA / PBZ hold s7a splits, PWL s7l
+    rnnt_status s2 = dw(gA_op, hsA, d.HA, (int64_t)d.B * d.T, p.s7a, PWA, PBZ, dWA, dbZ);
+    if (s2 != RNNT_OK) return s2;
+    // dW^L has no bias: its ones column goes to PBZ, free once db^Z is reduced
+    s2 = dw(gL_op, hsL, d.HL, (int64_t)d.B * p.U1, std::min(p.s7l, p.s7a), PWL, PBZ, dWL, nullptr);
+    if (s2 != RNNT_OK) return s2;
+    return RNNT_OK;
+  }
   {
     float* PWA = at<float>(workspace, L.w_PWA);
     float* PBZ = at<float>(workspace, L.w_PBZ);

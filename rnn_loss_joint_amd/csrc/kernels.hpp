@@ -203,6 +203,10 @@ struct RowGemmArgs {
   int M, N, K, c_cols;
 };
 hipError_t launch_rowgemm(const RowGemmArgs& a, hipStream_t st);
+// dst[r] = src[r] for rows r = b*Tdim + t with t < len[b] + add, else 0 (bf16
+// rows of `cols` elements; cols % 8 == 0)
+hipError_t launch_mask_rows(void* dst, const void* src, int64_t rows, int cols, int Tdim, const int32_t* len, int add,
+                            hipStream_t st);
 hipError_t launch_dz_dwo(const DzArgs& a, const DwoArgs& w, hipStream_t st);
 
 struct ScoresArgs {  // scores^T tiles: forward statistics or backward dh

@@ -223,6 +223,27 @@ hipError_t launch_rowgemm(const RowGemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+__global__ void mask_rows_kernel(bf16x8* __restrict__ dst, const bf16x8* __restrict__ src, int64_t n8, int c8,
+                                 int Tdim, const int32_t* __restrict__ len, int add) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / c8;
+    const int b = (int)(r / Tdim), t = (int)(r - (int64_t)b * Tdim);
+    dst[i] = t < len[b] + add ? src[i] : bf16x8{};
+  }
+}
+
+hipError_t launch_mask_rows(void* dst, const void* src, int64_t rows, int cols, int Tdim, const int32_t* len, int add,
+                            hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (cols % 8 || reinterpret_cast<uintptr_t>(dst) % 16 || reinterpret_cast<uintptr_t>(src) % 16)
+    return hipErrorInvalidValue;
+  const int64_t n8 = rows * (cols / 8);
+  const int blocks = (int)std::min<int64_t>((n8 + 255) / 256, 8192);
+  hipLaunchKernelGGL(mask_rows_kernel, dim3(blocks), dim3(256), 0, st, reinterpret_cast<bf16x8*>(dst),
+                     reinterpret_cast<const bf16x8*>(src), n8, cols / 8, Tdim, len, add);
+  return hipGetLastError();
+}
+
 // ============================================================================ scores^T tiles
 // C[v, c] = sum_k W^O[v, k] z[c, k] for a 256-score x 256-cell tile, so each
 // lane holds whole cells (columns) and the reductions over the vocabulary are

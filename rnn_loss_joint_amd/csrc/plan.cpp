@@ -278,6 +278,15 @@ Layout make_layout(const Plan& p) {
     const size_t wave_bytes = d.untiled ? 0 : ct * wrows * (size_t)(p.V_pad + p.H_pad);
     L.w_gb = gb <= wave_bytes ? L.w_dh : take(gb);
   }
+  // bf16: the encodings with their padding rows zeroed (operands of dW^A and
+  // dW^L), after the rounded gA, gL in the dead wave buffers when both fit
+  L.w_hs = 0;
+  if (d.bf16) {
+    const size_t gb = 2 * ((size_t)d.B * d.T + (size_t)d.B * p.U1) * d.H;
+    const size_t hs = 2 * ((size_t)d.B * d.T * d.HA + (size_t)d.B * p.U1 * d.HL);
+    const size_t wave_bytes = d.untiled ? 0 : ct * wrows * (size_t)(p.V_pad + p.H_pad);
+    L.w_hs = L.w_gb == L.w_dh && gb + hs <= wave_bytes ? L.w_dh + (gb + 255) / 256 * 256 : take(hs);
+  }
   L.w_WAT = d.bf16 ? take(2 * (size_t)d.HA * d.H) : 0;
   L.w_WLT = d.bf16 ? take(2 * (size_t)d.HL * d.H) : 0;
   L.workspace_bytes = o;

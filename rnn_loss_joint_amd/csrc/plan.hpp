@@ -61,6 +61,7 @@ struct Layout {
   size_t w_WOp, w_bl, w_coefA, w_coefB;  // bf16 tiled: persistent score kernels
   size_t w_gb;  // bf16: rounded gA, gL for the encoder-side products (may alias w_dh)
   size_t w_WAT, w_WLT;  // bf16: W^A^T [HA, H], W^L^T [HL, H] for dh^A, dh^L
+  size_t w_hs;          // bf16: h^A, h^L with padding rows zeroed, for dW^A, dW^L (may alias w_dh)
   size_t workspace_bytes;
 };
 
