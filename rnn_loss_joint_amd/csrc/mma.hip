@@ -216,10 +216,18 @@ __global__ void __launch_bounds__(256) rowgemm_kernel(RowGemmArgs p) {
 hipError_t launch_rowgemm(const RowGemmArgs& a, hipStream_t st) {
   if (a.M <= 0 || a.c_cols <= 0) return hipSuccess;
   if (a.K % 8 || a.lda % 8 || a.ldb % 8 || reinterpret_cast<uintptr_t>(a.A) % 16 ||
-      reinterpret_cast<uintptr_t>(a.B) % 16 || (a.M + 255) / 256 > 65535)
-    return hipErrorInvalidValue;  // 16-byte operand pieces; grid y bound
-  dim3 grid((a.c_cols + 127) / 128, (a.M + 255) / 256), block(256);
-  hipLaunchKernelGGL(rowgemm_kernel, grid, block, 0, st, a);
+      reinterpret_cast<uintptr_t>(a.B) % 16)
+    return hipErrorInvalidValue;  // 16-byte operand pieces
+  // at most 65535 row tiles per launch (grid y)
+  constexpr int kMaxRows = 65535 * 256;
+  for (int m0 = 0; m0 < a.M; m0 += kMaxRows) {
+    RowGemmArgs c = a;
+    c.A = reinterpret_cast<const bf16*>(a.A) + (int64_t)m0 * a.lda;
+    c.C = a.C + (int64_t)m0 * a.ldc;
+    c.M = std::min(kMaxRows, a.M - m0);
+    dim3 grid((a.c_cols + 127) / 128, (c.M + 255) / 256), block(256);
+    hipLaunchKernelGGL(rowgemm_kernel, grid, block, 0, st, c);
+  }
   return hipGetLastError();
 }
 
