@@ -166,6 +166,7 @@ struct Saved {
   const rnnt::Group* groups;
   const int32_t* gidx;
   float *a, *l, *lse, *phi, *psi, *alpha, *beta, *lnP;
+  double *alpha64, *beta64, *lnP64;  // fp32 mode (the same memory as alpha, beta, lnP), else null
   void* logits;
   void* z;
 };
@@ -185,6 +186,9 @@ Saved saved_view(void* s, const rnnt::Layout& L) {
   v.alpha = at<float>(s, L.off_alpha);
   v.beta = at<float>(s, L.off_beta);
   v.lnP = at<float>(s, L.off_lnP);
+  v.alpha64 = L.lat64 ? at<double>(s, L.off_alpha) : nullptr;
+  v.beta64 = L.lat64 ? at<double>(s, L.off_beta) : nullptr;
+  v.lnP64 = L.lat64 ? at<double>(s, L.off_lnP) : nullptr;
   v.logits = L.off_logits ? at<char>(s, L.off_logits) : nullptr;
   v.z = L.off_z ? at<char>(s, L.off_z) : nullptr;
   return v;
@@ -214,6 +218,9 @@ rnnt::JointArgs joint_args(const rnnt::Plan& p, const Saved& sv, const int32_t* 
   a.alpha = sv.alpha;
   a.beta = sv.beta;
   a.lnP = sv.lnP;
+  a.alpha64 = sv.alpha64;
+  a.beta64 = sv.beta64;
+  a.lnP64 = sv.lnP64;
   return a;
 }
 
@@ -497,8 +504,16 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
   // 3. lattice
   {
     rnnt::LatticeArgs la{sv.Tlen, sv.Ulen, sv.phi, sv.psi, sv.alpha, sv.beta, sv.lnP, costs, d.B, d.T, p.U1};
-    {
-      ProfScope ps_("lattice", st);
+    ProfScope ps_("lattice", st);
+    if (L.lat64) {
+      // fp32 mode: the fp64 arrays share the fp32 ones' memory, so the fp32
+      // ln P is not written
+      la.alpha = la.beta = la.lnP = nullptr;
+      la.alpha64 = sv.alpha64;
+      la.beta64 = sv.beta64;
+      la.lnP64 = sv.lnP64;
+      RNNT_HIP(rnnt::launch_lattice64(la, st));
+    } else {
       RNNT_HIP(rnnt::launch_lattice(la, p.U1, st));
     }
   }
@@ -591,6 +606,9 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       a.alpha = sv.alpha;
       a.beta = sv.beta;
       a.lnP = sv.lnP;
+      a.alpha64 = sv.alpha64;
+      a.beta64 = sv.beta64;
+      a.lnP64 = sv.lnP64;
       a.dcosts = dcosts;
       {
         ProfScope ps_("dh_inplace", st);

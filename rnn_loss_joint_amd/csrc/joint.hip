@@ -67,6 +67,24 @@ __device__ inline void store_wo_stage(const StageRegs<M>& r, char* buf, int tid)
 }
 
 // Locate the tile holding global row R0 among tiles [lo, hi].
+// Backward weights of cell (t, u) of sample b, each times the cost's
+// incoming gradient g: the occupancy exp(alpha + beta - ln P) and the blank
+// and label flows exp(alpha + phi + beta(t+1, u) - ln P), exp(alpha + psi +
+// beta(t, u+1) - ln P) (zero past the last label). R is the storage type of
+// alpha, beta and ln P; the exponents are formed in R and rounded once.
+template <typename R>
+__device__ inline void cell_weights(const R* al, const R* be, R lp, const float* phi, const float* psi, int b,
+                                    int t, int u, int T, int U1, int Tb, int Ub, float g, float& occ, float& cb,
+                                    float& cl) {
+  const int64_t idx = lat_ix(b, t, u, T, U1);
+  const R A = al[idx];
+  const R bn = (t + 1 < Tb) ? be[lat_ix(b, t + 1, u, T, U1)] : (u == Ub ? R(0) : R(kNegInf));
+  occ = g * fexp2((float)(A + be[idx] - lp) * kLog2e);
+  cb = g * fexp2((float)(A + (R)phi[idx] + bn - lp) * kLog2e);
+  cl = 0.0f;
+  if (u < Ub) cl = g * fexp2((float)(A + (R)psi[idx] + be[lat_ix(b, t, u + 1, T, U1)] - lp) * kLog2e);
+}
+
 __device__ inline int find_tile_by_row(const Tile* tiles, int lo, int hi, int R0) {
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
@@ -193,20 +211,14 @@ joint_kernel(JointArgs p) {
     if (g == 0) {
       if (row_ok) {
         size_t idx = (size_t)lat_ix(b, t_r, u, T, U1);
-        float lp = p.lnP[b];
         float gb = p.dcosts ? p.dcosts[b] : 1.0f;
-        float A = p.alpha[idx];
-        float Bt = p.beta[idx];
-        float ph = p.phi[idx];
         my_lse = p.lse[idx];
-        float bn = (t_r + 1 < Tb) ? p.beta[lat_ix(b, t_r + 1, u, T, U1)] : (u == Ub ? 0.0f : kNegInf);
-        my_occ = gb * fexp2((A + Bt - lp) * kLog2e);
-        my_cb = gb * fexp2((A + ph + bn - lp) * kLog2e);
-        if (u < Ub) {
-          float ps = p.psi[idx];
-          float ln = p.beta[lat_ix(b, t_r, u + 1, T, U1)];
-          my_cl = gb * fexp2((A + ps + ln - lp) * kLog2e);
-        }
+        if (p.alpha64)
+          cell_weights<double>(p.alpha64, p.beta64, p.lnP64[b], p.phi, p.psi, b, t_r, u, T, U1, Tb, Ub, gb, my_occ,
+                               my_cb, my_cl);
+        else
+          cell_weights<float>(p.alpha, p.beta, p.lnP[b], p.phi, p.psi, b, t_r, u, T, U1, Tb, Ub, gb, my_occ, my_cb,
+                              my_cl);
       }
       row_lds[wave][0][r] = my_lse;
       row_lds[wave][1][r] = my_occ;
@@ -398,17 +410,13 @@ __global__ void __launch_bounds__(256) dh_inplace_kernel(DhInplaceArgs p) {
     float lab = -1;
     if (valid) {
       size_t idx = (size_t)lat_ix(b, t, u, T, U1);
-      float lp = p.lnP[b];
       float gb = p.dcosts ? p.dcosts[b] : 1.0f;
-      float A = p.alpha[idx], Bt = p.beta[idx], ph = p.phi[idx];
       ls = p.lse[idx];
-      float bn = (t + 1 < Tb) ? p.beta[lat_ix(b, t + 1, u, T, U1)] : (u == Ub ? 0.0f : kNegInf);
-      co = gb * fexp2((A + Bt - lp) * kLog2e);
-      cb = gb * fexp2((A + ph + bn - lp) * kLog2e);
-      if (u < Ub) {
-        cl = gb * fexp2((A + p.psi[idx] + p.beta[lat_ix(b, t, u + 1, T, U1)] - lp) * kLog2e);
-        lab = (float)p.labels[(size_t)b * U1 + u + 1];
-      }
+      if (p.alpha64)
+        cell_weights<double>(p.alpha64, p.beta64, p.lnP64[b], p.phi, p.psi, b, t, u, T, U1, Tb, Ub, gb, co, cb, cl);
+      else
+        cell_weights<float>(p.alpha, p.beta, p.lnP[b], p.phi, p.psi, b, t, u, T, U1, Tb, Ub, gb, co, cb, cl);
+      if (u < Ub) lab = (float)p.labels[(size_t)b * U1 + u + 1];
     }
     coef[wave][0] = ls * kLog2e;
     coef[wave][1] = co;

@@ -39,6 +39,10 @@ struct JointArgs {
   const float* beta;
   const float* lnP;
   const float* dcosts;
+  // fp32 mode: alpha, beta, ln P in fp64 (null: the fp32 arrays above)
+  const double* alpha64;
+  const double* beta64;
+  const double* lnP64;
 };
 
 struct DhInplaceArgs {
@@ -58,6 +62,9 @@ struct DhInplaceArgs {
   const float* beta;
   const float* lnP;
   const float* dcosts;
+  const double* alpha64;  // as in JointArgs
+  const double* beta64;
+  const double* lnP64;
 };
 
 int joint_ks_for(int H);
@@ -75,8 +82,14 @@ struct LatticeArgs {
   float* lnP;   // [B] (may be null)
   float* costs; // [B] (may be null)
   int B, T, U1;
+  double* alpha64;  // fp64 sweep only: alpha, beta (lattice layout) and ln P [B]
+  double* beta64;
+  double* lnP64;
 };
 hipError_t launch_lattice(const LatticeArgs& a, int U1max, hipStream_t st);
+// The same recursions in fp64 from fp32 phi, psi: writes alpha64, beta64,
+// lnP64 and (when non-null) lnP and costs rounded to fp32.
+hipError_t launch_lattice64(const LatticeArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- GEMMs
 // C[m, n] = sum_k A[m, k] * B[n, k] over a K range, 128 x 128 workgroup tiles.

@@ -314,4 +314,76 @@ hipError_t launch_lattice(const LatticeArgs& a, int U1max, hipStream_t st) {
   return hipGetLastError();
 }
 
+// fp32 mode: the same recursions carried in fp64 (phi and psi widened from
+// fp32). One workgroup per (sample, direction) walks the anti-diagonals, one
+// barrier per diagonal; the previous diagonal is read back from the output
+// array, which the workgroup's own stores made visible at the barrier. This
+// sweep costs a few milliseconds at most at these sizes; its purpose is the
+// precision of alpha + beta - ln P, which the backward pass exponentiates.
+__device__ inline double lae64(double x, double y) {
+  const double m = fmax(x, y);
+  if (m == -INFINITY) return m;
+  return m + log1p(exp(-fabs(x - y)));
+}
+
+__global__ void __launch_bounds__(256) lattice64_kernel(LatticeArgs p) {
+  const int b = blockIdx.x;
+  const bool is_beta = blockIdx.y != 0;
+  const int Tb = p.T_len[b], Ub = p.U_len[b];
+  const int T = p.T, U1 = p.U1;
+  double* out = is_beta ? p.beta64 : p.alpha64;
+  const int D = Tb - 1 + Ub;  // last anti-diagonal
+  for (int k = 0; k <= D; ++k) {
+    const int dg = is_beta ? D - k : k;
+    for (int u = threadIdx.x; u <= Ub; u += blockDim.x) {
+      const int t = dg - u;
+      if (t < 0 || t >= Tb) continue;
+      const int64_t ix = lat_ix(b, t, u, T, U1);
+      double v;
+      if (!is_beta) {
+        if (t == 0 && u == 0) {
+          v = 0.0;
+        } else {
+          double x = -INFINITY, y = -INFINITY;
+          if (t > 0) {
+            const int64_t j = lat_ix(b, t - 1, u, T, U1);
+            x = out[j] + (double)p.phi[j];
+          }
+          if (u > 0) {
+            const int64_t j = lat_ix(b, t, u - 1, T, U1);
+            y = out[j] + (double)p.psi[j];
+          }
+          v = lae64(x, y);
+        }
+      } else {
+        const double ph = (double)p.phi[ix];
+        if (t == Tb - 1 && u == Ub) {
+          v = ph;
+        } else {
+          double x = -INFINITY, y = -INFINITY;
+          if (t + 1 < Tb) x = ph + out[lat_ix(b, t + 1, u, T, U1)];
+          if (u < Ub) y = (double)p.psi[ix] + out[lat_ix(b, t, u + 1, T, U1)];
+          v = lae64(x, y);
+        }
+      }
+      out[ix] = v;
+    }
+    __syncthreads();
+  }
+  if (!is_beta && threadIdx.x == 0) {
+    const int64_t ix = lat_ix(b, Tb - 1, Ub, T, U1);
+    const double v = out[ix] + (double)p.phi[ix];
+    p.lnP64[b] = v;
+    if (p.lnP) p.lnP[b] = (float)v;
+    if (p.costs) p.costs[b] = (float)-v;
+  }
+}
+
+hipError_t launch_lattice64(const LatticeArgs& a, hipStream_t st) {
+  if (a.B == 0) return hipSuccess;
+  if (!a.alpha64 || !a.beta64 || !a.lnP64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(lattice64_kernel, dim3(a.B, 2), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace rnnt

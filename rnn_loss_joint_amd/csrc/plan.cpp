@@ -228,9 +228,14 @@ Layout make_layout(const Plan& p) {
   L.off_lse = take(sizeof(float) * cells);
   L.off_phi = take(sizeof(float) * cells);
   L.off_psi = take(sizeof(float) * cells);
-  L.off_alpha = take(sizeof(float) * cells);
-  L.off_beta = take(sizeof(float) * cells);
-  L.off_lnP = take(sizeof(float) * d.B);
+  // fp32 mode keeps the forward-backward variables in fp64: in fp32 their
+  // magnitude (thousands of nats on long lattices) would limit the
+  // occupancies exp(alpha + beta - ln P) to about 1e-4 relative
+  L.lat64 = !d.bf16;
+  const size_t lat_el = L.lat64 ? sizeof(double) : sizeof(float);
+  L.off_alpha = take(lat_el * cells);
+  L.off_beta = take(lat_el * cells);
+  L.off_lnP = take(lat_el * d.B);
   L.off_logits = L.off_z = 0;
   if (d.untiled) {
     L.off_logits = take(ct * (size_t)p.total_rows * p.V_pad);

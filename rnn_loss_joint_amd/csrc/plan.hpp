@@ -54,6 +54,7 @@ struct Layout {
   size_t plan_bytes;  // lengths + tiles + groups + gidx (one host->device copy)
   size_t off_Tlen, off_Ulen, off_tiles, off_groups, off_gidx;
   size_t off_a, off_l, off_lse, off_phi, off_psi, off_alpha, off_beta, off_lnP;
+  bool lat64;  // alpha, beta, ln P held in fp64 (fp32 mode), else fp32
   size_t off_logits, off_z;  // untiled only; z is stored transposed [H_pad, total_rows]
   size_t saved_bytes;
   size_t w_dh, w_z, w_gA, w_gL, w_PA, w_PL, w_PW, w_PB, w_PWA, w_PBZ, w_PWL, w_WOT;

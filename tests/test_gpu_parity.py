@@ -218,12 +218,9 @@ def test_fp32_ragged_multitile(gpu_lib, mode, tile, tpw):
 @pytest.mark.parametrize("mode", ["tiled", "untiled"])
 def test_fp32_small_workload_shapes(gpu_lib, mode):
     """fp32 mode at the small workload's shapes (B=8, T=250, U=64, V=1024, H_A=H_L=512, H=640, ragged
-    lengths). Costs meet the 1e-5 target (measured 3.8e-7). The gradients do not meet the 1e-4-of-max-abs
-    target at these lattice lengths (measured 0.5e-4 .. 4.2e-4, dh^A worst): alpha and beta are stored
-    as fp32 log-probabilities (base 2) of magnitude up to ~2.7e3 here, whose spacing (2.4e-4) bounds
-    the precision of the occupancies exp(alpha + beta - ln P) that every gradient term carries. This
-    test holds the gradients to 1e-3 of max-abs, the bound that storage gives, so that a regression
-    beyond it fails."""
+    lengths), costs to 1e-5 relative and every gradient to 1e-4 of max-abs. alpha and beta reach
+    thousands of nats here: held in fp32 their spacing (~2.4e-4) alone would put the occupancies
+    exp(alpha + beta - ln P) outside 1e-4, so fp32 mode carries the lattice in fp64."""
     inp = make_inputs(8, 250, 64, 1024, 512, 512, 640, dtype="f32", seed=12, t_range=(150, 250),
                       u_range=(32, 64))
     say(f"fp32 small-workload shapes {mode}")
@@ -233,7 +230,7 @@ def test_fp32_small_workload_shapes(gpu_lib, mode):
     for k in GRADS:
         rel = float(np.max(np.abs(grads[k] - ref.grads[k])) / np.max(np.abs(ref.grads[k])))
         say(f"  {k} err / max-abs {rel:.2e}")
-        assert rel <= 1e-3, f"{k}: {rel:.3e} of max-abs"
+        assert rel <= TOL["f32"][1], f"{k}: {rel:.3e} of max-abs"
     for b in range(len(inp.T_len)):
         assert np.all(grads["dhA"][b, inp.T_len[b]:] == 0) and np.all(grads["dhL"][b, inp.U_len[b] + 1:] == 0)
 
