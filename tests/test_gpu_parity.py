@@ -235,6 +235,18 @@ def test_fp32_small_workload_shapes(gpu_lib, mode):
         assert np.all(grads["dhA"][b, inp.T_len[b]:] == 0) and np.all(grads["dhL"][b, inp.U_len[b] + 1:] == 0)
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("mode", ["tiled", "untiled"])
+def test_fp32_long_lattice(gpu_lib, mode):
+    """fp32 mode on lattices as long as the 40 s workload's (T_b up to 1000) with more label rows
+    than the fp64 sweep's workgroup has threads (U_b in 257..300), V and H kept narrow so the oracle
+    stays quick. Costs reach ~3.4e3 nats: costs to 1e-5 relative, gradients to 1e-4 of max-abs."""
+    inp = make_inputs(3, 1000, 300, 48, 32, 32, 32, dtype="f32", seed=17, t_range=(700, 1000),
+                      u_range=(257, 300))
+    say(f"fp32 long lattice B=3 T=1000 U=300 V=48 {mode}")
+    full_check(gpu_lib, inp, mode=mode)
+
+
 # ----------------------------------------------------------------------------- bf16 mode
 
 @pytest.mark.parametrize("mode", ["tiled", "untiled"])
