@@ -109,8 +109,10 @@ rnnt_status rnnt_waves_for_budget(const rnnt_desc* desc, const int32_t* T_len_ho
 
 /* Forward: per-sample costs[b] = -ln P(y_b | x_b) (fp32 [B], device).
  * Fills `saved` with the tile plan, the joint pre-activations, the per-cell
- * log-softmax denominators and two log-probs, alpha, beta and ln P (and, in
- * untiled mode, z and the scores). bf16 mode uses `workspace` (at least
+ * log-softmax denominators and two log-probs, alpha, beta and ln P (fp32 in
+ * bf16 mode, fp64 in fp32 mode, where the backward pass needs
+ * alpha + beta - ln P to better than fp32's spacing at these magnitudes) and,
+ * in untiled mode, z and the scores. bf16 mode uses `workspace` (at least
  * rnnt_loss_query's workspace_bytes) for one wave of z rows and per-tile
  * statistics; fp32 mode does not use it (it may be NULL). */
 rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
