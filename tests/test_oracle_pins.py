@@ -260,10 +260,10 @@ def torch_loss(inp, g):
     return float(total), grads
 
 
-def autograd_check(inp, g=None, tol=1e-12):
+def autograd_check(inp, g=None, tol=1e-12, **oracle_kw):
     B = len(inp.T_len)
     g = np.linspace(1.3, 0.7, B) if g is None else g
-    r = oracle.loss_and_grads(inp, dcosts=g)
+    r = oracle.loss_and_grads(inp, dcosts=g, **oracle_kw)
     L, tg = torch_loss(inp, g)
     assert abs(L - float(np.dot(g, r.costs))) <= tol * abs(L)
     for k in ("dhA", "dhL", "dWA", "dWL", "dbZ", "dWO", "dbO"):
@@ -281,6 +281,27 @@ def test_autograd_reduced_small():
     inp = make_inputs(2, 9, 5, 40, 12, 10, 16, dtype="bf16", seed=2, t_range=(5, 9), u_range=(2, 5),
                       bias_std=0.2)
     autograd_check(inp, tol=1e-11)
+
+
+def test_autograd_one_row_per_block():
+    """The oracle's blocking over t rows (which only bounds host memory) pinned to the independent
+    autograd implementation: with a byte budget of 1 every block holds a single t row, so each
+    sample's forward and backward run over T_b blocks, ragged lengths included."""
+    inp = make_inputs(3, 8, 4, 30, 12, 10, 16, dtype="bf16", seed=29, t_range=(3, 8), u_range=(0, 4),
+                      bias_std=0.2)
+    autograd_check(inp, tol=1e-11, mem_budget=1)
+
+
+def test_blocking_does_not_change_results():
+    """One t row per block against the default single block, on a ragged batch at the small
+    workload's widths: costs and every gradient agree to 1e-13 (only summation order differs)."""
+    inp = make_inputs(3, 40, 12, 300, 64, 48, 80, dtype="bf16", seed=33, t_range=(10, 40),
+                      u_range=(0, 12), bias_std=0.2)
+    a = oracle.loss_and_grads(inp)
+    b = oracle.loss_and_grads(inp, mem_budget=1)
+    assert np.max(np.abs(a.costs - b.costs) / np.abs(a.costs)) <= 1e-13
+    for k, v in a.grads.items():
+        assert np.max(np.abs(v - b.grads[k])) <= 1e-13 * max(1.0, np.max(np.abs(v))), k
 
 
 # ----------------------------------------------------------------------------- padding / batch structure
