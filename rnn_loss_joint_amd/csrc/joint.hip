@@ -462,15 +462,6 @@ static hipError_t launch_joint_h(const JointArgs& a, int KS, hipStream_t st) {
   return hipGetLastError();
 }
 
-int joint_ks_for(int H) {
-  int hp = (H + 63) / 64 * 64;
-  int ks = hp / 16;
-  static const int ok[] = {8, 16, 24, 32, 40, 48};  // even stage count per V chunk
-  for (int v : ok)
-    if (v >= ks) return v;
-  return -1;
-}
-
 hipError_t launch_joint(const JointArgs& a, bool bf16_mode, bool bwd, hipStream_t st) {
   int KS = a.H_pad / 16;
   if (bf16_mode) {

@@ -15,6 +15,27 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
+int joint_ks_for(int H) {
+  int hp = (H + 63) / 64 * 64;
+  int ks = hp / 16;
+  static const int ok[] = {8, 16, 24, 32, 40, 48};  // even stage count per V chunk
+  for (int v : ok)
+    if (v >= ks) return v;
+  return -1;
+}
+
+bool check_plan(const Plan& p, std::string& err) {
+  // row and strip numbers, wave row ranges and the 128-row rounding of the
+  // wave buffers are 32-bit in the plan records and the kernels
+  if (p.total_rows > kMaxPlanRows) {
+    err = "the tile plan has " + std::to_string(p.total_rows) + " rows, more than " + std::to_string(kMaxPlanRows) +
+          " (each tile holds tile_u columns of t rows padded to a multiple of 32: small tile_t values "
+          "multiply the rows)";
+    return false;
+  }
+  return true;
+}
+
 bool check_dims(const Dims& d, std::string& err, int& status) {
   status = -1;  // RNNT_E_INVALID
   if (d.B <= 0 || d.T <= 0 || d.U < 0 || d.V < 2 || d.HA <= 0 || d.HL <= 0 || d.H <= 0) {
@@ -216,12 +237,14 @@ Layout make_layout(const Plan& p) {
     o = align256(o + bytes);
     return at;
   };
+  L.off_status = take(2 * sizeof(int32_t));
   L.off_Tlen = take(sizeof(int32_t) * d.B);
   L.off_Ulen = take(sizeof(int32_t) * d.B);
   L.off_tiles = take(sizeof(TileH) * p.tiles.size());
   L.off_groups = take(sizeof(GroupH) * p.groups.size());
   L.off_gidx = take(sizeof(int32_t) * p.gidx.size());
   L.plan_bytes = o;
+  L.off_labels = take(sizeof(int32_t) * (size_t)d.B * p.U1);
   const size_t cells = (size_t)lat_cells(d.B, d.T, p.U1);
   L.off_a = take(sizeof(float) * (size_t)d.B * d.T * p.H_pad);
   L.off_l = take(sizeof(float) * (size_t)d.B * p.U1 * p.H_pad);

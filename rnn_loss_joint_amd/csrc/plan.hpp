@@ -51,8 +51,10 @@ struct Plan {
 
 // Byte offsets inside `saved` and `workspace` (all 256-byte aligned).
 struct Layout {
-  size_t plan_bytes;  // lengths + tiles + groups + gidx (one host->device copy)
+  size_t plan_bytes;  // status + lengths + tiles + groups + gidx (one host->device copy)
+  size_t off_status;  // int32 [2]: labels out of range, flat index of the first (-1 if none)
   size_t off_Tlen, off_Ulen, off_tiles, off_groups, off_gidx;
+  size_t off_labels;  // int32 [B, U+1]: the labels the kernels read (range-checked copy)
   size_t off_a, off_l, off_lse, off_phi, off_psi, off_alpha, off_beta, off_lnP;
   bool lat64;  // alpha, beta, ln P held in fp64 (fp32 mode), else fp32
   size_t off_logits, off_z;  // untiled only; z is stored transposed [H_pad, total_rows]
@@ -66,11 +68,21 @@ struct Layout {
   size_t workspace_bytes;
 };
 
+// Rows of the plan's row space (and so of any wave) must stay below this:
+// row numbers are int32 in the plan records and the kernels, and wave
+// buffers round the rows up to whole 128-row cell tiles.
+constexpr int64_t kMaxPlanRows = ((int64_t)1 << 31) - 1 - 256;
+
+// K steps of 16 for hidden size H on the MFMA cores (H_pad = 16 * result),
+// -1 if H is too large.
+int joint_ks_for(int H);
 // Validates dims and lengths; on failure returns false and sets err.
 bool check_dims(const Dims& d, std::string& err, int& status);
 bool check_lengths(const Dims& d, const int32_t* T_len, const int32_t* U_len, std::string& err);
 // Builds the tile plan (deterministic in its inputs).
 void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H_pad, Plan& p);
+// Checks a built plan against the library's 32-bit row limits (kMaxPlanRows).
+bool check_plan(const Plan& p, std::string& err);
 Layout make_layout(const Plan& p);
 // Serializes lengths, tiles, groups and gidx in layout order into out
 // (plan_bytes bytes, offsets relative to the start of `saved`).

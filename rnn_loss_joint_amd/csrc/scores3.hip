@@ -20,18 +20,19 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_core.hpp"
+#include "scores3_map.hpp"
 
 namespace rnnt {
 namespace s3 {
 
-constexpr int BN = 128;  // cells per item
-constexpr int BK = 64;
-constexpr int NST = 3;   // stages in flight
-constexpr int A_BYTES = 256 * BK * 2;
-constexpr int B_BYTES = BN * BK * 2;
+constexpr int BN = s3map::BN;  // cells per item
+constexpr int BK = s3map::BK;
+constexpr int NST = s3map::NST;  // stages in flight
+constexpr int A_BYTES = s3map::A_BYTES;
+constexpr int B_BYTES = s3map::B_BYTES;
 constexpr int STAGE = A_BYTES + B_BYTES;
-constexpr int NDA = A_BYTES / (256 * 16);  // 16-byte dma per thread per stage
-constexpr int NDB = B_BYTES / (256 * 16);
+constexpr int NDA = s3map::NDA;  // 16-byte dma per thread per stage
+constexpr int NDB = s3map::NDB;
 constexpr int OFF_BIAS = NST * STAGE;              // [2][256] f32: b^O log2 e
 constexpr int OFF_COEF = OFF_BIAS + 2 * 256 * 4;   // [2][128][2] f32: (lse log2 e, occupancy)
 constexpr int OFF_RED = OFF_COEF + 2 * 256 * 4;    // [2 wc][2 j][2][32] f32
@@ -68,12 +69,9 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
   const int r = lane & 31, g = lane >> 5;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int nvt = p.nvt, nq = p.H_pad / BK;
-  // items (ct, vt): cell tiles ct = 8 ctl + xcd of this XCD, all V tiles of a
-  // cell tile on neighbouring slots (their z rows shared in L2); cell tiles
-  // are taken from the end of the wave's rows backwards, so the z rows the
-  // z-row kernel wrote last (still in the last-level cache) are read first
-  const int nctl = (p.n_ct - xcd + 7) / 8;
-  const int n_items = max(0, (nctl * nvt - slot + 31) / 32);
+  // items (ct, vt) of this workgroup, see scores3_map.hpp
+  const int nctl = s3map::nctl_of(p.n_ct, xcd);
+  const int n_items = s3map::items_of(p.n_ct, nvt, xcd, slot);
   if (n_items == 0) return;
   constexpr int ND = NDA + NDB + (BWD ? 2 : 1);  // dma per thread per stage
 
@@ -84,9 +82,8 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
   uint32_t offA[2], offB[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int row = (i * 4 + wave) * 8 + (lane >> 3);
-    offA[i] = (uint32_t)(row * p.H_pad * 2 + (((lane & 7) ^ swz(row)) << 4));
-    offB[i] = (uint32_t)(row * (int)p.z_ld * 2 + (((lane & 7) ^ swz(row)) << 4));
+    offA[i] = s3map::dma_thread_off(i, wave, lane, p.H_pad);
+    offB[i] = s3map::dma_thread_off(i, wave, lane, (int)p.z_ld);
   }
   const int64_t stepA = (int64_t)32 * p.H_pad * 2, stepB = (int64_t)32 * p.z_ld * 2;
   // Fragment reads: row wr*128 + 32 f + r of A (wc*64 + 32 f + r of B), chunk
@@ -100,11 +97,9 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
   const char* cft = reinterpret_cast<const char*>(p.coefA);
 
   auto item_of = [&](int n, int& ct, int& vt) {
-    n = min(n, n_items - 1);
-    const int idx = slot + 32 * n;
-    const int c0 = idx / nvt;
-    vt = idx - c0 * nvt;
-    ct = (nctl - 1 - c0) * 8 + xcd;
+    const s3map::Item it = s3map::item_of(n, n_items, nctl, nvt, xcd, slot);
+    ct = it.ct;
+    vt = it.vt;
   };
   struct Src {
     const char *a, *b, *bias, *coef;
@@ -112,22 +107,20 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
     int par;
   };
   auto stage_src = [&](int S) {
-    const int n = S / nq, q = S - (S / nq) * nq;
-    int ct, vt;
-    item_of(n, ct, vt);
+    const s3map::StageSrc o = s3map::stage_src(S, nq, n_items, nctl, nvt, xcd, slot, p.H_pad, p.z_ld);
     Src s;
-    s.a = WOp + ((int64_t)vt * 256 * p.H_pad + q * BK) * 2;
-    s.b = zb + ((int64_t)ct * BN * p.z_ld + q * BK) * 2;
-    s.bias = blt + (int64_t)vt * 256 * 4;
-    s.coef = cft + (int64_t)ct * BN * 8;
+    s.a = WOp + o.a;
+    s.b = zb + o.b;
+    s.bias = blt + o.bias;
+    s.coef = cft + o.coef;
     s.st = lds + (S % NST) * STAGE;
-    s.par = min(n, n_items - 1) & 1;
+    s.par = o.par;
     return s;
   };
   auto issue_one = [&](const Src& s, int d) {
-    if (d < NDA) s3::dma_b128(s.a + (d >> 1) * 2 * stepA + offA[d & 1], s.st + (d * 4 + wave) * 1024);
+    if (d < NDA) s3::dma_b128(s.a + s3map::dma_off(d, offA[0], offA[1], stepA), s.st + (d * 4 + wave) * 1024);
     else if (d < NDA + NDB)
-      s3::dma_b128(s.b + ((d - NDA) >> 1) * 2 * stepB + offB[(d - NDA) & 1], s.st + A_BYTES + ((d - NDA) * 4 + wave) * 1024);
+      s3::dma_b128(s.b + s3map::dma_off(d - NDA, offB[0], offB[1], stepB), s.st + A_BYTES + ((d - NDA) * 4 + wave) * 1024);
     else if (d == NDA + NDB) s3::dma_b32(s.bias + tid * 4, lds + OFF_BIAS + s.par * 1024 + wave * 256);
     else s3::dma_b32(s.coef + tid * 4, lds + OFF_COEF + s.par * 1024 + wave * 256);
   };

@@ -106,6 +106,25 @@ def _zipf_labels(rng: np.random.Generator, n: int, V: int, s: float) -> np.ndarr
     return (np.searchsorted(cdf, u, side="left") + 1).astype(np.int32)
 
 
+def _draw_lengths(rng: np.random.Generator, B: int, T: int, U: int, t_range, u_range):
+    """The first draws of every batch: T_b, then U_b, integer-uniform over the inclusive ranges."""
+    t_lo, t_hi = t_range if t_range is not None else (T, T)
+    u_lo, u_hi = u_range if u_range is not None else (U, U)
+    if not (1 <= t_lo <= t_hi <= T and 0 <= u_lo <= u_hi <= U):
+        raise ValueError("bad length ranges")
+    T_len = rng.integers(t_lo, t_hi + 1, size=B).astype(np.int32)
+    U_len = rng.integers(u_lo, u_hi + 1, size=B).astype(np.int32)
+    return T_len, U_len
+
+
+def workload_lengths(cfg: str, *, seed: int | None = None):
+    """(T_len, U_len) of a named workload's batch without drawing the rest (the lengths are the
+    first draws, so they equal workload_inputs(cfg).T_len / .U_len)."""
+    w = WORKLOADS[cfg]
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    return _draw_lengths(rng, w.B, w.T, w.U, w.t_range, w.u_range)
+
+
 @dataclasses.dataclass
 class Inputs:
     """One batch of inputs. Float arrays are float32 holding dtype-exact values."""
@@ -154,13 +173,8 @@ def make_inputs(B: int, T: int, U: int, V: int, HA: int, HL: int, H: int, *,
     biases instead of zeros (used by tests that need non-zero biases).
     """
     rng = np.random.Generator(np.random.PCG64(seed))
-    t_lo, t_hi = t_range if t_range is not None else (T, T)
-    u_lo, u_hi = u_range if u_range is not None else (U, U)
-    if not (1 <= t_lo <= t_hi <= T and 0 <= u_lo <= u_hi <= U):
-        raise ValueError("bad length ranges")
     # 1. lengths
-    T_len = rng.integers(t_lo, t_hi + 1, size=B).astype(np.int32)
-    U_len = rng.integers(u_lo, u_hi + 1, size=B).astype(np.int32)
+    T_len, U_len = _draw_lengths(rng, B, T, U, t_range, u_range)
     # 2. labels (blank-prepended; entries past U_b are blank)
     if V < 2:
         raise ValueError("need V >= 2")

@@ -1,0 +1,186 @@
+// Host replay of the persistent score kernels' work and address mapping.
+//
+// For each case read from stdin, builds the tile plan and buffer layout with
+// the library's own host code (plan.cpp), then walks, for every wave of the
+// plan and for the forward and the backward kernel, every workgroup of the
+// 256-workgroup launch through every stage its pipeline issues (the
+// prologue's three, then one per stage, past the last item included) and
+// every item whose epilogue it runs, using the same constexpr mapping the
+// kernel uses (scores3_map.hpp). It checks that
+//   - every item's cell tile ct lies in [0, n_ct) and V tile vt in [0, nvt),
+//   - the n_ct cell tiles of 128 rows fit in the wave buffers,
+//   - every dma source byte range (padded W^O rows, z rows, bias values, the
+//     backward coefficients) and every epilogue store range (the forward's
+//     per-V-tile statistics, the backward's dh rows) lies inside the buffer
+//     region the layout reserves for it.
+// Nothing is launched: this is plain C++ against the plan and layout.
+//
+// Input, one case per line: B T U V HA HL H bf16 untiled tile_t tile_u tpw,
+// then B values of T_len and B values of U_len. Output per case: "ok
+// <stages checked>" or "skip <reason>" or "FAIL <what>".
+#include <stdint.h>
+
+#include <algorithm>
+#include <iostream>
+#include <sstream>
+#include <string>
+#include <vector>
+
+#include "plan.hpp"
+#include "scores3_map.hpp"
+
+using namespace rnnt;
+
+namespace {
+
+struct Region {
+  int64_t begin, end;
+};
+
+// The region that starts at `off`: up to the next region's offset (or the
+// end of the buffer), i.e. the bytes the layout reserves for it.
+Region region(int64_t off, const std::vector<int64_t>& offs, int64_t total) {
+  int64_t end = total;
+  for (int64_t o : offs)
+    if (o > off) end = std::min(end, o);
+  return Region{off, end};
+}
+
+bool inside(const Region& r, int64_t lo, int64_t hi) { return lo >= r.begin && hi <= r.end && lo <= hi; }
+
+std::string run_case(const Dims& d, const std::vector<int32_t>& T_len, const std::vector<int32_t>& U_len,
+                     int64_t& checked) {
+  std::string err;
+  int st = 0;
+  if (!check_dims(d, err, st)) return "skip " + err;
+  if (!check_lengths(d, T_len.data(), U_len.data(), err)) return "skip " + err;
+  const int ks = joint_ks_for(d.H);
+  if (ks < 0) return "skip H";
+  Plan p;
+  build_plan(d, T_len.data(), U_len.data(), ks * 16, p);
+  if (!check_plan(p, err)) return "skip " + err;
+  const Layout L = make_layout(p);
+  // the persistent score kernels run in bf16 tiled mode with at least 8 k-steps of 64
+  if (!d.bf16 || d.untiled || p.H_pad / 64 < 8) return "skip not the persistent score path";
+  std::vector<int64_t> offs = {
+      (int64_t)L.w_dh, (int64_t)L.w_z, (int64_t)L.w_gA, (int64_t)L.w_gL, (int64_t)L.w_PA, (int64_t)L.w_PL,
+      (int64_t)L.w_PW, (int64_t)L.w_PB, (int64_t)L.w_PWA, (int64_t)L.w_PBZ, (int64_t)L.w_PWL, (int64_t)L.w_WOT,
+      (int64_t)L.w_stats, (int64_t)L.w_hb, (int64_t)L.w_hy, (int64_t)L.w_WOp, (int64_t)L.w_bl,
+      (int64_t)L.w_coefA, (int64_t)L.w_coefB, (int64_t)L.w_WAT, (int64_t)L.w_WLT};
+  // the rounded gA / gL and the masked encodings live in the wave buffers
+  // (dead after the last wave) when they fit there, else in regions of their own
+  for (size_t o : {L.w_gb, L.w_hs})
+    if (o >= L.w_coefB) offs.push_back((int64_t)o);
+  const int64_t W = (int64_t)L.workspace_bytes;
+  const Region rz = region(L.w_z, offs, W), rdh = region(L.w_dh, offs, W), rst = region(L.w_stats, offs, W);
+  const Region rwo = region(L.w_WOp, offs, W), rbl = region(L.w_bl, offs, W), rco = region(L.w_coefA, offs, W);
+  const int64_t buf_rows = (p.max_wave_rows + 127) / 128 * 128;
+  const int nvt = p.nvt, nq = p.H_pad / s3map::BK;
+  const int64_t z_ld = p.H_pad;
+
+  // per-thread dma offsets relative to a stage's source, over all threads
+  // and instructions of an operand: [lo, hi) in bytes
+  auto dma_span = [&](int nd, int ld, int64_t& lo, int64_t& hi) {
+    lo = INT64_MAX;
+    hi = INT64_MIN;
+    const int64_t step32 = (int64_t)32 * ld * 2;
+    for (int tid = 0; tid < s3map::kThreads; ++tid) {
+      const int wave = tid >> 6, lane = tid & 63;
+      const uint32_t o0 = s3map::dma_thread_off(0, wave, lane, ld), o1 = s3map::dma_thread_off(1, wave, lane, ld);
+      for (int dd = 0; dd < nd; ++dd) {
+        const int64_t o = s3map::dma_off(dd, o0, o1, step32);
+        lo = std::min(lo, o);
+        hi = std::max(hi, o + 16);
+      }
+    }
+  };
+  int64_t a_lo, a_hi, b_lo, b_hi;
+  dma_span(s3map::NDA, p.H_pad, a_lo, a_hi);
+  dma_span(s3map::NDB, (int)z_ld, b_lo, b_hi);
+
+  for (size_t w = 0; w < p.waves.size(); ++w) {
+    const WaveInfo& wv = p.waves[w];
+    const int n_rows = wv.row_end - wv.row_begin;
+    const int n_ct = (n_rows + 127) / 128;
+    std::ostringstream where;
+    where << "wave " << w << " (rows " << n_rows << ", n_ct " << n_ct << ")";
+    if ((int64_t)n_ct * 128 > buf_rows) return "FAIL " + where.str() + ": cell tiles exceed the wave buffer rows";
+    if (n_rows <= 0) return "FAIL " + where.str() + ": empty wave";
+    for (int bwd = 0; bwd < 2; ++bwd) {
+      for (int blk = 0; blk < s3map::kGrid; ++blk) {
+        const int xcd = blk & 7, slot = blk >> 3;
+        const int nctl = s3map::nctl_of(n_ct, xcd);
+        const int n_items = s3map::items_of(n_ct, nvt, xcd, slot);
+        if (n_items == 0) continue;
+        auto bad = [&](const std::string& what, int S) {
+          std::ostringstream o;
+          o << "FAIL " << where.str() << (bwd ? " bwd" : " fwd") << " block " << blk << " stage " << S << ": "
+            << what;
+          return o.str();
+        };
+        // stages 0 .. 2 from the prologue, then S + 3 during stage S
+        const int last_S = n_items * nq - 1 + 3;
+        for (int S = 0; S <= last_S; ++S) {
+          const s3map::Item it = s3map::item_of(S / nq, n_items, nctl, nvt, xcd, slot);
+          if (it.ct < 0 || it.ct >= n_ct) return bad("cell tile " + std::to_string(it.ct) + " out of range", S);
+          if (it.vt < 0 || it.vt >= nvt) return bad("V tile " + std::to_string(it.vt) + " out of range", S);
+          const s3map::StageSrc o = s3map::stage_src(S, nq, n_items, nctl, nvt, xcd, slot, p.H_pad, z_ld);
+          if (!inside(rwo, L.w_WOp + o.a + a_lo, L.w_WOp + o.a + a_hi)) return bad("W^O rows outside", S);
+          if (!inside(rz, L.w_z + o.b + b_lo, L.w_z + o.b + b_hi)) return bad("z rows outside", S);
+          // the z rows a stage reads belong to its cell tile's 128 rows
+          if (o.b + b_lo < (int64_t)it.ct * 128 * z_ld * 2 || o.b + b_hi > ((int64_t)it.ct + 1) * 128 * z_ld * 2)
+            return bad("z bytes outside the item's cell tile", S);
+          if (!inside(rbl, L.w_bl + o.bias, L.w_bl + o.bias + 4 * s3map::kThreads)) return bad("bias outside", S);
+          if (bwd && !inside(rco, L.w_coefA + o.coef, L.w_coefA + o.coef + 4 * s3map::kThreads))
+            return bad("coefficients outside", S);
+          ++checked;
+        }
+        // epilogue stores of every item: rows ct*128 .. +127, V tile columns
+        for (int n = 0; n < n_items; ++n) {
+          const s3map::Item it = s3map::item_of(n, n_items, nctl, nvt, xcd, slot);
+          const int64_t r0 = (int64_t)it.ct * s3map::BN, r1 = r0 + s3map::BN;
+          if (!bwd) {
+            // stats[row][vt] as (max, sum) float pairs
+            if (!inside(rst, L.w_stats + 8 * (r0 * nvt + it.vt), L.w_stats + 8 * ((r1 - 1) * nvt + it.vt) + 8))
+              return bad("statistics store outside", -1);
+          } else {
+            if (!inside(rdh, L.w_dh + 2 * (r0 * p.V_pad + (int64_t)it.vt * 256),
+                        L.w_dh + 2 * ((r1 - 1) * p.V_pad + (int64_t)it.vt * 256 + 256)))
+              return bad("dh store outside", -1);
+          }
+        }
+      }
+    }
+  }
+  return "ok " + std::to_string(checked);
+}
+
+}  // namespace
+
+int main() {
+  std::string line;
+  int fails = 0;
+  while (std::getline(std::cin, line)) {
+    if (line.empty()) continue;
+    std::istringstream in(line);
+    Dims d{};
+    int bf = 0, un = 0;
+    in >> d.B >> d.T >> d.U >> d.V >> d.HA >> d.HL >> d.H >> bf >> un >> d.tile_t >> d.tile_u >> d.tiles_per_wave;
+    d.blank = 0;
+    d.bf16 = bf != 0;
+    d.untiled = un != 0;
+    std::vector<int32_t> T_len(d.B), U_len(d.B);
+    for (auto& x : T_len) in >> x;
+    for (auto& x : U_len) in >> x;
+    if (!in) {
+      std::cout << "FAIL bad input line" << std::endl;
+      ++fails;
+      continue;
+    }
+    int64_t checked = 0;
+    const std::string r = run_case(d, T_len, U_len, checked);
+    if (r.rfind("FAIL", 0) == 0) ++fails;
+    std::cout << r << std::endl;
+  }
+  return fails ? 1 : 0;
+}

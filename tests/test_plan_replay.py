@@ -1,0 +1,100 @@
+"""Host replay of the persistent score kernels' item and address mapping (no launch).
+
+tests/host/replay_scores3.cpp is built with g++ against the library's own plan code and
+the constexpr mapping the kernel compiles (rnn_loss_joint_amd/csrc/scores3_map.hpp). For
+every wave of every plan below, every workgroup, stage and item of the forward and backward
+launches, it checks that the cell tile and V tile indices are in range and that every dma
+source and epilogue store byte range lies inside the buffer region the layout reserves.
+Covered: the four bf16 workloads at their lengths with the tile sizes they are run with and
+more, default, single-tile, small and whole-batch waves, whole-sample tiles, and ragged or
+degenerate length sets.
+"""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import rnn_loss_joint_amd as rl
+from rnnt_inputs import WORKLOADS, workload_lengths
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "rnn_loss_joint_amd", "csrc")
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+
+
+@pytest.fixture(scope="module")
+def replay(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("replay") / "replay_scores3")
+    # AddressSanitizer and UBSan on the host code (the library's plan.cpp included)
+    cmd = ["g++", "-O2", "-std=c++17", *SANITIZE, f"-I{CSRC}", os.path.join(ROOT, "tests", "host", "replay_scores3.cpp"),
+           os.path.join(CSRC, "plan.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    return exe
+
+
+def case_line(B, T, U, V, HA, HL, H, tile, tpw, T_len, U_len, bf16=True, untiled=False):
+    vals = [B, T, U, V, HA, HL, H, int(bf16), int(untiled), tile[0], tile[1], tpw]
+    return " ".join(map(str, vals + list(map(int, T_len)) + list(map(int, U_len))))
+
+
+def run(exe, lines):
+    r = subprocess.run([exe], input="\n".join(lines) + "\n", capture_output=True, text=True, timeout=600)
+    out = r.stdout.strip().splitlines()
+    assert len(out) == len(lines), r.stdout + r.stderr
+    return r.returncode, out
+
+
+@pytest.mark.parametrize("name", ["small-bf16", "20s-bf16", "vocab4096-bf16", "40s-b256-bf16"])
+def test_workload_plans_stay_in_bounds(replay, name):
+    w = WORKLOADS[name]
+    T_len, U_len = workload_lengths(name)
+    tiles = sorted(set(w.tiles) | {(64, 32), (32, 16), (128, 64), (32, 8), (96, 40), (w.T, w.U + 1)})
+    lines = []
+    for tile in tiles:
+        for tpw in (0, 1, 3, w.B, 4 * w.B):
+            lines.append(case_line(w.B, w.T, w.U, w.V, w.HA, w.HL, w.H, tile, tpw, T_len, U_len))
+    rc, out = run(replay, lines)
+    bad = [(l.split()[:12], o) for l, o in zip(lines, out) if not o.startswith("ok")]
+    assert rc == 0 and not bad, bad[:3]
+
+
+def test_ragged_and_degenerate_plans_stay_in_bounds(replay):
+    rng = np.random.default_rng(7)
+    lines = []
+    for _ in range(40):
+        B = int(rng.integers(1, 40))
+        T = int(rng.integers(1, 700))
+        U = int(rng.integers(0, 300))
+        V = int(rng.choice([300, 1000, 1024, 1025, 4096, 5000]))
+        H = int(rng.choice([512, 576, 640, 768]))
+        T_len = rng.integers(1, T + 1, B)
+        U_len = rng.integers(0, U + 1, B)
+        tile = (int(rng.integers(1, 200)), int(rng.integers(1, 80)))
+        tpw = int(rng.choice([0, 1, 2, 7, B]))
+        lines.append(case_line(B, T, U, V, 64, 64, H, tile, tpw, T_len, U_len))
+    # every sample of length 1 x 1, one sample, a single full tile
+    lines.append(case_line(5, 9, 4, 1024, 64, 64, 640, (32, 2), 1, [1] * 5, [0] * 5))
+    lines.append(case_line(1, 1000, 200, 1024, 512, 512, 640, (64, 32), 0, [1000], [200]))
+    lines.append(case_line(3, 64, 31, 256, 64, 64, 512, (64, 32), 0, [64] * 3, [31] * 3))
+    rc, out = run(replay, lines)
+    bad = [(l.split()[:12], o) for l, o in zip(lines, out) if o.startswith("FAIL")]
+    assert rc == 0 and not bad, bad[:3]
+    assert sum(o.startswith("ok") for o in out) >= 30
+
+
+def test_plan_rows_beyond_32_bits_are_refused():
+    """A tiny tile_t pads every tile's t extent to 32 rows: 400 samples x 1000 frames with
+    1 x 201 tiles need ~2.6e9 rows, which the 32-bit row numbers cannot address. The query
+    refuses it (host only, nothing launched)."""
+    B, T, U = 400, 1000, 200
+    d = rl.make_desc(B, T, U, 1024, 512, 512, 640, tile=(1, 201))
+    with pytest.raises(rl.RnntError) as e:
+        rl.rnnt_loss_query(d, np.full(B, T), np.full(B, U))
+    assert e.value.status == rl.RNNT_E_UNSUPPORTED
+    assert "rows" in str(e.value)
+    # the same batch with 32-row tiles fits
+    d = rl.make_desc(B, T, U, 1024, 512, 512, 640, tile=(32, 201))
+    s, w = rl.rnnt_loss_query(d, np.full(B, T), np.full(B, U))
+    assert s > 0 and w > 0
