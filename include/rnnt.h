@@ -31,13 +31,29 @@
  *      hA [B,T,HA], hL [B,U+1,HL], WA [H,HA], WL [H,HL], bZ [H], WO [V,H], bO [V].
  *    labels is int32 [B,U+1] on the device; column 0 is the blank id, column
  *    u+1 (u < U_len[b]) is the label emitted from lattice row u. Entries past
- *    U_len[b] are never read. Label values must lie in [0,V) (precondition,
- *    not checked on the device).
- *    Padded positions (t >= T_len[b], u > U_len[b]) are never read.
+ *    U_len[b] (and column 0) are never read. Label values must lie in [0,V):
+ *    the forward copies the labels into `saved` and every kernel reads that
+ *    copy, in which a label outside [0,V) is replaced by the blank id, so a
+ *    bad label cannot address memory outside the output layer; it does make
+ *    the results those of the replaced label. After the forward, the first two
+ *    int32 of `saved` hold the number of such labels (0 if all are in range)
+ *    and the flat index b*(U+1)+u+1 of the first one (-1 if none).
+ *    Padded positions (t >= T_len[b], u > U_len[b]) of hA and hL may be read
+ *    (the joint pre-projections run over all B*T and B*(U+1) rows) but never
+ *    affect any cost or gradient: any values there, NaN and infinities
+ *    included, give the same results.
  *  - costs, dcosts and every gradient output are fp32. Gradients are
  *    overwritten, not accumulated; padded rows of dhA/dhL are written as 0.
  *  - `stream` is a hipStream_t (NULL = the null stream). Every call enqueues
- *    work on that stream and returns without synchronizing the device.
+ *    work on that stream and returns without synchronizing the device. The
+ *    forward's only host-to-device copy (the tile plan, a few hundred bytes
+ *    to a few hundred KB) goes through a ring of pinned staging slots, each
+ *    reused once its previous copy has completed; new slots are added while
+ *    all are in flight, so a call waits on the host only if 16 forward calls'
+ *    copies are still queued.
+ *  - Results are deterministic: every reduction (over tiles, waves, splits
+ *    and samples) runs in a fixed order with no floating-point atomics, so
+ *    repeated calls on the same inputs give identical bits.
  *  - Errors: every entry point validates its arguments on the host before
  *    launching anything and returns a status; no exception or exit crosses
  *    the ABI. rnnt_last_error() gives a thread-local description of the last
@@ -75,7 +91,8 @@ typedef struct {
   int32_t mode;                  /* rnnt_mode                                  */
   int32_t tile_t, tile_u;        /* tile extent in t and u (tiled mode), > 0   */
   int32_t tiles_per_wave;        /* tiles whose buffers coexist; 0 = default   */
-  int32_t reserved;              /* must be 0                                  */
+  int32_t reserved;              /* must be 0. (No "deterministic" switch is
+                                    needed: every call is deterministic.)    */
 } rnnt_desc;
 
 /* Limits of this library (RNNT_E_UNSUPPORTED beyond them): H, HA, HL multiples
@@ -83,7 +100,10 @@ typedef struct {
  * 4*NQ*US <= 2^29 with NQ = ceil((T+U)/4) and US = U+1 rounded up to a
  * multiple of 32 (the entries of the lattice arrays, see rnnt_lattice). Any tile size
  * is accepted; a tile's t extent is padded to a multiple of 32 rows inside the
- * library, so tile_t values that are multiples of 32 waste nothing. */
+ * library, so tile_t values that are multiples of 32 waste nothing. The
+ * padded rows of all tiles, sum over tiles of (tile's u extent) x (its t
+ * extent rounded up to 32), must not exceed 2^31 - 257 (row numbers are
+ * 32-bit); very small tile_t on large batches can exceed it. */
 
 /* Bytes of `saved` (lives from rnnt_loss_fwd to rnnt_loss_bwd, must not be
  * modified in between) and of `workspace` (scratch, reusable after each call)
@@ -129,7 +149,8 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
  * given to rnnt_loss_fwd, and `saved` the buffer it filled. In untiled mode
  * the backward overwrites the scores kept in `saved` with their gradients
  * (in place, as the scores are not needed afterwards), so it may run once
- * per forward; in tiled mode `saved` is only read. */
+ * per forward; in tiled mode `saved` is only read. The labels are read from
+ * the forward's checked copy in `saved` (labels must still be non-null). */
 rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
                           const int32_t* labels, const int32_t* T_len_host,
                           const int32_t* U_len_host, const void* WA, const void* WL,

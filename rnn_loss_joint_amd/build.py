@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librnnt_mi355.so")
 ARCH = "gfx950"
-SOURCES = ["api.hip", "joint.hip", "lattice.hip", "gemm.hip", "mma.hip", "dz_dwo.hip", "scores3.hip", "plan.cpp"]
+SOURCES = ["api.hip", "joint.hip", "lattice.hip", "gemm.hip", "mma.hip", "dz_dwo.hip", "scores3.hip", "labels.hip", "plan.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-variable", "-Wno-unused-but-set-variable",

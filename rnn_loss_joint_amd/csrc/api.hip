@@ -26,6 +26,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
+#include "staging.hpp"
 
 static_assert(sizeof(rnnt::Tile) == sizeof(rnnt::TileH), "tile record layout");
 static_assert(sizeof(rnnt::Group) == sizeof(rnnt::GroupH), "group record layout");
@@ -80,39 +81,39 @@ rnnt_status prepare(const rnnt_desc* desc, const int32_t* T_len, const int32_t* 
   int ks = rnnt::joint_ks_for(d.H);
   if (ks < 0) return fail(RNNT_E_UNSUPPORTED, "H too large for the fused joint kernel");
   rnnt::build_plan(d, T_len, U_len, ks * 16, p);
+  if (!rnnt::check_plan(p, err)) return fail(RNNT_E_UNSUPPORTED, err);
   L = rnnt::make_layout(p);
   return RNNT_OK;
 }
 
-// Pinned staging for the host -> device plan copy. The buffer is reused once
-// the previous copy (tracked by an event) has completed.
-struct Staging {
-  std::mutex mu;
-  void* host = nullptr;
-  size_t cap = 0;
-  hipEvent_t ev = nullptr;
-  bool pending = false;
+// Pinned staging for the host -> device plan copy: a ring of slots, each
+// reused once its previous copy has completed (staging.hpp), so no call
+// waits on the host in steady state.
+struct HipStagingBackend {
+  using Event = hipEvent_t;
+  using Stream = hipStream_t;
+  void* alloc(size_t n) {
+    void* p = nullptr;
+    return hipHostMalloc(&p, n, hipHostMallocDefault) == hipSuccess ? p : nullptr;
+  }
+  hipEvent_t make_event() {
+    hipEvent_t e = nullptr;
+    return hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess ? e : nullptr;
+  }
+  bool done(hipEvent_t e) { return hipEventQuery(e) == hipSuccess; }
+  bool wait(hipEvent_t e) { return hipEventSynchronize(e) == hipSuccess; }
+  bool copy(void* dst, const void* src, size_t n, hipStream_t st) {
+    return hipMemcpyAsync(dst, src, n, hipMemcpyHostToDevice, st) == hipSuccess;
+  }
+  bool record(hipEvent_t e, hipStream_t st) { return hipEventRecord(e, st) == hipSuccess; }
 };
-Staging g_staging;
+rnnt::StagingRing<HipStagingBackend> g_staging;
 
 rnnt_status upload(void* dst, const std::vector<char>& src, hipStream_t st) {
-  std::lock_guard<std::mutex> lk(g_staging.mu);
-  if (g_staging.pending) {
-    RNNT_HIP(hipEventSynchronize(g_staging.ev));
-    g_staging.pending = false;
-  }
-  if (!g_staging.ev) RNNT_HIP(hipEventCreateWithFlags(&g_staging.ev, hipEventDisableTiming));
-  if (g_staging.cap < src.size()) {
-    if (g_staging.host) RNNT_HIP(hipHostFree(g_staging.host));
-    g_staging.host = nullptr;
-    g_staging.cap = 0;
-    RNNT_HIP(hipHostMalloc(&g_staging.host, src.size(), hipHostMallocDefault));
-    g_staging.cap = src.size();
-  }
-  std::memcpy(g_staging.host, src.data(), src.size());
-  RNNT_HIP(hipMemcpyAsync(dst, g_staging.host, src.size(), hipMemcpyHostToDevice, st));
-  RNNT_HIP(hipEventRecord(g_staging.ev, st));
-  g_staging.pending = true;
+  const char* what = nullptr;
+  if (!g_staging.upload(dst, src.data(), src.size(), st, &what))
+    return fail(RNNT_E_HIP, std::string("plan upload: ") + (what ? what : "failed") + ": " +
+                                hipGetErrorString(hipGetLastError()));
   return RNNT_OK;
 }
 
@@ -160,6 +161,8 @@ template <class T> const T* at(const void* base, size_t off) {
 }
 
 struct Saved {
+  int32_t* status;
+  int32_t* labels;  // the range-checked labels every kernel reads
   const int32_t* Tlen;
   const int32_t* Ulen;
   const rnnt::Tile* tiles;
@@ -173,6 +176,8 @@ struct Saved {
 
 Saved saved_view(void* s, const rnnt::Layout& L) {
   Saved v;
+  v.status = at<int32_t>(s, L.off_status);
+  v.labels = at<int32_t>(s, L.off_labels);
   v.Tlen = at<int32_t>(s, L.off_Tlen);
   v.Ulen = at<int32_t>(s, L.off_Ulen);
   v.tiles = at<rnnt::Tile>(s, L.off_tiles);
@@ -194,13 +199,12 @@ Saved saved_view(void* s, const rnnt::Layout& L) {
   return v;
 }
 
-rnnt::JointArgs joint_args(const rnnt::Plan& p, const Saved& sv, const int32_t* labels, const void* WO,
-                           const void* bO) {
+rnnt::JointArgs joint_args(const rnnt::Plan& p, const Saved& sv, const void* WO, const void* bO) {
   rnnt::JointArgs a{};
   a.tiles = sv.tiles;
   a.T_len = sv.Tlen;
   a.U_len = sv.Ulen;
-  a.labels = labels;
+  a.labels = sv.labels;
   a.T = p.d.T;
   a.U1 = p.U1;
   a.V = p.d.V;
@@ -310,6 +314,10 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
   s = upload(saved, host_plan, st);
   if (s != RNNT_OK) return s;
   Saved sv = saved_view(saved, L);
+  {
+    ProfScope ps_("labels_check", st);
+    RNNT_HIP(rnnt::launch_labels_check(labels, sv.Ulen, d.B, p.U1, d.V, d.blank, sv.labels, sv.status, st));
+  }
 
   // 1. joint pre-activations (bf16: large-tile row GEMM, scaled for the z-row
   // kernel's base-2 exponential, the only reader of a and l in this mode)
@@ -404,7 +412,7 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
       z.n_ug = (d.tile_u + 7) / 8;
       z.buf_row_base = base;
       z.U_len = sv.Ulen;
-      z.labels = labels;
+      z.labels = sv.labels;
       z.T = d.T;
       z.U1 = p.U1;
       z.H = d.H;
@@ -483,7 +491,7 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
       }
     }
   } else {
-    rnnt::JointArgs a = joint_args(p, sv, labels, WO, bO);
+    rnnt::JointArgs a = joint_args(p, sv, WO, bO);
     a.tile_begin = 0;
     a.tile_end = (int)p.tiles.size();
     a.row_begin = 0;
@@ -592,7 +600,7 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       a.n_rows = wrows;
       a.T_len = sv.Tlen;
       a.U_len = sv.Ulen;
-      a.labels = labels;
+      a.labels = sv.labels;
       a.T = d.T;
       a.U1 = p.U1;
       a.V = d.V;
@@ -625,7 +633,7 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       z.n_ug = (d.tile_u + 7) / 8;
       z.buf_row_base = buf_base;
       z.U_len = sv.Ulen;
-      z.labels = labels;
+      z.labels = sv.labels;
       z.T = d.T;
       z.U1 = p.U1;
       z.H = d.H;
@@ -652,7 +660,7 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       sc.buf_row_base = wv.row_begin;
       sc.T_len = sv.Tlen;
       sc.U_len = sv.Ulen;
-      sc.labels = labels;
+      sc.labels = sv.labels;
       sc.T = d.T;
       sc.U1 = p.U1;
       sc.V = d.V;
@@ -681,7 +689,7 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
         a3.buf_row_base = wv.row_begin;
         a3.T_len = sv.Tlen;
         a3.U_len = sv.Ulen;
-        a3.labels = labels;
+        a3.labels = sv.labels;
         a3.T = d.T;
         a3.U1 = p.U1;
         a3.V = d.V;
@@ -720,7 +728,7 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
         RNNT_HIP(rnnt::launch_scores(sc, true, st));
       }
     } else {
-      rnnt::JointArgs a = joint_args(p, sv, labels, WO, bO);
+      rnnt::JointArgs a = joint_args(p, sv, WO, bO);
       a.tile_begin = wv.tile_begin;
       a.tile_end = wv.tile_end;
       a.row_begin = wv.row_begin;

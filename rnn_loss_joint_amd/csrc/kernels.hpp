@@ -67,7 +67,13 @@ struct DhInplaceArgs {
   const double* lnP64;
 };
 
-int joint_ks_for(int H);
+// Writes out = labels with every label of columns 1..U_len[b] outside [0, V)
+// (and every other column) set to blank; status = (count of such labels,
+// flat index of the first or -1). One workgroup.
+hipError_t launch_labels_check(const int32_t* labels, const int32_t* U_len, int B, int U1, int V, int blank,
+                               int32_t* out, int32_t* status, hipStream_t st);
+
+// (H_pad = 16 * joint_ks_for(H), declared in plan.hpp)
 hipError_t launch_joint(const JointArgs& a, bool bf16_mode, bool bwd, hipStream_t st);
 hipError_t launch_dh_inplace(const DhInplaceArgs& a, bool bf16_mode, hipStream_t st);
 
