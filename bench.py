@@ -2,10 +2,13 @@
 
 One step = rnnt_loss_fwd + rnnt_loss_bwd over one batch of the workload, with
 inputs already resident in HBM. K steps are timed after W warm-up steps.
-Prints one JSON line. Per-kernel durations come from the library's launch
-timing (hipEvent pairs on the launch stream over the timed steps); the
-roofline object reports the dominant kernel. The fp64 CPU oracle is timed on
-a bounded sample of the same workload as cpu_baseline.
+Prints one JSON line. The headline ms_per_step and value come from a timed
+pass with nothing but the library's launches; a second pass over the same K
+steps brackets every launch with a hipEvent pair on its stream (the library's
+launch timing) for the per-kernel durations, the roofline object of the
+dominant kernel and t_fwd / t_bwd. The fp64 CPU oracle is timed on a bounded
+sample of the same workload as cpu_baseline, one sample per worker process,
+before the GPU is initialised.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--workload 40s-b256-bf16]
     python bench.py --calibrate-copy BYTES   # counter calibration only
@@ -78,36 +81,96 @@ def mfma_flops(inp):
     }
 
 
-def cpu_baseline(inp, budget_s: float):
-    """Time the oracle (as it stands) on single samples of the workload."""
-    import oracle
-
+def _cpu_model():
     try:
-        from threadpoolctl import threadpool_info
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
-    order = np.argsort(inp.T_len * (inp.U_len + 1))  # smallest samples first
-    done_cells, t_used, used = 0, 0.0, []
-    for b in order:
+
+def _oracle_one_sample(args):
+    """Pool worker: the oracle's fwd + bwd of one sample (BLAS limited to one thread)."""
+    inp, b = args
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        oracle.loss_and_grads(inp, samples=[int(b)])
-        t_used += time.perf_counter() - t0
-        done_cells += int(inp.T_len[b] * (inp.U_len[b] + 1))
-        used.append(int(b))
-        if t_used >= budget_s:
-            break
-    # extrapolate to the whole batch by valid cells, report in padded cells/s
-    t_batch = t_used * inp.valid_cells / done_cells
+        oracle.loss_and_grads(inp, samples=[0])
+        return b, time.perf_counter() - t0
+
+
+def _one_sample_inputs(inp, b):
+    """The batch's sample b alone (B = 1, the same padded shapes), for shipping to a worker."""
+    import dataclasses
+
+    return dataclasses.replace(inp, T_len=inp.T_len[b:b + 1].copy(), U_len=inp.U_len[b:b + 1].copy(),
+                               labels=inp.labels[b:b + 1].copy(), hA=inp.hA[b:b + 1].copy(),
+                               hL=inp.hL[b:b + 1].copy())
+
+
+def cpu_baseline(inp, budget_s: float, workers: int | None = None):
+    """Time the oracle (as it stands) on the host cores: one sample per worker process, BLAS at one
+    thread per worker, over a bounded sample of the workload's batch.
+
+    Samples are taken in a fixed shuffled order (seed 0) so the sample's length mix follows the
+    batch's; new samples are started until budget_s of wall time has passed, and the samples in
+    flight are finished. The rate is the completed samples' valid cells over the wall time,
+    reported with the padded numerator like the GPU figure (x padded / valid cells of the batch).
+    Run before the GPU is initialised (the workers are fresh processes)."""
+    import multiprocessing as mp
+
+    n_cpu = len(os.sched_getaffinity(0))
+    workers = workers or max(1, min(16, n_cpu))
+    B = len(inp.T_len)
+    order = [int(b) for b in np.random.default_rng(0).permutation(B)]
+    env_keys = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+    saved_env = {k: os.environ.get(k) for k in env_keys}
+    for k in env_keys:
+        os.environ[k] = "1"
+    ctx = mp.get_context("spawn")
+    done, cells = [], 0
+    try:
+        with ctx.Pool(workers) as pool:
+            t0 = time.perf_counter()
+            pending = []
+            it = iter(order)
+            for _ in range(workers):  # one sample per worker to start
+                b = next(it, None)
+                if b is not None:
+                    pending.append(pool.apply_async(_oracle_one_sample, ((_one_sample_inputs(inp, b), b),)))
+            while pending:
+                r = pending.pop(0)
+                b, _ = r.get()
+                done.append(b)
+                cells += int(inp.T_len[b]) * (int(inp.U_len[b]) + 1)
+                if time.perf_counter() - t0 < budget_s:
+                    nb = next(it, None)
+                    if nb is not None:
+                        pending.append(pool.apply_async(_oracle_one_sample, ((_one_sample_inputs(inp, nb), nb),)))
+            wall = time.perf_counter() - t0
+    finally:
+        for k, v in saved_env.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    valid_rate = cells / wall
     return {
-        "value": inp.padded_cells / t_batch,
+        "value": valid_rate * inp.padded_cells / inp.valid_cells,
         "unit": "cells/s",
-        "cores": int(cores),
+        "cores": int(workers),
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle fwd+bwd on {len(used)} sample(s) {used} of the workload "
-                   f"({done_cells} valid cells, {t_used:.1f} s), extrapolated by valid cells to the "
-                   f"batch ({inp.valid_cells} valid / {inp.padded_cells} padded cells)"),
+        "sample": (f"fp64 numpy oracle fwd+bwd, one sample per worker process ({workers} processes, BLAS at 1 "
+                   f"thread each, {_cpu_model()}, {n_cpu} cores visible) on {len(done)} of the batch's {B} "
+                   f"samples in a fixed shuffled order ({cells} valid cells, {wall:.1f} s wall); rate = valid "
+                   f"cells/s x padded/valid cells of the batch ({inp.padded_cells}/{inp.valid_cells})"),
+        "valid_cells_per_s": valid_rate,
+        "cpu_model": _cpu_model(),
     }
 
 
@@ -144,7 +207,7 @@ def unfused_baseline(torch, rl, inp, steps, warmup):
     [B, T, U+1, V] scores, as a warp-transducer style implementation computes it ("Neural transducer
     training ...", section "Transducer training", f^W_1..4 as separate passes): torch GEMMs,
     log_softmax and elementwise ops over the padded batch, this library's lattice kernel for alpha /
-    beta. Benchmark only. Returns (ms per fwd+bwd, peak bytes, costs, dWO, dhA)."""
+    beta. Benchmark only. Returns (ms per fwd+bwd, peak bytes, costs, {gradient name: tensor})."""
     dev = torch.device("cuda:0")
     bf = torch.bfloat16
     B, T, HA = inp.hA.shape
@@ -215,7 +278,7 @@ def unfused_baseline(torch, rl, inp, steps, warmup):
         dWA = torch.matmul(gA.reshape(-1, H).t().contiguous(), hA.reshape(-1, HA).float())
         dWL = torch.matmul(gL.reshape(-1, H).t().contiguous(), hL.reshape(-1, HL).float())
         dbZ = gA.sum((0, 1))
-        return costs, dWO, dhA, dbO, dhL, dWA, dWL, dbZ
+        return costs, dict(dhA=dhA, dhL=dhL, dWA=dWA, dWL=dWL, dbZ=dbZ, dWO=dWO, dbO=dbO)
 
     for _ in range(warmup):
         out = fwd_bwd()
@@ -228,7 +291,7 @@ def unfused_baseline(torch, rl, inp, steps, warmup):
         out = fwd_bwd()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps, torch.cuda.max_memory_allocated(), out[0], out[1], out[2]
+    return e0.elapsed_time(e1) / steps, torch.cuda.max_memory_allocated(), out[0], out[1]
 
 
 def main():
@@ -257,10 +320,23 @@ def main():
               "(the library computes one GPU's share of a batch sharded by sample)", file=sys.stderr)
         sys.exit(2)
 
+    from rnnt_inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    inp = None
+    cpu = None
+    side_runs = args.calibrate_copy or args.reference_gemm or args.unfused_baseline
+    if not side_runs:
+        print(f"# generating {w.name} inputs", file=sys.stderr, flush=True)
+        inp = workload_inputs(args.workload)
+        if args.cpu_seconds > 0:
+            # the oracle's worker processes start before this process touches the GPU
+            print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+            cpu = cpu_baseline(inp, args.cpu_seconds)
+
     import torch
 
     import rnn_loss_joint_amd as rl
-    from rnnt_inputs import WORKLOADS, workload_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -277,13 +353,13 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": 4 * n}))
         return
     if args.reference_gemm:
-        reference_gemm(torch, WORKLOADS[args.workload])
+        reference_gemm(torch, w)
         return
     rl.load()
-    w = WORKLOADS[args.workload]
     tile = (w.T, w.U + 1) if args.tile == "sample" else tuple(int(x) for x in args.tile.split("x"))
-    print(f"# generating {w.name} inputs", file=sys.stderr, flush=True)
-    inp = workload_inputs(args.workload)
+    if inp is None:
+        print(f"# generating {w.name} inputs", file=sys.stderr, flush=True)
+        inp = workload_inputs(args.workload)
     if args.budget > 0:
         d = rl.make_desc(w.B, w.T, w.U, w.V, w.HA, w.HL, w.H, dtype=w.dtype, tile=tile)
         args.tiles_per_wave = rl.rnnt_waves_for_budget(d, inp.T_len, inp.U_len, int(args.budget))
@@ -291,29 +367,43 @@ def main():
     prob = rl.Problem(inp, mode=args.mode, tile=tile, tiles_per_wave=args.tiles_per_wave)
     stream = torch.cuda.current_stream()
 
-    def step():
-        prob.forward()
-        prob.backward()
-
     print("# warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        step()
+        prob.forward()
+        prob.backward()
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
-    rl.rnnt_profile_start()
+
+    # timed pass 1 (the headline figure): K steps, nothing but the library's launches
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(args.steps):
-        step()
+    for _ in range(args.steps):
+        prob.forward()
+        prob.backward()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    prof = rl.rnnt_profile_stop()
     ms = ev0.elapsed_time(ev1) / args.steps
     peak = torch.cuda.max_memory_allocated()
     print(f"# timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.2f} s)", file=sys.stderr, flush=True)
+
+    # timed pass 2 (the breakdown): the same K steps with every launch bracketed by a hipEvent
+    # pair on its stream (the library's launch timing), and the forward and backward separately
+    rl.rnnt_profile_start()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        e[0].record(stream)
+        prob.forward()
+        e[1].record(stream)
+        prob.backward()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    prof = rl.rnnt_profile_stop()
+    t_fwd = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    t_bwd = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    print(f"# profiled pass: fwd {t_fwd:.3f} + bwd {t_bwd:.3f} ms/step", file=sys.stderr, flush=True)
 
     flops = mfma_flops(inp)
     dtype = inp.dtype
@@ -332,12 +422,9 @@ def main():
     roof = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
             "frac": ach / PEAK_TFLOPS[dtype], "traffic": measured_traffic(dom, w.name),
             "per_launch": (f"{FLOP_FORMULA.get(dom, '2*H*V*valid_cells')} / launches = "
-                           f"{flops[dom] / max(1, dk['launches']):.4g} FLOP")}
-
-    cpu = None
-    if args.cpu_seconds > 0:
-        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(inp, args.cpu_seconds)
+                           f"{flops[dom] / max(1, dk['launches']):.4g} FLOP"),
+            "launch_ms": dk["ms_per_step"] / max(1, dk["launches"]),
+            "timing": "mean launch duration from hipEvent pairs on the launch stream over the profiled pass"}
 
     d = inp.dims
     value = inp.padded_cells / (ms * 1e-3)
@@ -362,6 +449,9 @@ def main():
         "input_bytes": int(input_bytes),
         "peak_hbm_minus_inputs_bytes": int(peak - input_bytes),
         "valid_cells_per_s": inp.valid_cells / (ms * 1e-3),
+        "t_fwd_ms": t_fwd,
+        "t_bwd_ms": t_bwd,
+        "ms_per_step_profiled": t_fwd + t_bwd,
         "config": {"workload": w.name, "B": d["B"], "T": d["T"], "U": d["U"],
                    "V": d["V"], "HA": d["HA"], "HL": d["HL"], "H": d["H"], "mode": args.mode,
                    "tile": list(tile), "tiles_per_wave": args.tiles_per_wave,
@@ -387,9 +477,9 @@ def unfused_line(torch, rl, inp, prob, name, ms, peak, args):
     del prob, grads, costs_f
     torch.cuda.empty_cache()
     print("# unfused comparator", file=sys.stderr, flush=True)
-    ms_u, peak_u, cu, dWO_u, dhA_u = unfused_baseline(torch, rl, inp, args.steps, max(1, args.warmup))
-    got = {"costs": cu.cpu().numpy().astype(np.float64), "dWO": dWO_u.cpu().numpy().astype(np.float64),
-           "dhA": dhA_u.cpu().numpy().astype(np.float64)}
+    ms_u, peak_u, cu, gu = unfused_baseline(torch, rl, inp, args.steps, max(1, args.warmup))
+    got = {"costs": cu.cpu().numpy().astype(np.float64), "dWO": gu["dWO"].cpu().numpy().astype(np.float64),
+           "dhA": gu["dhA"].cpu().numpy().astype(np.float64)}
     agree = {"costs_max_rel": float(np.max(np.abs(got["costs"] - ref["costs"]) / np.abs(ref["costs"])))}
     for k in ("dWO", "dhA"):
         agree[f"{k}_err_of_max_abs"] = float(np.max(np.abs(got[k] - ref[k])) / np.max(np.abs(ref[k])))

@@ -19,12 +19,13 @@ def test_bench_refuses_more_than_one_gpu():
 
 
 def test_cpu_baseline_record():
-    """One sample of a small batch through the oracle: the record carries the fields the bench line
-    reports, and the rate is the sample's time extrapolated to the batch's padded cells."""
-    inp = make_inputs(3, 12, 4, 40, 8, 8, 8, dtype="bf16", seed=5, t_range=(6, 12), u_range=(1, 4))
-    rec = bench.cpu_baseline(inp, 0.0)  # budget 0: exactly one sample, the smallest
-    assert set(rec) == {"value", "unit", "cores", "kind", "sample"}
+    """A small batch through the oracle pool (two worker processes, budget 0: each worker's first
+    sample only): the record carries the fields the bench line reports, and the rate is the
+    completed samples' valid cells over the wall time, with the padded numerator."""
+    inp = make_inputs(5, 12, 4, 40, 8, 8, 8, dtype="bf16", seed=5, t_range=(6, 12), u_range=(1, 4))
+    rec = bench.cpu_baseline(inp, 0.0, workers=2)
+    assert {"value", "unit", "cores", "kind", "sample"} <= set(rec)
     assert rec["kind"] == "oracle" and rec["unit"] == "cells/s"
-    assert rec["cores"] >= 1 and np.isfinite(rec["value"]) and rec["value"] > 0
-    smallest = int(np.argmin(inp.T_len * (inp.U_len + 1)))
-    assert f"[{smallest}]" in rec["sample"]
+    assert rec["cores"] == 2 and np.isfinite(rec["value"]) and rec["value"] > 0
+    assert "2 processes" in rec["sample"] and "2 of the batch's 5 samples" in rec["sample"]
+    assert abs(rec["value"] / rec["valid_cells_per_s"] - inp.padded_cells / inp.valid_cells) < 1e-9
