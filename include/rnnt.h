@@ -142,6 +142,28 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
                           void* saved, size_t saved_bytes, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Bytes of the static device array rnnt_loss_fwd_noalloc uses as its workspace. */
+#define RNNT_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * (code under stream capture, tight serving or evaluation loops, harnesses
+ * that forbid allocation). Same arguments, results and `saved` contents as
+ * rnnt_loss_fwd, without the workspace: the forward's working buffers live
+ * in a static device array of RNNT_NOALLOC_SCRATCH_BYTES (256 MiB) that the
+ * library holds on each GPU it runs on until the process ends. It calls no
+ * device or pinned-host allocation: the tile plan is copied from pageable
+ * host memory (so the call may wait for that copy to be staged). Every call
+ * on one GPU shares that GPU's array, so calls that overlap on one GPU (two
+ * streams, two threads) race and must be serialized by the caller. The
+ * forward's workspace need grows with tiles_per_wave x tile area; a request
+ * that needs more than the array returns RNNT_E_WORKSPACE before launching
+ * anything (a smaller tiles_per_wave fits). fp32 mode needs no workspace. */
+rnnt_status rnnt_loss_fwd_noalloc(const rnnt_desc* desc, const void* hA, const void* hL,
+                                  const int32_t* labels, const int32_t* T_len_host,
+                                  const int32_t* U_len_host, const void* WA, const void* WL,
+                                  const void* bZ, const void* WO, const void* bO, float* costs,
+                                  void* saved, size_t saved_bytes, void* stream);
+
 /* Backward: gradients of L = sum_b dcosts[b] * cost_b (dcosts fp32 [B] on the
  * device; NULL means all ones, i.e. L = sum of costs) with respect to every
  * input: dhA [B,T,HA], dhL [B,U+1,HL], dWA [H,HA], dWL [H,HL], dbZ [H],

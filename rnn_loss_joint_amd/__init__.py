@@ -38,8 +38,10 @@ class RnntDesc(ctypes.Structure):
         "tiles_per_wave", "reserved")]
 
 
-EXPORTS = ("rnnt_loss_query", "rnnt_waves_for_budget", "rnnt_loss_fwd", "rnnt_loss_bwd", "rnnt_lattice", "rnnt_profile_start",
-           "rnnt_profile_stop", "rnnt_profile_get", "rnnt_status_string", "rnnt_last_error")
+EXPORTS = ("rnnt_loss_query", "rnnt_waves_for_budget", "rnnt_loss_fwd", "rnnt_loss_fwd_noalloc", "rnnt_loss_bwd",
+           "rnnt_lattice", "rnnt_profile_start", "rnnt_profile_stop", "rnnt_profile_get", "rnnt_status_string",
+           "rnnt_last_error")
+NOALLOC_SCRATCH_BYTES = 256 << 20  # RNNT_NOALLOC_SCRATCH_BYTES
 
 
 def load(path: str = LIB_PATH):
@@ -54,11 +56,13 @@ def load(path: str = LIB_PATH):
     DP = ctypes.POINTER(RnntDesc)
     lib.rnnt_loss_query.argtypes = [DP, I32P, I32P, SZP, SZP]
     lib.rnnt_loss_fwd.argtypes = [DP, P, P, P, I32P, I32P, P, P, P, P, P, P, P, SZ, P, SZ, P]
+    lib.rnnt_loss_fwd_noalloc.argtypes = [DP, P, P, P, I32P, I32P, P, P, P, P, P, P, P, SZ, P]
     lib.rnnt_loss_bwd.argtypes = [DP, P, P, P, I32P, I32P, P, P, P, P, P, P, P, SZ, P, SZ,
                                   P, P, P, P, P, P, P, P]
     lib.rnnt_lattice.argtypes = [DP, P, P, P, P, P, P, P, P]
     lib.rnnt_waves_for_budget.argtypes = [DP, I32P, I32P, SZ, I32P]
-    for f in ("rnnt_loss_query", "rnnt_waves_for_budget", "rnnt_loss_fwd", "rnnt_loss_bwd", "rnnt_lattice"):
+    for f in ("rnnt_loss_query", "rnnt_waves_for_budget", "rnnt_loss_fwd", "rnnt_loss_fwd_noalloc", "rnnt_loss_bwd",
+              "rnnt_lattice"):
         getattr(lib, f).restype = ctypes.c_int
     lib.rnnt_profile_start.argtypes = []
     lib.rnnt_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_int32)]
@@ -141,6 +145,16 @@ def rnnt_loss_fwd(desc, hA, hL, labels, T_len, U_len, WA, WL, bZ, WO, bO, costs,
                              saved.numel() * saved.element_size(), _ptr(workspace),
                              0 if workspace is None else workspace.numel() * workspace.element_size(),
                              _stream(stream)))
+
+
+def rnnt_loss_fwd_noalloc(desc, hA, hL, labels, T_len, U_len, WA, WL, bZ, WO, bO, costs, saved, stream=None):
+    """rnnt_loss_fwd with the library's static scratch array as its workspace (no allocation)."""
+    lib = load()
+    T_len, tp = _lens(T_len)
+    U_len, up = _lens(U_len)
+    _check(lib.rnnt_loss_fwd_noalloc(ctypes.byref(desc), _ptr(hA), _ptr(hL), _ptr(labels), tp, up, _ptr(WA),
+                                     _ptr(WL), _ptr(bZ), _ptr(WO), _ptr(bO), _ptr(costs), _ptr(saved),
+                                     saved.numel() * saved.element_size(), _stream(stream)))
 
 
 def rnnt_loss_bwd(desc, hA, hL, labels, T_len, U_len, WA, WL, bZ, WO, bO, dcosts, saved, workspace,

@@ -232,6 +232,38 @@ inline int rows_per_chunk(bool bf16) { return bf16 ? 32 : 16; }
 
 }  // namespace
 
+// Workspace of rnnt_loss_fwd_noalloc: a static device array, one per GPU the
+// library runs on, held until the process ends. Host code never uses its
+// name as an address: the per-device address comes from hipGetSymbolAddress.
+static constexpr size_t kScratchBytes = RNNT_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+struct ScratchAddrs {
+  std::mutex mu;
+  std::vector<void*> ptr;  // by device id
+};
+ScratchAddrs g_scratch;
+
+// The current device's copy of `scratch`, looked up once per device.
+rnnt_status scratch_for_current_device(void** out) {
+  int dev = 0;
+  RNNT_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_scratch.mu);
+  if ((int)g_scratch.ptr.size() <= dev) g_scratch.ptr.resize(dev + 1, nullptr);
+  if (!g_scratch.ptr[dev]) {
+    void* p = nullptr;
+    RNNT_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(RNNT_E_HIP, "hipGetSymbolAddress returned a null address for the scratch array");
+    g_scratch.ptr[dev] = p;
+  }
+  *out = g_scratch.ptr[dev];
+  return RNNT_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* rnnt_status_string(rnnt_status s) {
@@ -291,28 +323,45 @@ rnnt_status rnnt_waves_for_budget(const rnnt_desc* desc, const int32_t* T_len_ho
   return RNNT_OK;
 }
 
-rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL, const int32_t* labels,
-                          const int32_t* T_len_host, const int32_t* U_len_host, const void* WA,
-                          const void* WL, const void* bZ, const void* WO, const void* bO, float* costs,
-                          void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
-                          void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+// The forward pass. scratch_mode: the workspace is the static scratch array
+// (rnnt_loss_fwd_noalloc): its regions follow the forward-only layout and
+// the plan is copied from pageable memory, so nothing is allocated.
+static rnnt_status forward_impl(const rnnt_desc* desc, const void* hA, const void* hL, const int32_t* labels,
+                                const int32_t* T_len_host, const int32_t* U_len_host, const void* WA,
+                                const void* WL, const void* bZ, const void* WO, const void* bO, float* costs,
+                                void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                                void* stream, bool scratch_mode) {
   rnnt::Plan p;
   rnnt::Layout L;
   rnnt_status s = prepare(desc, T_len_host, U_len_host, p, L);
   if (s != RNNT_OK) return s;
+  if (scratch_mode) L = rnnt::make_forward_layout(p);  // same saved layout, packed forward workspace
   if (!hA || !hL || !labels || !WA || !WL || !bZ || !WO || !bO || !costs || !saved)
     return fail(RNNT_E_INVALID, "null input, output or saved pointer");
   if (saved_bytes < L.saved_bytes) return fail(RNNT_E_WORKSPACE, "saved buffer smaller than rnnt_loss_query");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool bf = p.d.bf16;
   const rnnt::Dims& d = p.d;
+  if (bf) {
+    if (!workspace) return fail(RNNT_E_INVALID, "bf16 mode needs the workspace in the forward");
+    if (workspace_bytes < L.workspace_bytes) {
+      if (scratch_mode)
+        return fail(RNNT_E_WORKSPACE, "the forward needs " + std::to_string(L.workspace_bytes) +
+                                          " bytes of scratch, more than the " + std::to_string(workspace_bytes) +
+                                          " of rnnt_loss_fwd_noalloc (fewer tiles per wave need less)");
+      return fail(RNNT_E_WORKSPACE, "workspace buffer smaller than rnnt_loss_query");
+    }
+  }
 
   std::vector<char> host_plan;
   rnnt::serialize_plan(p, L, T_len_host, U_len_host, host_plan);
-  s = upload(saved, host_plan, st);
-  if (s != RNNT_OK) return s;
+  if (scratch_mode) {
+    // pageable source: the runtime has consumed it when the call returns
+    RNNT_HIP(hipMemcpyAsync(saved, host_plan.data(), host_plan.size(), hipMemcpyHostToDevice, st));
+  } else {
+    s = upload(saved, host_plan, st);
+    if (s != RNNT_OK) return s;
+  }
   Saved sv = saved_view(saved, L);
   {
     ProfScope ps_("labels_check", st);
@@ -387,9 +436,6 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
   if (bf) {
     // bf16: per wave of tiles, z rows (and the blank / label scores), then
     // 256 x 256 score tiles with per-tile (max, sum), then the merge
-    if (!workspace) return fail(RNNT_E_INVALID, "bf16 mode needs the workspace in the forward");
-    if (workspace_bytes < L.workspace_bytes)
-      return fail(RNNT_E_WORKSPACE, "workspace buffer smaller than rnnt_loss_query");
     void* zbuf = d.untiled ? sv.z : at<char>(workspace, L.w_z);
     auto* stats = at<rnnt::f32x2>(workspace, L.w_stats);
     float* hb = at<float>(workspace, L.w_hb);
@@ -526,6 +572,26 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
     }
   }
   return RNNT_OK;
+}
+
+rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL, const int32_t* labels,
+                          const int32_t* T_len_host, const int32_t* U_len_host, const void* WA,
+                          const void* WL, const void* bZ, const void* WO, const void* bO, float* costs,
+                          void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return forward_impl(desc, hA, hL, labels, T_len_host, U_len_host, WA, WL, bZ, WO, bO, costs, saved, saved_bytes,
+                      workspace, workspace_bytes, stream, false);
+}
+
+rnnt_status rnnt_loss_fwd_noalloc(const rnnt_desc* desc, const void* hA, const void* hL, const int32_t* labels,
+                                  const int32_t* T_len_host, const int32_t* U_len_host, const void* WA,
+                                  const void* WL, const void* bZ, const void* WO, const void* bO, float* costs,
+                                  void* saved, size_t saved_bytes, void* stream) {
+  void* ws = nullptr;
+  const rnnt_status s = scratch_for_current_device(&ws);
+  if (s != RNNT_OK) return s;
+  return forward_impl(desc, hA, hL, labels, T_len_host, U_len_host, WA, WL, bZ, WO, bO, costs, saved, saved_bytes,
+                      ws, kScratchBytes, stream, true);
 }
 
 rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL, const int32_t* labels,

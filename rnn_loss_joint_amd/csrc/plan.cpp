@@ -321,6 +321,34 @@ Layout make_layout(const Plan& p) {
   return L;
 }
 
+Layout make_forward_layout(const Plan& p) {
+  const Dims& d = p.d;
+  Layout L = make_layout(p);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  const size_t wrows = (size_t)cdiv(p.max_wave_rows, 128) * 128;
+  const size_t frows = d.untiled ? (size_t)p.total_rows : wrows;
+  L.w_dh = L.w_gA = L.w_gL = L.w_PA = L.w_PL = L.w_PW = L.w_PB = L.w_PWA = L.w_PBZ = L.w_PWL = L.w_WOT = 0;
+  L.w_coefA = L.w_coefB = L.w_gb = L.w_hs = L.w_WAT = L.w_WLT = 0;
+  L.w_z = L.w_stats = L.w_hb = L.w_hy = L.w_WOp = L.w_bl = 0;
+  if (d.bf16) {
+    if (!d.untiled) L.w_z = take(2 * wrows * p.H_pad);
+    L.w_stats = take(8 * frows * p.nvt);
+    L.w_hb = take(4 * frows);
+    L.w_hy = take(4 * frows);
+    if (!d.untiled) {
+      L.w_WOp = take(2 * (size_t)p.nvt * 256 * p.H_pad);
+      L.w_bl = take(4 * (size_t)p.nvt * 256);
+    }
+  }
+  L.workspace_bytes = o;
+  return L;
+}
+
 void serialize_plan(const Plan& p, const Layout& L, const int32_t* T_len, const int32_t* U_len,
                     std::vector<char>& out) {
   out.assign(L.plan_bytes, 0);

@@ -84,6 +84,11 @@ void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H
 // Checks a built plan against the library's 32-bit row limits (kMaxPlanRows).
 bool check_plan(const Plan& p, std::string& err);
 Layout make_layout(const Plan& p);
+// The same layout with only the forward pass's workspace regions (z rows,
+// V-tile statistics, blank / label scores, padded W^O and bias table) packed
+// from offset 0; workspace_bytes is then the forward's need alone. The other
+// workspace offsets are not valid in it.
+Layout make_forward_layout(const Plan& p);
 // Serializes lengths, tiles, groups and gidx in layout order into out
 // (plan_bytes bytes, offsets relative to the start of `saved`).
 void serialize_plan(const Plan& p, const Layout& L, const int32_t* T_len, const int32_t* U_len,
