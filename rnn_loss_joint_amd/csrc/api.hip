@@ -163,6 +163,7 @@ template <class T> const T* at(const void* base, size_t off) {
 struct Saved {
   int32_t* status;
   int32_t* labels;  // the range-checked labels every kernel reads
+  const int64_t* lat_off;  // packed lattice blocks
   const int32_t* Tlen;
   const int32_t* Ulen;
   const rnnt::Tile* tiles;
@@ -178,6 +179,7 @@ Saved saved_view(void* s, const rnnt::Layout& L) {
   Saved v;
   v.status = at<int32_t>(s, L.off_status);
   v.labels = at<int32_t>(s, L.off_labels);
+  v.lat_off = at<int64_t>(s, L.off_latoff);
   v.Tlen = at<int32_t>(s, L.off_Tlen);
   v.Ulen = at<int32_t>(s, L.off_Ulen);
   v.tiles = at<rnnt::Tile>(s, L.off_tiles);
@@ -205,6 +207,7 @@ rnnt::JointArgs joint_args(const rnnt::Plan& p, const Saved& sv, const void* WO,
   a.T_len = sv.Tlen;
   a.U_len = sv.Ulen;
   a.labels = sv.labels;
+  a.lat_off = sv.lat_off;
   a.T = p.d.T;
   a.U1 = p.U1;
   a.V = p.d.V;
@@ -523,6 +526,7 @@ static rnnt_status forward_impl(const rnnt_desc* desc, const void* hA, const voi
       mg.buf_row_base = wv.row_begin;
       mg.nvt = p.nvt;
       mg.U_len = sv.Ulen;
+      mg.lat_off = sv.lat_off;
       mg.T = d.T;
       mg.U1 = p.U1;
       mg.stats = stats;
@@ -558,6 +562,7 @@ static rnnt_status forward_impl(const rnnt_desc* desc, const void* hA, const voi
   // 3. lattice
   {
     rnnt::LatticeArgs la{sv.Tlen, sv.Ulen, sv.phi, sv.psi, sv.alpha, sv.beta, sv.lnP, costs, d.B, d.T, p.U1};
+    la.lat_off = sv.lat_off;
     ProfScope ps_("lattice", st);
     if (L.lat64) {
       // fp32 mode: the fp64 arrays share the fp32 ones' memory, so the fp32
@@ -667,6 +672,7 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       a.T_len = sv.Tlen;
       a.U_len = sv.Ulen;
       a.labels = sv.labels;
+      a.lat_off = sv.lat_off;
       a.T = d.T;
       a.U1 = p.U1;
       a.V = d.V;
@@ -727,6 +733,7 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
       sc.T_len = sv.Tlen;
       sc.U_len = sv.Ulen;
       sc.labels = sv.labels;
+      sc.lat_off = sv.lat_off;
       sc.T = d.T;
       sc.U1 = p.U1;
       sc.V = d.V;
@@ -756,6 +763,7 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
         a3.T_len = sv.Tlen;
         a3.U_len = sv.Ulen;
         a3.labels = sv.labels;
+        a3.lat_off = sv.lat_off;
         a3.T = d.T;
         a3.U1 = p.U1;
         a3.V = d.V;

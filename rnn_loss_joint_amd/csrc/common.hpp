@@ -42,6 +42,12 @@ struct Group {
   int32_t b, start, len, first, count, pad0, pad1, pad2;
 };
 
+// Sample b's block in the packed lattice arrays of `saved` (lat_off: the
+// block offsets, U_len: the label counts, both in `saved`).
+__device__ inline LatGeo lat_geo(const int64_t* lat_off, const int32_t* U_len, int b) {
+  return lat_geo_packed(lat_off[b], U_len[b]);
+}
+
 // ---------------------------------------------------------------- MFMA conventions
 // Both operand fragments are 16 bytes per lane. A lane holds row (A) or column
 // (B) `lane % ROWS` of a ROWS x ROWS output block and k-elements

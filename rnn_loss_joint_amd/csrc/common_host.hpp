@@ -32,4 +32,22 @@ constexpr int64_t lat_ix(int b, int t, int u, int T, int U1) {
   return (((int64_t)b * lat_nq(T, U1) + ((t + u) >> 2)) * lat_us(U1) + u) * 4 + ((t + u) & 3);
 }
 
+// That layout with every sample's block cut to its own lattice ("packed", the
+// layout inside `saved`): sample b's block holds lat_nq(T_b, U_b + 1) groups
+// of lat_us(U_b + 1) rows and starts at entry off[b], the prefix sum of the
+// blocks before it, so padding frames and padding labels take no space.
+// The padded layout above is the packed one with every sample at T_b = T,
+// U_b = U. A block is a multiple of 4 entries, so every block stays 16-byte
+// aligned.
+struct LatGeo {
+  int64_t base;  // first entry of the sample's block
+  int us;        // rows per group of four diagonals
+};
+constexpr int64_t lat_block(int Tb, int Ub) { return lat_sample(Tb, Ub + 1); }
+constexpr LatGeo lat_geo_padded(int b, int T, int U1) { return LatGeo{(int64_t)b * lat_sample(T, U1), lat_us(U1)}; }
+constexpr LatGeo lat_geo_packed(int64_t base, int Ub) { return LatGeo{base, lat_us(Ub + 1)}; }
+constexpr int64_t lat_at(const LatGeo& g, int t, int u) {
+  return g.base + ((int64_t)((t + u) >> 2) * g.us + u) * 4 + ((t + u) & 3);
+}
+
 }  // namespace rnnt

@@ -73,16 +73,16 @@ __device__ inline void store_wo_stage(const StageRegs<M>& r, char* buf, int tid)
 // beta(t, u+1) - ln P) (zero past the last label). R is the storage type of
 // alpha, beta and ln P; the exponents are formed in R and rounded once.
 template <typename R>
-__device__ inline void cell_weights(const R* al, const R* be, R lp, const float* phi, const float* psi, int b,
-                                    int t, int u, int T, int U1, int Tb, int Ub, float g, float& occ, float& cb,
+__device__ inline void cell_weights(const R* al, const R* be, R lp, const float* phi, const float* psi,
+                                    const LatGeo& geo, int t, int u, int Tb, int Ub, float g, float& occ, float& cb,
                                     float& cl) {
-  const int64_t idx = lat_ix(b, t, u, T, U1);
+  const int64_t idx = lat_at(geo, t, u);
   const R A = al[idx];
-  const R bn = (t + 1 < Tb) ? be[lat_ix(b, t + 1, u, T, U1)] : (u == Ub ? R(0) : R(kNegInf));
+  const R bn = (t + 1 < Tb) ? be[lat_at(geo, t + 1, u)] : (u == Ub ? R(0) : R(kNegInf));
   occ = g * fexp2((float)(A + be[idx] - lp) * kLog2e);
   cb = g * fexp2((float)(A + (R)phi[idx] + bn - lp) * kLog2e);
   cl = 0.0f;
-  if (u < Ub) cl = g * fexp2((float)(A + (R)psi[idx] + be[lat_ix(b, t, u + 1, T, U1)] - lp) * kLog2e);
+  if (u < Ub) cl = g * fexp2((float)(A + (R)psi[idx] + be[lat_at(geo, t, u + 1)] - lp) * kLog2e);
 }
 
 __device__ inline int find_tile_by_row(const Tile* tiles, int lo, int hi, int R0) {
@@ -210,14 +210,15 @@ joint_kernel(JointArgs p) {
   if (BWD) {
     if (g == 0) {
       if (row_ok) {
-        size_t idx = (size_t)lat_ix(b, t_r, u, T, U1);
+        const LatGeo geo = lat_geo(p.lat_off, p.U_len, b);
+        size_t idx = (size_t)lat_at(geo, t_r, u);
         float gb = p.dcosts ? p.dcosts[b] : 1.0f;
         my_lse = p.lse[idx];
         if (p.alpha64)
-          cell_weights<double>(p.alpha64, p.beta64, p.lnP64[b], p.phi, p.psi, b, t_r, u, T, U1, Tb, Ub, gb, my_occ,
+          cell_weights<double>(p.alpha64, p.beta64, p.lnP64[b], p.phi, p.psi, geo, t_r, u, Tb, Ub, gb, my_occ,
                                my_cb, my_cl);
         else
-          cell_weights<float>(p.alpha, p.beta, p.lnP[b], p.phi, p.psi, b, t_r, u, T, U1, Tb, Ub, gb, my_occ, my_cb,
+          cell_weights<float>(p.alpha, p.beta, p.lnP[b], p.phi, p.psi, geo, t_r, u, Tb, Ub, gb, my_occ, my_cb,
                               my_cl);
       }
       row_lds[wave][0][r] = my_lse;
@@ -366,7 +367,7 @@ joint_kernel(JointArgs p) {
     __syncthreads();
     if (row_ok && g == 0) {
       float ls = row_lds[wave][0][r];
-      size_t idx = (size_t)lat_ix(b, t_r, u, T, U1);
+      size_t idx = (size_t)lat_at(lat_geo(p.lat_off, p.U_len, b), t_r, u);
       p.lse_out[idx] = ls;
       p.phi_out[idx] = hb - ls;
       p.psi_out[idx] = (u < Ub) ? hy - ls : kNegInf;
@@ -409,13 +410,14 @@ __global__ void __launch_bounds__(256) dh_inplace_kernel(DhInplaceArgs p) {
     float ls = 0, co = 0, cb = 0, cl = 0;
     float lab = -1;
     if (valid) {
-      size_t idx = (size_t)lat_ix(b, t, u, T, U1);
+      const LatGeo geo = lat_geo(p.lat_off, p.U_len, b);
+      size_t idx = (size_t)lat_at(geo, t, u);
       float gb = p.dcosts ? p.dcosts[b] : 1.0f;
       ls = p.lse[idx];
       if (p.alpha64)
-        cell_weights<double>(p.alpha64, p.beta64, p.lnP64[b], p.phi, p.psi, b, t, u, T, U1, Tb, Ub, gb, co, cb, cl);
+        cell_weights<double>(p.alpha64, p.beta64, p.lnP64[b], p.phi, p.psi, geo, t, u, Tb, Ub, gb, co, cb, cl);
       else
-        cell_weights<float>(p.alpha, p.beta, p.lnP[b], p.phi, p.psi, b, t, u, T, U1, Tb, Ub, gb, co, cb, cl);
+        cell_weights<float>(p.alpha, p.beta, p.lnP[b], p.phi, p.psi, geo, t, u, Tb, Ub, gb, co, cb, cl);
       if (u < Ub) lab = (float)p.labels[(size_t)b * U1 + u + 1];
     }
     coef[wave][0] = ls * kLog2e;

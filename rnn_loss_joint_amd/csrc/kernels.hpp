@@ -17,12 +17,13 @@ struct JointArgs {
   const int32_t* T_len;
   const int32_t* U_len;
   const int32_t* labels;  // [B, U1]
+  const int64_t* lat_off;  // packed lattice blocks (lat_geo)
   int T, U1, V, H, H_pad, V_pad, blank;
   const float* a;  // [B*T, H_pad]  W^A h^A + b^Z
   const float* l;  // [B*U1, H_pad] W^L h^L
   const void* WO;  // [V, H]
   const void* bO;  // [V]
-  // forward outputs, lattice layout (lat_ix)
+  // forward outputs, packed lattice layout
   float* lse_out;
   float* phi_out;
   float* psi_out;
@@ -52,6 +53,7 @@ struct DhInplaceArgs {
   const int32_t* T_len;
   const int32_t* U_len;
   const int32_t* labels;
+  const int64_t* lat_off;  // packed lattice blocks
   int T, U1, V, V_pad, blank;
   void* logits;
   int buf_row_base;
@@ -81,7 +83,7 @@ hipError_t launch_dh_inplace(const DhInplaceArgs& a, bool bf16_mode, hipStream_t
 struct LatticeArgs {
   const int32_t* T_len;
   const int32_t* U_len;
-  const float* phi;  // lattice layout (lat_ix)
+  const float* phi;  // packed layout (lat_off non-null) or padded layout (lat_ix)
   const float* psi;
   float* alpha;
   float* beta;
@@ -89,6 +91,7 @@ struct LatticeArgs {
   float* costs; // [B] (may be null)
   int B, T, U1;
   double* alpha64;  // fp64 sweep only: alpha, beta (lattice layout) and ln P [B]
+  const int64_t* lat_off;  // packed blocks [B] (saved); null: the padded layout
   double* beta64;
   double* lnP64;
 };
@@ -234,6 +237,7 @@ struct ScoresArgs {  // scores^T tiles: forward statistics or backward dh
   const int32_t* T_len;
   const int32_t* U_len;
   const int32_t* labels;
+  const int64_t* lat_off;
   int T, U1, V, H, V_pad, blank;
   const void* WO;
   const void* bO;
@@ -261,6 +265,7 @@ struct Scores3Args {
   const int32_t* T_len;
   const int32_t* U_len;
   const int32_t* labels;
+  const int64_t* lat_off;
   int T, U1, V, H_pad, V_pad, nvt, blank;
   const void* WOp;   // [nvt*256][H_pad] bf16, zero-padded W^O
   const float* bl;   // [nvt*256] b^O log2 e, -1e30 past V
@@ -289,6 +294,7 @@ struct MergeArgs {
   const Tile* tiles;
   int tile_begin, tile_end, n_rows, buf_row_base, nvt;
   const int32_t* U_len;
+  const int64_t* lat_off;
   int T, U1;
   const f32x2* stats;
   const float* hb;

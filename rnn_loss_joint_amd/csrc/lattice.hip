@@ -10,9 +10,10 @@
 // Every cell of anti-diagonal d = t + u depends only on diagonal d - 1
 // (alpha) or d + 1 (beta), so the sweep runs over diagonals with one lattice
 // row u per lane. The arrays hold four consecutive diagonals of a row as one
-// aligned 16-byte piece (lat_ix), so a lane reads its operands and writes its
-// results for four diagonals with one 16-byte buffer access, and a wave's
-// 64 pieces are one contiguous kilobyte.
+// aligned 16-byte piece (lat_at: the packed layout of `saved`, or the padded
+// layout lat_ix of the rnnt_lattice entry point), so a lane reads its operands
+// and writes its results for four diagonals with one 16-byte buffer access,
+// and a wave's 64 pieces are one contiguous kilobyte.
 //
 // A workgroup of NW waves serves one (sample, direction); wave w owns rows
 // u = 64 w + lane. The sweep is cut into windows whose loads and stores are
@@ -113,9 +114,11 @@ __device__ __attribute__((always_inline)) inline void lattice_body(const Lattice
   const int lane = threadIdx.x & 63;
   const int u = 64 * wave + lane;
   const int Tb = p.T_len[b], Ub = p.U_len[b];
-  const int US = lat_us(p.U1);
-  const size_t base0 = (size_t)b * lat_sample(p.T, p.U1);
-  const unsigned blk = (unsigned)lat_sample(p.T, p.U1) * 4u;
+  // the sample's block: packed (inside saved) or padded (the rnnt_lattice layout)
+  const LatGeo geo = p.lat_off ? lat_geo_packed(p.lat_off[b], Ub) : lat_geo_padded(b, p.T, p.U1);
+  const int US = geo.us;
+  const size_t base0 = (size_t)geo.base;
+  const unsigned blk = (unsigned)(p.lat_off ? lat_block(Tb, Ub) : lat_sample(p.T, p.U1)) * 4u;
   const float* phi = p.phi + base0;
   const auto rphi = sample_rsrc(phi, blk);
   const auto rpsi = sample_rsrc(p.psi + base0, blk);
@@ -282,7 +285,7 @@ __device__ __attribute__((always_inline)) inline void lattice_body(const Lattice
     for (int j = 0; j <= PF; ++j) step(s + j, rp[(j + 1) % (PF + 1)], rs[(j + 1) % (PF + 1)], rp[j], rs[j]);
   }
   if (!is_beta && u == Ub) {
-    const float v = lnP2 * kLn2 + phi[lat_ix(0, Tb - 1, Ub, p.T, p.U1)];
+    const float v = lnP2 * kLn2 + phi[lat_at(LatGeo{0, US}, Tb - 1, Ub)];
     if (p.lnP) p.lnP[b] = v;
     if (p.costs) p.costs[b] = -v;
   }
@@ -330,7 +333,7 @@ __global__ void __launch_bounds__(256) lattice64_kernel(LatticeArgs p) {
   const int b = blockIdx.x;
   const bool is_beta = blockIdx.y != 0;
   const int Tb = p.T_len[b], Ub = p.U_len[b];
-  const int T = p.T, U1 = p.U1;
+  const LatGeo geo = p.lat_off ? lat_geo_packed(p.lat_off[b], Ub) : lat_geo_padded(b, p.T, p.U1);
   double* out = is_beta ? p.beta64 : p.alpha64;
   const int D = Tb - 1 + Ub;  // last anti-diagonal
   for (int k = 0; k <= D; ++k) {
@@ -338,7 +341,7 @@ __global__ void __launch_bounds__(256) lattice64_kernel(LatticeArgs p) {
     for (int u = threadIdx.x; u <= Ub; u += blockDim.x) {
       const int t = dg - u;
       if (t < 0 || t >= Tb) continue;
-      const int64_t ix = lat_ix(b, t, u, T, U1);
+      const int64_t ix = lat_at(geo, t, u);
       double v;
       if (!is_beta) {
         if (t == 0 && u == 0) {
@@ -346,11 +349,11 @@ __global__ void __launch_bounds__(256) lattice64_kernel(LatticeArgs p) {
         } else {
           double x = -INFINITY, y = -INFINITY;
           if (t > 0) {
-            const int64_t j = lat_ix(b, t - 1, u, T, U1);
+            const int64_t j = lat_at(geo, t - 1, u);
             x = out[j] + (double)p.phi[j];
           }
           if (u > 0) {
-            const int64_t j = lat_ix(b, t, u - 1, T, U1);
+            const int64_t j = lat_at(geo, t, u - 1);
             y = out[j] + (double)p.psi[j];
           }
           v = lae64(x, y);
@@ -361,8 +364,8 @@ __global__ void __launch_bounds__(256) lattice64_kernel(LatticeArgs p) {
           v = ph;
         } else {
           double x = -INFINITY, y = -INFINITY;
-          if (t + 1 < Tb) x = ph + out[lat_ix(b, t + 1, u, T, U1)];
-          if (u < Ub) y = (double)p.psi[ix] + out[lat_ix(b, t, u + 1, T, U1)];
+          if (t + 1 < Tb) x = ph + out[lat_at(geo, t + 1, u)];
+          if (u < Ub) y = (double)p.psi[ix] + out[lat_at(geo, t, u + 1)];
           v = lae64(x, y);
         }
       }
@@ -371,7 +374,7 @@ __global__ void __launch_bounds__(256) lattice64_kernel(LatticeArgs p) {
     __syncthreads();
   }
   if (!is_beta && threadIdx.x == 0) {
-    const int64_t ix = lat_ix(b, Tb - 1, Ub, T, U1);
+    const int64_t ix = lat_at(geo, Tb - 1, Ub);
     const double v = out[ix] + (double)p.phi[ix];
     p.lnP64[b] = v;
     if (p.lnP) p.lnP[b] = (float)v;

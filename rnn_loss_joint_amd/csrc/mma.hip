@@ -301,16 +301,17 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoresArgs p) {
       if (tloc < tl.ht) {
         const int b = tl.b, u = tl.u0 + ul, t = tl.t0 + tloc;
         const int Tb = p.T_len[b], Ub = p.U_len[b];
-        const size_t idx = (size_t)lat_ix(b, t, u, p.T, p.U1);
+        const LatGeo geo = lat_geo(p.lat_off, p.U_len, b);
+        const size_t idx = (size_t)lat_at(geo, t, u);
         const float lp = p.lnP[b];
         const float gb = p.dcosts ? p.dcosts[b] : 1.0f;
         const float A = p.alpha[idx], Bt = p.beta[idx];
         ls = p.lse[idx];
-        const float bn = (t + 1 < Tb) ? p.beta[lat_ix(b, t + 1, u, p.T, p.U1)] : (u == Ub ? 0.0f : kNegInf);
+        const float bn = (t + 1 < Tb) ? p.beta[lat_at(geo, t + 1, u)] : (u == Ub ? 0.0f : kNegInf);
         co = gb * fexp2((A + Bt - lp) * kLog2e);
         cb = gb * fexp2((A + p.phi[idx] + bn - lp) * kLog2e);
         if (u < Ub) {
-          cl = gb * fexp2((A + p.psi[idx] + p.beta[lat_ix(b, t, u + 1, p.T, p.U1)] - lp) * kLog2e);
+          cl = gb * fexp2((A + p.psi[idx] + p.beta[lat_at(geo, t, u + 1)] - lp) * kLog2e);
           lab = (float)p.labels[(size_t)b * p.U1 + u + 1];
         }
       }
@@ -490,6 +491,7 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(MergeArgs p) {
   if (tb >= tl.ht || ub >= tl.wu) return;
   const int nt = min(kMB, tl.ht - tb), nu = min(kMB, tl.wu - ub);
   const int b = tl.b, Ub = p.U_len[b];
+  const LatGeo geo = lat_geo(p.lat_off, p.U_len, b);
 #pragma unroll
   for (int i = threadIdx.x; i < kMB * kMB; i += 256) {
     const int ul = i / kMB, tt = i % kMB;
@@ -516,7 +518,7 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(MergeArgs p) {
     const int e = i & 3, ul = (i >> 2) % kMB, gq = (i >> 2) / kMB;
     const int tt = 4 * (q0 + gq) + e - T0 - U0 - ul;  // t - T0 of the cell on that diagonal
     if (ul >= nu || tt < 0 || tt >= nt) continue;
-    const size_t idx = (size_t)lat_ix(b, T0 + tt, U0 + ul, p.T, p.U1);
+    const size_t idx = (size_t)lat_at(geo, T0 + tt, U0 + ul);
     p.lse[idx] = sm[0][ul * kMS + tt];
     p.phi[idx] = sm[1][ul * kMS + tt];
     p.psi[idx] = sm[2][ul * kMS + tt];

@@ -139,6 +139,9 @@ void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H
       for (int b = 0; b < d.B; ++b)
         if (k < nt[b] * nu[b]) p.tiles.push_back(make_tile(b, k));
   }
+  // packed lattice blocks: sample b's block is cut to its own T_b x (U_b + 1)
+  p.lat_off.assign(d.B + 1, 0);
+  for (int b = 0; b < d.B; ++b) p.lat_off[b + 1] = p.lat_off[b] + lat_block(T_len[b], U_len[b]);
   int64_t row = 0, strip = 0;
   for (auto& t : p.tiles) {
     t.row0 = (int32_t)row;
@@ -243,9 +246,11 @@ Layout make_layout(const Plan& p) {
   L.off_tiles = take(sizeof(TileH) * p.tiles.size());
   L.off_groups = take(sizeof(GroupH) * p.groups.size());
   L.off_gidx = take(sizeof(int32_t) * p.gidx.size());
+  L.off_latoff = take(sizeof(int64_t) * p.lat_off.size());
   L.plan_bytes = o;
   L.off_labels = take(sizeof(int32_t) * (size_t)d.B * p.U1);
-  const size_t cells = (size_t)lat_cells(d.B, d.T, p.U1);
+  const size_t cells = (size_t)p.lat_off[d.B];
+  L.lat_entries = cells;
   L.off_a = take(sizeof(float) * (size_t)d.B * d.T * p.H_pad);
   L.off_l = take(sizeof(float) * (size_t)d.B * p.U1 * p.H_pad);
   L.off_lse = take(sizeof(float) * cells);
@@ -358,6 +363,7 @@ void serialize_plan(const Plan& p, const Layout& L, const int32_t* T_len, const 
   if (!p.tiles.empty()) std::memcpy(out.data() + L.off_tiles, p.tiles.data(), sizeof(TileH) * p.tiles.size());
   if (!p.groups.empty()) std::memcpy(out.data() + L.off_groups, p.groups.data(), sizeof(GroupH) * p.groups.size());
   if (!p.gidx.empty()) std::memcpy(out.data() + L.off_gidx, p.gidx.data(), sizeof(int32_t) * p.gidx.size());
+  std::memcpy(out.data() + L.off_latoff, p.lat_off.data(), sizeof(int64_t) * p.lat_off.size());
 }
 
 }  // namespace rnnt

@@ -43,6 +43,7 @@ struct Plan {
   std::vector<WaveInfo> waves;
   std::vector<GroupH> groups;
   std::vector<int32_t> gidx;
+  std::vector<int64_t> lat_off;  // [B + 1] packed lattice block offsets (entries)
   int64_t total_rows = 0;
   int max_wave_rows = 0, max_wave_tiles = 0;
   int s6 = 1, s7a = 1, s7l = 1;  // split-K counts
@@ -55,6 +56,8 @@ struct Layout {
   size_t off_status;  // int32 [2]: labels out of range, flat index of the first (-1 if none)
   size_t off_Tlen, off_Ulen, off_tiles, off_groups, off_gidx;
   size_t off_labels;  // int32 [B, U+1]: the labels the kernels read (range-checked copy)
+  size_t off_latoff;  // int64 [B + 1]: packed lattice block offsets (part of the plan copy)
+  size_t lat_entries; // entries of each lattice array (lat_off[B])
   size_t off_a, off_l, off_lse, off_phi, off_psi, off_alpha, off_beta, off_lnP;
   bool lat64;  // alpha, beta, ln P held in fp64 (fp32 mode), else fp32
   size_t off_logits, off_z;  // untiled only; z is stored transposed [H_pad, total_rows]

@@ -454,6 +454,7 @@ __global__ void __launch_bounds__(256) coef_kernel(Scores3Args p) {
   const int nt = min(kCB, tl.ht - tb), nu = min(kCB, tl.wu - ub);
   const int b = tl.b, Tb = p.T_len[b], Ub = p.U_len[b];
   const int t0 = tl.t0 + tb, u0 = tl.u0 + ub;
+  const LatGeo geo = lat_geo(p.lat_off, p.U_len, b);
   // lattice -> LDS for the (33 x 33) region, whose diagonals t0 + u0 ..
   // t0 + u0 + 64 lie in 17 groups from q0 on; all loads of the thread are
   // issued before any is stored (masked slots read entry 0)
@@ -473,7 +474,7 @@ __global__ void __launch_bounds__(256) coef_kernel(Scores3Args p) {
     slot_of(i, ul, tt);
     const bool okb = i < kSlots && tt >= 0 && tt <= kCB && t0 + tt < Tb && u0 + ul <= Ub;
     const bool oka = okb && tt < nt && ul < nu;
-    const size_t idx = okb ? (size_t)lat_ix(b, t0 + tt, u0 + ul, p.T, p.U1) : 0;
+    const size_t idx = okb ? (size_t)lat_at(geo, t0 + tt, u0 + ul) : 0;
     const size_t ia = oka ? idx : 0;
     vb[q] = p.beta[idx];
     va[q] = p.alpha[ia];
