@@ -86,9 +86,14 @@ __device__ inline void buf_st(float v, __amdgpu_buffer_rsrc_t r, unsigned voff, 
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
 }
 
-// x + raw log2 e with the operand made finite or -inf first (NaN and +inf
-// become 1e30), so that a -inf x stays -inf
-__device__ inline float add_operand2(float x, float raw) { return __builtin_fmaf(fminf(raw, 1e30f), kLog2e, x); }
+// x + raw log2 e, with a NaN sum made -inf: an operand outside the lattice
+// (any value, NaN and infinities included) only ever meets x = -inf, and
+// -inf + (NaN, +inf) is NaN; the maximum with -inf returns the other operand
+// unless that is NaN (the sum of an fma is a quiet NaN, so no canonicalizing
+// is needed)
+__device__ inline float add_operand2(float x, float raw) {
+  return __builtin_fmaxf(__builtin_fmaf(raw, kLog2e, x), kNegInf);
+}
 
 // base-2 log-add-exp; a = b = -inf gives NaN, which only occurs on cells the
 // caller masks
@@ -176,7 +181,6 @@ __device__ __attribute__((always_inline)) inline void lattice_body(const Lattice
   // alpha: the result on diagonal wlo(k), computed by the previous window
   // (at first the values on diagonal 0) and stored with window k's groups
   float prev = cur;
-  float lnP2 = cur;  // alpha(T_b-1, U_b) in base 2 (diagonal 0 when D = 0)
 
   // Step s: issue the loads of window s + PF - lag into np / ns, compute
   // window k = s - lag (if this wave has it) from rp / rs, which its loads
@@ -215,6 +219,12 @@ __device__ __attribute__((always_inline)) inline void lattice_body(const Lattice
         blkv[4 * q + 3] = v.w;
       }
       vn[0] = my_ring[(is_beta ? slot + SW : slot - 1) & (SRING - 1)];
+      // the ring values arrive before the window's first diagonal (a
+      // scheduling boundary), not read just ahead of each use
+#pragma unroll
+      for (int q = 0; q < SW / 4; ++q)
+        asm volatile("" ::"v"(blkv[4 * q]), "v"(blkv[4 * q + 1]), "v"(blkv[4 * q + 2]), "v"(blkv[4 * q + 3]));
+      asm volatile("" ::"v"(vn[0]));
 #pragma unroll
       for (int w = 1; w < SW; ++w) vn[w] = is_beta ? blkv[SW - w] : blkv[w - 1];
 #pragma unroll
@@ -226,7 +236,6 @@ __device__ __attribute__((always_inline)) inline void lattice_body(const Lattice
         const bool ok = (unsigned)(w - w_lo) < cnt;
         cur = ok ? nxt : (w < keep ? cur : kNegInf);
         res[w] = cur;
-        if (!is_beta && w == D - dstart && u == Ub) lnP2 = cur;
       }
       // the edge lane's values go to the neighbour wave's ring, by diagonal
       const int nbw = is_beta ? wave - 1 : wave + 1;
@@ -285,7 +294,11 @@ __device__ __attribute__((always_inline)) inline void lattice_body(const Lattice
     for (int j = 0; j <= PF; ++j) step(s + j, rp[(j + 1) % (PF + 1)], rs[(j + 1) % (PF + 1)], rp[j], rs[j]);
   }
   if (!is_beta && u == Ub) {
-    const float v = lnP2 * kLn2 + phi[lat_at(LatGeo{0, US}, Tb - 1, Ub)];
+    // alpha(T_b-1, U_b) as this lane stored it (its last window's stores
+    // complete first)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int64_t last = lat_at(LatGeo{0, US}, Tb - 1, Ub);
+    const float v = p.alpha[base0 + last] + phi[last];
     if (p.lnP) p.lnP[b] = v;
     if (p.costs) p.costs[b] = -v;
   }
