@@ -44,17 +44,23 @@ def run_gpu(rl, inp, mode="tiled", tile=(64, 32), tpw=0, dcosts=None):
 def check_costs(inp, got, ref, samples=None):
     rc, _ = TOL[inp.dtype]
     idx = range(len(ref)) if samples is None else samples
+    worst = 0.0
     for b in idx:
         err = abs(got[b] - ref[b]) / abs(ref[b])
+        worst = max(worst, err)
         assert err <= rc, f"sample {b}: cost {got[b]} vs {ref[b]} (rel {err:.2e})"
+    say(f"  parity: cost max rel err {worst:.2e} (tolerance {rc:g})")
 
 
 def check_grads(inp, got, ref):
     _, rg = TOL[inp.dtype]
+    errs = {}
     for k in GRADS:
         scale = np.max(np.abs(ref[k]))
         err = np.max(np.abs(got[k] - ref[k]))
+        errs[k] = err / max(scale, 1e-30)
         assert err <= rg * max(scale, 1e-30), f"{k}: max err {err:.3e} vs max-abs {scale:.3e}"
+    say("  parity: grad err / max-abs " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()) + f" (tolerance {rg:g})")
     for b in range(len(inp.T_len)):
         assert np.all(got["dhA"][b, inp.T_len[b]:] == 0), "padded dhA rows"
         assert np.all(got["dhL"][b, inp.U_len[b] + 1:] == 0), "padded dhL rows"
