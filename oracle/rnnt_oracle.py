@@ -51,6 +51,15 @@ previous one), which is the recursion itself, vectorised. The joint/output
 steps are evaluated over blocks of t rows only to bound host memory; each
 cell's value is the same function of its own inputs whatever the block.
 
+Pruned lattice (the pruning named in "Neural transducer training ...",
+Introduction and Conclusion, and the title of its reference 14; the pages
+give no definition, so this is the reading implemented): given a band of S
+label positions per frame, lo[t] <= u < lo[t] + S, cells outside the band are
+removed from the lattice: their two log-probs are taken as -inf, so the loss
+sums the probability of the alignments whose every cell lies in the band,
+and such cells get no gradient (their occupancy and flows are 0). The band
+is an input (where it comes from is outside the method on these pages).
+
 Pins (tests/test_oracle_pins.py): brute-force enumeration of every monotone
 alignment on tiny lattices, the alpha/beta identity, closed forms with
 W^O = 0, occupancy closed form, torch fp64 log_softmax, flow and row-sum
@@ -222,13 +231,22 @@ def _rows_per_block(U1, V, H, budget_bytes):
     return max(1, int(budget_bytes // max(1, U1 * (V + 2 * H) * 8)))
 
 
+def band_mask(lo_b, S, Tb, U1):
+    """In-band cells of a pruned lattice: lo[t] <= u < lo[t] + S, [T_b, U_b+1] booleans."""
+    u = np.arange(U1)[None, :]
+    lo = np.asarray(lo_b[:Tb], dtype=np.int64)[:, None]
+    return (u >= lo) & (u < lo + S)
+
+
 def sample_forward_backward(inp, b, g=1.0, *, want_grads=True, keep_flows=False,
-                            mem_budget=512 << 20):
+                            mem_budget=512 << 20, band=None):
     """Loss and gradients of sample b alone (Algorithm 1's loop body).
 
-    g is dL/dcost_b. Returns a SampleResult whose grads dict holds this
-    sample's contributions: dWO, dbO, dWA, dWL, dbZ (parameter shaped) and
-    dhA_b [T_b, HA], dhL_b [U_b+1, HL].
+    g is dL/dcost_b. band: None, or (lo [T] int array of this sample, S) for
+    the pruned lattice (cells outside lo[t] <= u < lo[t] + S removed).
+    Returns a SampleResult whose grads dict holds this sample's contributions:
+    dWO, dbO, dWA, dWL, dbZ (parameter shaped) and dhA_b [T_b, HA],
+    dhL_b [U_b+1, HL].
     """
     Tb, Ub = int(inp.T_len[b]), int(inp.U_len[b])
     if Tb < 1 or Ub < 0:
@@ -253,6 +271,11 @@ def sample_forward_backward(inp, b, g=1.0, *, want_grads=True, keep_flows=False,
         h = output_layer(z, WO, bO)
         lse[t0:t1] = log_softmax_denominator(h)
         phi[t0:t1], psi[t0:t1] = two_log_probs(h, lse[t0:t1], y_b, Ub, blank)
+    if band is not None:
+        # pruned lattice: no emission leaves a cell outside the band
+        out = ~band_mask(band[0], band[1], Tb, U1)
+        phi[out] = NEG_INF
+        psi[out] = NEG_INF
 
     alpha = alpha_recursion(phi, psi)
     beta = beta_recursion(phi, psi)
@@ -299,13 +322,14 @@ class BatchResult:
 
 
 def loss_and_grads(inp, dcosts=None, *, samples=None, want_grads=True, keep_flows=False,
-                   mem_budget=512 << 20):
+                   mem_budget=512 << 20, band=None):
     """Batch loss and gradients: per-sample results summed over b in order.
 
     dcosts: [B] upstream gradient (None = all ones, i.e. L = sum of costs).
     samples: optional subset of sample indices to compute; the others get
     cost NaN and contribute nothing to the gradients (so the gradients equal
     the full-batch ones when dcosts is zero outside the subset).
+    band: None, or (lo [B, T] int array, S) for the pruned lattice.
     """
     d = inp.dims
     B, T, U, V, HA, HL, H = (d[k] for k in ("B", "T", "U", "V", "HA", "HL", "H"))
@@ -320,7 +344,8 @@ def loss_and_grads(inp, dcosts=None, *, samples=None, want_grads=True, keep_flow
                      dWO=np.zeros((V, H)), dbO=np.zeros(V))
     for b in which:
         r = sample_forward_backward(inp, b, float(g[b]), want_grads=want_grads,
-                                    keep_flows=keep_flows, mem_budget=mem_budget)
+                                    keep_flows=keep_flows, mem_budget=mem_budget,
+                                    band=None if band is None else (band[0][b], band[1]))
         costs[b] = r.cost
         out[b] = r
         if want_grads:

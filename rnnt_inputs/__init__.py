@@ -259,3 +259,26 @@ def poison_padding(inp: Inputs) -> Inputs:
         hL[b, inp.U_len[b] + 1:] = np.nan
         y[b, inp.U_len[b] + 1:] = V + 7
     return dataclasses.replace(inp, hA=hA, hL=hL, labels=y)
+
+
+def diagonal_band(T_len, U_len, T: int, S: int) -> np.ndarray:
+    """Label-position bands of width S for a pruned lattice, lo [B, T] int32: per frame t
+    the band lo[t] <= u < lo[t] + S is centred on the straight line from (0, 0) to
+    (T_b - 1, U_b), clipped to [0, U_b], with lo[0] = 0, lo non-decreasing, steps of at
+    most S - 1 and the last frame's band reaching U_b (so the band holds an alignment).
+    Frames past T_b get 0. A synthetic stand-in for bounds that come from a model."""
+    B = len(T_len)
+    lo = np.zeros((B, T), dtype=np.int32)
+    for b in range(B):
+        Tb, Ub = int(T_len[b]), int(U_len[b])
+        top = max(0, Ub - S + 1)
+        prev = 0
+        for t in range(Tb):
+            c = (t * Ub) // max(1, Tb - 1)
+            v = min(max(c - (S - 1) // 2, 0), top)
+            v = min(max(v, prev), prev + S - 1)
+            lo[b, t] = v
+            prev = v
+        if lo[b, Tb - 1] + S - 1 < Ub:
+            raise ValueError(f"band width {S} too narrow for sample {b} (T_b={Tb}, U_b={Ub})")
+    return lo

@@ -21,7 +21,7 @@ import torch
 
 import oracle
 from oracle import rnnt_oracle as ro
-from rnnt_inputs import make_inputs, poison_padding, workload_inputs
+from rnnt_inputs import diagonal_band, make_inputs, poison_padding, workload_inputs
 
 
 def tiny(B=2, T=5, U=3, V=6, H=4, HA=3, HL=5, seed=0, t_range=None, u_range=None, bias_std=0.3,
@@ -182,16 +182,16 @@ def test_fd_logits(Tb, Ub):
     assert np.max(np.abs(fd - dh)) <= 1e-7 * max(1.0, np.max(np.abs(dh)))
 
 
-def total_loss(inp, g):
-    r = oracle.loss_and_grads(inp, want_grads=False)
+def total_loss(inp, g, band=None):
+    r = oracle.loss_and_grads(inp, want_grads=False, band=band)
     return float(np.dot(g, r.costs))
 
 
-def fd_check(inp, names=("hA", "hL", "WA", "WL", "bZ", "WO", "bO"), g=None, eps=1e-6, tol=1e-7):
+def fd_check(inp, names=("hA", "hL", "WA", "WL", "bZ", "WO", "bO"), g=None, eps=1e-6, tol=1e-7, band=None):
     """Central differences of sum_b g_b cost_b for every element of the named arrays."""
     B = len(inp.T_len)
     g = np.linspace(0.5, 1.5, B) if g is None else g
-    r = oracle.loss_and_grads(inp, dcosts=g)
+    r = oracle.loss_and_grads(inp, dcosts=g, band=band)
     key = dict(hA="dhA", hL="dhL", WA="dWA", WL="dWL", bZ="dbZ", WO="dWO", bO="dbO")
     for name in names:
         arr = getattr(inp, name)
@@ -207,9 +207,9 @@ def fd_check(inp, names=("hA", "hL", "WA", "WL", "bZ", "WO", "bO"), g=None, eps=
                 continue
             old = base[idx]
             base[idx] = old + eps
-            lp = total_loss(inp, g)
+            lp = total_loss(inp, g, band)
             base[idx] = old - eps
-            lm = total_loss(inp, g)
+            lm = total_loss(inp, g, band)
             base[idx] = old
             fd[idx] = (lp - lm) / (2 * eps)
         setattr(inp, name, arr)
@@ -223,6 +223,81 @@ def test_fd_every_parameter_tiny():
 
 def test_fd_ragged_batch_with_biases():
     fd_check(tiny(B=3, T=5, U=3, seed=13, t_range=(1, 5), u_range=(0, 3)))
+
+
+# ----------------------------------------------------------------------------- pruned lattice
+
+def brute_force_band_cost(phi, psi, lo, S):
+    """-log of the summed probability of the alignments whose every cell lies in the band
+    lo[t] <= u < lo[t] + S, by enumeration with an explicit membership test on each visited
+    cell (the unpruned log-probs phi, psi; independent of the oracle's masking)."""
+    import itertools
+
+    Tb, U1 = phi.shape
+    Ub = U1 - 1
+    n = Tb - 1 + Ub
+    inb = lambda t, u: lo[t] <= u < lo[t] + S
+    logps = []
+    for label_steps in itertools.combinations(range(n), Ub):
+        ls = set(label_steps)
+        t = u = 0
+        lp, ok = 0.0, True
+        for step in range(n):
+            ok = ok and inb(t, u)
+            if step in ls:
+                lp += psi[t, u]
+                u += 1
+            else:
+                lp += phi[t, u]
+                t += 1
+        ok = ok and inb(Tb - 1, Ub)
+        if ok:
+            logps.append(lp + phi[Tb - 1, Ub])
+    logps = np.array(logps)
+    m = logps.max()
+    return -(m + np.log(np.sum(np.exp(logps - m)))), len(logps)
+
+
+@pytest.mark.parametrize("Tb,Ub,S", [(6, 3, 2), (7, 5, 3), (5, 4, 2), (8, 0, 1), (4, 6, 4)])
+def test_pruned_cost_equals_band_brute_force(Tb, Ub, S):
+    inp = tiny(B=1, T=Tb, U=Ub, seed=100 + Tb * 10 + Ub)
+    lo = diagonal_band(inp.T_len, inp.U_len, Tb, S)
+    full = oracle.loss_and_grads(inp, want_grads=False)
+    pruned = oracle.loss_and_grads(inp, want_grads=False, band=(lo, S))
+    bf, n_paths = brute_force_band_cost(full.samples[0].phi, full.samples[0].psi, lo[0], S)
+    assert n_paths >= 1
+    assert abs(bf - pruned.costs[0]) <= 1e-12 * abs(bf)
+    # pruning removes alignments: the cost can only grow
+    assert pruned.costs[0] >= full.costs[0] - 1e-12
+
+
+def test_pruned_wide_band_is_the_full_loss():
+    inp = tiny(B=3, T=7, U=4, seed=41, t_range=(2, 7), u_range=(0, 4))
+    S = 5  # every row of every frame
+    lo = np.zeros((3, 7), dtype=np.int32)
+    a = oracle.loss_and_grads(inp)
+    b = oracle.loss_and_grads(inp, band=(lo, S))
+    assert np.array_equal(a.costs, b.costs)
+    for k, v in a.grads.items():
+        assert np.array_equal(v, b.grads[k]), k
+
+
+def test_pruned_fd_every_parameter():
+    """Central differences of the pruned loss for every input and parameter (ragged batch)."""
+    inp = tiny(B=2, T=6, U=4, seed=43, t_range=(4, 6), u_range=(2, 4))
+    lo = diagonal_band(inp.T_len, inp.U_len, 6, 2)
+    fd_check(inp, band=(lo, 2))
+
+
+def test_pruned_cells_get_no_gradient():
+    inp = tiny(B=1, T=6, U=4, seed=47)
+    S = 2
+    lo = diagonal_band(inp.T_len, inp.U_len, 6, S)
+    r = oracle.loss_and_grads(inp, band=(lo, S), keep_flows=True)
+    s = r.samples[0]
+    out = ~ro.band_mask(lo[0], S, 6, 5)
+    assert np.all(s.occ[out] == 0) and np.all(s.bflow[out] == 0) and np.all(s.lflow[out] == 0)
+    assert abs(s.occ.sum() - (6 + 4)) < 1e-10  # every alignment still visits T_b + U_b cells
 
 
 # ----------------------------------------------------------------------------- independent autograd
@@ -407,6 +482,13 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
     attr, fn = MUTANTS[name]
     monkeypatch.setattr(ro, attr, fn)
     assert pin_suite(), f"no pin caught: {name}"
+
+
+def test_pins_catch_band_off_by_one(monkeypatch):
+    orig = ro.band_mask
+    monkeypatch.setattr(ro, "band_mask", lambda lo, S, Tb, U1: orig(lo, S - 1, Tb, U1) | orig(lo, 1, Tb, U1))
+    with pytest.raises(AssertionError):
+        test_pruned_cost_equals_band_brute_force(6, 3, 2)
 
 
 def test_pins_catch_wrong_dtanh(monkeypatch):
