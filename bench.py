@@ -306,6 +306,8 @@ def main():
     ap.add_argument("--tiles-per-wave", type=int, default=0)
     ap.add_argument("--budget", type=float, default=0, metavar="BYTES",
                     help="pick tiles_per_wave as the largest whose saved + workspace bytes fit (tiled mode)")
+    ap.add_argument("--prune-width", type=int, default=0, metavar="S",
+                    help="pruned lattice: a band of S label positions per frame around the diagonal (0 = full lattice)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget; 0 = skip")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (counter calibration)")
@@ -329,7 +331,7 @@ def main():
     if not side_runs:
         print(f"# generating {w.name} inputs", file=sys.stderr, flush=True)
         inp = workload_inputs(args.workload)
-        if args.cpu_seconds > 0:
+        if args.cpu_seconds > 0 and args.prune_width == 0:
             # the oracle's worker processes start before this process touches the GPU
             print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
             cpu = cpu_baseline(inp, args.cpu_seconds)
@@ -364,7 +366,12 @@ def main():
         d = rl.make_desc(w.B, w.T, w.U, w.V, w.HA, w.HL, w.H, dtype=w.dtype, tile=tile)
         args.tiles_per_wave = rl.rnnt_waves_for_budget(d, inp.T_len, inp.U_len, int(args.budget))
         print(f"# budget {args.budget:.3g} B -> {args.tiles_per_wave} tiles per wave", file=sys.stderr, flush=True)
-    prob = rl.Problem(inp, mode=args.mode, tile=tile, tiles_per_wave=args.tiles_per_wave)
+    band = None
+    if args.prune_width > 0:
+        from rnnt_inputs import diagonal_band
+
+        band = (diagonal_band(inp.T_len, inp.U_len, w.T, args.prune_width), args.prune_width)
+    prob = rl.Problem(inp, mode=args.mode, tile=tile, tiles_per_wave=args.tiles_per_wave, band=band)
     stream = torch.cuda.current_stream()
 
     print("# warmup", file=sys.stderr, flush=True)
@@ -454,7 +461,7 @@ def main():
         "ms_per_step_profiled": t_fwd + t_bwd,
         "config": {"workload": w.name, "B": d["B"], "T": d["T"], "U": d["U"],
                    "V": d["V"], "HA": d["HA"], "HL": d["HL"], "H": d["H"], "mode": args.mode,
-                   "tile": list(tile), "tiles_per_wave": args.tiles_per_wave,
+                   "tile": list(tile), "tiles_per_wave": args.tiles_per_wave, "prune_width": args.prune_width,
                    "padded_cells": inp.padded_cells, "valid_cells": inp.valid_cells,
                    "saved_bytes": prob.saved_bytes, "workspace_bytes": prob.ws_bytes},
         "roofline": roof,

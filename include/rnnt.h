@@ -142,6 +142,46 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
                           void* saved, size_t saved_bytes, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Pruned lattice (an approximation). "Neural transducer training ...",
+ * Introduction and Conclusion, name pruning (its reference 14) among the ways
+ * to cut the memory of the output tensor but do not define it; this library's
+ * reading: frame t of sample b keeps the label positions
+ *   lo_host[b*T + t] <= u < lo_host[b*T + t] + width
+ * and every other cell of the lattice is removed (its two log-probs are -inf),
+ * so the loss sums the alignments whose every cell lies in the band, pruned
+ * cells get no gradient, and tiles holding no kept cell are not computed at
+ * all (the saving). The bands are the caller's (computing them, e.g. from a
+ * cheaper model, is outside this library). A band must hold an alignment:
+ * width >= 1, lo[b, 0] = 0, lo non-decreasing in t with steps of at most
+ * width - 1, 0 <= lo <= U_len[b], lo[b, T_len[b]-1] + width - 1 >= U_len[b];
+ * otherwise RNNT_E_INVALID. Frames t >= T_len[b] are not read. lo_host is a
+ * HOST int32 array [B, T], read during the call and copied into `saved`. */
+typedef struct {
+  const int32_t* lo_host;
+  int32_t width;
+} rnnt_band;
+
+/* rnnt_loss_query, rnnt_loss_fwd and rnnt_loss_bwd on the pruned lattice of
+ * `band` (the same band for the three calls; saved, workspace and results
+ * are those of the pruned lattice). Every mode and dtype is supported. */
+rnnt_status rnnt_loss_query_pruned(const rnnt_desc* desc, const int32_t* T_len_host,
+                                   const int32_t* U_len_host, const rnnt_band* band,
+                                   size_t* saved_bytes, size_t* workspace_bytes);
+rnnt_status rnnt_loss_fwd_pruned(const rnnt_desc* desc, const void* hA, const void* hL,
+                                 const int32_t* labels, const int32_t* T_len_host,
+                                 const int32_t* U_len_host, const rnnt_band* band, const void* WA,
+                                 const void* WL, const void* bZ, const void* WO, const void* bO,
+                                 float* costs, void* saved, size_t saved_bytes, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+rnnt_status rnnt_loss_bwd_pruned(const rnnt_desc* desc, const void* hA, const void* hL,
+                                 const int32_t* labels, const int32_t* T_len_host,
+                                 const int32_t* U_len_host, const rnnt_band* band, const void* WA,
+                                 const void* WL, const void* bZ, const void* WO, const void* bO,
+                                 const float* dcosts, void* saved, size_t saved_bytes,
+                                 void* workspace, size_t workspace_bytes, float* dhA, float* dhL,
+                                 float* dWA, float* dWL, float* dbZ, float* dWO, float* dbO,
+                                 void* stream);
+
 /* Bytes of the static device array rnnt_loss_fwd_noalloc uses as its workspace. */
 #define RNNT_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
 

@@ -32,6 +32,10 @@ class RnntError(RuntimeError):
         self.status = status
 
 
+class RnntBand(ctypes.Structure):
+    _fields_ = [("lo_host", ctypes.POINTER(ctypes.c_int32)), ("width", ctypes.c_int32)]
+
+
 class RnntDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "B", "T", "U", "V", "HA", "HL", "H", "blank", "dtype", "mode", "tile_t", "tile_u",
@@ -39,6 +43,7 @@ class RnntDesc(ctypes.Structure):
 
 
 EXPORTS = ("rnnt_loss_query", "rnnt_waves_for_budget", "rnnt_loss_fwd", "rnnt_loss_fwd_noalloc", "rnnt_loss_bwd",
+           "rnnt_loss_query_pruned", "rnnt_loss_fwd_pruned", "rnnt_loss_bwd_pruned",
            "rnnt_lattice", "rnnt_profile_start", "rnnt_profile_stop", "rnnt_profile_get", "rnnt_status_string",
            "rnnt_last_error")
 NOALLOC_SCRATCH_BYTES = 256 << 20  # RNNT_NOALLOC_SCRATCH_BYTES
@@ -57,12 +62,17 @@ def load(path: str = LIB_PATH):
     lib.rnnt_loss_query.argtypes = [DP, I32P, I32P, SZP, SZP]
     lib.rnnt_loss_fwd.argtypes = [DP, P, P, P, I32P, I32P, P, P, P, P, P, P, P, SZ, P, SZ, P]
     lib.rnnt_loss_fwd_noalloc.argtypes = [DP, P, P, P, I32P, I32P, P, P, P, P, P, P, P, SZ, P]
+    BP = ctypes.POINTER(RnntBand)
+    lib.rnnt_loss_query_pruned.argtypes = [DP, I32P, I32P, BP, SZP, SZP]
+    lib.rnnt_loss_fwd_pruned.argtypes = [DP, P, P, P, I32P, I32P, BP, P, P, P, P, P, P, P, SZ, P, SZ, P]
+    lib.rnnt_loss_bwd_pruned.argtypes = [DP, P, P, P, I32P, I32P, BP, P, P, P, P, P, P, P, SZ, P, SZ,
+                                         P, P, P, P, P, P, P, P]
     lib.rnnt_loss_bwd.argtypes = [DP, P, P, P, I32P, I32P, P, P, P, P, P, P, P, SZ, P, SZ,
                                   P, P, P, P, P, P, P, P]
     lib.rnnt_lattice.argtypes = [DP, P, P, P, P, P, P, P, P]
     lib.rnnt_waves_for_budget.argtypes = [DP, I32P, I32P, SZ, I32P]
     for f in ("rnnt_loss_query", "rnnt_waves_for_budget", "rnnt_loss_fwd", "rnnt_loss_fwd_noalloc", "rnnt_loss_bwd",
-              "rnnt_lattice"):
+              "rnnt_loss_query_pruned", "rnnt_loss_fwd_pruned", "rnnt_loss_bwd_pruned", "rnnt_lattice"):
         getattr(lib, f).restype = ctypes.c_int
     lib.rnnt_profile_start.argtypes = []
     lib.rnnt_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_int32)]
@@ -123,6 +133,50 @@ def rnnt_loss_query(desc: RnntDesc, T_len, U_len):
     s, w = ctypes.c_size_t(0), ctypes.c_size_t(0)
     _check(lib.rnnt_loss_query(ctypes.byref(desc), tp, up, ctypes.byref(s), ctypes.byref(w)))
     return s.value, w.value
+
+
+def make_band(lo, width):
+    """An rnnt_band over a host int32 [B, T] array (keep the returned array alive with the struct)."""
+    lo = np.ascontiguousarray(np.asarray(lo, dtype=np.int32))
+    return RnntBand(lo.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(width)), lo
+
+
+def rnnt_loss_query_pruned(desc: RnntDesc, T_len, U_len, lo, width):
+    """(saved_bytes, workspace_bytes) of the pruned lattice with bands lo [B, T], width."""
+    lib = load()
+    T_len, tp = _lens(T_len)
+    U_len, up = _lens(U_len)
+    band, keep = make_band(lo, width)
+    s, w = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib.rnnt_loss_query_pruned(ctypes.byref(desc), tp, up, ctypes.byref(band), ctypes.byref(s),
+                                      ctypes.byref(w)))
+    return s.value, w.value
+
+
+def rnnt_loss_fwd_pruned(desc, hA, hL, labels, T_len, U_len, lo, width, WA, WL, bZ, WO, bO, costs, saved,
+                         workspace=None, stream=None):
+    lib = load()
+    T_len, tp = _lens(T_len)
+    U_len, up = _lens(U_len)
+    band, keep = make_band(lo, width)
+    _check(lib.rnnt_loss_fwd_pruned(ctypes.byref(desc), _ptr(hA), _ptr(hL), _ptr(labels), tp, up, ctypes.byref(band),
+                                    _ptr(WA), _ptr(WL), _ptr(bZ), _ptr(WO), _ptr(bO), _ptr(costs), _ptr(saved),
+                                    saved.numel() * saved.element_size(), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                    _stream(stream)))
+
+
+def rnnt_loss_bwd_pruned(desc, hA, hL, labels, T_len, U_len, lo, width, WA, WL, bZ, WO, bO, dcosts, saved,
+                         workspace, dhA, dhL, dWA, dWL, dbZ, dWO, dbO, stream=None):
+    lib = load()
+    T_len, tp = _lens(T_len)
+    U_len, up = _lens(U_len)
+    band, keep = make_band(lo, width)
+    _check(lib.rnnt_loss_bwd_pruned(ctypes.byref(desc), _ptr(hA), _ptr(hL), _ptr(labels), tp, up, ctypes.byref(band),
+                                    _ptr(WA), _ptr(WL), _ptr(bZ), _ptr(WO), _ptr(bO), _ptr(dcosts), _ptr(saved),
+                                    saved.numel() * saved.element_size(), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _ptr(dhA), _ptr(dhL), _ptr(dWA),
+                                    _ptr(dWL), _ptr(dbZ), _ptr(dWO), _ptr(dbO), _stream(stream)))
 
 
 def rnnt_waves_for_budget(desc: RnntDesc, T_len, U_len, budget_bytes: int) -> int:
@@ -199,7 +253,7 @@ class Problem:
     bZ, WO, bO (numpy, float values exact in the dtype), e.g. rnnt_inputs.Inputs.
     """
 
-    def __init__(self, inputs, *, mode="tiled", tile=(64, 32), tiles_per_wave=0, device="cuda:0"):
+    def __init__(self, inputs, *, mode="tiled", tile=(64, 32), tiles_per_wave=0, device="cuda:0", band=None):
         import torch
 
         self.torch = torch
@@ -220,7 +274,12 @@ class Problem:
         self.WA, self.WL, self.bZ = up(inputs.WA), up(inputs.WL), up(inputs.bZ)
         self.WO, self.bO = up(inputs.WO), up(inputs.bO)
         self.labels = torch.from_numpy(np.ascontiguousarray(inputs.labels, dtype=np.int32)).to(dev)
-        self.saved_bytes, self.ws_bytes = rnnt_loss_query(self.desc, self.T_len, self.U_len)
+        # band: None, or (lo [B, T], width) for the pruned lattice
+        self.band = None if band is None else (np.ascontiguousarray(band[0], dtype=np.int32), int(band[1]))
+        if self.band is None:
+            self.saved_bytes, self.ws_bytes = rnnt_loss_query(self.desc, self.T_len, self.U_len)
+        else:
+            self.saved_bytes, self.ws_bytes = rnnt_loss_query_pruned(self.desc, self.T_len, self.U_len, *self.band)
         self.saved = torch.empty(max(self.saved_bytes, 1), dtype=torch.uint8, device=dev)
         self.workspace = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
         self.costs = torch.empty(B, dtype=torch.float32, device=dev)
@@ -229,13 +288,22 @@ class Problem:
                           dWO=f(V, H), dbO=f(V))
 
     def forward(self, stream=None):
-        rnnt_loss_fwd(self.desc, self.hA, self.hL, self.labels, self.T_len, self.U_len, self.WA, self.WL,
-                      self.bZ, self.WO, self.bO, self.costs, self.saved, self.workspace, stream)
+        if self.band is None:
+            rnnt_loss_fwd(self.desc, self.hA, self.hL, self.labels, self.T_len, self.U_len, self.WA, self.WL,
+                          self.bZ, self.WO, self.bO, self.costs, self.saved, self.workspace, stream)
+        else:
+            rnnt_loss_fwd_pruned(self.desc, self.hA, self.hL, self.labels, self.T_len, self.U_len, *self.band, self.WA,
+                                 self.WL, self.bZ, self.WO, self.bO, self.costs, self.saved, self.workspace, stream)
         return self.costs
 
     def backward(self, dcosts=None, stream=None):
         g = self.grads
-        rnnt_loss_bwd(self.desc, self.hA, self.hL, self.labels, self.T_len, self.U_len, self.WA, self.WL,
-                      self.bZ, self.WO, self.bO, dcosts, self.saved, self.workspace, g["dhA"], g["dhL"],
-                      g["dWA"], g["dWL"], g["dbZ"], g["dWO"], g["dbO"], stream)
+        if self.band is None:
+            rnnt_loss_bwd(self.desc, self.hA, self.hL, self.labels, self.T_len, self.U_len, self.WA, self.WL,
+                          self.bZ, self.WO, self.bO, dcosts, self.saved, self.workspace, g["dhA"], g["dhL"],
+                          g["dWA"], g["dWL"], g["dbZ"], g["dWO"], g["dbO"], stream)
+        else:
+            rnnt_loss_bwd_pruned(self.desc, self.hA, self.hL, self.labels, self.T_len, self.U_len, *self.band,
+                                 self.WA, self.WL, self.bZ, self.WO, self.bO, dcosts, self.saved, self.workspace,
+                                 g["dhA"], g["dhL"], g["dWA"], g["dWL"], g["dbZ"], g["dWO"], g["dbO"], stream)
         return g

@@ -71,16 +71,23 @@ rnnt_status to_dims(const rnnt_desc* desc, rnnt::Dims& d) {
   return RNNT_OK;
 }
 
+// band: null, or the bands of a pruned lattice (validated here).
 rnnt_status prepare(const rnnt_desc* desc, const int32_t* T_len, const int32_t* U_len, rnnt::Plan& p,
-                    rnnt::Layout& L) {
+                    rnnt::Layout& L, const rnnt_band* band = nullptr) {
   rnnt::Dims d;
   rnnt_status s = to_dims(desc, d);
   if (s != RNNT_OK) return s;
   std::string err;
   if (!rnnt::check_lengths(d, T_len, U_len, err)) return fail(RNNT_E_INVALID, err);
+  rnnt::Band bd;
+  if (band) {
+    bd.lo = band->lo_host;
+    bd.S = band->width;
+    if (!rnnt::check_band(d, T_len, U_len, bd, err)) return fail(RNNT_E_INVALID, err);
+  }
   int ks = rnnt::joint_ks_for(d.H);
   if (ks < 0) return fail(RNNT_E_UNSUPPORTED, "H too large for the fused joint kernel");
-  rnnt::build_plan(d, T_len, U_len, ks * 16, p);
+  rnnt::build_plan(d, T_len, U_len, ks * 16, p, bd);
   if (!rnnt::check_plan(p, err)) return fail(RNNT_E_UNSUPPORTED, err);
   L = rnnt::make_layout(p);
   return RNNT_OK;
@@ -164,6 +171,7 @@ struct Saved {
   int32_t* status;
   int32_t* labels;  // the range-checked labels every kernel reads
   const int64_t* lat_off;  // packed lattice blocks
+  const int32_t* band_lo;  // pruned lattice bands [B, T], else null
   const int32_t* Tlen;
   const int32_t* Ulen;
   const rnnt::Tile* tiles;
@@ -180,6 +188,7 @@ Saved saved_view(void* s, const rnnt::Layout& L) {
   v.status = at<int32_t>(s, L.off_status);
   v.labels = at<int32_t>(s, L.off_labels);
   v.lat_off = at<int64_t>(s, L.off_latoff);
+  v.band_lo = L.off_band ? at<int32_t>(s, L.off_band) : nullptr;
   v.Tlen = at<int32_t>(s, L.off_Tlen);
   v.Ulen = at<int32_t>(s, L.off_Ulen);
   v.tiles = at<rnnt::Tile>(s, L.off_tiles);
@@ -208,6 +217,8 @@ rnnt::JointArgs joint_args(const rnnt::Plan& p, const Saved& sv, const void* WO,
   a.U_len = sv.Ulen;
   a.labels = sv.labels;
   a.lat_off = sv.lat_off;
+  a.band_lo = sv.band_lo;
+  a.band_S = p.band_S;
   a.T = p.d.T;
   a.U1 = p.U1;
   a.V = p.d.V;
@@ -293,6 +304,18 @@ rnnt_status rnnt_loss_query(const rnnt_desc* desc, const int32_t* T_len_host, co
   return RNNT_OK;
 }
 
+rnnt_status rnnt_loss_query_pruned(const rnnt_desc* desc, const int32_t* T_len_host, const int32_t* U_len_host,
+                                   const rnnt_band* band, size_t* saved_bytes, size_t* workspace_bytes) {
+  if (!band) return fail(RNNT_E_INVALID, "band is null");
+  rnnt::Plan p;
+  rnnt::Layout L;
+  rnnt_status s = prepare(desc, T_len_host, U_len_host, p, L, band);
+  if (s != RNNT_OK) return s;
+  if (saved_bytes) *saved_bytes = L.saved_bytes;
+  if (workspace_bytes) *workspace_bytes = L.workspace_bytes;
+  return RNNT_OK;
+}
+
 rnnt_status rnnt_waves_for_budget(const rnnt_desc* desc, const int32_t* T_len_host, const int32_t* U_len_host,
                                   size_t budget_bytes, int32_t* tiles_per_wave) {
   if (!desc || !tiles_per_wave) return fail(RNNT_E_INVALID, "null descriptor or output pointer");
@@ -333,10 +356,10 @@ static rnnt_status forward_impl(const rnnt_desc* desc, const void* hA, const voi
                                 const int32_t* T_len_host, const int32_t* U_len_host, const void* WA,
                                 const void* WL, const void* bZ, const void* WO, const void* bO, float* costs,
                                 void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
-                                void* stream, bool scratch_mode) {
+                                void* stream, bool scratch_mode, const rnnt_band* band) {
   rnnt::Plan p;
   rnnt::Layout L;
-  rnnt_status s = prepare(desc, T_len_host, U_len_host, p, L);
+  rnnt_status s = prepare(desc, T_len_host, U_len_host, p, L, band);
   if (s != RNNT_OK) return s;
   if (scratch_mode) L = rnnt::make_forward_layout(p);  // same saved layout, packed forward workspace
   if (!hA || !hL || !labels || !WA || !WL || !bZ || !WO || !bO || !costs || !saved)
@@ -369,6 +392,11 @@ static rnnt_status forward_impl(const rnnt_desc* desc, const void* hA, const voi
   {
     ProfScope ps_("labels_check", st);
     RNNT_HIP(rnnt::launch_labels_check(labels, sv.Ulen, d.B, p.U1, d.V, d.blank, sv.labels, sv.status, st));
+  }
+  if (sv.band_lo) {
+    ProfScope ps_("band_fill", st);
+    RNNT_HIP(rnnt::launch_band_fill(sv.Tlen, sv.Ulen, sv.lat_off, sv.band_lo, p.band_S, d.B, d.T, p.U1, sv.phi, sv.psi,
+                                    st));
   }
 
   // 1. joint pre-activations (bf16: large-tile row GEMM, scaled for the z-row
@@ -527,6 +555,8 @@ static rnnt_status forward_impl(const rnnt_desc* desc, const void* hA, const voi
       mg.nvt = p.nvt;
       mg.U_len = sv.Ulen;
       mg.lat_off = sv.lat_off;
+      mg.band_lo = sv.band_lo;
+      mg.band_S = p.band_S;
       mg.T = d.T;
       mg.U1 = p.U1;
       mg.stats = stats;
@@ -585,7 +615,17 @@ rnnt_status rnnt_loss_fwd(const rnnt_desc* desc, const void* hA, const void* hL,
                           void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
                           void* stream) {
   return forward_impl(desc, hA, hL, labels, T_len_host, U_len_host, WA, WL, bZ, WO, bO, costs, saved, saved_bytes,
-                      workspace, workspace_bytes, stream, false);
+                      workspace, workspace_bytes, stream, false, nullptr);
+}
+
+rnnt_status rnnt_loss_fwd_pruned(const rnnt_desc* desc, const void* hA, const void* hL, const int32_t* labels,
+                                 const int32_t* T_len_host, const int32_t* U_len_host, const rnnt_band* band,
+                                 const void* WA, const void* WL, const void* bZ, const void* WO, const void* bO,
+                                 float* costs, void* saved, size_t saved_bytes, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!band) return fail(RNNT_E_INVALID, "band is null");
+  return forward_impl(desc, hA, hL, labels, T_len_host, U_len_host, WA, WL, bZ, WO, bO, costs, saved, saved_bytes,
+                      workspace, workspace_bytes, stream, false, band);
 }
 
 rnnt_status rnnt_loss_fwd_noalloc(const rnnt_desc* desc, const void* hA, const void* hL, const int32_t* labels,
@@ -596,8 +636,15 @@ rnnt_status rnnt_loss_fwd_noalloc(const rnnt_desc* desc, const void* hA, const v
   const rnnt_status s = scratch_for_current_device(&ws);
   if (s != RNNT_OK) return s;
   return forward_impl(desc, hA, hL, labels, T_len_host, U_len_host, WA, WL, bZ, WO, bO, costs, saved, saved_bytes,
-                      ws, kScratchBytes, stream, true);
+                      ws, kScratchBytes, stream, true, nullptr);
 }
+
+static rnnt_status backward_impl(const rnnt_desc* desc, const void* hA, const void* hL, const int32_t* labels,
+                                 const int32_t* T_len_host, const int32_t* U_len_host, const void* WA,
+                                 const void* WL, const void* bZ, const void* WO, const void* bO,
+                                 const float* dcosts, void* saved, size_t saved_bytes, void* workspace,
+                                 size_t workspace_bytes, float* dhA, float* dhL, float* dWA, float* dWL,
+                                 float* dbZ, float* dWO, float* dbO, void* stream, const rnnt_band* band);
 
 rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL, const int32_t* labels,
                           const int32_t* T_len_host, const int32_t* U_len_host, const void* WA,
@@ -605,10 +652,31 @@ rnnt_status rnnt_loss_bwd(const rnnt_desc* desc, const void* hA, const void* hL,
                           const float* dcosts, void* saved, size_t saved_bytes, void* workspace,
                           size_t workspace_bytes, float* dhA, float* dhL, float* dWA, float* dWL,
                           float* dbZ, float* dWO, float* dbO, void* stream) {
+  return backward_impl(desc, hA, hL, labels, T_len_host, U_len_host, WA, WL, bZ, WO, bO, dcosts, saved, saved_bytes,
+                       workspace, workspace_bytes, dhA, dhL, dWA, dWL, dbZ, dWO, dbO, stream, nullptr);
+}
+
+rnnt_status rnnt_loss_bwd_pruned(const rnnt_desc* desc, const void* hA, const void* hL, const int32_t* labels,
+                                 const int32_t* T_len_host, const int32_t* U_len_host, const rnnt_band* band,
+                                 const void* WA, const void* WL, const void* bZ, const void* WO, const void* bO,
+                                 const float* dcosts, void* saved, size_t saved_bytes, void* workspace,
+                                 size_t workspace_bytes, float* dhA, float* dhL, float* dWA, float* dWL,
+                                 float* dbZ, float* dWO, float* dbO, void* stream) {
+  if (!band) return fail(RNNT_E_INVALID, "band is null");
+  return backward_impl(desc, hA, hL, labels, T_len_host, U_len_host, WA, WL, bZ, WO, bO, dcosts, saved, saved_bytes,
+                       workspace, workspace_bytes, dhA, dhL, dWA, dWL, dbZ, dWO, dbO, stream, band);
+}
+
+static rnnt_status backward_impl(const rnnt_desc* desc, const void* hA, const void* hL, const int32_t* labels,
+                                 const int32_t* T_len_host, const int32_t* U_len_host, const void* WA,
+                                 const void* WL, const void* bZ, const void* WO, const void* bO,
+                                 const float* dcosts, void* saved, size_t saved_bytes, void* workspace,
+                                 size_t workspace_bytes, float* dhA, float* dhL, float* dWA, float* dWL,
+                                 float* dbZ, float* dWO, float* dbO, void* stream, const rnnt_band* band) {
   (void)bZ;
   rnnt::Plan p;
   rnnt::Layout L;
-  rnnt_status s = prepare(desc, T_len_host, U_len_host, p, L);
+  rnnt_status s = prepare(desc, T_len_host, U_len_host, p, L, band);
   if (s != RNNT_OK) return s;
   if (!hA || !hL || !labels || !WA || !WL || !WO || !bO || !saved || !workspace || !dhA || !dhL || !dWA ||
       !dWL || !dbZ || !dWO || !dbO)

@@ -368,9 +368,15 @@ joint_kernel(JointArgs p) {
     if (row_ok && g == 0) {
       float ls = row_lds[wave][0][r];
       size_t idx = (size_t)lat_at(lat_geo(p.lat_off, p.U_len, b), t_r, u);
+      // a pruned lattice's cells outside their frame's band emit nothing
+      bool in_band = true;
+      if (p.band_lo) {
+        const int lo = p.band_lo[(size_t)b * T + t_r];
+        in_band = u >= lo && u < lo + p.band_S;
+      }
       p.lse_out[idx] = ls;
-      p.phi_out[idx] = hb - ls;
-      p.psi_out[idx] = (u < Ub) ? hy - ls : kNegInf;
+      p.phi_out[idx] = in_band ? hb - ls : kNegInf;
+      p.psi_out[idx] = (in_band && u < Ub) ? hy - ls : kNegInf;
     }
   } else {
     // the label column: g*occ*softmax - g*lflow (- g*bflow when the label is blank)

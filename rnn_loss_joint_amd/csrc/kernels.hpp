@@ -18,6 +18,8 @@ struct JointArgs {
   const int32_t* U_len;
   const int32_t* labels;  // [B, U1]
   const int64_t* lat_off;  // packed lattice blocks (lat_geo)
+  const int32_t* band_lo;  // pruned lattice: [B, T] band starts (null: not pruned)
+  int band_S;
   int T, U1, V, H, H_pad, V_pad, blank;
   const float* a;  // [B*T, H_pad]  W^A h^A + b^Z
   const float* l;  // [B*U1, H_pad] W^L h^L
@@ -96,6 +98,11 @@ struct LatticeArgs {
   double* lnP64;
 };
 hipError_t launch_lattice(const LatticeArgs& a, int U1max, hipStream_t st);
+// Pruned lattice: phi = psi = -inf on every lattice cell (t < T_b, u <= U_b)
+// outside its frame's band lo[b, t] <= u < lo[b, t] + S (packed layout).
+hipError_t launch_band_fill(const int32_t* T_len, const int32_t* U_len, const int64_t* lat_off,
+                            const int32_t* band_lo, int S, int B, int T, int U1, float* phi, float* psi,
+                            hipStream_t st);
 // The same recursions in fp64 from fp32 phi, psi: writes alpha64, beta64,
 // lnP64 and (when non-null) lnP and costs rounded to fp32.
 hipError_t launch_lattice64(const LatticeArgs& a, hipStream_t st);
@@ -295,6 +302,8 @@ struct MergeArgs {
   int tile_begin, tile_end, n_rows, buf_row_base, nvt;
   const int32_t* U_len;
   const int64_t* lat_off;
+  const int32_t* band_lo;  // pruned lattice: [B, T] band starts (null: not pruned)
+  int band_S;
   int T, U1;
   const f32x2* stats;
   const float* hb;

@@ -52,6 +52,8 @@
 // step issues the same number of loads and stores, so the compiler's wait
 // counts do not fall back to the shortest path; the loads of a window are
 // issued PF windows ahead.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -96,7 +98,7 @@ __device__ inline float add_operand2(float x, float raw) {
 }
 
 // base-2 log-add-exp; a = b = -inf gives NaN, which only occurs on cells the
-// caller masks
+// caller masks or (a pruned lattice) outside the band, and the stores map to -inf
 __device__ inline float lae2(float a, float b) {
   return __builtin_fmaxf(a, b) + flog2(1.0f + fexp2(-__builtin_fabsf(a - b)));
 }
@@ -262,7 +264,9 @@ __device__ __attribute__((always_inline)) inline void lattice_body(const Lattice
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int w = is_beta ? SW - 1 - 4 * g - e : 4 * g + e - 1;
-        v[e] = (w < 0 ? prev : res[w]) * kLn2;
+        // a cell whose two terms are both -inf (only outside a pruned
+        // lattice's band) gets NaN from the log-add-exp: stored as -inf
+        v[e] = __builtin_fmaxf((w < 0 ? prev : res[w]) * kLn2, kNegInf);
         o[e] = w < 0 ? prev_ok : (unsigned)(w - w_lo) < cnt;
       }
       const unsigned so = (unsigned)((wb >> 2) + g) * gstride;
@@ -327,6 +331,38 @@ hipError_t launch_lattice(const LatticeArgs& a, int U1max, hipStream_t st) {
   else if (nw <= 12) hipLaunchKernelGGL((lattice_kernel<12, 8>), grid, dim3(768), 0, st, a);
   else if (nw <= 16) hipLaunchKernelGGL((lattice_kernel<16, 8>), grid, dim3(1024), 0, st, a);
   else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// Pruned lattice: the two log-probs of every cell outside its frame's band
+// are -inf, so no alignment leaves such a cell (tiles the plan left out are
+// never computed; the forward's merge writes the in-band cells of the others).
+__global__ void band_fill_kernel(const int32_t* __restrict__ T_len, const int32_t* __restrict__ U_len,
+                                 const int64_t* __restrict__ lat_off, const int32_t* __restrict__ band_lo, int S,
+                                 int T, int U1, float* __restrict__ phi, float* __restrict__ psi) {
+  const int b = blockIdx.y;
+  const int Tb = T_len[b], Ub = U_len[b];
+  const int64_t n = (int64_t)Tb * (Ub + 1);
+  const LatGeo geo = lat_geo(lat_off, U_len, b);
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int t = (int)(i / (Ub + 1)), u = (int)(i - (int64_t)t * (Ub + 1));
+    const int lo = band_lo[(size_t)b * T + t];
+    if (u < lo || u >= lo + S) {
+      const int64_t ix = lat_at(geo, t, u);
+      phi[ix] = kNegInf;
+      psi[ix] = kNegInf;
+    }
+  }
+}
+
+hipError_t launch_band_fill(const int32_t* T_len, const int32_t* U_len, const int64_t* lat_off,
+                            const int32_t* band_lo, int S, int B, int T, int U1, float* phi, float* psi,
+                            hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  const int64_t cells = (int64_t)T * U1;
+  const int bx = (int)std::min<int64_t>(64, (cells + 255) / 256);
+  hipLaunchKernelGGL(band_fill_kernel, dim3(bx, B), dim3(256), 0, st, T_len, U_len, lat_off, band_lo, S, T, U1, phi,
+                     psi);
   return hipGetLastError();
 }
 

@@ -505,9 +505,16 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(MergeArgs p) {
       S += st[1] * fexp2((st[0] - M) * kLog2e);
     }
     const float lse = M + kLn2 * flog2(S);
+    const int t = tl.t0 + tb + tt, u = tl.u0 + ub + ul;
+    // a pruned lattice's cells outside their frame's band emit nothing
+    bool in_band = true;
+    if (p.band_lo) {
+      const int lo = p.band_lo[(size_t)b * p.T + t];
+      in_band = u >= lo && u < lo + p.band_S;
+    }
     sm[0][ul * kMS + tt] = lse;
-    sm[1][ul * kMS + tt] = p.hb[rr] - lse;
-    sm[2][ul * kMS + tt] = tl.u0 + ub + ul < Ub ? p.hy[rr] - lse : kNegInf;
+    sm[1][ul * kMS + tt] = in_band ? p.hb[rr] - lse : kNegInf;
+    sm[2][ul * kMS + tt] = in_band && u < Ub ? p.hy[rr] - lse : kNegInf;
   }
   __syncthreads();
   // the block's diagonals T0 + U0 .. T0 + U0 + 62 lie in 17 groups from q0 on

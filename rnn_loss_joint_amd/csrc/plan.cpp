@@ -100,9 +100,40 @@ bool check_lengths(const Dims& d, const int32_t* T_len, const int32_t* U_len, st
   return true;
 }
 
-void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H_pad, Plan& p) {
+bool check_band(const Dims& d, const int32_t* T_len, const int32_t* U_len, const Band& band, std::string& err) {
+  if (!band.lo) {
+    err = "band lo array must not be null";
+    return false;
+  }
+  if (band.S < 1) {
+    err = "band width must be >= 1";
+    return false;
+  }
+  for (int b = 0; b < d.B; ++b) {
+    const int32_t* lo = band.lo + (size_t)b * d.T;
+    const int Tb = T_len[b], Ub = U_len[b];
+    auto bad = [&](int t, const char* what) {
+      err = "band of sample " + std::to_string(b) + ", frame " + std::to_string(t) + ": " + what;
+      return false;
+    };
+    if (lo[0] != 0) return bad(0, "lo must be 0 at the first frame");
+    for (int t = 0; t < Tb; ++t) {
+      if (lo[t] < 0 || lo[t] > Ub) return bad(t, "lo must lie in [0, U_b]");
+      if (t + 1 < Tb && (lo[t + 1] < lo[t] || lo[t + 1] > lo[t] + band.S - 1))
+        return bad(t, "lo must not decrease and must step by at most S - 1");
+    }
+    if ((int64_t)lo[Tb - 1] + band.S - 1 < Ub) return bad(Tb - 1, "the last frame's band must reach U_b");
+  }
+  return true;
+}
+
+void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H_pad, Plan& p, const Band& band) {
   p = Plan{};
   p.d = d;
+  if (band.lo) {
+    p.band_lo.assign(band.lo, band.lo + (size_t)d.B * d.T);
+    p.band_S = band.S;
+  }
   p.U1 = d.U + 1;
   p.H_pad = H_pad;
   // bf16: whole 256-score tiles (the score kernels write every column of dh)
@@ -129,15 +160,32 @@ void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H
     t.htp = (int)cdiv(t.ht, 32) * 32;
     return t;
   };
+  // A pruned lattice keeps a tile iff some frame's band meets its u range:
+  // consecutive bands overlap or touch (steps of at most S - 1), so the
+  // bands of the tile's frames cover [lo(t0), lo(t_last) + S - 1] without gaps.
+  auto kept = [&](const TileH& t) {
+    if (p.band_lo.empty()) return true;
+    const int32_t* lo = p.band_lo.data() + (size_t)t.b * d.T;
+    return lo[t.t0] <= t.u0 + t.wu - 1 && (int64_t)lo[t.t0 + t.ht - 1] + p.band_S - 1 >= t.u0;
+  };
+  // per sample, its kept tiles in (t, u) order
+  std::vector<std::vector<TileH>> per(d.B);
+  for (int b = 0; b < d.B; ++b)
+    for (int k = 0; k < nt[b] * nu[b]; ++k) {
+      const TileH t = make_tile(b, k);
+      if (kept(t)) per[b].push_back(t);
+    }
+  max_tiles = 0;
+  for (int b = 0; b < d.B; ++b) max_tiles = std::max(max_tiles, (int)per[b].size());
   if (d.untiled) {
     // one wave holding every tile, sample by sample
     for (int b = 0; b < d.B; ++b)
-      for (int k = 0; k < nt[b] * nu[b]; ++k) p.tiles.push_back(make_tile(b, k));
+      for (const TileH& t : per[b]) p.tiles.push_back(t);
   } else {
     // round robin over samples, so consecutive tiles belong to different samples
     for (int k = 0; k < max_tiles; ++k)
       for (int b = 0; b < d.B; ++b)
-        if (k < nt[b] * nu[b]) p.tiles.push_back(make_tile(b, k));
+        if (k < (int)per[b].size()) p.tiles.push_back(per[b][k]);
   }
   // packed lattice blocks: sample b's block is cut to its own T_b x (U_b + 1)
   p.lat_off.assign(d.B + 1, 0);
@@ -247,6 +295,7 @@ Layout make_layout(const Plan& p) {
   L.off_groups = take(sizeof(GroupH) * p.groups.size());
   L.off_gidx = take(sizeof(int32_t) * p.gidx.size());
   L.off_latoff = take(sizeof(int64_t) * p.lat_off.size());
+  L.off_band = p.band_lo.empty() ? 0 : take(sizeof(int32_t) * p.band_lo.size());
   L.plan_bytes = o;
   L.off_labels = take(sizeof(int32_t) * (size_t)d.B * p.U1);
   const size_t cells = (size_t)p.lat_off[d.B];
@@ -364,6 +413,7 @@ void serialize_plan(const Plan& p, const Layout& L, const int32_t* T_len, const 
   if (!p.groups.empty()) std::memcpy(out.data() + L.off_groups, p.groups.data(), sizeof(GroupH) * p.groups.size());
   if (!p.gidx.empty()) std::memcpy(out.data() + L.off_gidx, p.gidx.data(), sizeof(int32_t) * p.gidx.size());
   std::memcpy(out.data() + L.off_latoff, p.lat_off.data(), sizeof(int64_t) * p.lat_off.size());
+  if (!p.band_lo.empty()) std::memcpy(out.data() + L.off_band, p.band_lo.data(), sizeof(int32_t) * p.band_lo.size());
 }
 
 }  // namespace rnnt

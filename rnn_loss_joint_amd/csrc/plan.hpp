@@ -36,8 +36,17 @@ struct WaveInfo {
   int maxA_len, maxL_len;
 };
 
+// Pruned lattice: frame t of sample b keeps the label positions
+// lo[b*T + t] <= u < lo[b*T + t] + S (host array; null lo = no pruning).
+struct Band {
+  const int32_t* lo = nullptr;
+  int S = 0;
+};
+
 struct Plan {
   Dims d;
+  std::vector<int32_t> band_lo;  // [B * T] copy of the caller's bands (empty: not pruned)
+  int band_S = 0;
   int U1, H_pad, V_pad, KS, tile_tp, tpw;
   std::vector<TileH> tiles;
   std::vector<WaveInfo> waves;
@@ -57,6 +66,7 @@ struct Layout {
   size_t off_Tlen, off_Ulen, off_tiles, off_groups, off_gidx;
   size_t off_labels;  // int32 [B, U+1]: the labels the kernels read (range-checked copy)
   size_t off_latoff;  // int64 [B + 1]: packed lattice block offsets (part of the plan copy)
+  size_t off_band;    // int32 [B, T]: the bands of a pruned lattice (part of the plan copy; 0 if none)
   size_t lat_entries; // entries of each lattice array (lat_off[B])
   size_t off_a, off_l, off_lse, off_phi, off_psi, off_alpha, off_beta, off_lnP;
   bool lat64;  // alpha, beta, ln P held in fp64 (fp32 mode), else fp32
@@ -82,8 +92,14 @@ int joint_ks_for(int H);
 // Validates dims and lengths; on failure returns false and sets err.
 bool check_dims(const Dims& d, std::string& err, int& status);
 bool check_lengths(const Dims& d, const int32_t* T_len, const int32_t* U_len, std::string& err);
-// Builds the tile plan (deterministic in its inputs).
-void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H_pad, Plan& p);
+// A band must hold an alignment: S >= 1, lo[b, 0] = 0, lo non-decreasing in t
+// with steps of at most S - 1, 0 <= lo <= U_b, and the last frame's band
+// reaching U_b. Frames t >= T_b are not read.
+bool check_band(const Dims& d, const int32_t* T_len, const int32_t* U_len, const Band& band, std::string& err);
+// Builds the tile plan (deterministic in its inputs). With a band, tiles
+// holding no cell of any frame's band are left out.
+void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H_pad, Plan& p,
+                const Band& band = Band());
 // Checks a built plan against the library's 32-bit row limits (kMaxPlanRows).
 bool check_plan(const Plan& p, std::string& err);
 Layout make_layout(const Plan& p);

@@ -16,8 +16,9 @@
 // Nothing is launched: this is plain C++ against the plan and layout.
 //
 // Input, one case per line: B T U V HA HL H bf16 untiled tile_t tile_u tpw,
-// then B values of T_len and B values of U_len. Output per case: "ok
-// <stages checked>" or "skip <reason>" or "FAIL <what>".
+// then B values of T_len and B values of U_len, optionally followed by a
+// band width S and B * T band starts (a pruned lattice). Output per case:
+// "ok <stages checked> tiles <n>" or "skip <reason>" or "FAIL <what>".
 #include <stdint.h>
 
 #include <algorithm>
@@ -49,15 +50,16 @@ Region region(int64_t off, const std::vector<int64_t>& offs, int64_t total) {
 bool inside(const Region& r, int64_t lo, int64_t hi) { return lo >= r.begin && hi <= r.end && lo <= hi; }
 
 std::string run_case(const Dims& d, const std::vector<int32_t>& T_len, const std::vector<int32_t>& U_len,
-                     int64_t& checked) {
+                     const Band& band, int64_t& checked) {
   std::string err;
   int st = 0;
   if (!check_dims(d, err, st)) return "skip " + err;
   if (!check_lengths(d, T_len.data(), U_len.data(), err)) return "skip " + err;
+  if (band.lo && !check_band(d, T_len.data(), U_len.data(), band, err)) return "skip " + err;
   const int ks = joint_ks_for(d.H);
   if (ks < 0) return "skip H";
   Plan p;
-  build_plan(d, T_len.data(), U_len.data(), ks * 16, p);
+  build_plan(d, T_len.data(), U_len.data(), ks * 16, p, band);
   if (!check_plan(p, err)) return "skip " + err;
   const Layout L = make_layout(p);
   // the persistent score kernels run in bf16 tiled mode with at least 8 k-steps of 64
@@ -152,7 +154,7 @@ std::string run_case(const Dims& d, const std::vector<int32_t>& T_len, const std
       }
     }
   }
-  return "ok " + std::to_string(checked);
+  return "ok " + std::to_string(checked) + " tiles " + std::to_string(p.tiles.size());
 }
 
 }  // namespace
@@ -172,13 +174,24 @@ int main() {
     std::vector<int32_t> T_len(d.B), U_len(d.B);
     for (auto& x : T_len) in >> x;
     for (auto& x : U_len) in >> x;
+    // optional: band width S > 0, then B * T band starts
+    Band band;
+    std::vector<int32_t> lo;
+    int S = 0;
+    if (in >> S && S > 0) {
+      lo.resize((size_t)d.B * d.T);
+      for (auto& x : lo) in >> x;
+      band.lo = lo.data();
+      band.S = S;
+    }
+    in.clear();
     if (!in) {
       std::cout << "FAIL bad input line" << std::endl;
       ++fails;
       continue;
     }
     int64_t checked = 0;
-    const std::string r = run_case(d, T_len, U_len, checked);
+    const std::string r = run_case(d, T_len, U_len, band, checked);
     if (r.rfind("FAIL", 0) == 0) ++fails;
     std::cout << r << std::endl;
   }

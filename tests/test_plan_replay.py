@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import rnn_loss_joint_amd as rl
-from rnnt_inputs import WORKLOADS, workload_lengths
+from rnnt_inputs import WORKLOADS, diagonal_band, workload_lengths
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "rnn_loss_joint_amd", "csrc")
@@ -34,9 +34,12 @@ def replay(tmp_path_factory):
     return exe
 
 
-def case_line(B, T, U, V, HA, HL, H, tile, tpw, T_len, U_len, bf16=True, untiled=False):
+def case_line(B, T, U, V, HA, HL, H, tile, tpw, T_len, U_len, bf16=True, untiled=False, band=None):
     vals = [B, T, U, V, HA, HL, H, int(bf16), int(untiled), tile[0], tile[1], tpw]
-    return " ".join(map(str, vals + list(map(int, T_len)) + list(map(int, U_len))))
+    vals += list(map(int, T_len)) + list(map(int, U_len))
+    if band is not None:
+        vals += [int(band[1])] + list(map(int, np.asarray(band[0]).reshape(-1)))
+    return " ".join(map(str, vals))
 
 
 def run(exe, lines):
@@ -98,3 +101,45 @@ def test_plan_rows_beyond_32_bits_are_refused():
     d = rl.make_desc(B, T, U, 1024, 512, 512, 640, tile=(32, 201))
     s, w = rl.rnnt_loss_query(d, np.full(B, T), np.full(B, U))
     assert s > 0 and w > 0
+
+
+@pytest.mark.parametrize("S", [8, 32, 64])
+def test_pruned_plans_stay_in_bounds_and_skip_tiles(replay, S):
+    """Pruned lattices at the 40 s x 256 lengths (bands around the diagonal): every wave's
+    mapping stays in bounds, and the plan keeps fewer tiles than the full lattice's."""
+    name = "40s-b256-bf16"
+    w = WORKLOADS[name]
+    T_len, U_len = workload_lengths(name)
+    lo = diagonal_band(T_len, U_len, w.T, S)
+    lines = [case_line(w.B, w.T, w.U, w.V, w.HA, w.HL, w.H, (64, 32), 0, T_len, U_len),
+             case_line(w.B, w.T, w.U, w.V, w.HA, w.HL, w.H, (64, 32), 0, T_len, U_len, band=(lo, S)),
+             case_line(w.B, w.T, w.U, w.V, w.HA, w.HL, w.H, (32, 16), 0, T_len, U_len, band=(lo, S))]
+    rc, out = run(replay, lines)
+    assert rc == 0 and all(o.startswith("ok") for o in out), out
+    full, pruned = int(out[0].split()[-1]), int(out[1].split()[-1])
+    assert pruned < full
+    # a band of S label positions per frame keeps about S / (U_b + 1) of the cells; 64 x 32 tiles
+    # straddle the band, so at most S/32 + 2 of a sample's ~7 tile columns survive per tile row
+    assert pruned <= full * min(1.0, (S / 32 + 2) / 5)
+
+
+def test_pruned_band_validation():
+    B, T, U = 3, 20, 6
+    T_len, U_len = np.array([20, 12, 5]), np.array([6, 3, 0])
+    d = rl.make_desc(B, T, U, 64, 64, 64, 128)
+    lo = diagonal_band(T_len, U_len, T, 3)
+    s_ok, w_ok = rl.rnnt_loss_query_pruned(d, T_len, U_len, lo, 3)
+    assert s_ok > 0 and w_ok > 0
+    bad = []
+    x = lo.copy(); x[0, 0] = 1; bad.append((x, 3))                   # first frame must start at 0
+    x = lo.copy(); x[0, 5] = x[0, 4] - 1 if x[0, 4] > 0 else -1; bad.append((x, 3))  # decreasing / negative
+    x = lo.copy(); x[0, 16:] = 6; bad.append((x, 3))                 # a step of 3 > width - 1
+    bad.append((lo, 0))                                              # width 0
+    x = lo.copy(); x[1, :] = 0; bad.append((x, 3))                   # the last frame's band misses U_b
+    for lo_bad, S in bad:
+        with pytest.raises(rl.RnntError) as e:
+            rl.rnnt_loss_query_pruned(d, T_len, U_len, lo_bad, S)
+        assert e.value.status == rl.RNNT_E_INVALID
+    # frames past T_b are not read
+    x = lo.copy(); x[2, 5:] = -7
+    assert rl.rnnt_loss_query_pruned(d, T_len, U_len, x, 3) == (s_ok, w_ok)
