@@ -32,38 +32,64 @@ GEMM_KERNELS = ("joint_fwd", "joint_bwd", "scores_fwd", "scores_bwd", "dz", "dWO
 # HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled
 # by a 1 GiB device copy: x2.000 / x1.000) on the 40 s x 256 workload; the
 # figure applies only while the kernel's sources hash to `src` (else null).
+# The kernel's sources: whole files, or (file, "struct Name") for one struct's definition in a
+# shared header (the argument structs the kernel takes).
 TRAFFIC = {
     "dz_dwo": {"bytes": 4.121e9, "src": "2a389e2fc2768ac1",
                "files": ("rnn_loss_joint_amd/csrc/dz_dwo.hip", "rnn_loss_joint_amd/csrc/mfma_core.hpp",
                          "rnn_loss_joint_amd/csrc/common.hpp", "rnn_loss_joint_amd/csrc/common_host.hpp",
-                         "rnn_loss_joint_amd/csrc/kernels.hpp"),
+                         ("rnn_loss_joint_amd/csrc/kernels.hpp", "struct DzArgs"),
+                         ("rnn_loss_joint_amd/csrc/kernels.hpp", "struct DwoArgs")),
                "profile": "profiles/hbm_traffic_40s_b256_bf16.md", "workload": "40s-b256-bf16"},
 }
 
 
-def measured_traffic(kernel, workload):
-    """Measured HBM bytes per launch if the kernel's sources are unchanged."""
+def source_hash(files):
+    """First 16 hex digits of the sha256 over the listed sources (see TRAFFIC)."""
     import hashlib
 
+    h = hashlib.sha256()
+    for f in files:
+        path, struct = (f, None) if isinstance(f, str) else f
+        with open(os.path.join(ROOT, path), "rb") as fh:
+            text = fh.read()
+        if struct is not None:
+            i = text.index(struct.encode() + b" {")
+            text = text[i:text.index(b"\n};", i) + 3]
+        h.update(text)
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """Measured HBM bytes per launch if the kernel's sources are unchanged."""
     t = TRAFFIC.get(kernel)
     if t is None or t["workload"] != workload:
         return None
-    h = hashlib.sha256()
-    for f in t["files"]:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    return t["bytes"] if h.hexdigest()[:16] == t["src"] else None
+    return t["bytes"] if source_hash(t["files"]) == t["src"] else None
 
 
 FLOP_FORMULA = {"dz_dwo": "4*H*V*valid_cells", "preproj_gemm": "2*H*(rows_a*HA + rows_l*HL)",
                 "dh_enc_gemm": "2*H*(rows_a*HA + rows_l*HL)", "dW_enc_gemm": "2*H*(rows_a*HA + rows_l*HL)"}
 
 
-def mfma_flops(inp):
-    """Algorithmic FLOP of each MFMA kernel class over one step (valid cells only)."""
+def band_cells(inp, band):
+    """Lattice cells inside a pruned lattice's bands: per frame t < T_b, the label positions
+    lo[b, t] <= u < lo[b, t] + S that are at most U_b."""
+    lo, S = band
+    n = 0
+    for b in range(len(inp.T_len)):
+        Tb, Ub = int(inp.T_len[b]), int(inp.U_len[b])
+        l = lo[b, :Tb].astype(np.int64)
+        n += int(np.sum(np.minimum(l + S, Ub + 1) - l))
+    return n
+
+
+def mfma_flops(inp, cells=None):
+    """Algorithmic FLOP of each MFMA kernel class over one step (valid cells only, or the given
+    count of computed lattice cells: the in-band cells of a pruned lattice)."""
     d = inp.dims
     H, V, HA, HL = d["H"], d["V"], d["HA"], d["HL"]
-    Nc = inp.valid_cells
+    Nc = inp.valid_cells if cells is None else cells
     rows_a = int(np.sum(inp.T_len))
     rows_l = int(np.sum(inp.U_len + 1))
     pre = 2.0 * H * (rows_a * HA + rows_l * HL)
@@ -412,7 +438,9 @@ def main():
     t_bwd = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     print(f"# profiled pass: fwd {t_fwd:.3f} + bwd {t_bwd:.3f} ms/step", file=sys.stderr, flush=True)
 
-    flops = mfma_flops(inp)
+    cells = inp.valid_cells if band is None else band_cells(inp, band)
+    cell_name = "valid_cells" if band is None else "band_cells"
+    flops = mfma_flops(inp, cells)
     dtype = inp.dtype
     kernels = {}
     for name, (launches, tot) in prof.items():
@@ -420,7 +448,7 @@ def main():
         if name in flops and tot > 0:
             k["tflops"] = flops[name] * args.steps / (tot * 1e-3) / 1e12
         if name == "lattice" and tot > 0:
-            k["gbs"] = 24.0 * inp.valid_cells * args.steps / (tot * 1e-3) / 1e9
+            k["gbs"] = 24.0 * inp.valid_cells * args.steps / (tot * 1e-3) / 1e9  # the sweep visits every cell
         kernels[name] = k
     mfma_names = [n for n in kernels if n in flops and n in GEMM_KERNELS]
     dom = max(mfma_names, key=lambda n: kernels[n]["ms_per_step"])
@@ -428,7 +456,7 @@ def main():
     ach = dk["tflops"]
     roof = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
             "frac": ach / PEAK_TFLOPS[dtype], "traffic": measured_traffic(dom, w.name),
-            "per_launch": (f"{FLOP_FORMULA.get(dom, '2*H*V*valid_cells')} / launches = "
+            "per_launch": (f"{FLOP_FORMULA.get(dom, '2*H*V*valid_cells').replace('valid_cells', cell_name)} / launches = "
                            f"{flops[dom] / max(1, dk['launches']):.4g} FLOP"),
             "launch_ms": dk["ms_per_step"] / max(1, dk["launches"]),
             "timing": "mean launch duration from hipEvent pairs on the launch stream over the profiled pass"}
@@ -463,6 +491,7 @@ def main():
                    "V": d["V"], "HA": d["HA"], "HL": d["HL"], "H": d["H"], "mode": args.mode,
                    "tile": list(tile), "tiles_per_wave": args.tiles_per_wave, "prune_width": args.prune_width,
                    "padded_cells": inp.padded_cells, "valid_cells": inp.valid_cells,
+                   "band_cells": None if band is None else cells,
                    "saved_bytes": prob.saved_bytes, "workspace_bytes": prob.ws_bytes},
         "roofline": roof,
         "kernels": kernels,
