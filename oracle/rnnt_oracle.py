@@ -60,6 +60,20 @@ sums the probability of the alignments whose every cell lies in the band,
 and such cells get no gradient (their occupancy and flows are 0). The band
 is an input (where it comes from is outside the method on these pages).
 
+Reduced-precision output layer ("Neural transducer training ...",
+Introduction, reduced precision among the ways to cut memory, and its
+Conclusion, mixed precision as future work; the pages do not define it, so
+this is the reading implemented): with fp8_scores, the product W^O z of the
+output layer takes its two operands rounded to the OCP FP8 E4M3 format
+(1 sign, 4 exponent bits with bias 7, 3 mantissa bits, largest finite value
+448, round to nearest with ties to even) after power-of-two scaling: z by
+2^8 (|z| <= 1), W^O by 2^e_w with e_w the largest integer for which
+max|W^O| 2^e_w <= 448; the exact product of the rounded values is scaled
+back by 2^-(8 + e_w) and b^O added. Everything else is unchanged: lse, phi,
+psi and dh come from these scores (the forward and the backward's), and the
+two backward products dz = W^O^T dh and dW^O = dh z^T take the unrounded
+W^O and z, as does 1 - z^2.
+
 Pins (tests/test_oracle_pins.py): brute-force enumeration of every monotone
 alignment on tiny lattices, the alpha/beta identity, closed forms with
 W^O = 0, occupancy closed form, torch fp64 log_softmax, flow and row-sum
@@ -108,6 +122,46 @@ def encoding_grad(g, W):
 def output_layer(z, WO, bO):
     """Eqs. (5)-(6): h[t,u] = W^O z[t,u] + b^O -> [..., V]."""
     return z @ _f64(WO).T + _f64(bO)
+
+
+E4M3_MAX = 448.0
+Z_SCALE_EXP = 8  # z in [-1, 1] is scaled by 2^8 before rounding
+
+
+def e4m3_round(x):
+    """Nearest OCP FP8 E4M3 value of each element (ties to even), as fp64.
+
+    The format's normal numbers have exponents -6..8 and 3 fraction bits, so
+    in the binade [2^k, 2^(k+1)) the spacing is 2^(k-3); below 2^-6 the
+    subnormals keep the spacing 2^-9. Rounding the value divided by its
+    spacing to the nearest integer (ties to even) is rounding to the
+    format. Magnitudes above 448 are outside what this oracle uses.
+    """
+    x = _f64(x)
+    a = np.abs(x)
+    if np.any(a > E4M3_MAX):
+        raise ValueError("value beyond the E4M3 range")
+    _, e = np.frexp(a)  # a = m 2^e with m in [0.5, 1): binade exponent e - 1
+    k = np.maximum(e - 1, -6)
+    q = np.ldexp(np.round(np.ldexp(a, 3 - k)), k - 3)
+    return np.copysign(q, x)
+
+
+def wo_scale_exp(WO):
+    """Largest integer e with max|W^O| 2^e <= 448 (0 for an all-zero W^O)."""
+    amax = float(np.max(np.abs(_f64(WO)))) if np.size(WO) else 0.0
+    if amax == 0.0:
+        return 0
+    m, e = np.frexp(amax)  # amax = m 2^e, m in [0.5, 1); 448 = 0.875 2^9
+    return int(9 - e if m <= 0.875 else 8 - e)
+
+
+def output_layer_fp8(z, WO, bO):
+    """Eqs. (5)-(6) with the product on E4M3-rounded, power-of-two scaled operands."""
+    ew = wo_scale_exp(WO)
+    zq = e4m3_round(np.ldexp(_f64(z), Z_SCALE_EXP))
+    wq = e4m3_round(np.ldexp(_f64(WO), ew))
+    return np.ldexp(zq @ wq.T, -(Z_SCALE_EXP + ew)) + _f64(bO)
 
 
 def log_softmax_denominator(h):
@@ -239,11 +293,13 @@ def band_mask(lo_b, S, Tb, U1):
 
 
 def sample_forward_backward(inp, b, g=1.0, *, want_grads=True, keep_flows=False,
-                            mem_budget=512 << 20, band=None):
+                            mem_budget=512 << 20, band=None, fp8_scores=False):
     """Loss and gradients of sample b alone (Algorithm 1's loop body).
 
     g is dL/dcost_b. band: None, or (lo [T] int array of this sample, S) for
     the pruned lattice (cells outside lo[t] <= u < lo[t] + S removed).
+    fp8_scores: the output layer's product on E4M3-rounded operands
+    (output_layer_fp8); the backward products keep the unrounded ones.
     Returns a SampleResult whose grads dict holds this sample's contributions:
     dWO, dbO, dWA, dWL, dbZ (parameter shaped) and dhA_b [T_b, HA],
     dhL_b [U_b+1, HL].
@@ -260,6 +316,7 @@ def sample_forward_backward(inp, b, g=1.0, *, want_grads=True, keep_flows=False,
     hL_b = _f64(inp.hL[b, :U1])
     y_b = np.asarray(inp.labels[b])
     rows = _rows_per_block(U1, V, H, mem_budget)
+    scores = output_layer_fp8 if fp8_scores else output_layer
 
     # forward: per-cell lse, phi, psi (z and h are discarded per block)
     lse = np.empty((Tb, U1))
@@ -268,7 +325,7 @@ def sample_forward_backward(inp, b, g=1.0, *, want_grads=True, keep_flows=False,
     for t0 in range(0, Tb, rows):
         t1 = min(Tb, t0 + rows)
         z = joint(hA_b[t0:t1], hL_b, WA, WL, bZ)
-        h = output_layer(z, WO, bO)
+        h = scores(z, WO, bO)
         lse[t0:t1] = log_softmax_denominator(h)
         phi[t0:t1], psi[t0:t1] = two_log_probs(h, lse[t0:t1], y_b, Ub, blank)
     if band is not None:
@@ -296,7 +353,7 @@ def sample_forward_backward(inp, b, g=1.0, *, want_grads=True, keep_flows=False,
     for t0 in range(0, Tb, rows):
         t1 = min(Tb, t0 + rows)
         z = joint(hA_b[t0:t1], hL_b, WA, WL, bZ)
-        h = output_layer(z, WO, bO)
+        h = scores(z, WO, bO)
         dh = logits_grad(h, lse[t0:t1], occ[t0:t1], bflow[t0:t1], lflow[t0:t1],
                          y_b, Ub, blank, g)
         dz = dh @ WO  # [t, U1, H]
@@ -322,7 +379,7 @@ class BatchResult:
 
 
 def loss_and_grads(inp, dcosts=None, *, samples=None, want_grads=True, keep_flows=False,
-                   mem_budget=512 << 20, band=None):
+                   mem_budget=512 << 20, band=None, fp8_scores=False):
     """Batch loss and gradients: per-sample results summed over b in order.
 
     dcosts: [B] upstream gradient (None = all ones, i.e. L = sum of costs).
@@ -330,6 +387,7 @@ def loss_and_grads(inp, dcosts=None, *, samples=None, want_grads=True, keep_flow
     cost NaN and contribute nothing to the gradients (so the gradients equal
     the full-batch ones when dcosts is zero outside the subset).
     band: None, or (lo [B, T] int array, S) for the pruned lattice.
+    fp8_scores: the output layer's product on E4M3-rounded operands.
     """
     d = inp.dims
     B, T, U, V, HA, HL, H = (d[k] for k in ("B", "T", "U", "V", "HA", "HL", "H"))
@@ -345,7 +403,8 @@ def loss_and_grads(inp, dcosts=None, *, samples=None, want_grads=True, keep_flow
     for b in which:
         r = sample_forward_backward(inp, b, float(g[b]), want_grads=want_grads,
                                     keep_flows=keep_flows, mem_budget=mem_budget,
-                                    band=None if band is None else (band[0][b], band[1]))
+                                    band=None if band is None else (band[0][b], band[1]),
+                                    fp8_scores=fp8_scores)
         costs[b] = r.cost
         out[b] = r
         if want_grads:

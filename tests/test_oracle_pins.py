@@ -13,6 +13,7 @@ Each check is independent of the oracle's own formulas:
 The mutation tests at the end plant plausible mistakes into the oracle and
 check that these pins catch every one of them.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -500,3 +501,144 @@ def test_pins_catch_transposed_encoder_weight(monkeypatch):
     # the tiny workload has H = H_A = H_L = 8, so a transposed W^A is shape-valid
     monkeypatch.setattr(ro, "encoding_grad", lambda g, W: g @ W.T)
     assert "autograd" in pin_suite()
+
+
+# ----------------------------------------------------------------------------- fp8 (E4M3) output layer
+
+def e4m3_decode(code):
+    """Value of an OCP FP8 E4M3 byte from the format's definition: sign, 4 exponent bits (bias 7),
+    3 fraction bits; exponent field 0 holds the subnormals m/8 2^-6; S.1111.111 is NaN (None)."""
+    s, e, m = code >> 7, (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return None
+    v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return -v if s else v
+
+
+def e4m3_table():
+    """{value: code} over every finite code, non-negative values only."""
+    return {e4m3_decode(c): c for c in range(128) if e4m3_decode(c) is not None}
+
+
+def test_e4m3_table_fixed_points_and_ties():
+    tab = e4m3_table()
+    vals = np.array(sorted(tab))
+    assert len(vals) == 127 and vals[-1] == 448.0 and vals[1] == 2.0 ** -9
+    # every finite value (both signs) rounds to itself
+    assert np.array_equal(ro.e4m3_round(vals), vals)
+    assert np.array_equal(ro.e4m3_round(-vals), -vals)
+    # the midpoint of two neighbours goes to the one with an even code; just off it, to the nearer
+    mid = (vals[:-1] + vals[1:]) / 2
+    even = np.array([lo if tab[lo] % 2 == 0 else hi for lo, hi in zip(vals[:-1], vals[1:])])
+    assert np.array_equal(ro.e4m3_round(mid), even)
+    gap = vals[1:] - vals[:-1]
+    assert np.array_equal(ro.e4m3_round(mid - gap / 64), vals[:-1])
+    assert np.array_equal(ro.e4m3_round(mid + gap / 64), vals[1:])
+
+
+def test_e4m3_round_matches_torch_float8():
+    """Against torch's float8_e4m3fn conversion (a library routine) on float32 values: random
+    magnitudes over the whole range and every midpoint of neighbouring values."""
+    rng = np.random.default_rng(5)
+    x = (rng.choice([-1.0, 1.0], 20000) * 2.0 ** rng.uniform(-12, np.log2(448), 20000)).astype(np.float32)
+    vals = np.array(sorted(e4m3_table()))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    x = np.concatenate([x, mids, -mids, np.float32([0.0, 448.0, -448.0])])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(ro.e4m3_round(x.astype(np.float64)), ref)
+
+
+@pytest.mark.parametrize("amax", [448.0, 224.0, 447.0, 449.0, 0.875, 0.87, 0.88, 0.0604, 1.0, 3e-3, 7.0])
+def test_wo_scale_exponent(amax):
+    W = np.array([[0.5 * amax, -amax], [0.0, 0.25 * amax]])
+    e = ro.wo_scale_exp(W)
+    assert amax * 2.0 ** e <= 448.0 < amax * 2.0 ** (e + 1)
+
+
+def torch_fp8_loss(inp, g):
+    """Cell-by-cell loss in torch fp64 whose scores are the product of E4M3-rounded operands (z by
+    2^8, W^O by 2^e), rounded by torch's float8_e4m3fn conversion, while autograd differentiates the
+    unrounded product (the value of the rounded one is added as a constant). Independent of the
+    oracle; the scale exponent from log2."""
+    P = {k: torch.tensor(np.asarray(getattr(inp, k), dtype=np.float64), requires_grad=True)
+         for k in ("hA", "hL", "WA", "WL", "bZ", "WO", "bO")}
+    amax = float(np.max(np.abs(np.asarray(inp.WO, dtype=np.float64))))
+    ew = math.floor(math.log2(448.0 / amax))
+    q = lambda x, e: x.detach().mul(2.0 ** e).to(torch.float32).to(torch.float8_e4m3fn).to(torch.float64)
+    wq = q(P["WO"], ew)
+    total = torch.zeros((), dtype=torch.float64)
+    for b in range(len(inp.T_len)):
+        Tb, Ub = int(inp.T_len[b]), int(inp.U_len[b])
+        y = [int(v) for v in inp.labels[b]]
+        logp = {}
+        for t in range(Tb):
+            for u in range(Ub + 1):
+                z = torch.tanh(P["WA"] @ P["hA"][b, t] + P["WL"] @ P["hL"][b, u] + P["bZ"])
+                exact = P["WO"] @ z
+                rounded = (wq @ q(z, 8)) * 2.0 ** -(8 + ew)
+                logits = exact + (rounded - exact).detach() + P["bO"]
+                logp[t, u] = torch.log_softmax(logits, dim=0)
+        alpha = {}
+        for t in range(Tb):
+            for u in range(Ub + 1):
+                if t == 0 and u == 0:
+                    alpha[t, u] = torch.zeros((), dtype=torch.float64)
+                    continue
+                terms = []
+                if t > 0:
+                    terms.append(alpha[t - 1, u] + logp[t - 1, u][inp.blank])
+                if u > 0:
+                    terms.append(alpha[t, u - 1] + logp[t, u - 1][y[u]])
+                alpha[t, u] = torch.logsumexp(torch.stack(terms), dim=0)
+        total = total - float(g[b]) * (alpha[Tb - 1, Ub] + logp[Tb - 1, Ub][inp.blank])
+    total.backward()
+    return float(total), {"d" + k: P[k].grad.numpy() for k in P}
+
+
+@pytest.mark.parametrize("which", ["tiny", "reduced"])
+def test_fp8_scores_against_independent_autograd(which):
+    if which == "tiny":
+        inp = workload_inputs("tiny-f32")
+    else:
+        inp = make_inputs(2, 9, 5, 40, 12, 10, 16, dtype="bf16", seed=2, t_range=(5, 9), u_range=(2, 5),
+                          bias_std=0.2)
+    g = np.linspace(1.3, 0.7, len(inp.T_len))
+    r = oracle.loss_and_grads(inp, dcosts=g, fp8_scores=True)
+    L, tg = torch_fp8_loss(inp, g)
+    assert abs(L - float(np.dot(g, r.costs))) <= 1e-12 * abs(L)
+    for k in ("dhA", "dhL", "dWA", "dWL", "dbZ", "dWO", "dbO"):
+        err = np.max(np.abs(r.grads[k] - tg[k]))
+        assert err <= 1e-11 * max(1.0, np.max(np.abs(tg[k]))), (k, err)
+    # the rounding is not a no-op: the plain loss differs
+    plain = oracle.loss_and_grads(inp, dcosts=g, want_grads=False)
+    assert np.max(np.abs(plain.costs - r.costs)) > 1e-6
+
+
+def test_fp8_scores_zero_projection_is_the_closed_form():
+    """W^O = 0 rounds to 0, so the fp8 loss is the bias-only closed form at any lattice size."""
+    inp = make_inputs(2, 30, 7, 9, 8, 8, 8, dtype="f32", seed=3, t_range=(20, 30), u_range=(3, 7),
+                      bias_std=0.4)
+    inp = dataclasses.replace(inp, WO=np.zeros_like(inp.WO))
+    a = oracle.loss_and_grads(inp, want_grads=False, fp8_scores=True)
+    b = oracle.loss_and_grads(inp, want_grads=False)
+    assert np.allclose(a.costs, b.costs, rtol=1e-14, atol=0)
+
+
+def test_fp8_pins_catch_ties_away_from_zero(monkeypatch):
+    def away(x):
+        x = np.asarray(x, dtype=np.float64)
+        a = np.abs(x)
+        _, e = np.frexp(a)
+        k = np.maximum(e - 1, -6)
+        return np.copysign(np.ldexp(np.floor(np.ldexp(a, 3 - k) + 0.5), k - 3), x)
+
+    monkeypatch.setattr(ro, "e4m3_round", away)
+    with pytest.raises(AssertionError):
+        test_e4m3_table_fixed_points_and_ties()
+
+
+def test_fp8_pins_catch_unscaled_projection_weights(monkeypatch):
+    # without its scale W^O (|w| < 0.5 here) falls partly into the subnormals
+    monkeypatch.setattr(ro, "wo_scale_exp", lambda WO: 0)
+    with pytest.raises(AssertionError):
+        test_fp8_scores_against_independent_autograd("reduced")
