@@ -26,7 +26,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}  # MI355X dense MFMA
+FP8_KERNELS = ("scores_fwd", "scores_bwd")  # the products on E4M3 operands with --fp8
 PEAK_HBM_GBS = 8000.0
 GEMM_KERNELS = ("joint_fwd", "joint_bwd", "scores_fwd", "scores_bwd", "dz", "dWO_gemm", "dz_dwo")
 # HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled
@@ -334,6 +335,8 @@ def main():
                     help="pick tiles_per_wave as the largest whose saved + workspace bytes fit (tiled mode)")
     ap.add_argument("--prune-width", type=int, default=0, metavar="S",
                     help="pruned lattice: a band of S label positions per frame around the diagonal (0 = full lattice)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="bf16 workloads: the output layer's score products on OCP E4M3 operands (an approximation)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget; 0 = skip")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (counter calibration)")
@@ -357,7 +360,7 @@ def main():
     if not side_runs:
         print(f"# generating {w.name} inputs", file=sys.stderr, flush=True)
         inp = workload_inputs(args.workload)
-        if args.cpu_seconds > 0 and args.prune_width == 0:
+        if args.cpu_seconds > 0 and args.prune_width == 0 and not args.fp8:
             # the oracle's worker processes start before this process touches the GPU
             print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
             cpu = cpu_baseline(inp, args.cpu_seconds)
@@ -397,7 +400,7 @@ def main():
         from rnnt_inputs import diagonal_band
 
         band = (diagonal_band(inp.T_len, inp.U_len, w.T, args.prune_width), args.prune_width)
-    prob = rl.Problem(inp, mode=args.mode, tile=tile, tiles_per_wave=args.tiles_per_wave, band=band)
+    prob = rl.Problem(inp, mode=args.mode, tile=tile, tiles_per_wave=args.tiles_per_wave, band=band, fp8=args.fp8)
     stream = torch.cuda.current_stream()
 
     print("# warmup", file=sys.stderr, flush=True)
@@ -454,8 +457,12 @@ def main():
     dom = max(mfma_names, key=lambda n: kernels[n]["ms_per_step"])
     dk = kernels[dom]
     ach = dk["tflops"]
-    roof = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
-            "frac": ach / PEAK_TFLOPS[dtype], "traffic": measured_traffic(dom, w.name),
+    peak_of = lambda name: PEAK_TFLOPS["fp8" if args.fp8 and name in FP8_KERNELS else dtype]
+    for name, k in kernels.items():
+        if "tflops" in k and name in GEMM_KERNELS:
+            k["frac"] = k["tflops"] / peak_of(name)
+    roof = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": peak_of(dom), "unit": "TFLOP/s",
+            "frac": ach / peak_of(dom), "traffic": measured_traffic(dom, w.name),
             "per_launch": (f"{FLOP_FORMULA.get(dom, '2*H*V*valid_cells').replace('valid_cells', cell_name)} / launches = "
                            f"{flops[dom] / max(1, dk['launches']):.4g} FLOP"),
             "launch_ms": dk["ms_per_step"] / max(1, dk["launches"]),
@@ -478,7 +485,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": "fp8+bf16" if args.fp8 else dtype,
         "data": "synthetic",
         "peak_hbm_bytes": int(peak),
         "input_bytes": int(input_bytes),
@@ -490,6 +497,7 @@ def main():
         "config": {"workload": w.name, "B": d["B"], "T": d["T"], "U": d["U"],
                    "V": d["V"], "HA": d["HA"], "HL": d["HL"], "H": d["H"], "mode": args.mode,
                    "tile": list(tile), "tiles_per_wave": args.tiles_per_wave, "prune_width": args.prune_width,
+                   "fp8_scores": bool(args.fp8),
                    "padded_cells": inp.padded_cells, "valid_cells": inp.valid_cells,
                    "band_cells": None if band is None else cells,
                    "saved_bytes": prob.saved_bytes, "workspace_bytes": prob.ws_bytes},

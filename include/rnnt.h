@@ -27,7 +27,8 @@
  *    during the call and not retained (the forward copies them, with the tile
  *    plan, into `saved`). 1 <= T_len[b] <= T, 0 <= U_len[b] <= U.
  *  - Float inputs (h^A, h^L, W^A, W^L, b^Z, W^O, b^O) all have the dtype of
- *    desc->dtype (fp32 or bf16), row-major, densely packed:
+ *    desc->dtype (fp32, or bf16 for RNNT_BF16 and RNNT_BF16_FP8), row-major,
+ *    densely packed:
  *      hA [B,T,HA], hL [B,U+1,HL], WA [H,HA], WL [H,HL], bZ [H], WO [V,H], bO [V].
  *    labels is int32 [B,U+1] on the device; column 0 is the blank id, column
  *    u+1 (u < U_len[b]) is the label emitted from lattice row u. Entries past
@@ -77,7 +78,16 @@ typedef enum {
   RNNT_E_UNSUPPORTED = -4  /* valid request outside the library's limits      */
 } rnnt_status;
 
-typedef enum { RNNT_F32 = 0, RNNT_BF16 = 1 } rnnt_dtype;
+/* RNNT_BF16_FP8: bf16 inputs as in RNNT_BF16, with the output layer's product
+ * W^O z in the score kernels (forward and the backward's recompute) taken on
+ * OCP FP8 E4M3 operands: z scaled by 2^8 and W^O by 2^e (e the largest
+ * integer with max|W^O| 2^e <= 448), each rounded to nearest even, the fp32
+ * product scaled back by 2^-(8+e). The backward products dz = dh W^O and
+ * dW^O = dh^T z stay bf16. An approximation of the bf16 result: "Neural
+ * transducer training ...", Introduction and Conclusion, name reduced and
+ * mixed precision without defining them; this is the library's reading.
+ * Tiled mode only (RNNT_E_UNSUPPORTED in untiled mode). */
+typedef enum { RNNT_F32 = 0, RNNT_BF16 = 1, RNNT_BF16_FP8 = 2 } rnnt_dtype;
 
 /* Tiled: the joint/output intermediates exist one wave of tiles at a time and
  * are recomputed in the backward. Untiled: the forward keeps z and the scores

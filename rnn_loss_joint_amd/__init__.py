@@ -20,7 +20,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "librnnt_mi355.so")
 
 RNNT_OK, RNNT_E_INVALID, RNNT_E_WORKSPACE, RNNT_E_HIP, RNNT_E_UNSUPPORTED = 0, -1, -2, -3, -4
-RNNT_F32, RNNT_BF16 = 0, 1
+RNNT_F32, RNNT_BF16, RNNT_BF16_FP8 = 0, 1, 2
 RNNT_TILED, RNNT_UNTILED = 0, 1
 
 _lib = None
@@ -94,9 +94,13 @@ def _check(status):
         raise RnntError(status, (lib.rnnt_last_error() or b"").decode())
 
 
+_DTYPES = {"f32": RNNT_F32, "bf16": RNNT_BF16, "bf16-fp8": RNNT_BF16_FP8}
+
+
 def make_desc(B, T, U, V, HA, HL, H, *, blank=0, dtype="bf16", mode="tiled", tile=(64, 32),
               tiles_per_wave=0) -> RnntDesc:
-    return RnntDesc(B, T, U, V, HA, HL, H, blank, RNNT_BF16 if dtype == "bf16" else RNNT_F32,
+    """dtype: "f32", "bf16", or "bf16-fp8" (bf16 inputs, the output layer's score product on E4M3)."""
+    return RnntDesc(B, T, U, V, HA, HL, H, blank, _DTYPES[dtype],
                     RNNT_UNTILED if mode == "untiled" else RNNT_TILED, tile[0], tile[1], tiles_per_wave, 0)
 
 
@@ -253,7 +257,9 @@ class Problem:
     bZ, WO, bO (numpy, float values exact in the dtype), e.g. rnnt_inputs.Inputs.
     """
 
-    def __init__(self, inputs, *, mode="tiled", tile=(64, 32), tiles_per_wave=0, device="cuda:0", band=None):
+    def __init__(self, inputs, *, mode="tiled", tile=(64, 32), tiles_per_wave=0, device="cuda:0", band=None,
+                 fp8=False):
+        """fp8: bf16 inputs with the output layer's score product on E4M3 operands (RNNT_BF16_FP8)."""
         import torch
 
         self.torch = torch
@@ -263,8 +269,11 @@ class Problem:
         U = inputs.hL.shape[1] - 1
         HL = inputs.hL.shape[2]
         V, H = inputs.WO.shape
-        self.desc = make_desc(B, T, U, V, HA, HL, H, blank=int(inputs.blank), dtype=inputs.dtype, mode=mode,
-                              tile=tile, tiles_per_wave=tiles_per_wave)
+        if fp8 and inputs.dtype != "bf16":
+            raise ValueError("the fp8 output layer takes bf16 inputs")
+        self.desc = make_desc(B, T, U, V, HA, HL, H, blank=int(inputs.blank),
+                              dtype="bf16-fp8" if fp8 else inputs.dtype, mode=mode, tile=tile,
+                              tiles_per_wave=tiles_per_wave)
         self.T_len = np.ascontiguousarray(inputs.T_len, dtype=np.int32)
         self.U_len = np.ascontiguousarray(inputs.U_len, dtype=np.int32)
         dev = torch.device(device)

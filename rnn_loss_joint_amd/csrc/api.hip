@@ -55,16 +55,18 @@ rnnt_status fail(rnnt_status s, const std::string& msg) {
 
 // The persistent score kernels need at least 8 stages of 64 k per item
 // (the previous item's epilogue runs in the first five).
-bool use_scores3(const rnnt::Plan& p) { return p.d.bf16 && !p.d.untiled && p.H_pad / 64 >= 8; }
+// fp8 always uses them (its operand rows are padded to at least five stages).
+bool use_scores3(const rnnt::Plan& p) { return p.d.fp8 || (p.d.bf16 && !p.d.untiled && p.H_pad / 64 >= 8); }
 
 rnnt_status to_dims(const rnnt_desc* desc, rnnt::Dims& d) {
   if (!desc) return fail(RNNT_E_INVALID, "desc is null");
-  if (desc->dtype != RNNT_F32 && desc->dtype != RNNT_BF16) return fail(RNNT_E_INVALID, "unknown dtype");
+  if (desc->dtype != RNNT_F32 && desc->dtype != RNNT_BF16 && desc->dtype != RNNT_BF16_FP8)
+    return fail(RNNT_E_INVALID, "unknown dtype");
   if (desc->mode != RNNT_TILED && desc->mode != RNNT_UNTILED) return fail(RNNT_E_INVALID, "unknown mode");
   if (desc->reserved != 0) return fail(RNNT_E_INVALID, "reserved field must be 0");
   d = rnnt::Dims{desc->B, desc->T, desc->U, desc->V, desc->HA, desc->HL, desc->H, desc->blank,
-                 desc->dtype == RNNT_BF16, desc->mode == RNNT_UNTILED, desc->tile_t, desc->tile_u,
-                 desc->tiles_per_wave};
+                 desc->dtype != RNNT_F32, desc->mode == RNNT_UNTILED, desc->dtype == RNNT_BF16_FP8,
+                 desc->tile_t, desc->tile_u, desc->tiles_per_wave};
   std::string err;
   int st = 0;
   if (!rnnt::check_dims(d, err, st)) return fail((rnnt_status)st, err);
@@ -472,10 +474,21 @@ static rnnt_status forward_impl(const rnnt_desc* desc, const void* hA, const voi
     float* hb = at<float>(workspace, L.w_hb);
     float* hy = at<float>(workspace, L.w_hy);
     const bool s3 = use_scores3(p);
-    if (s3) {
+    char* z8buf = d.fp8 ? at<char>(workspace, L.w_z8) : nullptr;
+    int* ew = d.fp8 ? at<int>(workspace, L.w_ew) : nullptr;
+    if (d.fp8) {
+      ProfScope ps_("score_tables", st);
+      RNNT_HIP(rnnt::launch_score_tables8(WO, bO, at<char>(workspace, L.w_WO8), at<float>(workspace, L.w_bl), ew, d.V,
+                                          d.H, p.H8, p.nvt, st));
+    } else if (s3) {
       ProfScope ps_("score_tables", st);
       RNNT_HIP(rnnt::launch_score_tables(WO, bO, at<char>(workspace, L.w_WOp), at<float>(workspace, L.w_bl), d.V,
                                          d.H, p.H_pad, p.nvt, st));
+    }
+    if (d.fp8 && p.H8 > p.H_pad) {
+      // the z-row kernel writes H_pad columns; the score kernels read H8
+      ProfScope ps_("fill", st);
+      RNNT_HIP(rnnt::launch_fill_bytes(z8buf, (int64_t)((p.max_wave_rows + 127) / 128 * 128) * p.H8, st));
     }
     for (const rnnt::WaveInfo& wv : p.waves) {
       const int wrows = wv.row_end - wv.row_begin;
@@ -499,10 +512,17 @@ static rnnt_status forward_impl(const rnnt_desc* desc, const void* hA, const voi
       z.l = sv.l;
       z.WO = WO;
       z.bO = bO;
-      z.z = zbuf;
+      z.z = d.fp8 ? nullptr : zbuf;  // fp8: the forward reads only the E4M3 rows
       z.z_ld = p.H_pad;
       z.hb = hb - (wv.row_begin - base);  // hb/hy indexed by wave-relative row
       z.hy = hy - (wv.row_begin - base);
+      if (d.fp8) {
+        z.z8 = z8buf;
+        z.z8_ld = p.H8;
+        z.WO8 = at<char>(workspace, L.w_WO8);
+        z.H8 = p.H8;
+        z.ew = ew;
+      }
       {
         ProfScope ps_("zrow", st);
         RNNT_HIP(rnnt::launch_zrow(z, st));
@@ -535,11 +555,18 @@ static rnnt_status forward_impl(const rnnt_desc* desc, const void* hA, const voi
         a3.V_pad = p.V_pad;
         a3.nvt = p.nvt;
         a3.blank = d.blank;
-        a3.WOp = at<char>(workspace, L.w_WOp);
+        a3.WOp = d.fp8 ? nullptr : at<char>(workspace, L.w_WOp);
         a3.bl = at<float>(workspace, L.w_bl);
-        a3.z = sc.z;
+        a3.z = d.fp8 ? nullptr : sc.z;
         a3.z_ld = p.H_pad;
         a3.stats = stats;
+        if (d.fp8) {
+          a3.WO8 = at<char>(workspace, L.w_WO8);
+          a3.z8 = z8buf;
+          a3.z8_ld = p.H8;
+          a3.H8 = p.H8;
+          a3.ew = ew;
+        }
         ProfScope ps_("scores_fwd", st);
         RNNT_HIP(rnnt::launch_scores3(a3, false, st));
       } else {
@@ -703,10 +730,20 @@ static rnnt_status backward_impl(const rnnt_desc* desc, const void* hA, const vo
     RNNT_HIP(rnnt::launch_transpose_wo(WOT, WO, d.V, d.H, p.V_pad, bf, st));
   }
   const bool s3 = use_scores3(p);
-  if (s3) {
+  char* z8buf = d.fp8 ? at<char>(workspace, L.w_z8) : nullptr;
+  int* ew = d.fp8 ? at<int>(workspace, L.w_ew) : nullptr;
+  if (d.fp8) {
+    ProfScope ps_("score_tables", st);
+    RNNT_HIP(rnnt::launch_score_tables8(WO, bO, at<char>(workspace, L.w_WO8), at<float>(workspace, L.w_bl), ew, d.V,
+                                        d.H, p.H8, p.nvt, st));
+  } else if (s3) {
     ProfScope ps_("score_tables", st);
     RNNT_HIP(rnnt::launch_score_tables(WO, bO, at<char>(workspace, L.w_WOp), at<float>(workspace, L.w_bl), d.V, d.H,
                                        p.H_pad, p.nvt, st));
+  }
+  if (d.fp8 && p.H8 > p.H_pad) {
+    ProfScope ps_("fill", st);
+    RNNT_HIP(rnnt::launch_fill_bytes(z8buf, (int64_t)((p.max_wave_rows + 127) / 128 * 128) * p.H8, st));
   }
 
   {
@@ -787,6 +824,13 @@ static rnnt_status backward_impl(const rnnt_desc* desc, const void* hA, const vo
       z.z_ld = p.H_pad;
       z.hb = nullptr;  // the backward needs z only
       z.hy = nullptr;
+      if (d.fp8) {  // and the E4M3 rows of the recomputed scores
+        z.z8 = z8buf;
+        z.z8_ld = p.H8;
+        z.WO8 = at<char>(workspace, L.w_WO8);
+        z.H8 = p.H8;
+        z.ew = ew;
+      }
       {
         ProfScope ps_("zrow", st);
         RNNT_HIP(rnnt::launch_zrow(z, st));
@@ -839,11 +883,18 @@ static rnnt_status backward_impl(const rnnt_desc* desc, const void* hA, const vo
         a3.V_pad = p.V_pad;
         a3.nvt = p.nvt;
         a3.blank = d.blank;
-        a3.WOp = at<char>(workspace, L.w_WOp);
+        a3.WOp = d.fp8 ? nullptr : at<char>(workspace, L.w_WOp);
         a3.bl = at<float>(workspace, L.w_bl);
-        a3.z = z_buf;
+        a3.z = d.fp8 ? nullptr : z_buf;
         a3.z_ld = p.H_pad;
         a3.dh = dh_buf;
+        if (d.fp8) {
+          a3.WO8 = at<char>(workspace, L.w_WO8);
+          a3.z8 = z8buf;
+          a3.z8_ld = p.H8;
+          a3.H8 = p.H8;
+          a3.ew = ew;
+        }
         a3.coefA = at<char>(workspace, L.w_coefA);
         a3.coefB = at<char>(workspace, L.w_coefB);
         a3.lse = sv.lse;

@@ -210,10 +210,18 @@ struct ZArgs {  // z rows and (hb != null) the blank / label scores of a wave's 
   const float* l;
   const void* WO;
   const void* bO;
-  void* z;  // [rows, z_ld] bf16
+  void* z;  // [rows, z_ld] bf16 (null: not written)
   int64_t z_ld;
   float* hb;
   float* hy;
+  // fp8 output layer: z8 [rows, z8_ld] = E4M3(z 2^8) (null: not written);
+  // with hb, the blank / label scores are those of the E4M3 operands (W^O
+  // rows from WO8 scaled by 2^-(8+e))
+  void* z8;
+  int64_t z8_ld;
+  const void* WO8;
+  int H8;
+  const int* ew;
 };
 hipError_t launch_zrow(const ZArgs& a, hipStream_t st);
 
@@ -282,6 +290,12 @@ struct Scores3Args {
   void* dh;          // backward: [n_ct*128][V_pad] bf16
   void* coefA;       // [n_ct*128] (lse log2 e, occupancy)
   void* coefB;       // [n_ct*128] (cb, cl, label, 0)
+  // fp8 output layer (WO8 non-null): E4M3 operands, rows of H8 bytes
+  const void* WO8;   // [nvt*256][H8] W^O 2^e, zero-padded
+  const void* z8;    // [n_ct*128][z8_ld] z 2^8
+  int64_t z8_ld;
+  int H8;
+  const int* ew;     // the scale exponent e of W^O
   const float* lse;
   const float* phi;
   const float* psi;
@@ -293,6 +307,11 @@ struct Scores3Args {
 hipError_t launch_scores3(const Scores3Args& a, bool bwd, hipStream_t st);
 hipError_t launch_score_tables(const void* WO, const void* bO, void* WOp, float* bl, int V, int H, int H_pad,
                                int nvt, hipStream_t st);
+// fp8 output layer: ew = the largest e with max|W^O| 2^e <= 448 (0 if W^O is
+// all zero), WO8 = E4M3(W^O 2^e) as [nvt*256][H8] bytes (0 past V and H), the
+// bias table bl as launch_score_tables writes it.
+hipError_t launch_score_tables8(const void* WO, const void* bO, void* WO8, float* bl, int* ew, int V, int H, int H8,
+                                int nvt, hipStream_t st);
 // grid over the wave's tiles x 32 x 32 blocks (+1 for the padding rows)
 hipError_t launch_coef(const Scores3Args& a, int tile_t, int tile_u, hipStream_t st);
 hipError_t launch_dh_fix(const Scores3Args& a, hipStream_t st);

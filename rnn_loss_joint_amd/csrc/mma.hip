@@ -27,9 +27,14 @@ namespace rnnt {
 // for k < H (0 up to z_ld and on padding rows t >= t0 + ht) and, with
 // SCORES, the blank and label scores of each row as dot products of that
 // bf16 z with the two W^O rows (plus the biases).
+// ZM selects the outputs: bit 0 the bf16 z rows, bit 1 the E4M3 rows
+// z8 = E4M3(z 2^8) of the fp8 output layer; with bit 1 the two scores are
+// those of the E4M3 operands: the rounded z (exact in bf16) against the W^O
+// rows of WO8 (decoded to bf16, also exact), scaled back by 2^-(8+e).
 constexpr int kZHmax = 768;  // H_pad bound (the library's H <= 768)
-template <bool SCORES, int NCH>
+template <bool SCORES, int NCH, int ZM>
 __global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
+  constexpr bool Z16 = (ZM & 1) != 0, F8 = (ZM & 2) != 0;
   __shared__ __attribute__((aligned(16))) char smem[8 * kZHmax * 4 + (SCORES ? 9 * kZHmax * 2 : 0)];
   float* const ls = reinterpret_cast<float*>(smem);                 // [8][H_pad] l rows
   bf16* const ws = reinterpret_cast<bf16*>(smem + 8 * kZHmax * 4);  // [9][H_pad] blank, label rows
@@ -81,7 +86,23 @@ __global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
     for (int i = tid; i < 9 * n8; i += 256) {
       const int r = i / n8, k = 8 * (i - r * n8);
       const int v = r == 0 ? p.blank : max(lab[r - 1], 0);
-      reinterpret_cast<bf16x8*>(ws)[i] = k < p.H ? ldg<bf16x8>(WO + (size_t)v * p.H + k) : bf16x8{};
+      if constexpr (F8) {
+        // E4M3 W^O 2^e (zero past H) decoded; every E4M3 value is exact in bf16
+        const u32x2 w8 = ldg<u32x2>(reinterpret_cast<const char*>(p.WO8) + (size_t)v * p.H8 + k);
+        f32x8 wf;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w8[h], false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w8[h], true);
+          wf[4 * h] = lo[0];
+          wf[4 * h + 1] = lo[1];
+          wf[4 * h + 2] = hi[0];
+          wf[4 * h + 3] = hi[1];
+        }
+        reinterpret_cast<bf16x8*>(ws)[i] = __builtin_convertvector(wf, bf16x8);
+      } else {
+        reinterpret_cast<bf16x8*>(ws)[i] = k < p.H ? ldg<bf16x8>(WO + (size_t)v * p.H + k) : bf16x8{};
+      }
     }
   }
   __syncthreads();
@@ -120,6 +141,31 @@ __global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
       for (int e = 0; e < 4; ++e) zf[e + 4] = tanh_from_scaled(a1[e] + l1[e]);
       bf16x8 z = __builtin_convertvector(zf, bf16x8);  // adjacent pairs: one packed convert each
       if (!kok) z = bf16x8{};
+      if constexpr (F8) {
+        // E4M3(z 2^8), two packed converts per four values (round to nearest even)
+        u32x2 q8;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(zf[4 * h] * 256.0f, zf[4 * h + 1] * 256.0f, 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(zf[4 * h + 2] * 256.0f, zf[4 * h + 3] * 256.0f, w, true);
+          q8[h] = kok ? (uint32_t)w : 0u;
+        }
+        *reinterpret_cast<u32x2*>(reinterpret_cast<char*>(p.z8) + (row0 + (int64_t)uu * tl.htp) * p.z8_ld + k) = q8;
+        if constexpr (SCORES) {
+          // the scores' operand is the rounded value
+          f32x8 zq;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)q8[h], false);
+            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)q8[h], true);
+            zq[4 * h] = lo[0];
+            zq[4 * h + 1] = lo[1];
+            zq[4 * h + 2] = hi[0];
+            zq[4 * h + 3] = hi[1];
+          }
+          z = __builtin_convertvector(zq, bf16x8);
+        }
+      }
       if constexpr (SCORES) {
         const bf16x8 xy = *reinterpret_cast<const bf16x8*>(ws + (uu + 1) * Hp + kk);
 #pragma unroll
@@ -129,12 +175,13 @@ __global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
           hy[uu] = __builtin_amdgcn_fdot2_f32_bf16(zz, bf16x2{xy[e], xy[e + 1]}, hy[uu], false);
         }
       }
-      *reinterpret_cast<bf16x8*>(zb + (row0 + (int64_t)uu * tl.htp) * p.z_ld + k) = z;
+      if constexpr (Z16) *reinterpret_cast<bf16x8*>(zb + (row0 + (int64_t)uu * tl.htp) * p.z_ld + k) = z;
     }
     }
   }
   if constexpr (SCORES) {
     const float bb = (float)bO[p.blank];
+    const float sc = F8 ? __builtin_ldexpf(1.0f, -(8 + *p.ew)) : 1.0f;
 #pragma unroll
     for (int uu = 0; uu < 8; ++uu) {
       float vb = hb[uu], vy = hy[uu];
@@ -145,8 +192,8 @@ __global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
       }
       if (q == 0 && uu < nu) {
         const int64_t rr = row0 + (int64_t)uu * tl.htp;
-        p.hb[rr] = vb + bb;
-        p.hy[rr] = lab[uu] >= 0 ? vy + (float)bO[lab[uu]] : 0.0f;
+        p.hb[rr] = __builtin_fmaf(vb, sc, bb);
+        p.hy[rr] = lab[uu] >= 0 ? __builtin_fmaf(vy, sc, (float)bO[lab[uu]]) : 0.0f;
       }
     }
   }
@@ -155,12 +202,22 @@ __global__ void __launch_bounds__(256) zrow_kernel(ZArgs p) {
 hipError_t launch_zrow(const ZArgs& a, hipStream_t st) {
   if (a.n_strips == 0) return hipSuccess;
   if (a.H_pad > kZHmax || a.H_pad % 8 != 0 || a.z_ld > a.H_pad) return hipErrorInvalidValue;  // LDS staging bound
+  const int zm = (a.z ? 1 : 0) | (a.z8 ? 2 : 0);
+  if (zm == 0 || (a.z8 && (!a.WO8 || !a.ew || a.z8_ld < a.z_ld || a.H8 < a.z_ld))) return hipErrorInvalidValue;
   dim3 grid(a.n_strips * a.n_ug), block(256);
   switch (a.z_ld) {
-#define RNNT_ZROW(N)                                                                   \
-  case 64 * N:                                                                         \
-    if (a.hb) hipLaunchKernelGGL((zrow_kernel<true, N>), grid, block, 0, st, a);       \
-    else hipLaunchKernelGGL((zrow_kernel<false, N>), grid, block, 0, st, a);           \
+#define RNNT_ZROW(N)                                                                         \
+  case 64 * N:                                                                               \
+    if (zm == 1) {                                                                           \
+      if (a.hb) hipLaunchKernelGGL((zrow_kernel<true, N, 1>), grid, block, 0, st, a);        \
+      else hipLaunchKernelGGL((zrow_kernel<false, N, 1>), grid, block, 0, st, a);            \
+    } else if (zm == 2) {                                                                    \
+      if (!a.hb) return hipErrorInvalidValue;                                                \
+      hipLaunchKernelGGL((zrow_kernel<true, N, 2>), grid, block, 0, st, a);                  \
+    } else {                                                                                 \
+      if (a.hb) return hipErrorInvalidValue;                                                 \
+      hipLaunchKernelGGL((zrow_kernel<false, N, 3>), grid, block, 0, st, a);                 \
+    }                                                                                        \
     break;
     RNNT_ZROW(2) RNNT_ZROW(4) RNNT_ZROW(6) RNNT_ZROW(8) RNNT_ZROW(10) RNNT_ZROW(12)
 #undef RNNT_ZROW

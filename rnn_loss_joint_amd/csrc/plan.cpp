@@ -55,6 +55,10 @@ bool check_dims(const Dims& d, std::string& err, int& status) {
     return false;
   }
   status = -4;  // RNNT_E_UNSUPPORTED
+  if (d.fp8 && (!d.bf16 || d.untiled)) {
+    err = "the fp8 output layer runs in tiled mode only";
+    return false;
+  }
   if (d.H % 8 || d.HA % 8 || d.HL % 8) {
     err = "this library needs H, HA and HL to be multiples of 8";
     return false;
@@ -139,6 +143,8 @@ void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H
   // bf16: whole 256-score tiles (the score kernels write every column of dh)
   p.V_pad = d.bf16 ? (int)cdiv(d.V, 256) * 256 : (int)cdiv(d.V, 64) * 64;
   p.KS = H_pad / 16;
+  // fp8: the score kernels take 128 k per stage and at least five stages per item
+  p.H8 = d.fp8 ? std::max(640, (int)cdiv(H_pad, 128) * 128) : 0;
   p.tile_tp = (int)cdiv(d.tile_t, 32) * 32;
 
   // per-sample tile grids
@@ -352,6 +358,12 @@ Layout make_layout(const Plan& p) {
     L.w_coefA = take(8 * wrows);
     L.w_coefB = take(16 * wrows);
   }
+  L.w_WO8 = L.w_z8 = L.w_ew = 0;
+  if (d.fp8) {
+    L.w_WO8 = take((size_t)p.nvt * 256 * p.H8);
+    L.w_z8 = take(wrows * p.H8);
+    L.w_ew = take(sizeof(int32_t));
+  }
   // bf16: gA and gL rounded to bf16 for the encoder-side products, in the
   // wave buffers (dh then z, contiguous, dead after the last wave) when they fit
   L.w_gb = 0;
@@ -388,15 +400,20 @@ Layout make_forward_layout(const Plan& p) {
   const size_t frows = d.untiled ? (size_t)p.total_rows : wrows;
   L.w_dh = L.w_gA = L.w_gL = L.w_PA = L.w_PL = L.w_PW = L.w_PB = L.w_PWA = L.w_PBZ = L.w_PWL = L.w_WOT = 0;
   L.w_coefA = L.w_coefB = L.w_gb = L.w_hs = L.w_WAT = L.w_WLT = 0;
-  L.w_z = L.w_stats = L.w_hb = L.w_hy = L.w_WOp = L.w_bl = 0;
+  L.w_z = L.w_stats = L.w_hb = L.w_hy = L.w_WOp = L.w_bl = L.w_WO8 = L.w_z8 = L.w_ew = 0;
   if (d.bf16) {
-    if (!d.untiled) L.w_z = take(2 * wrows * p.H_pad);
+    if (!d.untiled && !d.fp8) L.w_z = take(2 * wrows * p.H_pad);  // fp8: the forward needs no bf16 z
     L.w_stats = take(8 * frows * p.nvt);
     L.w_hb = take(4 * frows);
     L.w_hy = take(4 * frows);
     if (!d.untiled) {
-      L.w_WOp = take(2 * (size_t)p.nvt * 256 * p.H_pad);
+      if (!d.fp8) L.w_WOp = take(2 * (size_t)p.nvt * 256 * p.H_pad);  // fp8: the E4M3 rows instead
       L.w_bl = take(4 * (size_t)p.nvt * 256);
+    }
+    if (d.fp8) {
+      L.w_WO8 = take((size_t)p.nvt * 256 * p.H8);
+      L.w_z8 = take(wrows * p.H8);
+      L.w_ew = take(sizeof(int32_t));
     }
   }
   L.workspace_bytes = o;

@@ -24,6 +24,7 @@ struct Dims {
   int B, T, U, V, HA, HL, H, blank;
   bool bf16;
   bool untiled;
+  bool fp8;  // bf16 inputs, output-layer product of the score kernels on E4M3 operands (tiled only)
   int tile_t, tile_u, tiles_per_wave;
 };
 
@@ -57,6 +58,7 @@ struct Plan {
   int max_wave_rows = 0, max_wave_tiles = 0;
   int s6 = 1, s7a = 1, s7l = 1;  // split-K counts
   int nvt = 1;                   // 256-score tiles of the vocabulary (bf16 path)
+  int H8 = 0;                    // fp8: bytes per row of the E4M3 operands (>= H_pad, >= 640; 0 otherwise)
 };
 
 // Byte offsets inside `saved` and `workspace` (all 256-byte aligned).
@@ -75,6 +77,7 @@ struct Layout {
   size_t w_dh, w_z, w_gA, w_gL, w_PA, w_PL, w_PW, w_PB, w_PWA, w_PBZ, w_PWL, w_WOT;
   size_t w_zf, w_stats, w_hb, w_hy;  // bf16 forward: z rows, V-tile statistics, blank/label scores
   size_t w_WOp, w_bl, w_coefA, w_coefB;  // bf16 tiled: persistent score kernels
+  size_t w_WO8, w_z8, w_ew;              // fp8: E4M3 W^O rows, z rows, W^O scale exponent (int)
   size_t w_gb;  // bf16: rounded gA, gL for the encoder-side products (may alias w_dh)
   size_t w_WAT, w_WLT;  // bf16: W^A^T [HA, H], W^L^T [HL, H] for dh^A, dh^L
   size_t w_hs;          // bf16: h^A, h^L with padding rows zeroed, for dW^A, dW^L (may alias w_dh)

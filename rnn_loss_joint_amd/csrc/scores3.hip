@@ -17,6 +17,15 @@
 // item n+1, a few VALU instructions after each MFMA, on the second of two
 // accumulator sets, so exp2 and the other vector work overlap the matrix
 // cores. Per-item bias and cell coefficients arrive by dma with the stages.
+//
+// FP8 variant: the same pipeline over OCP E4M3 operands (z scaled by 2^8,
+// W^O by 2^e): a stage's 128 bytes per row are 128 k values, taken by two
+// 32 x 32 x 64 MFMAs per block; an fp8 fragment (32 bytes per lane) is the
+// pair of 16-byte pieces the bf16 kernel reads for two k-steps, so the LDS
+// layout, swizzle and dma are unchanged. The fragments are single-buffered
+// (each one re-read right after its last MFMA of the k-step), which keeps
+// the register count of the bf16 kernel's double buffers. The scores are
+// scaled back by 2^-(8+e) in the epilogue.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_core.hpp"
@@ -33,18 +42,27 @@ constexpr int B_BYTES = s3map::B_BYTES;
 constexpr int STAGE = A_BYTES + B_BYTES;
 constexpr int NDA = s3map::NDA;  // 16-byte dma per thread per stage
 constexpr int NDB = s3map::NDB;
-constexpr int OFF_BIAS = NST * STAGE;              // [2][256] f32: b^O log2 e
-constexpr int OFF_COEF = OFF_BIAS + 2 * 256 * 4;   // [2][128][2] f32: (lse log2 e, occupancy)
-constexpr int OFF_RED = OFF_COEF + 2 * 256 * 4;    // [2 wc][2 j][2][32] f32
-constexpr int LDS_BYTES = OFF_RED + 2 * 2 * 2 * 32 * 4;
 // backward: per wave, one finished 32 x 32 block of dh (bf16) [cell][score],
 // rows of 80 bytes (64 used), so dh goes out as whole 64-byte row pieces
 constexpr int DHS_ROW = 80, DHS_WAVE = 32 * DHS_ROW;
-constexpr int OFF_DHS = LDS_BYTES;
-constexpr int LDS_BYTES_BWD = OFF_DHS + 4 * DHS_WAVE;
+// LDS regions after the stages. Item n's bias (and, backward, coefficients)
+// sit in buffer n mod NBUF: with bf16 an item has at least 8 stages, so the
+// dma of item n+1's first stages (issued three stages ahead) starts after
+// item n-1's epilogue (in item n's first five stages) has read its buffers;
+// with fp8 (5 stages per item at H = 640) it does not, so three buffers.
+template <bool BWD, bool FP8>
+struct Lay {
+  static constexpr int NBUF = FP8 ? 3 : 2;
+  static constexpr int OFF_BIAS = NST * STAGE;               // [NBUF][256] f32: b^O log2 e
+  static constexpr int OFF_COEF = OFF_BIAS + NBUF * 256 * 4; // [NBUF][128][2] f32: (lse log2 e, occupancy)
+  static constexpr int OFF_RED = OFF_COEF + NBUF * 256 * 4;  // [2 wc][2 j][2][32] f32 (forward)
+  static constexpr int RED_BYTES = (BWD && FP8) ? 0 : 2 * 2 * 2 * 32 * 4;
+  static constexpr int OFF_DHS = OFF_RED + RED_BYTES;
+  static constexpr int BYTES = BWD ? OFF_DHS + 4 * DHS_WAVE : OFF_RED + RED_BYTES;
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
 constexpr int WM = 4, WN = 2;  // 32 x 32 blocks per wave
 constexpr int EPI_STAGES = 5;  // stages of item n+1 that carry the epilogue of item n
-static_assert(LDS_BYTES_BWD <= 160 * 1024, "LDS budget");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -57,18 +75,26 @@ __device__ inline void dma_b32(const char* g, char* l) {
 
 }  // namespace s3
 
-template <bool BWD>
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <bool BWD, bool FP8>
 __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
   using namespace s3;
   using m3::lds_barrier;
   using m3::wait_vm;
-  __shared__ __attribute__((aligned(1024))) char lds[BWD ? LDS_BYTES_BWD : LDS_BYTES];
+  using LY = Lay<BWD, FP8>;
+  constexpr int NBUF = LY::NBUF, OFF_BIAS = LY::OFF_BIAS, OFF_COEF = LY::OFF_COEF, OFF_RED = LY::OFF_RED,
+                OFF_DHS = LY::OFF_DHS;
+  __shared__ __attribute__((aligned(1024))) char lds[LY::BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
   const int r = lane & 31, g = lane >> 5;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int nvt = p.nvt, nq = p.H_pad / BK;
+  // row lengths in 2-byte units (fp8: 128 values per stage and row)
+  const int hrow = FP8 ? p.H8 / 2 : p.H_pad;
+  const int64_t zld = FP8 ? p.z8_ld / 2 : p.z_ld;
+  const int nvt = p.nvt, nq = hrow / BK;
   // items (ct, vt) of this workgroup, see scores3_map.hpp
   const int nctl = s3map::nctl_of(p.n_ct, xcd);
   const int n_items = s3map::items_of(p.n_ct, nvt, xcd, slot);
@@ -82,17 +108,19 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
   uint32_t offA[2], offB[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    offA[i] = s3map::dma_thread_off(i, wave, lane, p.H_pad);
-    offB[i] = s3map::dma_thread_off(i, wave, lane, (int)p.z_ld);
+    offA[i] = s3map::dma_thread_off(i, wave, lane, hrow);
+    offB[i] = s3map::dma_thread_off(i, wave, lane, (int)zld);
   }
-  const int64_t stepA = (int64_t)32 * p.H_pad * 2, stepB = (int64_t)32 * p.z_ld * 2;
+  const int64_t stepA = (int64_t)32 * hrow * 2, stepB = (int64_t)32 * zld * 2;
   // Fragment reads: row wr*128 + 32 f + r of A (wc*64 + 32 f + r of B), chunk
   // (2 ss + g) ^ swz(row); swz(row) = s0 ^ 4 (f & 1) with s0 = swz(r), so the
   // per-lane part is rb + (c0[ss] ^ 64 (f & 1)) and 4096 f is an immediate.
   const int s0 = swz(r);
   const uint32_t rbA = (uint32_t)((wr * 128 + r) * 128), rbB = (uint32_t)(A_BYTES + (wc * 64 + r) * 128);
-  const char* WOp = reinterpret_cast<const char*>(p.WOp);
-  const char* zb = reinterpret_cast<const char*>(p.z);
+  const char* WOp = reinterpret_cast<const char*>(FP8 ? p.WO8 : p.WOp);
+  const char* zb = reinterpret_cast<const char*>(FP8 ? p.z8 : p.z);
+  // scores in log2 units: acc (log2 e) for bf16, acc 2^-(8+e) (log2 e) for fp8
+  const float ysc = FP8 ? kLog2e * __builtin_ldexpf(1.0f, -(8 + *p.ew)) : kLog2e;
   const char* blt = reinterpret_cast<const char*>(p.bl);
   const char* cft = reinterpret_cast<const char*>(p.coefA);
 
@@ -107,7 +135,7 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
     int par;
   };
   auto stage_src = [&](int S) {
-    const s3map::StageSrc o = s3map::stage_src(S, nq, n_items, nctl, nvt, xcd, slot, p.H_pad, p.z_ld);
+    const s3map::StageSrc o = s3map::stage_src(S, nq, n_items, nctl, nvt, xcd, slot, hrow, zld, NBUF);
     Src s;
     s.a = WOp + o.a;
     s.b = zb + o.b;
@@ -136,8 +164,27 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
     }
   };
 
+  // fp8 fragment f of k-step ks (0, 1) of a stage: the 16-byte pieces of the
+  // bf16 k-steps 2 ks and 2 ks + 1, i.e. chunks (4 ks + g) ^ s0 and
+  // (4 ks + 2 + g) ^ s0 of the row, with bit 2 of the chunk flipped for odd
+  // f. Rows start at multiples of 128 bytes, so every piece's offset is the
+  // lane's base rb + ((g ^ s0) << 4) XOR a constant below 128. The base
+  // passes through an empty asm at each read so the compiler forms the XOR
+  // there instead of keeping all sixteen offsets live (which spilled).
+  const uint32_t baseA8 = rbA + (uint32_t)((g ^ s0) << 4), baseB8 = rbB + (uint32_t)((g ^ s0) << 4);
+  auto read_frag8 = [&](int f, const char* st, int ks, i32x8* a, i32x8* b) {
+    const int ff = f < WM ? f : f - WM;
+    uint32_t base = f < WM ? baseA8 : baseB8;
+    asm volatile("" : "+v"(base));
+    const uint32_t k0 = (uint32_t)(64 * ks) ^ (uint32_t)(64 * (ff & 1));
+    i32x8* dst = f < WM ? &a[ff] : &b[ff];
+    reinterpret_cast<u32x4*>(dst)[0] = *reinterpret_cast<const u32x4*>(st + (base ^ k0) + 4096 * ff);
+    reinterpret_cast<u32x4*>(dst)[1] = *reinterpret_cast<const u32x4*>(st + (base ^ k0 ^ 32u) + 4096 * ff);
+  };
+
   f32x16 acc[2][WM][WN];
   bf16x8 af[2][WM], bfr[2][WN];
+  i32x8 af8[WM], bf8[WN];
 
   // ---------------------------------------------------------------- epilogue state
   // The item being finalized: its cell tile, V tile and parity (LDS buffers).
@@ -179,7 +226,7 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
           }
 #pragma unroll
           for (int e = 2 * X; e < 2 * X + 2; ++e) {
-            y[e] = __builtin_fmaf(acc[E][i][j][e], kLog2e, bq[e >> 2][e & 3]);
+            y[e] = __builtin_fmaf(acc[E][i][j][e], ysc, bq[e >> 2][e & 3]);
             ebm = __builtin_fmaxf(ebm, y[e]);
           }
         } else {
@@ -253,7 +300,7 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
             bq[q4] = *reinterpret_cast<const f32x4*>(bias + wr * 128 + i * 32 + 8 * q4 + 4 * g);
         }
         constexpr int e = 8 * hh + X;
-        y[e] = es[j] * fexp2(__builtin_fmaf(acc[E][i][j][e], kLog2e, bq[e >> 2][e & 3]) - em[j]);
+        y[e] = es[j] * fexp2(__builtin_fmaf(acc[E][i][j][e], ysc, bq[e >> 2][e & 3]) - em[j]);
         if constexpr (X == 3 || X == 7) {
           // scores 8 (e4 / 4) + 4 g .. +3 of the block for cell r, into the staging buffer
           constexpr int e4 = e - 3;
@@ -305,6 +352,47 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // fp8 k-step (64 k): 8 MFMAs 32 x 32 x 64 into set C, column block j
+  // outer, so fragment B0 is free after MFMA 3 and A_i after MFMA 4 + i; each
+  // is then re-read for (rd_st, rd_ks). Epilogue tasks T (chunks after MFMAs
+  // 0-3, two each) and T + 1 (after 4-7) on set C^1, in order.
+  auto kstep8 = [&](auto CC, auto ZERO, auto TT, const char* rd_st, int rd_ks, bool dma,
+                    int dma_s) __attribute__((always_inline)) {
+    constexpr int C = decltype(CC)::value;
+    constexpr bool zero = decltype(ZERO)::value;
+    constexpr int T = decltype(TT)::value;
+    Src ds{};
+    if (dma) ds = stage_src(dma_s);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int x = 0; x < WM * WN; ++x) {
+      const int i = x % WM, j = x / WM;
+      acc[C][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af8[i], bf8[j], zero ? f32x16{} : acc[C][i][j],
+                                                                    0, 0, 0, 0, 0, 0);
+      if (x == WM - 1) read_frag8(WM, rd_st, rd_ks, af8, bf8);       // B0
+      if (x >= WM) read_frag8(x - WM, rd_st, rd_ks, af8, bf8);       // A_i
+      if (x == 2 * WM - 1) read_frag8(WM + 1, rd_st, rd_ks, af8, bf8);  // B1
+      if (dma) {
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+          if (d * 8 / ND == x) issue_one(ds, d);
+      }
+      if constexpr (T >= 0) {
+        using Cx = std::integral_constant<int, C ^ 1>;
+        using Ta = std::integral_constant<int, T>;
+        using Tb = std::integral_constant<int, T + 1>;
+        if (x == 0) { epi_chunk(Cx{}, Ta{}, std::integral_constant<int, 0>{}); epi_chunk(Cx{}, Ta{}, std::integral_constant<int, 1>{}); }
+        if (x == 1) { epi_chunk(Cx{}, Ta{}, std::integral_constant<int, 2>{}); epi_chunk(Cx{}, Ta{}, std::integral_constant<int, 3>{}); }
+        if (x == 2) { epi_chunk(Cx{}, Ta{}, std::integral_constant<int, 4>{}); epi_chunk(Cx{}, Ta{}, std::integral_constant<int, 5>{}); }
+        if (x == 3) { epi_chunk(Cx{}, Ta{}, std::integral_constant<int, 6>{}); epi_chunk(Cx{}, Ta{}, std::integral_constant<int, 7>{}); }
+        if (x == 4) { epi_chunk(Cx{}, Tb{}, std::integral_constant<int, 0>{}); epi_chunk(Cx{}, Tb{}, std::integral_constant<int, 1>{}); }
+        if (x == 5) { epi_chunk(Cx{}, Tb{}, std::integral_constant<int, 2>{}); epi_chunk(Cx{}, Tb{}, std::integral_constant<int, 3>{}); }
+        if (x == 6) { epi_chunk(Cx{}, Tb{}, std::integral_constant<int, 4>{}); epi_chunk(Cx{}, Tb{}, std::integral_constant<int, 5>{}); }
+        if (x == 7) { epi_chunk(Cx{}, Tb{}, std::integral_constant<int, 6>{}); epi_chunk(Cx{}, Tb{}, std::integral_constant<int, 7>{}); }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
   using F = std::integral_constant<bool, false>;
@@ -321,7 +409,10 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
     wait_vm<ND>();
     lds_barrier();
 #pragma unroll
-    for (int f = 0; f < WM + WN; ++f) read_frag(f, lds, 0, af[0], bfr[0]);
+    for (int f = 0; f < WM + WN; ++f) {
+      if constexpr (FP8) read_frag8(f, lds, 0, af8, bf8);
+      else read_frag(f, lds, 0, af[0], bfr[0]);
+    }
     const Src s2 = stage_src(2);
 #pragma unroll
     for (int d = 0; d < ND; ++d) issue_one(s2, d);
@@ -333,7 +424,16 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
     constexpr int C = decltype(CC)::value;
     constexpr int Q = decltype(QQ)::value;  // < 0: a stage without epilogue work
     const char* cur = lds + (S % NST) * STAGE;
-    if constexpr (Q >= 0) {
+    if constexpr (FP8) {
+      // two k-steps of 64: tasks 4Q, 4Q+1 before the hand-over, 4Q+2, 4Q+3 after
+      using Z = std::integral_constant<bool, Q == 0>;
+      using T0 = std::integral_constant<int, Q >= 0 ? 4 * Q : -1>;
+      using T2 = std::integral_constant<int, Q >= 0 ? 4 * Q + 2 : -1>;
+      kstep8(CC, Z{}, T0{}, cur, 1, false, 0);
+      wait_vm<ND>();  // stage S+1 landed; stage S+2 may be in flight
+      lds_barrier();  // every wave is done with slot S
+      kstep8(CC, F{}, T2{}, lds + ((S + 1) % NST) * STAGE, 0, true, S + 3);
+    } else if constexpr (Q >= 0) {
       using Z = std::integral_constant<bool, Q == 0>;
       kstep(C0{}, CC, Z{}, std::integral_constant<int, 4 * Q + 0>{}, cur, 1, false, 0);
       kstep(C1{}, CC, F{}, std::integral_constant<int, 4 * Q + 1>{}, cur, 2, false, 0);
@@ -361,7 +461,7 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
     // this item is the one finalized during the next
     e_live = true;
     item_of(n, e_ct, e_vt);
-    e_par = n & 1;
+    e_par = n % NBUF;
   };
 
   for (int n = 0; n < n_items; n += 2) {
@@ -394,8 +494,18 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
 hipError_t launch_scores3(const Scores3Args& a, bool bwd, hipStream_t st) {
   if (a.n_ct == 0) return hipSuccess;
   dim3 grid(256), block(256);
-  if (bwd) hipLaunchKernelGGL(scores3_kernel<true>, grid, block, 0, st, a);
-  else hipLaunchKernelGGL(scores3_kernel<false>, grid, block, 0, st, a);
+  const bool fp8 = a.WO8 != nullptr;
+  // at least EPI_STAGES stages per item; fp8 rows are whole stages of 128 bytes
+  if (fp8 ? (a.H8 % 128 != 0 || a.H8 / 128 < s3::EPI_STAGES || a.z8_ld % 128 != 0 || !a.z8 || !a.ew)
+          : (a.H_pad % 64 != 0 || a.H_pad / 64 < 8))
+    return hipErrorInvalidValue;
+  if (fp8) {
+    if (bwd) hipLaunchKernelGGL((scores3_kernel<true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((scores3_kernel<false, true>), grid, block, 0, st, a);
+  } else {
+    if (bwd) hipLaunchKernelGGL((scores3_kernel<true, false>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((scores3_kernel<false, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -421,6 +531,72 @@ hipError_t launch_score_tables(const void* WO, const void* bO, void* WOp, float*
   const int rows = nvt * 256;
   hipLaunchKernelGGL(pad_wo_kernel, dim3(512), dim3(256), 0, st, reinterpret_cast<const bf16*>(WO),
                      reinterpret_cast<bf16*>(WOp), V, H, H_pad, rows);
+  hipLaunchKernelGGL(bias_table_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, reinterpret_cast<const bf16*>(bO),
+                     bl, V, rows);
+  return hipGetLastError();
+}
+
+// fp8 output layer: the scale exponent of W^O, one workgroup. |x| of a bf16
+// orders like its bits with the sign cleared, so the largest magnitude is the
+// largest such bit pattern (NaN and infinity are clamped to the largest
+// finite value). e is the largest integer with amax 2^e <= 448 = 0.875 2^9:
+// with amax = m 2^x, m in [0.5, 1), e = 9 - x if m <= 0.875, else 8 - x.
+__global__ void __launch_bounds__(1024) wo_scale_kernel(const u32x4* __restrict__ WO, int64_t n16, int* ew) {
+  __shared__ uint32_t red[16];
+  uint32_t m = 0;
+  for (int64_t i = threadIdx.x; i < n16; i += 1024) {
+    const u32x4 v = WO[i];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m = max(m, max(v[q] & 0x7fffu, (v[q] >> 16) & 0x7fffu));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = 0;
+    for (int i = 0; i < 16; ++i) a = max(a, red[i]);
+    a = min(a, 0x7f7fu);
+    int e = 0;
+    if (a != 0) {
+      int x = 0;
+      const float mnt = __builtin_frexpf(__uint_as_float(a << 16), &x);
+      e = mnt <= 0.875f ? 9 - x : 8 - x;
+    }
+    *ew = e;
+  }
+}
+
+// WO8[v][k] = E4M3(W^O[v][k] 2^e) for v < V, k < H (the product is exact in
+// fp32), 0 elsewhere up to [nvt*256][H8]; four bytes per thread.
+__global__ void pad_wo8_kernel(const bf16* __restrict__ WO, uint32_t* __restrict__ WO8, const int* __restrict__ ew,
+                               int V, int H, int H8, int rows) {
+  const int e = *ew;
+  const int q4 = H8 / 4;
+  const int64_t n = (int64_t)rows * q4;
+  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < n; x += (int64_t)gridDim.x * blockDim.x) {
+    const int v = (int)(x / q4), k = 4 * (int)(x - (int64_t)v * q4);
+    uint32_t w = 0;
+    if (v < V && k < H) {  // H % 4 == 0: the four values are all inside or all outside
+      const bf16* src = WO + (int64_t)v * H + k;
+      int r = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf((float)src[0], e), __builtin_ldexpf((float)src[1], e),
+                                              0, false);
+      r = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf((float)src[2], e), __builtin_ldexpf((float)src[3], e), r,
+                                          true);
+      w = (uint32_t)r;
+    }
+    WO8[x] = w;
+  }
+}
+
+hipError_t launch_score_tables8(const void* WO, const void* bO, void* WO8, float* bl, int* ew, int V, int H, int H8,
+                                int nvt, hipStream_t st) {
+  const int rows = nvt * 256;
+  if (H % 8 != 0 || H8 % 4 != 0 || H8 < H) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(wo_scale_kernel, dim3(1), dim3(1024), 0, st, reinterpret_cast<const u32x4*>(WO),
+                     (int64_t)V * H / 8, ew);
+  hipLaunchKernelGGL(pad_wo8_kernel, dim3(512), dim3(256), 0, st, reinterpret_cast<const bf16*>(WO),
+                     reinterpret_cast<uint32_t*>(WO8), ew, V, H, H8, rows);
   hipLaunchKernelGGL(bias_table_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, reinterpret_cast<const bf16*>(bO),
                      bl, V, rows);
   return hipGetLastError();

@@ -54,20 +54,22 @@ constexpr Item item_of(int n, int n_items, int nctl, int nvt, int xcd, int slot)
   return Item{(nctl - 1 - c0) * 8 + xcd, idx - c0 * nvt};
 }
 
-// Byte offsets of stage S's sources (S = n * nq + q, nq = H_pad / BK k-steps
+// Byte offsets of stage S's sources (S = n * nq + q, nq = H_pad / BK stages
 // per item) from the base of each buffer: A = padded W^O rows of V tile vt,
 // B = z rows of cell tile ct, the V tile's 256 bias values, the cell tile's
-// 128 backward coefficient pairs.
+// 128 backward coefficient pairs. Row lengths H_pad and z_ld count 2-byte
+// units: a stage moves 128 bytes of each row (64 bf16, or 128 fp8 values
+// with the row lengths halved).
 struct StageSrc {
   int64_t a, b, bias, coef;
-  int par;  // parity of the (clamped) item: which LDS bias / coefficient buffer
+  int par;  // (clamped) item index mod nbuf: which LDS bias / coefficient buffer
 };
 constexpr StageSrc stage_src(int S, int nq, int n_items, int nctl, int nvt, int xcd, int slot, int H_pad,
-                             int64_t z_ld) {
+                             int64_t z_ld, int nbuf = 2) {
   const int n = S / nq, q = S - (S / nq) * nq;
   const Item it = item_of(n, n_items, nctl, nvt, xcd, slot);
   return StageSrc{((int64_t)it.vt * 256 * H_pad + q * BK) * 2, ((int64_t)it.ct * BN * z_ld + q * BK) * 2,
-                  (int64_t)it.vt * 256 * 4, (int64_t)it.ct * BN * 8, imin(n, n_items - 1) & 1};
+                  (int64_t)it.vt * 256 * 4, (int64_t)it.ct * BN * 8, imin(n, n_items - 1) % nbuf};
 }
 
 // Per-thread part of the operand dma: instruction d of an operand (d < NDA

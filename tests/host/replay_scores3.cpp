@@ -15,7 +15,8 @@
 //     region the layout reserves for it.
 // Nothing is launched: this is plain C++ against the plan and layout.
 //
-// Input, one case per line: B T U V HA HL H bf16 untiled tile_t tile_u tpw,
+// Input, one case per line: B T U V HA HL H dtype untiled tile_t tile_u tpw
+// (dtype 0 fp32, 1 bf16, 2 bf16 with the fp8 output layer),
 // then B values of T_len and B values of U_len, optionally followed by a
 // band width S and B * T band starts (a pruned lattice). Output per case:
 // "ok <stages checked> tiles <n>" or "skip <reason>" or "FAIL <what>".
@@ -62,23 +63,31 @@ std::string run_case(const Dims& d, const std::vector<int32_t>& T_len, const std
   build_plan(d, T_len.data(), U_len.data(), ks * 16, p, band);
   if (!check_plan(p, err)) return "skip " + err;
   const Layout L = make_layout(p);
-  // the persistent score kernels run in bf16 tiled mode with at least 8 k-steps of 64
-  if (!d.bf16 || d.untiled || p.H_pad / 64 < 8) return "skip not the persistent score path";
+  // the persistent score kernels run in bf16 tiled mode with at least 8 k-steps of 64, and
+  // always with the fp8 output layer (E4M3 rows of H8 >= 640 bytes)
+  if (!d.fp8 && (!d.bf16 || d.untiled || p.H_pad / 64 < 8)) return "skip not the persistent score path";
   std::vector<int64_t> offs = {
       (int64_t)L.w_dh, (int64_t)L.w_z, (int64_t)L.w_gA, (int64_t)L.w_gL, (int64_t)L.w_PA, (int64_t)L.w_PL,
       (int64_t)L.w_PW, (int64_t)L.w_PB, (int64_t)L.w_PWA, (int64_t)L.w_PBZ, (int64_t)L.w_PWL, (int64_t)L.w_WOT,
       (int64_t)L.w_stats, (int64_t)L.w_hb, (int64_t)L.w_hy, (int64_t)L.w_WOp, (int64_t)L.w_bl,
       (int64_t)L.w_coefA, (int64_t)L.w_coefB, (int64_t)L.w_WAT, (int64_t)L.w_WLT};
+  if (d.fp8)
+    for (size_t o : {L.w_WO8, L.w_z8, L.w_ew}) offs.push_back((int64_t)o);
   // the rounded gA / gL and the masked encodings live in the wave buffers
   // (dead after the last wave) when they fit there, else in regions of their own
   for (size_t o : {L.w_gb, L.w_hs})
     if (o >= L.w_coefB) offs.push_back((int64_t)o);
   const int64_t W = (int64_t)L.workspace_bytes;
-  const Region rz = region(L.w_z, offs, W), rdh = region(L.w_dh, offs, W), rst = region(L.w_stats, offs, W);
-  const Region rwo = region(L.w_WOp, offs, W), rbl = region(L.w_bl, offs, W), rco = region(L.w_coefA, offs, W);
+  // the operands: bf16 rows of H_pad values, or (fp8) E4M3 rows of H8 bytes, which the
+  // kernel addresses as rows of H8 / 2 two-byte units
+  const size_t off_z = d.fp8 ? L.w_z8 : L.w_z, off_wo = d.fp8 ? L.w_WO8 : L.w_WOp;
+  const Region rz = region(off_z, offs, W), rdh = region(L.w_dh, offs, W), rst = region(L.w_stats, offs, W);
+  const Region rwo = region(off_wo, offs, W), rbl = region(L.w_bl, offs, W), rco = region(L.w_coefA, offs, W);
   const int64_t buf_rows = (p.max_wave_rows + 127) / 128 * 128;
-  const int nvt = p.nvt, nq = p.H_pad / s3map::BK;
-  const int64_t z_ld = p.H_pad;
+  const int hrow = d.fp8 ? p.H8 / 2 : p.H_pad;
+  const int nvt = p.nvt, nq = hrow / s3map::BK, nbuf = d.fp8 ? 3 : 2;
+  const int64_t z_ld = hrow;
+  if (d.fp8 && (p.H8 % 128 != 0 || nq < 5)) return "FAIL fp8 operand rows shorter than five stages";
 
   // per-thread dma offsets relative to a stage's source, over all threads
   // and instructions of an operand: [lo, hi) in bytes
@@ -97,7 +106,7 @@ std::string run_case(const Dims& d, const std::vector<int32_t>& T_len, const std
     }
   };
   int64_t a_lo, a_hi, b_lo, b_hi;
-  dma_span(s3map::NDA, p.H_pad, a_lo, a_hi);
+  dma_span(s3map::NDA, hrow, a_lo, a_hi);
   dma_span(s3map::NDB, (int)z_ld, b_lo, b_hi);
 
   for (size_t w = 0; w < p.waves.size(); ++w) {
@@ -126,9 +135,10 @@ std::string run_case(const Dims& d, const std::vector<int32_t>& T_len, const std
           const s3map::Item it = s3map::item_of(S / nq, n_items, nctl, nvt, xcd, slot);
           if (it.ct < 0 || it.ct >= n_ct) return bad("cell tile " + std::to_string(it.ct) + " out of range", S);
           if (it.vt < 0 || it.vt >= nvt) return bad("V tile " + std::to_string(it.vt) + " out of range", S);
-          const s3map::StageSrc o = s3map::stage_src(S, nq, n_items, nctl, nvt, xcd, slot, p.H_pad, z_ld);
-          if (!inside(rwo, L.w_WOp + o.a + a_lo, L.w_WOp + o.a + a_hi)) return bad("W^O rows outside", S);
-          if (!inside(rz, L.w_z + o.b + b_lo, L.w_z + o.b + b_hi)) return bad("z rows outside", S);
+          const s3map::StageSrc o = s3map::stage_src(S, nq, n_items, nctl, nvt, xcd, slot, hrow, z_ld, nbuf);
+          if (!inside(rwo, off_wo + o.a + a_lo, off_wo + o.a + a_hi)) return bad("W^O rows outside", S);
+          if (!inside(rz, off_z + o.b + b_lo, off_z + o.b + b_hi)) return bad("z rows outside", S);
+          if (o.par < 0 || o.par >= nbuf) return bad("bias buffer index out of range", S);
           // the z rows a stage reads belong to its cell tile's 128 rows
           if (o.b + b_lo < (int64_t)it.ct * 128 * z_ld * 2 || o.b + b_hi > ((int64_t)it.ct + 1) * 128 * z_ld * 2)
             return bad("z bytes outside the item's cell tile", S);
@@ -170,6 +180,7 @@ int main() {
     in >> d.B >> d.T >> d.U >> d.V >> d.HA >> d.HL >> d.H >> bf >> un >> d.tile_t >> d.tile_u >> d.tiles_per_wave;
     d.blank = 0;
     d.bf16 = bf != 0;
+    d.fp8 = bf == 2;
     d.untiled = un != 0;
     std::vector<int32_t> T_len(d.B), U_len(d.B);
     for (auto& x : T_len) in >> x;

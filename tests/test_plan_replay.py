@@ -34,8 +34,8 @@ def replay(tmp_path_factory):
     return exe
 
 
-def case_line(B, T, U, V, HA, HL, H, tile, tpw, T_len, U_len, bf16=True, untiled=False, band=None):
-    vals = [B, T, U, V, HA, HL, H, int(bf16), int(untiled), tile[0], tile[1], tpw]
+def case_line(B, T, U, V, HA, HL, H, tile, tpw, T_len, U_len, bf16=True, untiled=False, band=None, fp8=False):
+    vals = [B, T, U, V, HA, HL, H, 2 if fp8 else int(bf16), int(untiled), tile[0], tile[1], tpw]
     vals += list(map(int, T_len)) + list(map(int, U_len))
     if band is not None:
         vals += [int(band[1])] + list(map(int, np.asarray(band[0]).reshape(-1)))
@@ -85,6 +85,42 @@ def test_ragged_and_degenerate_plans_stay_in_bounds(replay):
     bad = [(l.split()[:12], o) for l, o in zip(lines, out) if o.startswith("FAIL")]
     assert rc == 0 and not bad, bad[:3]
     assert sum(o.startswith("ok") for o in out) >= 30
+
+
+def test_fp8_plans_stay_in_bounds(replay):
+    """The fp8 output layer's score kernels read E4M3 rows of H8 bytes (H_pad rounded up to
+    128, at least 640) with three bias buffers: the bf16 workloads' plans and small hidden
+    sizes (rows padded to 640) at several tiles and wave sizes."""
+    lines = []
+    for name in ("small-bf16", "20s-bf16", "vocab4096-bf16", "40s-b256-bf16"):
+        w = WORKLOADS[name]
+        T_len, U_len = workload_lengths(name)
+        for tile in sorted(set(w.tiles) | {(64, 32), (32, 8)}):
+            for tpw in (0, 1, 3):
+                lines.append(case_line(w.B, w.T, w.U, w.V, w.HA, w.HL, w.H, tile, tpw, T_len, U_len, fp8=True))
+    rng = np.random.default_rng(11)
+    for _ in range(20):
+        B, T, U = int(rng.integers(1, 20)), int(rng.integers(1, 300)), int(rng.integers(0, 120))
+        H = int(rng.choice([64, 128, 256, 512, 640, 768]))
+        V = int(rng.choice([300, 1000, 1024, 4096]))
+        tile = (int(rng.integers(1, 100)), int(rng.integers(1, 40)))
+        lines.append(case_line(B, T, U, V, 64, 64, H, tile, int(rng.choice([0, 1, 5])), rng.integers(1, T + 1, B),
+                               rng.integers(0, U + 1, B), fp8=True))
+    rc, out = run(replay, lines)
+    bad = [(l.split()[:12], o) for l, o in zip(lines, out) if not o.startswith("ok")]
+    assert rc == 0 and not bad, bad[:3]
+
+
+def test_fp8_is_tiled_only():
+    d = rl.make_desc(2, 8, 2, 64, 64, 64, 64, dtype="bf16-fp8", mode="untiled")
+    with pytest.raises(rl.RnntError) as e:
+        rl.rnnt_loss_query(d, np.full(2, 8), np.full(2, 2))
+    assert e.value.status == rl.RNNT_E_UNSUPPORTED
+    d = rl.make_desc(2, 8, 2, 64, 64, 64, 64, dtype="bf16-fp8")
+    s, w = rl.rnnt_loss_query(d, np.full(2, 8), np.full(2, 2))
+    d16 = rl.make_desc(2, 8, 2, 64, 64, 64, 64, dtype="bf16")
+    s16, w16 = rl.rnnt_loss_query(d16, np.full(2, 8), np.full(2, 2))
+    assert s == s16 and w > w16  # same saved state; the E4M3 operand rows in the workspace
 
 
 def test_plan_rows_beyond_32_bits_are_refused():
