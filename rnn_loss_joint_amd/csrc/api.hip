@@ -620,6 +620,7 @@ static rnnt_status forward_impl(const rnnt_desc* desc, const void* hA, const voi
   {
     rnnt::LatticeArgs la{sv.Tlen, sv.Ulen, sv.phi, sv.psi, sv.alpha, sv.beta, sv.lnP, costs, d.B, d.T, p.U1};
     la.lat_off = sv.lat_off;
+    la.clamp = sv.band_lo != nullptr;
     ProfScope ps_("lattice", st);
     if (L.lat64) {
       // fp32 mode: the fp64 arrays share the fp32 ones' memory, so the fp32
@@ -1304,6 +1305,7 @@ rnnt_status rnnt_lattice(const rnnt_desc* desc, const int32_t* T_len_dev, const 
       rnnt::lat_sample(desc->T, desc->U + 1) > ((int64_t)1 << 29))
     return fail(RNNT_E_UNSUPPORTED, "the lattice arrays exceed B*4*NQ*US <= 2^30 or 4*NQ*US <= 2^29 entries");
   rnnt::LatticeArgs la{T_len_dev, U_len_dev, phi, psi, alpha, beta, nullptr, costs, desc->B, desc->T, desc->U + 1};
+  la.clamp = true;  // the caller's log-probs may hold -inf anywhere
   RNNT_HIP(rnnt::launch_lattice(la, desc->U + 1, reinterpret_cast<hipStream_t>(stream)));
   return RNNT_OK;
 }

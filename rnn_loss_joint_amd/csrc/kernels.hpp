@@ -96,6 +96,10 @@ struct LatticeArgs {
   const int64_t* lat_off;  // packed blocks [B] (saved); null: the padded layout
   double* beta64;
   double* lnP64;
+  // fp32 sweep: a cell's two terms may both be -inf (a pruned lattice's
+  // cells outside the band, or caller-given log-probs); false for the loss's
+  // own full lattice, whose log-probs are finite
+  bool clamp;
 };
 hipError_t launch_lattice(const LatticeArgs& a, int U1max, hipStream_t st);
 // Pruned lattice: phi = psi = -inf on every lattice cell (t < T_b, u <= U_b)

@@ -92,15 +92,25 @@ __device__ inline void buf_st(float v, __amdgpu_buffer_rsrc_t r, unsigned voff, 
 // (any value, NaN and infinities included) only ever meets x = -inf, and
 // -inf + (NaN, +inf) is NaN; the maximum with -inf returns the other operand
 // unless that is NaN (the sum of an fma is a quiet NaN, so no canonicalizing
-// is needed)
+// is needed). Only one operand of each direction can lie outside the
+// lattice at a cell: alpha's phi(t-1, u) at t = 0, and beta's psi(t, U_b)
+// (not a label emission, so the caller's value there is arbitrary); the
+// other operand of a cell is always a lattice entry (finite or -inf), and
+// where it is not, the cell is not one and its result is discarded.
 __device__ inline float add_operand2(float x, float raw) {
   return __builtin_fmaxf(__builtin_fmaf(raw, kLog2e, x), kNegInf);
 }
+__device__ inline float add_operand(float x, float raw) { return __builtin_fmaf(raw, kLog2e, x); }
 
-// base-2 log-add-exp; a = b = -inf gives NaN, which only occurs on cells the
-// caller masks or (a pruned lattice) outside the band, and the stores map to -inf
+// base-2 log-add-exp. With CLAMP the exponent is clamped at -126 so that
+// a = b = -inf gives -inf instead of NaN (cells outside a pruned lattice's
+// band, or log-probs a caller passes); below -126 the correction
+// log2(1 + 2^d) is 0 in fp32 either way. Without it (the loss's own
+// log-probs, all finite) every cell has a finite term.
+template <bool CLAMP>
 __device__ inline float lae2(float a, float b) {
-  return __builtin_fmaxf(a, b) + flog2(1.0f + fexp2(-__builtin_fabsf(a - b)));
+  const float d = -__builtin_fabsf(a - b);
+  return __builtin_fmaxf(a, b) + flog2(1.0f + fexp2(CLAMP ? __builtin_fmaxf(d, -126.0f) : d));
 }
 
 // neighbour rows through DPP wave shifts: lane l receives lane l-1's
@@ -112,7 +122,7 @@ __device__ inline float from_next_lane(float v, float old) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), 0x130, 0xf, 0xf, false));
 }
 
-template <int NW, int SW, int PF, bool is_beta>
+template <int NW, int SW, int PF, bool is_beta, bool CLAMP>
 __device__ __attribute__((always_inline)) inline void lattice_body(const LatticeArgs& p, float* ring) {
   static_assert(SW % 4 == 0 && 3 * SW <= SRING, "a window's ring slots must not wrap onto unread ones");
   constexpr int NG = SW / 4;  // groups of four diagonals per window
@@ -234,7 +244,8 @@ __device__ __attribute__((always_inline)) inline void lattice_body(const Lattice
         const float op_p = rp[is_beta ? SW - 1 - w : w];
         const float op_s = rs[is_beta ? SW - 1 - w : w];
         const float nb = is_beta ? from_next_lane(cur, vn[w]) : from_prev_lane(cur, vn[w]);
-        const float nxt = lae2(add_operand2(cur, op_p), add_operand2(nb, op_s));
+        const float nxt = is_beta ? lae2<CLAMP>(add_operand(cur, op_p), add_operand2(nb, op_s))
+                                  : lae2<CLAMP>(add_operand2(cur, op_p), add_operand(nb, op_s));
         const bool ok = (unsigned)(w - w_lo) < cnt;
         cur = ok ? nxt : (w < keep ? cur : kNegInf);
         res[w] = cur;
@@ -264,9 +275,7 @@ __device__ __attribute__((always_inline)) inline void lattice_body(const Lattice
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int w = is_beta ? SW - 1 - 4 * g - e : 4 * g + e - 1;
-        // a cell whose two terms are both -inf (only outside a pruned
-        // lattice's band) gets NaN from the log-add-exp: stored as -inf
-        v[e] = __builtin_fmaxf((w < 0 ? prev : res[w]) * kLn2, kNegInf);
+        v[e] = (w < 0 ? prev : res[w]) * kLn2;
         o[e] = w < 0 ? prev_ok : (unsigned)(w - w_lo) < cnt;
       }
       const unsigned so = (unsigned)((wb >> 2) + g) * gstride;
@@ -310,28 +319,33 @@ __device__ __attribute__((always_inline)) inline void lattice_body(const Lattice
 
 // PF: windows of loads in flight ahead of the one computed (each costs
 // 2 SW registers; 3 windows measured no faster than 2)
-template <int NW, int SW>
+template <int NW, int SW, bool CLAMP>
 __global__ void __launch_bounds__(64 * NW) lattice_kernel(LatticeArgs p) {
   constexpr int PF = 2;
   __shared__ __attribute__((aligned(16))) float ring[NW * SRING];
-  if (blockIdx.y == 0) lattice_body<NW, SW, PF, false>(p, ring);
-  else lattice_body<NW, SW, PF, true>(p, ring);
+  if (blockIdx.y == 0) lattice_body<NW, SW, PF, false, CLAMP>(p, ring);
+  else lattice_body<NW, SW, PF, true, CLAMP>(p, ring);
+}
+
+template <bool CLAMP>
+hipError_t launch_lattice_t(const LatticeArgs& a, int nw, hipStream_t st) {
+  const dim3 grid(a.B, 2);
+  if (nw <= 1) hipLaunchKernelGGL((lattice_kernel<1, 16, CLAMP>), grid, dim3(64), 0, st, a);
+  else if (nw <= 2) hipLaunchKernelGGL((lattice_kernel<2, 16, CLAMP>), grid, dim3(128), 0, st, a);
+  else if (nw <= 3) hipLaunchKernelGGL((lattice_kernel<3, 16, CLAMP>), grid, dim3(192), 0, st, a);
+  else if (nw <= 4) hipLaunchKernelGGL((lattice_kernel<4, 16, CLAMP>), grid, dim3(256), 0, st, a);
+  else if (nw <= 6) hipLaunchKernelGGL((lattice_kernel<6, 16, CLAMP>), grid, dim3(384), 0, st, a);
+  else if (nw <= 8) hipLaunchKernelGGL((lattice_kernel<8, 16, CLAMP>), grid, dim3(512), 0, st, a);
+  else if (nw <= 12) hipLaunchKernelGGL((lattice_kernel<12, 8, CLAMP>), grid, dim3(768), 0, st, a);
+  else if (nw <= 16) hipLaunchKernelGGL((lattice_kernel<16, 8, CLAMP>), grid, dim3(1024), 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_lattice(const LatticeArgs& a, int U1max, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
-  const dim3 grid(a.B, 2);
   const int nw = (U1max + 63) / 64;
-  if (nw <= 1) hipLaunchKernelGGL((lattice_kernel<1, 16>), grid, dim3(64), 0, st, a);
-  else if (nw <= 2) hipLaunchKernelGGL((lattice_kernel<2, 16>), grid, dim3(128), 0, st, a);
-  else if (nw <= 3) hipLaunchKernelGGL((lattice_kernel<3, 16>), grid, dim3(192), 0, st, a);
-  else if (nw <= 4) hipLaunchKernelGGL((lattice_kernel<4, 16>), grid, dim3(256), 0, st, a);
-  else if (nw <= 6) hipLaunchKernelGGL((lattice_kernel<6, 16>), grid, dim3(384), 0, st, a);
-  else if (nw <= 8) hipLaunchKernelGGL((lattice_kernel<8, 16>), grid, dim3(512), 0, st, a);
-  else if (nw <= 12) hipLaunchKernelGGL((lattice_kernel<12, 8>), grid, dim3(768), 0, st, a);
-  else if (nw <= 16) hipLaunchKernelGGL((lattice_kernel<16, 8>), grid, dim3(1024), 0, st, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  return a.clamp ? launch_lattice_t<true>(a, nw, st) : launch_lattice_t<false>(a, nw, st);
 }
 
 // Pruned lattice: the two log-probs of every cell outside its frame's band
