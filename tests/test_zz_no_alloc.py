@@ -3,7 +3,8 @@
 Through the C ABI, on two calls in a row (the second on a smaller batch), the allocation-free
 forward gives the same costs as rnnt_loss_fwd bit for bit, and its `saved` drives rnnt_loss_bwd to
 the same gradients bit for bit; device memory is not allocated by the call; a request whose
-forward needs more than the array is refused before any launch; fp32 mode needs no scratch.
+forward needs more than the array is refused before any launch; fp32 mode needs no scratch; the
+fp8 output layer's forward runs from the array as well.
 """
 import numpy as np
 import pytest
@@ -15,10 +16,10 @@ pytestmark = pytest.mark.gpu
 GRADS = ("dhA", "dhL", "dWA", "dWL", "dbZ", "dWO", "dbO")
 
 
-def both_ways(rl, inp, tile=(64, 32), tpw=0):
+def both_ways(rl, inp, tile=(64, 32), tpw=0, fp8=False):
     import torch
 
-    prob = rl.Problem(inp, tile=tile, tiles_per_wave=tpw)
+    prob = rl.Problem(inp, tile=tile, tiles_per_wave=tpw, fp8=fp8)
     ref_costs = prob.forward().clone()
     ref_grads = {k: v.clone() for k, v in prob.backward().items()}
     torch.cuda.synchronize()
@@ -50,6 +51,14 @@ def test_noalloc_forward_matches_forward(gpu_lib):
     both_ways(rl, big)
     free0, free1 = both_ways(rl, small, tile=(32, 16), tpw=5)
     assert free0 == free1, (free0, free1)  # the call itself allocates no device memory
+
+
+def test_noalloc_forward_fp8(gpu_lib):
+    """The fp8 output layer's forward (E4M3 W^O table and z rows in the scratch array)."""
+    inp = make_inputs(4, 120, 30, 1024, 256, 192, 640, dtype="bf16", seed=304, t_range=(60, 120),
+                      u_range=(5, 30), bias_std=0.1)
+    print("noalloc forward: fp8 output layer", flush=True)
+    both_ways(gpu_lib, inp, fp8=True)
 
 
 def test_noalloc_forward_fp32_and_limit(gpu_lib):
