@@ -112,3 +112,23 @@ def test_fp8_40s_b256(gpu_lib):
     check_costs(inp, costs, ref.costs, samples=[9])
     check_grads(inp, grads, ref.grads)
     distance_from_exact(inp, costs, grads, samples=[9], dcosts=e)
+
+
+def test_fp8_with_pruned_lattice(gpu_lib):
+    """The fp8 output layer on a pruned lattice (both options together) against the oracle with both."""
+    import torch
+
+    from rnnt_inputs import diagonal_band
+
+    inp = make_inputs(3, 90, 37, 1024, 96, 64, 640, dtype="bf16", seed=181, t_range=(40, 90), u_range=(10, 37),
+                      bias_std=0.1)
+    S = 8
+    lo = diagonal_band(inp.T_len, inp.U_len, 90, S)
+    say("fp8 output layer on a pruned lattice, S = 8")
+    prob = gpu_lib.Problem(inp, tile=(32, 16), tiles_per_wave=5, band=(lo, S), fp8=True)
+    costs = prob.forward().clone().cpu().numpy().astype(np.float64)
+    grads = {k: v.cpu().numpy().astype(np.float64) for k, v in prob.backward().items()}
+    torch.cuda.synchronize()
+    ref = oracle.loss_and_grads(inp, band=(lo, S), fp8_scores=True)
+    check_costs(inp, costs, ref.costs)
+    check_grads(inp, grads, ref.grads)
