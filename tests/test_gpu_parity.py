@@ -505,6 +505,26 @@ def test_edge_cases(gpu_lib, dtype):
     full_check(gpu_lib, inp, mode="untiled")
 
 
+@pytest.mark.parametrize("dtype,mode", [("f32", "tiled"), ("bf16", "tiled"), ("bf16", "untiled"), ("fp8", "tiled")])
+def test_largest_vocabulary(gpu_lib, dtype, mode):
+    """V = 65536, the library's limit (256 V tiles of 256 scores), on a small ragged lattice with
+    labels near the top of the vocabulary and the blank id at V - 1."""
+    import torch
+
+    inp = make_inputs(2, 20, 5, 65536, 64, 40, 64, dtype="f32" if dtype == "f32" else "bf16", seed=73,
+                      t_range=(9, 20), u_range=(2, 5), bias_std=0.3, blank=65535)
+    inp.labels[0, 1] = 65534
+    inp.labels[1, 2] = 1
+    say(f"V = 65536 {dtype} {mode}")
+    prob = gpu_lib.Problem(inp, mode=mode, tile=(16, 4), tiles_per_wave=3, fp8=dtype == "fp8")
+    costs = prob.forward().clone().cpu().numpy().astype(np.float64)
+    grads = {k: v.cpu().numpy().astype(np.float64) for k, v in prob.backward().items()}
+    torch.cuda.synchronize()
+    ref = oracle.loss_and_grads(inp, fp8_scores=dtype == "fp8")
+    check_costs(inp, costs, ref.costs)
+    check_grads(inp, grads, ref.grads)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_out_of_range_labels_are_counted_and_contained(gpu_lib, dtype):
     """Labels outside [0, V) in the transcript: the forward's checked copy replaces them with the
