@@ -53,11 +53,6 @@ rnnt_status fail(rnnt_status s, const std::string& msg) {
     if (s_ != RNNT_OK) return s_;      \
   } while (0)
 
-// The persistent score kernels need at least 8 stages of 64 k per item
-// (the previous item's epilogue runs in the first five).
-// fp8 always uses them (its operand rows are padded to at least five stages).
-bool use_scores3(const rnnt::Plan& p) { return p.d.fp8 || (p.d.bf16 && !p.d.untiled && p.H_pad / 64 >= 8); }
-
 rnnt_status to_dims(const rnnt_desc* desc, rnnt::Dims& d) {
   if (!desc) return fail(RNNT_E_INVALID, "desc is null");
   if (desc->dtype != RNNT_F32 && desc->dtype != RNNT_BF16 && desc->dtype != RNNT_BF16_FP8)
@@ -473,7 +468,7 @@ static rnnt_status forward_impl(const rnnt_desc* desc, const void* hA, const voi
     auto* stats = at<rnnt::f32x2>(workspace, L.w_stats);
     float* hb = at<float>(workspace, L.w_hb);
     float* hy = at<float>(workspace, L.w_hy);
-    const bool s3 = use_scores3(p);
+    const bool s3 = rnnt::persistent_scores(p);
     char* z8buf = d.fp8 ? at<char>(workspace, L.w_z8) : nullptr;
     int* ew = d.fp8 ? at<int>(workspace, L.w_ew) : nullptr;
     if (d.fp8) {
@@ -560,6 +555,8 @@ static rnnt_status forward_impl(const rnnt_desc* desc, const void* hA, const voi
         a3.z = d.fp8 ? nullptr : sc.z;
         a3.z_ld = p.H_pad;
         a3.stats = stats;
+        // untiled: the scores are kept for the backward (the wave's rows)
+        a3.logits = d.untiled ? at<char>(sv.logits, (size_t)wv.row_begin * p.V_pad * 2) : nullptr;
         if (d.fp8) {
           a3.WO8 = at<char>(workspace, L.w_WO8);
           a3.z8 = z8buf;
@@ -730,7 +727,7 @@ static rnnt_status backward_impl(const rnnt_desc* desc, const void* hA, const vo
     ProfScope ps_("transpose_wo", st);
     RNNT_HIP(rnnt::launch_transpose_wo(WOT, WO, d.V, d.H, p.V_pad, bf, st));
   }
-  const bool s3 = use_scores3(p);
+  const bool s3 = rnnt::persistent_scores(p);
   char* z8buf = d.fp8 ? at<char>(workspace, L.w_z8) : nullptr;
   int* ew = d.fp8 ? at<int>(workspace, L.w_ew) : nullptr;
   if (d.fp8) {
@@ -768,7 +765,43 @@ static rnnt_status backward_impl(const rnnt_desc* desc, const void* hA, const vo
     const int wrows = wv.row_end - wv.row_begin;
     const int buf_base = d.untiled ? 0 : wv.row_begin;
     // 4. dh (and z) for the wave's cells
-    if (d.untiled) {
+    if (d.untiled && bf) {
+      // dh in place of the kept scores, from the per-row coefficients
+      rnnt::Scores3Args a3{};
+      a3.tiles = sv.tiles;
+      a3.tile_begin = wv.tile_begin;
+      a3.tile_end = wv.tile_end;
+      a3.n_rows = wrows;
+      a3.n_ct = (wrows + 127) / 128;
+      a3.buf_row_base = wv.row_begin;
+      a3.T_len = sv.Tlen;
+      a3.U_len = sv.Ulen;
+      a3.labels = sv.labels;
+      a3.lat_off = sv.lat_off;
+      a3.T = d.T;
+      a3.U1 = p.U1;
+      a3.V = d.V;
+      a3.V_pad = p.V_pad;
+      a3.blank = d.blank;
+      a3.logits = at<char>(sv.logits, (size_t)wv.row_begin * p.V_pad * 2);
+      a3.coefA = at<char>(workspace, L.w_coefA);
+      a3.coefB = at<char>(workspace, L.w_coefB);
+      a3.lse = sv.lse;
+      a3.phi = sv.phi;
+      a3.psi = sv.psi;
+      a3.alpha = sv.alpha;
+      a3.beta = sv.beta;
+      a3.lnP = sv.lnP;
+      a3.dcosts = dcosts;
+      {
+        ProfScope ps_("coef", st);
+        RNNT_HIP(rnnt::launch_coef(a3, d.tile_t, d.tile_u, st));
+      }
+      {
+        ProfScope ps_("dh_logits", st);
+        RNNT_HIP(rnnt::launch_dh_logits(a3, st));
+      }
+    } else if (d.untiled) {
       rnnt::DhInplaceArgs a{};
       a.tiles = sv.tiles;
       a.tile_begin = wv.tile_begin;
@@ -798,7 +831,7 @@ static rnnt_status backward_impl(const rnnt_desc* desc, const void* hA, const vo
       a.dcosts = dcosts;
       {
         ProfScope ps_("dh_inplace", st);
-        RNNT_HIP(rnnt::launch_dh_inplace(a, bf, st));
+        RNNT_HIP(rnnt::launch_dh_inplace(a, st));
       }
     } else if (bf) {
       // z rows for the wave, then dh from 256 x 256 score tiles

@@ -389,8 +389,8 @@ joint_kernel(JointArgs p) {
   }
 }
 
-// Backward of the untiled mode: the forward kept the scores (bias included),
-// so dh is formed in place from them without recomputation.
+// Backward of the fp32 untiled mode: the forward kept the scores (bias
+// included), so dh is formed in place from them without recomputation.
 template <class CT>
 __global__ void __launch_bounds__(256) dh_inplace_kernel(DhInplaceArgs p) {
   __shared__ float coef[4][5];
@@ -478,11 +478,10 @@ hipError_t launch_joint(const JointArgs& a, bool bf16_mode, bool bwd, hipStream_
   return bwd ? launch_joint_h<MfmaF32, true>(a, KS, st) : launch_joint_h<MfmaF32, false>(a, KS, st);
 }
 
-hipError_t launch_dh_inplace(const DhInplaceArgs& a, bool bf16_mode, hipStream_t st) {
+hipError_t launch_dh_inplace(const DhInplaceArgs& a, hipStream_t st) {
   dim3 grid((unsigned)((a.n_rows + 3) / 4)), block(256);
   if (grid.x == 0) return hipSuccess;
-  if (bf16_mode) hipLaunchKernelGGL(dh_inplace_kernel<bf16>, grid, block, 0, st, a);
-  else hipLaunchKernelGGL(dh_inplace_kernel<float>, grid, block, 0, st, a);
+  hipLaunchKernelGGL(dh_inplace_kernel<float>, grid, block, 0, st, a);
   return hipGetLastError();
 }
 

@@ -79,7 +79,7 @@ hipError_t launch_labels_check(const int32_t* labels, const int32_t* U_len, int 
 
 // (H_pad = 16 * joint_ks_for(H), declared in plan.hpp)
 hipError_t launch_joint(const JointArgs& a, bool bf16_mode, bool bwd, hipStream_t st);
-hipError_t launch_dh_inplace(const DhInplaceArgs& a, bool bf16_mode, hipStream_t st);
+hipError_t launch_dh_inplace(const DhInplaceArgs& a, hipStream_t st);  // fp32 untiled mode
 
 // Forward-backward variables over each sample's lattice.
 struct LatticeArgs {
@@ -263,7 +263,7 @@ struct ScoresArgs {  // scores^T tiles: forward statistics or backward dh
   const void* z;
   int64_t z_ld;
   f32x2* stats;   // forward: [rows, V tiles] (max, sum)
-  void* logits;   // forward, untiled: scores [rows, V_pad] (global rows)
+  void* logits;   // forward, untiled: y = h log2 e as bf16 [rows, V_pad] (global rows)
   void* dh;       // backward: [rows, V_pad]
   const float* lse;
   const float* phi;
@@ -292,6 +292,7 @@ struct Scores3Args {
   int64_t z_ld;
   f32x2* stats;      // forward: [n_ct*128][nvt]
   void* dh;          // backward: [n_ct*128][V_pad] bf16
+  void* logits;      // forward, untiled mode: [n_rows][V_pad] bf16 y = (W^O z + b^O) log2 e (null: not stored)
   void* coefA;       // [n_ct*128] (lse log2 e, occupancy)
   void* coefB;       // [n_ct*128] (cb, cl, label, 0)
   // fp8 output layer (WO8 non-null): E4M3 operands, rows of H8 bytes
@@ -319,6 +320,9 @@ hipError_t launch_score_tables8(const void* WO, const void* bO, void* WO8, float
 // grid over the wave's tiles x 32 x 32 blocks (+1 for the padding rows)
 hipError_t launch_coef(const Scores3Args& a, int tile_t, int tile_u, hipStream_t st);
 hipError_t launch_dh_fix(const Scores3Args& a, hipStream_t st);
+// untiled mode: dh in place of the stored scores a.logits [n_rows][V_pad],
+// from the coefficients coefA / coefB of launch_coef
+hipError_t launch_dh_logits(const Scores3Args& a, hipStream_t st);
 
 struct MergeArgs {
   const Tile* tiles;

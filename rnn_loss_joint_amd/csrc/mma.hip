@@ -458,7 +458,7 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoresArgs p) {
         if (rr < p.n_rows) p.stats[((int64_t)rr * nvt + vt)] = f32x2{mn * kLn2, sv};
       }
     }
-    if (p.logits) {  // untiled: keep the scores (bias included), 4 consecutive v per store
+    if (p.logits) {  // untiled: keep y = h log2 e (bias included), 4 consecutive v per store
       bf16* lg = reinterpret_cast<bf16*>(p.logits);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -473,7 +473,7 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoresArgs p) {
             bf16x4 w;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float y = __builtin_fmaf(acc.c[i][j][4 * g + q], kLog2e, bq[g][q]) * kLn2;
+              const float y = __builtin_fmaf(acc.c[i][j][4 * g + q], kLog2e, bq[g][q]);
               w[q] = (bf16)(v + q < p.V ? y : 0.0f);
             }
             if (rr < p.n_rows && v < p.V_pad)

@@ -36,6 +36,8 @@ bool check_plan(const Plan& p, std::string& err) {
   return true;
 }
 
+bool persistent_scores(const Plan& p) { return p.d.fp8 || (p.d.bf16 && p.H_pad / 64 >= 8); }
+
 bool check_dims(const Dims& d, std::string& err, int& status) {
   status = -1;  // RNNT_E_INVALID
   if (d.B <= 0 || d.T <= 0 || d.U < 0 || d.V < 2 || d.HA <= 0 || d.HL <= 0 || d.H <= 0) {
@@ -322,7 +324,10 @@ Layout make_layout(const Plan& p) {
   L.off_logits = L.off_z = 0;
   if (d.untiled) {
     L.off_logits = take(ct * (size_t)p.total_rows * p.V_pad);
-    L.off_z = take(ct * (size_t)p.total_rows * p.H_pad);
+    // bf16: z rows, with the rows up to the next multiple of 128 and 128 more
+    // as padding that the score kernels' last cell tile reads (never used)
+    const size_t zrows = d.bf16 ? (size_t)(p.total_rows + 255) / 128 * 128 : (size_t)p.total_rows;
+    L.off_z = take(ct * zrows * p.H_pad);
   }
   L.saved_bytes = o;
 
@@ -344,17 +349,18 @@ Layout make_layout(const Plan& p) {
   L.w_PBZ = take(sizeof(float) * (size_t)p.s7a * d.H);
   L.w_PWL = take(sizeof(float) * (size_t)p.s7l * d.H * d.HL);
   L.w_WOT = take(ct * (size_t)d.H * p.V_pad);
-  // bf16 forward buffers, one wave of rows (all rows in untiled mode)
-  const size_t frows = d.untiled ? (size_t)p.total_rows : wrows;
+  // bf16 forward buffers, one wave of rows (wave-relative, whole cell tiles)
   L.w_zf = 0;  // the tiled forward's z rows reuse the backward's z buffer (w_z)
-  L.w_stats = d.bf16 ? take(8 * frows * p.nvt) : 0;
-  L.w_hb = d.bf16 ? take(4 * frows) : 0;
-  L.w_hy = d.bf16 ? take(4 * frows) : 0;
-  // persistent score kernels (bf16, tiled): padded W^O, bias table, cell coefficients
+  L.w_stats = d.bf16 ? take(8 * wrows * p.nvt) : 0;
+  L.w_hb = d.bf16 ? take(4 * wrows) : 0;
+  L.w_hy = d.bf16 ? take(4 * wrows) : 0;
+  // persistent score kernels: padded W^O, bias table; bf16 backward
+  // coefficients per wave row (persistent score kernels, untiled mode)
   L.w_WOp = L.w_bl = L.w_coefA = L.w_coefB = 0;
-  if (d.bf16 && !d.untiled) {
-    L.w_WOp = take(2 * (size_t)p.nvt * 256 * p.H_pad);
-    L.w_bl = take(4 * (size_t)p.nvt * 256);
+  const bool s3 = persistent_scores(p);
+  if (s3 && !d.fp8) L.w_WOp = take(2 * (size_t)p.nvt * 256 * p.H_pad);
+  if (s3) L.w_bl = take(4 * (size_t)p.nvt * 256);
+  if (d.bf16 && (s3 || d.untiled)) {
     L.w_coefA = take(8 * wrows);
     L.w_coefB = take(16 * wrows);
   }
@@ -397,16 +403,15 @@ Layout make_forward_layout(const Plan& p) {
     return at;
   };
   const size_t wrows = (size_t)cdiv(p.max_wave_rows, 128) * 128;
-  const size_t frows = d.untiled ? (size_t)p.total_rows : wrows;
   L.w_dh = L.w_gA = L.w_gL = L.w_PA = L.w_PL = L.w_PW = L.w_PB = L.w_PWA = L.w_PBZ = L.w_PWL = L.w_WOT = 0;
   L.w_coefA = L.w_coefB = L.w_gb = L.w_hs = L.w_WAT = L.w_WLT = 0;
   L.w_z = L.w_stats = L.w_hb = L.w_hy = L.w_WOp = L.w_bl = L.w_WO8 = L.w_z8 = L.w_ew = 0;
   if (d.bf16) {
     if (!d.untiled && !d.fp8) L.w_z = take(2 * wrows * p.H_pad);  // fp8: the forward needs no bf16 z
-    L.w_stats = take(8 * frows * p.nvt);
-    L.w_hb = take(4 * frows);
-    L.w_hy = take(4 * frows);
-    if (!d.untiled) {
+    L.w_stats = take(8 * wrows * p.nvt);
+    L.w_hb = take(4 * wrows);
+    L.w_hy = take(4 * wrows);
+    if (persistent_scores(p)) {
       if (!d.fp8) L.w_WOp = take(2 * (size_t)p.nvt * 256 * p.H_pad);  // fp8: the E4M3 rows instead
       L.w_bl = take(4 * (size_t)p.nvt * 256);
     }

@@ -72,11 +72,15 @@ struct Layout {
   size_t lat_entries; // entries of each lattice array (lat_off[B])
   size_t off_a, off_l, off_lse, off_phi, off_psi, off_alpha, off_beta, off_lnP;
   bool lat64;  // alpha, beta, ln P held in fp64 (fp32 mode), else fp32
-  size_t off_logits, off_z;  // untiled only; z is stored transposed [H_pad, total_rows]
+  // untiled only: the scores [total_rows, V_pad] (bf16 mode: scaled by log2 e,
+  // bias included) and z (bf16: rows [total_rows + 128 rows of padding, H_pad],
+  // the padding read by the last 128-row cell tile; fp32: z^T [H_pad, total_rows])
+  size_t off_logits, off_z;
   size_t saved_bytes;
   size_t w_dh, w_z, w_gA, w_gL, w_PA, w_PL, w_PW, w_PB, w_PWA, w_PBZ, w_PWL, w_WOT;
   size_t w_zf, w_stats, w_hb, w_hy;  // bf16 forward: z rows, V-tile statistics, blank/label scores
-  size_t w_WOp, w_bl, w_coefA, w_coefB;  // bf16 tiled: persistent score kernels
+  size_t w_WOp, w_bl;        // persistent score kernels: padded W^O, bias table
+  size_t w_coefA, w_coefB;   // bf16 backward coefficients per wave row (persistent kernels, untiled mode)
   size_t w_WO8, w_z8, w_ew;              // fp8: E4M3 W^O rows, z rows, W^O scale exponent (int)
   size_t w_gb;  // bf16: rounded gA, gL for the encoder-side products (may alias w_dh)
   size_t w_WAT, w_WLT;  // bf16: W^A^T [HA, H], W^L^T [HL, H] for dh^A, dh^L
@@ -105,6 +109,11 @@ void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H
                 const Band& band = Band());
 // Checks a built plan against the library's 32-bit row limits (kMaxPlanRows).
 bool check_plan(const Plan& p, std::string& err);
+// Whether the bf16 score products run on the persistent score kernels: they
+// need at least 8 stages of 64 k per item (the previous item's epilogue runs
+// in the first five); the fp8 output layer always uses them (its operand rows
+// are padded to at least five stages of 128 bytes).
+bool persistent_scores(const Plan& p);
 Layout make_layout(const Plan& p);
 // The same layout with only the forward pass's workspace regions (z rows,
 // V-tile statistics, blank / label scores, padded W^O and bias table) packed

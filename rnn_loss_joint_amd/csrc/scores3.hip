@@ -8,7 +8,9 @@
 //             scaled scores y = (W^O z + b^O) log2 e (the log-softmax
 //             denominator of Eq. (5) in pieces, merged afterwards);
 //   backward: dh = occupancy * softmax (Eq. (10) without the blank / label
-//             terms, which a separate pass subtracts) written as bf16.
+//             terms, which a separate pass subtracts) written as bf16;
+//   forward with a store (untiled mode): also the scaled scores y
+//             themselves, as bf16, for a backward without recomputation.
 //
 // One workgroup per CU (256 threads, 4 waves of 128 x 64 outputs) walks its
 // list of items; the A operand (a 256-row slice of a zero-padded copy of
@@ -50,7 +52,8 @@ constexpr int DHS_ROW = 80, DHS_WAVE = 32 * DHS_ROW;
 // dma of item n+1's first stages (issued three stages ahead) starts after
 // item n-1's epilogue (in item n's first five stages) has read its buffers;
 // with fp8 (5 stages per item at H = 640) it does not, so three buffers.
-template <bool BWD, bool FP8>
+// The block staging area serves the backward's dh and the stored scores.
+template <bool BWD, bool FP8, bool STORE>
 struct Lay {
   static constexpr int NBUF = FP8 ? 3 : 2;
   static constexpr int OFF_BIAS = NST * STAGE;               // [NBUF][256] f32: b^O log2 e
@@ -58,7 +61,7 @@ struct Lay {
   static constexpr int OFF_RED = OFF_COEF + NBUF * 256 * 4;  // [2 wc][2 j][2][32] f32 (forward)
   static constexpr int RED_BYTES = (BWD && FP8) ? 0 : 2 * 2 * 2 * 32 * 4;
   static constexpr int OFF_DHS = OFF_RED + RED_BYTES;
-  static constexpr int BYTES = BWD ? OFF_DHS + 4 * DHS_WAVE : OFF_RED + RED_BYTES;
+  static constexpr int BYTES = (BWD || STORE) ? OFF_DHS + 4 * DHS_WAVE : OFF_DHS;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 constexpr int WM = 4, WN = 2;  // 32 x 32 blocks per wave
@@ -77,12 +80,13 @@ __device__ inline void dma_b32(const char* g, char* l) {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-template <bool BWD, bool FP8>
+template <bool BWD, bool FP8, bool STORE>
 __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
+  static_assert(!STORE || (!BWD && !FP8), "scores are stored by the bf16 forward only");
   using namespace s3;
   using m3::lds_barrier;
   using m3::wait_vm;
-  using LY = Lay<BWD, FP8>;
+  using LY = Lay<BWD, FP8, STORE>;
   constexpr int NBUF = LY::NBUF, OFF_BIAS = LY::OFF_BIAS, OFF_COEF = LY::OFF_COEF, OFF_RED = LY::OFF_RED,
                 OFF_DHS = LY::OFF_DHS;
   __shared__ __attribute__((aligned(1024))) char lds[LY::BYTES];
@@ -198,7 +202,8 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
   f32x4 bq[4];
   float* stats2 = reinterpret_cast<float*>(p.stats);
   bf16* dh = reinterpret_cast<bf16*>(p.dh);
-  char* const dhs = lds + OFF_DHS + wave * DHS_WAVE;  // backward block staging
+  bf16* lg = reinterpret_cast<bf16*>(p.logits);
+  char* const dhs = lds + OFF_DHS + wave * DHS_WAVE;  // block staging (backward dh, stored scores)
   bf16x8 fl[2];
 
   // One chunk (issued after one MFMA) of epilogue task T on accumulator set E.
@@ -229,11 +234,41 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
             y[e] = __builtin_fmaf(acc[E][i][j][e], ysc, bq[e >> 2][e & 3]);
             ebm = __builtin_fmaxf(ebm, y[e]);
           }
+          if constexpr (STORE && (X & 1) == 1) {
+            // scores 8 (e4 / 4) + 4 g .. +3 of the block for cell r, into the
+            // staging buffer. The store path's per-lane offsets are formed
+            // from the lane index at each use (laundered through an empty
+            // asm) rather than kept live across the loop, where the registers
+            // are needed by the pipeline.
+            constexpr int e4 = 2 * X - 2;
+            bf16x4 w;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] = (bf16)y[e4 + q];
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            *reinterpret_cast<bf16x4*>(dhs + (ln & 31) * DHS_ROW + (8 * (e4 >> 2) + 4 * (ln >> 5)) * 2) = w;
+          }
         } else {
           // task B(b): fold 2^(y - max) into the running sum
           if constexpr (X == 0) es[j] *= fexp2(em[j] - ebm);
           es[j] += fexp2(y[2 * X] - ebm) + fexp2(y[2 * X + 1] - ebm);
           if constexpr (X == 7) em[j] = ebm;
+          if constexpr (STORE && X < 4) {
+            // block b, staged in task A(b), leaves the staging buffer (cells
+            // 16 h + lane / 4, scores 8 (lane % 4) .. +7, h = X / 2) before
+            // block b + 1 is written there in task A(b + 1); one piece is read
+            // per even chunk and stored in the next; rows past the wave are not stored
+            constexpr int h = X >> 1;
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            if constexpr ((X & 1) == 0) {
+              fl[0] = *reinterpret_cast<const bf16x8*>(dhs + (16 * h + (ln >> 2)) * DHS_ROW + (ln & 3) * 16);
+            } else {
+              const int rr = e_ct * BN + wc * 64 + j * 32 + 16 * h + (ln >> 2);
+              const int v = e_vt * 256 + wr * 128 + i * 32 + 8 * (ln & 3);
+              if (e_live && rr < p.n_rows) *reinterpret_cast<bf16x8*>(lg + (int64_t)rr * p.V_pad + v) = fl[0];
+            }
+          }
         }
       } else if constexpr (T == 16 && X == 0) {
         // combine the two half-waves (same cells, other score rows); wave row 1 -> LDS
@@ -245,24 +280,28 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
           em[j] = mn;
         }
         float* red = reinterpret_cast<float*>(lds + OFF_RED);
-        if (wr == 1 && lane < 32) {
+        int ln = lane;
+        if constexpr (STORE) asm volatile("" : "+v"(ln));  // formed here, not kept live (see the store path)
+        if (wr == 1 && ln < 32) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            red[((wc * 2 + j) * 2 + 0) * 32 + lane] = em[j];
-            red[((wc * 2 + j) * 2 + 1) * 32 + lane] = es[j];
+            red[((wc * 2 + j) * 2 + 0) * 32 + ln] = em[j];
+            red[((wc * 2 + j) * 2 + 1) * 32 + ln] = es[j];
           }
         }
       } else if constexpr (T == 19 && X == 0) {
         // after the stage barrier: wave row 0 merges and stores (max ln 2, sum)
         const float* red = reinterpret_cast<const float*>(lds + OFF_RED);
-        if (wr == 0 && lane < 32 && e_live) {
+        int ln = lane;
+        if constexpr (STORE) asm volatile("" : "+v"(ln));  // formed here, not kept live (see the store path)
+        if (wr == 0 && ln < 32 && e_live) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            const float m2 = red[((wc * 2 + j) * 2 + 0) * 32 + lane];
-            const float s2 = red[((wc * 2 + j) * 2 + 1) * 32 + lane];
+            const float m2 = red[((wc * 2 + j) * 2 + 0) * 32 + ln];
+            const float s2 = red[((wc * 2 + j) * 2 + 1) * 32 + ln];
             const float mn = __builtin_fmaxf(em[j], m2);
             const float sv = es[j] * fexp2(em[j] - mn) + s2 * fexp2(m2 - mn);
-            const int64_t rr = (int64_t)e_ct * BN + wc * 64 + j * 32 + lane;
+            const int64_t rr = (int64_t)e_ct * BN + wc * 64 + j * 32 + ln;
             *reinterpret_cast<f32x2*>(stats2 + 2 * (rr * nvt + e_vt)) = f32x2{mn * kLn2, sv};
           }
         }
@@ -499,12 +538,16 @@ hipError_t launch_scores3(const Scores3Args& a, bool bwd, hipStream_t st) {
   if (fp8 ? (a.H8 % 128 != 0 || a.H8 / 128 < s3::EPI_STAGES || a.z8_ld % 128 != 0 || !a.z8 || !a.ew)
           : (a.H_pad % 64 != 0 || a.H_pad / 64 < 8))
     return hipErrorInvalidValue;
+  if (a.logits && (bwd || fp8)) return hipErrorInvalidValue;  // only the bf16 forward stores the scores
   if (fp8) {
-    if (bwd) hipLaunchKernelGGL((scores3_kernel<true, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((scores3_kernel<false, true>), grid, block, 0, st, a);
+    if (bwd) hipLaunchKernelGGL((scores3_kernel<true, true, false>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((scores3_kernel<false, true, false>), grid, block, 0, st, a);
+  } else if (bwd) {
+    hipLaunchKernelGGL((scores3_kernel<true, false, false>), grid, block, 0, st, a);
+  } else if (a.logits) {
+    hipLaunchKernelGGL((scores3_kernel<false, false, true>), grid, block, 0, st, a);
   } else {
-    if (bwd) hipLaunchKernelGGL((scores3_kernel<true, false>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((scores3_kernel<false, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((scores3_kernel<false, false, false>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }
@@ -719,6 +762,39 @@ hipError_t launch_coef(const Scores3Args& a, int tile_t, int tile_u, hipStream_t
 hipError_t launch_dh_fix(const Scores3Args& a, hipStream_t st) {
   if (a.n_rows == 0) return hipSuccess;
   hipLaunchKernelGGL(dh_fix_kernel, dim3((a.n_rows + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// Untiled mode: dh from the scores the forward kept (y = h log2 e as bf16,
+// rows of V_pad), in place (Eq. (10)): dh = occ 2^(y - lse log2 e), minus
+// the blank and label terms of the row's coefficients. Eight consecutive
+// scores (16 bytes) per thread; a score past V holds y = -1e30, so its dh is 0.
+__global__ void __launch_bounds__(256) dh_logits_kernel(Scores3Args p) {
+  const int per_row = p.V_pad / 8;
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (x >= (int64_t)p.n_rows * per_row) return;
+  const int rr = (int)(x / per_row);
+  const int v0 = (int)(x - (int64_t)rr * per_row) * 8;
+  const f32x2 ca = reinterpret_cast<const f32x2*>(p.coefA)[rr];
+  const f32x4 cb = reinterpret_cast<const f32x4*>(p.coefB)[rr];
+  const int lab = (int)cb[2];
+  bf16x8* q = reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(p.logits) + (int64_t)rr * p.V_pad + v0);
+  bf16x8 w = *q;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float d = ca[1] * fexp2((float)w[k] - ca[0]);
+    if (v0 + k == p.blank) d -= cb[0];
+    if (v0 + k == lab) d -= cb[1];
+    w[k] = (bf16)d;
+  }
+  *q = w;
+}
+
+hipError_t launch_dh_logits(const Scores3Args& a, hipStream_t st) {
+  if (a.n_rows == 0) return hipSuccess;
+  if (a.V_pad % 8 != 0 || !a.logits || !a.coefA || !a.coefB) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)a.n_rows * (a.V_pad / 8);
+  hipLaunchKernelGGL(dh_logits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

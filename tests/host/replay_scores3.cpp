@@ -13,6 +13,9 @@
 //     backward coefficients) and every epilogue store range (the forward's
 //     per-V-tile statistics, the backward's dh rows) lies inside the buffer
 //     region the layout reserves for it.
+// In untiled mode (one wave; the forward alone runs on these kernels) the z
+// rows are the ones kept in `saved`, and the stored scores (rows of the wave
+// only) must lie inside the saved scores.
 // Nothing is launched: this is plain C++ against the plan and layout.
 //
 // Input, one case per line: B T U V HA HL H dtype untiled tile_t tile_u tpw
@@ -63,9 +66,9 @@ std::string run_case(const Dims& d, const std::vector<int32_t>& T_len, const std
   build_plan(d, T_len.data(), U_len.data(), ks * 16, p, band);
   if (!check_plan(p, err)) return "skip " + err;
   const Layout L = make_layout(p);
-  // the persistent score kernels run in bf16 tiled mode with at least 8 k-steps of 64, and
+  // the persistent score kernels run in bf16 mode with at least 8 k-steps of 64, and
   // always with the fp8 output layer (E4M3 rows of H8 >= 640 bytes)
-  if (!d.fp8 && (!d.bf16 || d.untiled || p.H_pad / 64 < 8)) return "skip not the persistent score path";
+  if (!persistent_scores(p)) return "skip not the persistent score path";
   std::vector<int64_t> offs = {
       (int64_t)L.w_dh, (int64_t)L.w_z, (int64_t)L.w_gA, (int64_t)L.w_gL, (int64_t)L.w_PA, (int64_t)L.w_PL,
       (int64_t)L.w_PW, (int64_t)L.w_PB, (int64_t)L.w_PWA, (int64_t)L.w_PBZ, (int64_t)L.w_PWL, (int64_t)L.w_WOT,
@@ -81,7 +84,14 @@ std::string run_case(const Dims& d, const std::vector<int32_t>& T_len, const std
   // the operands: bf16 rows of H_pad values, or (fp8) E4M3 rows of H8 bytes, which the
   // kernel addresses as rows of H8 / 2 two-byte units
   const size_t off_z = d.fp8 ? L.w_z8 : L.w_z, off_wo = d.fp8 ? L.w_WO8 : L.w_WOp;
-  const Region rz = region(off_z, offs, W), rdh = region(L.w_dh, offs, W), rst = region(L.w_stats, offs, W);
+  const Region rdh = region(L.w_dh, offs, W), rst = region(L.w_stats, offs, W);
+  // untiled: z and the scores in `saved` (global rows), the last two regions there
+  const std::vector<int64_t> soffs = {(int64_t)L.off_a, (int64_t)L.off_l, (int64_t)L.off_lse, (int64_t)L.off_phi,
+                                      (int64_t)L.off_psi, (int64_t)L.off_alpha, (int64_t)L.off_beta,
+                                      (int64_t)L.off_lnP, (int64_t)L.off_logits, (int64_t)L.off_z};
+  const int64_t SB = (int64_t)L.saved_bytes;
+  const Region rz = d.untiled ? region(L.off_z, soffs, SB) : region(off_z, offs, W);
+  const Region rlg = d.untiled ? region(L.off_logits, soffs, SB) : Region{0, 0};
   const Region rwo = region(off_wo, offs, W), rbl = region(L.w_bl, offs, W), rco = region(L.w_coefA, offs, W);
   const int64_t buf_rows = (p.max_wave_rows + 127) / 128 * 128;
   const int hrow = d.fp8 ? p.H8 / 2 : p.H_pad;
@@ -117,7 +127,9 @@ std::string run_case(const Dims& d, const std::vector<int32_t>& T_len, const std
     where << "wave " << w << " (rows " << n_rows << ", n_ct " << n_ct << ")";
     if ((int64_t)n_ct * 128 > buf_rows) return "FAIL " + where.str() + ": cell tiles exceed the wave buffer rows";
     if (n_rows <= 0) return "FAIL " + where.str() + ": empty wave";
-    for (int bwd = 0; bwd < 2; ++bwd) {
+    // untiled: the wave's z rows start at its first global row
+    const int64_t zbase = d.untiled ? (int64_t)L.off_z + (int64_t)wv.row_begin * z_ld * 2 : (int64_t)off_z;
+    for (int bwd = 0; bwd < (d.untiled ? 1 : 2); ++bwd) {
       for (int blk = 0; blk < s3map::kGrid; ++blk) {
         const int xcd = blk & 7, slot = blk >> 3;
         const int nctl = s3map::nctl_of(n_ct, xcd);
@@ -137,7 +149,7 @@ std::string run_case(const Dims& d, const std::vector<int32_t>& T_len, const std
           if (it.vt < 0 || it.vt >= nvt) return bad("V tile " + std::to_string(it.vt) + " out of range", S);
           const s3map::StageSrc o = s3map::stage_src(S, nq, n_items, nctl, nvt, xcd, slot, hrow, z_ld, nbuf);
           if (!inside(rwo, off_wo + o.a + a_lo, off_wo + o.a + a_hi)) return bad("W^O rows outside", S);
-          if (!inside(rz, off_z + o.b + b_lo, off_z + o.b + b_hi)) return bad("z rows outside", S);
+          if (!inside(rz, zbase + o.b + b_lo, zbase + o.b + b_hi)) return bad("z rows outside", S);
           if (o.par < 0 || o.par >= nbuf) return bad("bias buffer index out of range", S);
           // the z rows a stage reads belong to its cell tile's 128 rows
           if (o.b + b_lo < (int64_t)it.ct * 128 * z_ld * 2 || o.b + b_hi > ((int64_t)it.ct + 1) * 128 * z_ld * 2)
@@ -155,6 +167,13 @@ std::string run_case(const Dims& d, const std::vector<int32_t>& T_len, const std
             // stats[row][vt] as (max, sum) float pairs
             if (!inside(rst, L.w_stats + 8 * (r0 * nvt + it.vt), L.w_stats + 8 * ((r1 - 1) * nvt + it.vt) + 8))
               return bad("statistics store outside", -1);
+            // untiled: the scores of rows r0 .. min(r1, n_rows) - 1, V tile columns
+            if (d.untiled && r0 < n_rows) {
+              const int64_t g0 = (int64_t)wv.row_begin + r0, g1 = (int64_t)wv.row_begin + std::min<int64_t>(r1, n_rows);
+              if (!inside(rlg, L.off_logits + 2 * (g0 * p.V_pad + (int64_t)it.vt * 256),
+                          L.off_logits + 2 * ((g1 - 1) * p.V_pad + (int64_t)it.vt * 256 + 256)))
+                return bad("scores store outside", -1);
+            }
           } else {
             if (!inside(rdh, L.w_dh + 2 * (r0 * p.V_pad + (int64_t)it.vt * 256),
                         L.w_dh + 2 * ((r1 - 1) * p.V_pad + (int64_t)it.vt * 256 + 256)))

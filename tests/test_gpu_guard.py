@@ -5,7 +5,7 @@ query declares.
 device allocation with 64 KiB of a byte pattern before and after; after a forward and a
 backward the pattern must be intact (and the results must still match the oracle, so the
 buffers were really used). Covered: bf16 tiled (two tile shapes, ragged lengths), bf16
-untiled, fp32 tiled, the fp8 output layer and a pruned lattice.
+untiled (both score kernels), fp32 tiled, the fp8 output layer and a pruned lattice.
 """
 import numpy as np
 import pytest
@@ -78,17 +78,19 @@ def run_guarded(rl, inp, mode="tiled", tile=(64, 32), tpw=0, fp8=False, band=Non
 
 
 CASES = [
-    ("bf16 tiled 64x32", dict(dtype="bf16"), dict()),
-    ("bf16 tiled 20x7, 3 tiles per wave", dict(dtype="bf16"), dict(tile=(20, 7), tpw=3)),
-    ("bf16 untiled", dict(dtype="bf16"), dict(mode="untiled")),
-    ("fp32 tiled 32x16", dict(dtype="f32"), dict(tile=(32, 16), tpw=5)),
-    ("fp8 output layer", dict(dtype="bf16"), dict(fp8=True)),
+    ("bf16 tiled 64x32", dict(dtype="bf16"), dict(), 128),
+    ("bf16 tiled 20x7, 3 tiles per wave", dict(dtype="bf16"), dict(tile=(20, 7), tpw=3), 128),
+    ("bf16 untiled", dict(dtype="bf16"), dict(mode="untiled"), 128),
+    # H = 640: the persistent forward score kernel stores the scores; its last cell tile
+    # reads the padding rows after the z rows kept in `saved`
+    ("bf16 untiled, persistent score kernel", dict(dtype="bf16"), dict(mode="untiled"), 640),
+    ("fp32 tiled 32x16", dict(dtype="f32"), dict(tile=(32, 16), tpw=5), 128),
+    ("fp8 output layer", dict(dtype="bf16"), dict(fp8=True), 640),
 ]
 
 
-@pytest.mark.parametrize("name,inkw,kw", CASES, ids=[c[0] for c in CASES])
-def test_writes_stay_inside_declared_buffers(gpu_lib, name, inkw, kw):
-    H = 640 if kw.get("fp8") else 128
+@pytest.mark.parametrize("name,inkw,kw,H", CASES, ids=[c[0] for c in CASES])
+def test_writes_stay_inside_declared_buffers(gpu_lib, name, inkw, kw, H):
     inp = make_inputs(3, 90, 37, 700, 96, 64, H, seed=171, t_range=(30, 90), u_range=(0, 37), bias_std=0.1, **inkw)
     say(f"guard bytes: {name}")
     costs, grads = run_guarded(gpu_lib, inp, **kw)

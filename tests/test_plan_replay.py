@@ -6,8 +6,9 @@ every wave of every plan below, every workgroup, stage and item of the forward a
 launches, it checks that the cell tile and V tile indices are in range and that every dma
 source and epilogue store byte range lies inside the buffer region the layout reserves.
 Covered: the four bf16 workloads at their lengths with the tile sizes they are run with and
-more, default, single-tile, small and whole-batch waves, whole-sample tiles, and ragged or
-degenerate length sets.
+more, default, single-tile, small and whole-batch waves, whole-sample tiles, ragged or
+degenerate length sets, untiled mode (the forward's z rows and stored scores in `saved`),
+the fp8 output layer and pruned lattices.
 """
 import os
 import subprocess
@@ -85,6 +86,29 @@ def test_ragged_and_degenerate_plans_stay_in_bounds(replay):
     bad = [(l.split()[:12], o) for l, o in zip(lines, out) if o.startswith("FAIL")]
     assert rc == 0 and not bad, bad[:3]
     assert sum(o.startswith("ok") for o in out) >= 30
+
+
+def test_untiled_plans_stay_in_bounds(replay):
+    """Untiled bf16 mode runs the forward score kernel with a store of the scores: one wave
+    of every row, its z rows read from `saved` (the last cell tile reads into the padding
+    rows kept there) and the scores of the wave's rows stored into `saved`."""
+    lines = []
+    for name in ("small-bf16", "20s-bf16", "vocab4096-bf16"):
+        w = WORKLOADS[name]
+        T_len, U_len = workload_lengths(name)
+        for tile in ((64, 32), (32, 16), (w.T, w.U + 1)):
+            lines.append(case_line(w.B, w.T, w.U, w.V, w.HA, w.HL, w.H, tile, 0, T_len, U_len, untiled=True))
+    rng = np.random.default_rng(13)
+    for _ in range(20):
+        B, T, U = int(rng.integers(1, 20)), int(rng.integers(1, 300)), int(rng.integers(0, 120))
+        H = int(rng.choice([512, 576, 640, 768]))
+        V = int(rng.choice([300, 1000, 1024, 4096]))
+        tile = (int(rng.integers(1, 100)), int(rng.integers(1, 40)))
+        lines.append(case_line(B, T, U, V, 64, 64, H, tile, 0, rng.integers(1, T + 1, B), rng.integers(0, U + 1, B),
+                               untiled=True))
+    rc, out = run(replay, lines)
+    bad = [(l.split()[:12], o) for l, o in zip(lines, out) if not o.startswith("ok")]
+    assert rc == 0 and not bad, bad[:3]
 
 
 def test_fp8_plans_stay_in_bounds(replay):
