@@ -429,6 +429,21 @@ def test_40s_b256_closed_form_and_sample(gpu_lib):
     sampled_check(gpu_lib, inp, [11])
 
 
+@pytest.mark.timeout(600)
+def test_40s_b256_untiled_closed_form_and_sample(gpu_lib):
+    """Untiled mode at the 40 s x 256 workload: the scores and z of all 31 M rows are kept
+    (about 98 GB of `saved`, which one GPU's HBM holds), the backward forms dh from them."""
+    import torch
+
+    inp = workload_inputs("40s-b256-bf16")
+    say("40s-b256 full untiled, W^O = 0: closed-form cost for every sample")
+    closed_form_costs(gpu_lib, inp, mode="untiled")
+    torch.cuda.empty_cache()
+    say("40s-b256 full untiled, sampled oracle")
+    sampled_check(gpu_lib, inp, [11], mode="untiled")
+    torch.cuda.empty_cache()
+
+
 # ----------------------------------------------------------------------------- structure
 
 @pytest.mark.timeout(400)
