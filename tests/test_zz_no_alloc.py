@@ -4,7 +4,7 @@ Through the C ABI, on two calls in a row (the second on a smaller batch), the al
 forward gives the same costs as rnnt_loss_fwd bit for bit, and its `saved` drives rnnt_loss_bwd to
 the same gradients bit for bit; device memory is not allocated by the call; a request whose
 forward needs more than the array is refused before any launch; fp32 mode needs no scratch; the
-fp8 output layer's forward runs from the array as well.
+fp8 output layer's forward and the untiled mode's forward run from the array as well.
 """
 import numpy as np
 import pytest
@@ -16,10 +16,10 @@ pytestmark = pytest.mark.gpu
 GRADS = ("dhA", "dhL", "dWA", "dWL", "dbZ", "dWO", "dbO")
 
 
-def both_ways(rl, inp, tile=(64, 32), tpw=0, fp8=False):
+def both_ways(rl, inp, tile=(64, 32), tpw=0, fp8=False, mode="tiled"):
     import torch
 
-    prob = rl.Problem(inp, tile=tile, tiles_per_wave=tpw, fp8=fp8)
+    prob = rl.Problem(inp, mode=mode, tile=tile, tiles_per_wave=tpw, fp8=fp8)
     ref_costs = prob.forward().clone()
     ref_grads = {k: v.clone() for k, v in prob.backward().items()}
     torch.cuda.synchronize()
@@ -59,6 +59,16 @@ def test_noalloc_forward_fp8(gpu_lib):
                       u_range=(5, 30), bias_std=0.1)
     print("noalloc forward: fp8 output layer", flush=True)
     both_ways(gpu_lib, inp, fp8=True)
+
+
+def test_noalloc_forward_untiled(gpu_lib):
+    """Untiled mode: the forward keeps the scores and z in `saved` (the score kernel's store
+    path), its statistics and score tables in the scratch array; the backward forms dh from the
+    kept scores in place."""
+    inp = make_inputs(4, 120, 30, 1000, 256, 192, 640, dtype="bf16", seed=305, t_range=(60, 120),
+                      u_range=(0, 30), bias_std=0.1)
+    print("noalloc forward: untiled", flush=True)
+    both_ways(gpu_lib, inp, mode="untiled")
 
 
 def test_noalloc_forward_fp32_and_limit(gpu_lib):
