@@ -5,7 +5,9 @@ Each case draws (from a fixed seed, so the sweep is the same every run) the batc
 blank id, the mode (tiled / untiled), the dtype (fp32, bf16, bf16 with the fp8 output layer),
 the tile shape and tiles per wave, optionally a pruned lattice, and non-unit upstream gradients,
 then compares every cost and gradient with the fp64 oracle at the dtype's tolerances (the fp8
-cases against the oracle's fp8 reading). Sizes keep the oracle at about a second per case.
+cases against the oracle's fp8 reading). Sizes keep the oracle at about a second per case. A
+second sweep draws bf16 untiled problems with H >= 512 only: the persistent forward score kernel
+with its score store and the backward's dh formed in place of the kept scores.
 """
 import numpy as np
 import pytest
@@ -39,11 +41,35 @@ def draw_case(i):
     return inp, kind, mode, tile, tpw, pruned, dcosts
 
 
+def draw_untiled_case(i):
+    rng = np.random.default_rng(4000 + i)
+    B = int(rng.integers(1, 7))
+    T = int(rng.integers(1, 120))
+    U = int(rng.integers(0, 64))
+    V = int(rng.choice([7, 300, 513, 1000, 1024, 1030, 2100]))
+    H = int(rng.choice([512, 520, 640, 768]))
+    HA, HL = int(rng.choice([8, 64, 96])), int(rng.choice([8, 40, 64]))
+    blank = int(rng.choice([0, V - 1, V // 2]))
+    pruned = rng.random() < 0.3
+    inp = make_inputs(B, T, U, V, HA, HL, H, dtype="bf16", seed=5000 + i, t_range=(1, T), u_range=(0, U),
+                      bias_std=0.2, blank=blank)
+    dcosts = rng.uniform(-1.5, 2.0, B)
+    return inp, "bf16", "untiled", (64, 32), 0, pruned, dcosts
+
+
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_case(gpu_lib, i):
+    run_case(gpu_lib, i, *draw_case(i))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_untiled_case(gpu_lib, i):
+    run_case(gpu_lib, 1000 + i, *draw_untiled_case(i))
+
+
+def run_case(gpu_lib, i, inp, kind, mode, tile, tpw, pruned, dcosts):
     import torch
 
-    inp, kind, mode, tile, tpw, pruned, dcosts = draw_case(i)
     B, T, _ = inp.hA.shape
     U = inp.hL.shape[1] - 1
     V, H = inp.WO.shape
