@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -119,6 +120,33 @@ rnnt_status upload(void* dst, const std::vector<char>& src, hipStream_t st) {
     return fail(RNNT_E_HIP, std::string("plan upload: ") + (what ? what : "failed") + ": " +
                                 hipGetErrorString(hipGetLastError()));
   return RNNT_OK;
+}
+
+// Under stream capture the copy becomes a graph node that reads its host
+// source at every replay, so a captured forward copies its plan from a host
+// buffer of its own, kept unchanged until the process ends (one per captured
+// call: a staging slot is reused by later calls, and its event is not
+// recorded during a capture). Ordinary heap memory: no pinned allocation.
+std::mutex g_captured_mu;
+std::vector<std::unique_ptr<char[]>> g_captured_plans;
+
+rnnt_status plan_copy(void* dst, const std::vector<char>& src, hipStream_t st, bool scratch_mode) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  RNNT_HIP(hipStreamIsCapturing(st, &cs));
+  if (cs == hipStreamCaptureStatusActive) {
+    std::unique_ptr<char[]> buf(new char[src.size()]);
+    std::memcpy(buf.get(), src.data(), src.size());
+    RNNT_HIP(hipMemcpyAsync(dst, buf.get(), src.size(), hipMemcpyHostToDevice, st));
+    std::lock_guard<std::mutex> lk(g_captured_mu);
+    g_captured_plans.push_back(std::move(buf));
+    return RNNT_OK;
+  }
+  if (scratch_mode) {
+    // pageable source: the runtime has consumed it when the call returns
+    RNNT_HIP(hipMemcpyAsync(dst, src.data(), src.size(), hipMemcpyHostToDevice, st));
+    return RNNT_OK;
+  }
+  return upload(dst, src, st);
 }
 
 // ---------------------------------------------------------------- launch timing
@@ -378,13 +406,8 @@ static rnnt_status forward_impl(const rnnt_desc* desc, const void* hA, const voi
 
   std::vector<char> host_plan;
   rnnt::serialize_plan(p, L, T_len_host, U_len_host, host_plan);
-  if (scratch_mode) {
-    // pageable source: the runtime has consumed it when the call returns
-    RNNT_HIP(hipMemcpyAsync(saved, host_plan.data(), host_plan.size(), hipMemcpyHostToDevice, st));
-  } else {
-    s = upload(saved, host_plan, st);
-    if (s != RNNT_OK) return s;
-  }
+  s = plan_copy(saved, host_plan, st, scratch_mode);
+  if (s != RNNT_OK) return s;
   Saved sv = saved_view(saved, L);
   {
     ProfScope ps_("labels_check", st);
