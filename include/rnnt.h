@@ -52,6 +52,10 @@
  *    reused once its previous copy has completed; new slots are added while
  *    all are in flight, so a call waits on the host only if 16 forward calls'
  *    copies are still queued.
+ *  - The calls can be captured into a HIP graph (stream capture): a forward
+ *    called while its stream is capturing copies the plan from a host buffer
+ *    the library keeps until the process ends, so every replay of the graph
+ *    copies that call's plan.
  *  - Results are deterministic: every reduction (over tiles, waves, splits
  *    and samples) runs in a fixed order with no floating-point atomics, so
  *    repeated calls on the same inputs give identical bits.
