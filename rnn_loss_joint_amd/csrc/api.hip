@@ -807,6 +807,7 @@ static rnnt_status backward_impl(const rnnt_desc* desc, const void* hA, const vo
       a3.V_pad = p.V_pad;
       a3.blank = d.blank;
       a3.logits = at<char>(sv.logits, (size_t)wv.row_begin * p.V_pad * 2);
+      a3.bO = bO;
       a3.coefA = at<char>(workspace, L.w_coefA);
       a3.coefB = at<char>(workspace, L.w_coefB);
       a3.lse = sv.lse;

@@ -206,7 +206,8 @@ joint_kernel(JointArgs p) {
 
   // ---- per-row backward coefficients: lse, g*occ, g*bflow, g*lflow
   float r_lse[NACC], r_occ[NACC];
-  float my_lse = 0.0f, my_occ = 0.0f, my_cb = 0.0f, my_cl = 0.0f;
+  // rows that are no cell keep lse = +inf: their dh is exactly 0 for any score
+  float my_lse = kPosInf, my_occ = 0.0f, my_cb = 0.0f, my_cl = 0.0f;
   if (BWD) {
     if (g == 0) {
       if (row_ok) {

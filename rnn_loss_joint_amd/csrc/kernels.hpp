@@ -263,7 +263,7 @@ struct ScoresArgs {  // scores^T tiles: forward statistics or backward dh
   const void* z;
   int64_t z_ld;
   f32x2* stats;   // forward: [rows, V tiles] (max, sum)
-  void* logits;   // forward, untiled: y = h log2 e as bf16 [rows, V_pad] (global rows)
+  void* logits;   // forward, untiled: fp16 (W^O z) log2 e [rows, V_pad] (global rows)
   void* dh;       // backward: [rows, V_pad]
   const float* lse;
   const float* phi;
@@ -292,7 +292,8 @@ struct Scores3Args {
   int64_t z_ld;
   f32x2* stats;      // forward: [n_ct*128][nvt]
   void* dh;          // backward: [n_ct*128][V_pad] bf16
-  void* logits;      // forward, untiled mode: [n_rows][V_pad] bf16 y = (W^O z + b^O) log2 e (null: not stored)
+  void* logits;      // untiled mode: [n_rows][V_pad] fp16 (W^O z) log2 e (forward; null: not stored), dh in place (backward)
+  const void* bO;    // untiled backward: b^O [V] (bf16)
   void* coefA;       // [n_ct*128] (lse log2 e, occupancy)
   void* coefB;       // [n_ct*128] (cb, cl, label, 0)
   // fp8 output layer (WO8 non-null): E4M3 operands, rows of H8 bytes

@@ -344,7 +344,8 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoresArgs p) {
   // per-cell coefficients (backward)
   if (BWD) {
     const int rr = c0 + tid;  // buffer row
-    float ls = 0.0f, co = 0.0f, cb = 0.0f, cl = 0.0f, lab = -1.0f;
+    // rows that are no cell keep lse = +inf: their dh is exactly 0 for any score
+    float ls = kPosInf, co = 0.0f, cb = 0.0f, cl = 0.0f, lab = -1.0f;
     if (rr < p.n_rows) {
       const int R = rr + p.buf_row_base;
       int lo = p.tile_begin, hi = p.tile_end - 1;
@@ -458,8 +459,8 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoresArgs p) {
         if (rr < p.n_rows) p.stats[((int64_t)rr * nvt + vt)] = f32x2{mn * kLn2, sv};
       }
     }
-    if (p.logits) {  // untiled: keep y = h log2 e (bias included), 4 consecutive v per store
-      bf16* lg = reinterpret_cast<bf16*>(p.logits);
+    if (p.logits) {  // untiled: keep (W^O z) log2 e as fp16 (no bias), 4 consecutive v per store
+      f16* lg = reinterpret_cast<f16*>(p.logits);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f32x4 bq[4];
@@ -470,14 +471,12 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoresArgs p) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int v = vt * 256 + acc_row(wr, i, 4 * g, lane);
-            bf16x4 w;
+            f16x4 w;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float y = __builtin_fmaf(acc.c[i][j][4 * g + q], kLog2e, bq[g][q]);
-              w[q] = (bf16)(v + q < p.V ? y : 0.0f);
-            }
+            for (int q = 0; q < 4; ++q)
+              w[q] = (f16)__builtin_amdgcn_fmed3f(acc.c[i][j][4 * g + q] * kLog2e, -kF16Max, kF16Max);
             if (rr < p.n_rows && v < p.V_pad)
-              *reinterpret_cast<bf16x4*>(lg + (int64_t)(rr + p.buf_row_base) * p.V_pad + v) = w;
+              *reinterpret_cast<f16x4*>(lg + (int64_t)(rr + p.buf_row_base) * p.V_pad + v) = w;
           }
         }
       }

@@ -9,8 +9,9 @@
 //             denominator of Eq. (5) in pieces, merged afterwards);
 //   backward: dh = occupancy * softmax (Eq. (10) without the blank / label
 //             terms, which a separate pass subtracts) written as bf16;
-//   forward with a store (untiled mode): also the scaled scores y
-//             themselves, as bf16, for a backward without recomputation.
+//   forward with a store (untiled mode): also the scaled products
+//             (W^O z) log2 e without the bias, as fp16, for a backward
+//             without recomputation (which adds b^O log2 e back in fp32).
 //
 // One workgroup per CU (256 threads, 4 waves of 128 x 64 outputs) walks its
 // list of items; the A operand (a 256-row slice of a zero-padded copy of
@@ -202,7 +203,7 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
   f32x4 bq[4];
   float* stats2 = reinterpret_cast<float*>(p.stats);
   bf16* dh = reinterpret_cast<bf16*>(p.dh);
-  bf16* lg = reinterpret_cast<bf16*>(p.logits);
+  bf16* lg = reinterpret_cast<bf16*>(p.logits);  // 2-byte pieces moved as they are (fp16 values)
   char* const dhs = lds + OFF_DHS + wave * DHS_WAVE;  // block staging (backward dh, stored scores)
   bf16x8 fl[2];
 
@@ -235,18 +236,21 @@ __global__ void __launch_bounds__(256) scores3_kernel(Scores3Args p) {
             ebm = __builtin_fmaxf(ebm, y[e]);
           }
           if constexpr (STORE && (X & 1) == 1) {
-            // scores 8 (e4 / 4) + 4 g .. +3 of the block for cell r, into the
-            // staging buffer. The store path's per-lane offsets are formed
-            // from the lane index at each use (laundered through an empty
-            // asm) rather than kept live across the loop, where the registers
-            // are needed by the pipeline.
+            // products 8 (e4 / 4) + 4 g .. +3 of the block for cell r, scaled
+            // to log2 units without the bias (y minus it: the bias can be far
+            // larger, and the backward adds it back in fp32), as fp16 (clamped
+            // to its range), into the staging buffer. The store path's per-lane
+            // offsets are formed from the lane index at each use (laundered
+            // through an empty asm) rather than kept live across the loop,
+            // where the registers are needed by the pipeline.
             constexpr int e4 = 2 * X - 2;
-            bf16x4 w;
+            f16x4 w;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) w[q] = (bf16)y[e4 + q];
+            for (int q = 0; q < 4; ++q)
+              w[q] = (f16)__builtin_amdgcn_fmed3f(y[e4 + q] - bq[(e4 + q) >> 2][(e4 + q) & 3], -kF16Max, kF16Max);
             int ln = lane;
             asm volatile("" : "+v"(ln));
-            *reinterpret_cast<bf16x4*>(dhs + (ln & 31) * DHS_ROW + (8 * (e4 >> 2) + 4 * (ln >> 5)) * 2) = w;
+            *reinterpret_cast<f16x4*>(dhs + (ln & 31) * DHS_ROW + (8 * (e4 >> 2) + 4 * (ln >> 5)) * 2) = w;
           }
         } else {
           // task B(b): fold 2^(y - max) into the running sum
@@ -662,7 +666,7 @@ __global__ void __launch_bounds__(256) coef_kernel(Scores3Args p) {
   if ((int)blockIdx.x == p.tile_end - p.tile_begin) {
     if (blockIdx.y == 0 && blockIdx.z == 0)
       for (int rr = p.n_rows + threadIdx.x; rr < p.n_ct * s3::BN; rr += 256) {
-        coefA[rr] = f32x2{0.0f, 0.0f};
+        coefA[rr] = f32x2{kPosInf, 0.0f};
         coefB[rr] = f32x4{0.0f, 0.0f, -1.0f, 0.0f};
       }
     return;
@@ -724,8 +728,11 @@ __global__ void __launch_bounds__(256) coef_kernel(Scores3Args p) {
     const int ul = i / kCB, tt = i % kCB;
     if (ul >= nu) continue;
     const int rr = tl.row0 + (ub + ul) * tl.htp + tb + tt - p.buf_row_base;
-    float ls = 0.0f, co = 0.0f, cb = 0.0f, cl = 0.0f, lab = -1.0f;
-    if (tt < nt) {  // rows past ht (up to htp) are padding
+    // rows past ht (up to htp) are padding: lse = +inf makes the exponent of
+    // every score -inf there, so their dh is exactly 0 however large the
+    // score (0 x inf would be NaN)
+    float ls = kPosInf, co = 0.0f, cb = 0.0f, cl = 0.0f, lab = -1.0f;
+    if (tt < nt) {
       const int t = t0 + tt, u = u0 + ul;
       const float A = sm[0][ul * kCS + tt], Bt = sb[ul * kCS + tt];
       ls = sm[3][ul * kCS + tt];
@@ -765,10 +772,11 @@ hipError_t launch_dh_fix(const Scores3Args& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Untiled mode: dh from the scores the forward kept (y = h log2 e as bf16,
-// rows of V_pad), in place (Eq. (10)): dh = occ 2^(y - lse log2 e), minus
-// the blank and label terms of the row's coefficients. Eight consecutive
-// scores (16 bytes) per thread; a score past V holds y = -1e30, so its dh is 0.
+// Untiled mode: dh from the products the forward kept ((W^O z) log2 e as
+// fp16, rows of V_pad), written in place as bf16 (Eq. (10)): with
+// y = product + b^O log2 e (in fp32), dh = occ 2^(y - lse log2 e), minus the
+// blank and label terms of the row's coefficients. Eight consecutive scores
+// (16 bytes) per thread; past V the exponent is -inf, so dh is 0.
 __global__ void __launch_bounds__(256) dh_logits_kernel(Scores3Args p) {
   const int per_row = p.V_pad / 8;
   const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -778,21 +786,25 @@ __global__ void __launch_bounds__(256) dh_logits_kernel(Scores3Args p) {
   const f32x2 ca = reinterpret_cast<const f32x2*>(p.coefA)[rr];
   const f32x4 cb = reinterpret_cast<const f32x4*>(p.coefB)[rr];
   const int lab = (int)cb[2];
-  bf16x8* q = reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(p.logits) + (int64_t)rr * p.V_pad + v0);
-  bf16x8 w = *q;
+  const bf16* bO = reinterpret_cast<const bf16*>(p.bO);
+  char* row = reinterpret_cast<char*>(p.logits) + ((int64_t)rr * p.V_pad + v0) * 2;
+  const f16x8 w = *reinterpret_cast<const f16x8*>(row);
+  bf16x8 out;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    float d = ca[1] * fexp2((float)w[k] - ca[0]);
-    if (v0 + k == p.blank) d -= cb[0];
-    if (v0 + k == lab) d -= cb[1];
-    w[k] = (bf16)d;
+    const int v = v0 + k;
+    const float yb = v < p.V ? (float)bO[v] * kLog2e : kNegInf;
+    float d = ca[1] * fexp2((float)w[k] + yb - ca[0]);
+    if (v == p.blank) d -= cb[0];
+    if (v == lab) d -= cb[1];
+    out[k] = (bf16)d;
   }
-  *q = w;
+  *reinterpret_cast<bf16x8*>(row) = out;
 }
 
 hipError_t launch_dh_logits(const Scores3Args& a, hipStream_t st) {
   if (a.n_rows == 0) return hipSuccess;
-  if (a.V_pad % 8 != 0 || !a.logits || !a.coefA || !a.coefB) return hipErrorInvalidValue;
+  if (a.V_pad % 8 != 0 || !a.logits || !a.coefA || !a.coefB || !a.bO) return hipErrorInvalidValue;
   const int64_t n = (int64_t)a.n_rows * (a.V_pad / 8);
   hipLaunchKernelGGL(dh_logits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
