@@ -513,6 +513,21 @@ def test_large_output_biases(gpu_lib, dtype, mode, H):
     check_grads(inp, grads, ref.grads)
 
 
+@pytest.mark.parametrize("dtype,mode", [("f32", "tiled"), ("bf16", "tiled"), ("bf16", "untiled")])
+def test_longest_label_sequence(gpu_lib, dtype, mode):
+    """U + 1 = 1024, the library's limit (the lattice sweep on sixteen waves), and a long utterance
+    (T = 3000) in one batch, against the oracle."""
+    inp = make_inputs(3, 3000, 1023, 40, 32, 32, 64, dtype=dtype, seed=79, t_range=(2, 12), u_range=(900, 1023),
+                      bias_std=0.3)
+    inp.U_len[1] = 1023
+    inp.T_len[2], inp.U_len[2] = 3000, 7
+    say(f"U + 1 = 1024 and T = 3000, {dtype} {mode}: T_len={list(inp.T_len)} U_len={list(inp.U_len)}")
+    costs, grads = run_gpu(gpu_lib, inp, mode=mode, tile=(64, 32))
+    ref = oracle.loss_and_grads(inp)
+    check_costs(inp, costs, ref.costs)
+    check_grads(inp, grads, ref.grads)
+
+
 def test_deterministic_repeats(gpu_lib):
     inp = workload_inputs("small-bf16")
     say("determinism small")
