@@ -494,21 +494,28 @@ def test_padding_poison_is_ignored(gpu_lib, dtype, mode):
 
 
 @pytest.mark.parametrize("dtype,mode,H", [("bf16", "tiled", 640), ("bf16", "untiled", 640), ("bf16", "tiled", 128),
-                                          ("bf16", "untiled", 128), ("f32", "tiled", 64), ("f32", "untiled", 64)])
+                                          ("bf16", "untiled", 128), ("f32", "tiled", 64), ("f32", "untiled", 64),
+                                          ("fp8", "tiled", 640)])
 def test_large_output_biases(gpu_lib, dtype, mode, H):
     """Output biases far beyond exp's fp32 range (+-100 nats): every cell's softmax is dominated by
     them, and rows that are no cell (a tile's t extent padded to 32 rows, the rows after a wave's
     last cell) must still contribute exactly nothing, so costs and gradients match the oracle."""
     import dataclasses
 
-    inp = make_inputs(3, 45, 12, 300, 64, 48, H, dtype=dtype, seed=67, t_range=(17, 45), u_range=(0, 12),
-                      bias_std=0.1)
+    import torch
+
+    fp8 = dtype == "fp8"
+    inp = make_inputs(3, 45, 12, 300, 64, 48, H, dtype="bf16" if fp8 else dtype, seed=67, t_range=(17, 45),
+                      u_range=(0, 12), bias_std=0.1)
     bO = inp.bO.copy()
     bO[[3, 150, 299]] = [100.0, 95.0, -100.0]
     inp = dataclasses.replace(inp, bO=bO)
     say(f"large output biases {dtype} {mode} H={H}")
-    costs, grads = run_gpu(gpu_lib, inp, mode=mode, tile=(20, 7), tpw=2)
-    ref = oracle.loss_and_grads(inp)
+    prob = gpu_lib.Problem(inp, mode=mode, tile=(20, 7), tiles_per_wave=2, fp8=fp8)
+    costs = prob.forward().clone().cpu().numpy().astype(np.float64)
+    grads = {k: v.cpu().numpy().astype(np.float64) for k, v in prob.backward().items()}
+    torch.cuda.synchronize()
+    ref = oracle.loss_and_grads(inp, fp8_scores=fp8)
     check_costs(inp, costs, ref.costs)
     check_grads(inp, grads, ref.grads)
 
