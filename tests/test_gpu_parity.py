@@ -535,6 +535,19 @@ def test_longest_label_sequence(gpu_lib, dtype, mode):
     check_grads(inp, grads, ref.grads)
 
 
+@pytest.mark.parametrize("dtype,mode,H", [("f32", "tiled", 32), ("bf16", "tiled", 32), ("bf16", "tiled", 640),
+                                          ("bf16", "untiled", 640)])
+def test_smallest_vocabulary(gpu_lib, dtype, mode, H):
+    """V = 2 (the blank and one label), the library's smallest vocabulary: one 256-score V tile
+    holding 254 scores past V."""
+    inp = make_inputs(3, 20, 5, 2, 16, 24, H, dtype=dtype, seed=83, t_range=(1, 20), u_range=(0, 5), bias_std=0.5)
+    say(f"V = 2 {dtype} {mode} H={H}")
+    costs, grads = run_gpu(gpu_lib, inp, mode=mode, tile=(16, 4))
+    ref = oracle.loss_and_grads(inp)
+    check_costs(inp, costs, ref.costs)
+    check_grads(inp, grads, ref.grads)
+
+
 def test_deterministic_repeats(gpu_lib):
     inp = workload_inputs("small-bf16")
     say("determinism small")
