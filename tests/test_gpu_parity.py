@@ -548,6 +548,20 @@ def test_smallest_vocabulary(gpu_lib, dtype, mode, H):
     check_grads(inp, grads, ref.grads)
 
 
+@pytest.mark.parametrize("dtype,mode,tpw", [("f32", "tiled", 0), ("bf16", "tiled", 0), ("bf16", "tiled", 100),
+                                            ("bf16", "untiled", 0)])
+def test_large_batch_of_short_lattices(gpu_lib, dtype, mode, tpw):
+    """B = 1024 lattices of at most 10 x 5 cells: a wave of a thousand one-tile samples (or waves of
+    100), a thousand reduction groups of each kind, the lattice sweep on 2048 workgroups."""
+    inp = make_inputs(1024, 10, 4, 60, 16, 16, 64 if dtype == "f32" else 512, dtype=dtype, seed=85, t_range=(1, 10),
+                      u_range=(0, 4), bias_std=0.3)
+    say(f"B = 1024 short lattices {dtype} {mode} tpw={tpw}")
+    costs, grads = run_gpu(gpu_lib, inp, mode=mode, tile=(16, 8), tpw=tpw)
+    ref = oracle.loss_and_grads(inp)
+    check_costs(inp, costs, ref.costs)
+    check_grads(inp, grads, ref.grads)
+
+
 def test_deterministic_repeats(gpu_lib):
     inp = workload_inputs("small-bf16")
     say("determinism small")
