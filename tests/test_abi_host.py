@@ -28,6 +28,21 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
+def test_header_is_c_and_host_calls_work_from_c(tmp_path):
+    """include/rnnt.h compiles as C99 on its own; a C client (tests/host/abi_c_client.c) links to
+    the library and calls the host-only entry points."""
+    import subprocess
+
+    exe = str(tmp_path / "abi_c_client")
+    lib_dir = os.path.dirname(rl.LIB_PATH)
+    r = subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Werror", f"-I{os.path.join(ROOT, 'include')}",
+                        os.path.join(ROOT, "tests", "host", "abi_c_client.c"), f"-L{lib_dir}", "-lrnnt_mi355",
+                        f"-Wl,-rpath,{lib_dir}", "-o", exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout + r.stderr
+
+
 def test_status_strings():
     assert rl.rnnt_status_string(0) == "ok"
     assert "workspace" in rl.rnnt_status_string(-2)
