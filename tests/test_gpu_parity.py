@@ -444,6 +444,41 @@ def test_40s_b256_untiled_closed_form_and_sample(gpu_lib):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("mode,fp8", [("tiled", False), ("untiled", False), ("tiled", True)])
+def test_40s_b256_bitwise_repeats(gpu_lib, mode, fp8):
+    """Two fwd+bwd passes over the 40 s x 256 workload give the same bits in every cost and gradient.
+    Every reduction is ordered, so they must; and at this size every CU is busy, so a load or store
+    whose result depended on timing would show here first (the lattice sweep's bitwise test makes the
+    same check for the sweep alone)."""
+    import torch
+
+    inp = workload_inputs("40s-b256-bf16")
+    say(f"40s-b256 {mode}{' fp8' if fp8 else ''}: two passes, bitwise")
+    prob = gpu_lib.Problem(inp, mode=mode, fp8=fp8)
+    dc = torch.tensor(np.random.default_rng(5).uniform(0.5, 1.5, len(inp.T_len)).astype(np.float32),
+                      device=prob.device)
+    runs = []
+    for _ in range(2):
+        c = prob.forward().clone()
+        g = {k: v.clone() for k, v in prob.backward(dc).items()}
+        torch.cuda.synchronize()
+        runs.append((c, g))
+    bits = lambda t: t.contiguous().view(torch.int32)
+    assert torch.equal(bits(runs[0][0]), bits(runs[1][0])), "costs differ between the passes"
+    for k in GRADS:
+        a, b = bits(runs[0][1][k]), bits(runs[1][1][k])
+        if not torch.equal(a, b):
+            diff = (a != b).flatten()
+            raise AssertionError(f"{k}: {int(diff.sum())} entries differ, first at flat index "
+                                 f"{int(diff.nonzero()[0])}")
+    assert bool(torch.isfinite(runs[0][0]).all())
+    for k in GRADS:
+        assert bool(torch.isfinite(runs[0][1][k]).all()), k
+    del prob, runs
+    torch.cuda.empty_cache()
+
+
 # ----------------------------------------------------------------------------- structure
 
 @pytest.mark.timeout(400)
