@@ -196,6 +196,7 @@ struct Saved {
   int32_t* status;
   int32_t* labels;  // the range-checked labels every kernel reads
   const int64_t* lat_off;  // packed lattice blocks
+  const int32_t* lat_pair;  // lattice sweep pairing [2 B]
   const int32_t* band_lo;  // pruned lattice bands [B, T], else null
   const int32_t* Tlen;
   const int32_t* Ulen;
@@ -213,6 +214,7 @@ Saved saved_view(void* s, const rnnt::Layout& L) {
   v.status = at<int32_t>(s, L.off_status);
   v.labels = at<int32_t>(s, L.off_labels);
   v.lat_off = at<int64_t>(s, L.off_latoff);
+  v.lat_pair = at<int32_t>(s, L.off_latpair);
   v.band_lo = L.off_band ? at<int32_t>(s, L.off_band) : nullptr;
   v.Tlen = at<int32_t>(s, L.off_Tlen);
   v.Ulen = at<int32_t>(s, L.off_Ulen);
@@ -640,6 +642,7 @@ static rnnt_status forward_impl(const rnnt_desc* desc, const void* hA, const voi
   {
     rnnt::LatticeArgs la{sv.Tlen, sv.Ulen, sv.phi, sv.psi, sv.alpha, sv.beta, sv.lnP, costs, d.B, d.T, p.U1};
     la.lat_off = sv.lat_off;
+    la.pair = sv.lat_pair;
     la.clamp = sv.band_lo != nullptr;
     ProfScope ps_("lattice", st);
     if (L.lat64) {

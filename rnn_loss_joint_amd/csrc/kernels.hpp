@@ -100,6 +100,10 @@ struct LatticeArgs {
   // cells outside the band, or caller-given log-probs); false for the loss's
   // own full lattice, whose log-probs are finite
   bool clamp;
+  // [2 B] (may be null): the paired sweep's workgroup j runs alpha of sample
+  // pair[2 j] and beta of sample pair[2 j + 1]; each sample appears once in
+  // each role
+  const int32_t* pair;
 };
 hipError_t launch_lattice(const LatticeArgs& a, int U1max, hipStream_t st);
 // Pruned lattice: phi = psi = -inf on every lattice cell (t < T_b, u <= U_b)

@@ -198,6 +198,20 @@ void build_plan(const Dims& d, const int32_t* T_len, const int32_t* U_len, int H
   // packed lattice blocks: sample b's block is cut to its own T_b x (U_b + 1)
   p.lat_off.assign(d.B + 1, 0);
   for (int b = 0; b < d.B; ++b) p.lat_off[b + 1] = p.lat_off[b] + lat_block(T_len[b], U_len[b]);
+  // lattice sweep pairing: the j-th longest sample's alpha with the j-th
+  // shortest's beta (longest first by T_b - 1 + U_b, ties by index)
+  {
+    std::vector<int32_t> order(d.B);
+    for (int b = 0; b < d.B; ++b) order[b] = b;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+      return T_len[x] + U_len[x] > T_len[y] + U_len[y];
+    });
+    p.lat_pair.assign(2 * (size_t)d.B, 0);
+    for (int j = 0; j < d.B; ++j) {
+      p.lat_pair[2 * j] = order[j];
+      p.lat_pair[2 * j + 1] = order[d.B - 1 - j];
+    }
+  }
   int64_t row = 0, strip = 0;
   for (auto& t : p.tiles) {
     t.row0 = (int32_t)row;
@@ -303,6 +317,7 @@ Layout make_layout(const Plan& p) {
   L.off_groups = take(sizeof(GroupH) * p.groups.size());
   L.off_gidx = take(sizeof(int32_t) * p.gidx.size());
   L.off_latoff = take(sizeof(int64_t) * p.lat_off.size());
+  L.off_latpair = take(sizeof(int32_t) * p.lat_pair.size());
   L.off_band = p.band_lo.empty() ? 0 : take(sizeof(int32_t) * p.band_lo.size());
   L.plan_bytes = o;
   L.off_labels = take(sizeof(int32_t) * (size_t)d.B * p.U1);
@@ -435,6 +450,8 @@ void serialize_plan(const Plan& p, const Layout& L, const int32_t* T_len, const 
   if (!p.groups.empty()) std::memcpy(out.data() + L.off_groups, p.groups.data(), sizeof(GroupH) * p.groups.size());
   if (!p.gidx.empty()) std::memcpy(out.data() + L.off_gidx, p.gidx.data(), sizeof(int32_t) * p.gidx.size());
   std::memcpy(out.data() + L.off_latoff, p.lat_off.data(), sizeof(int64_t) * p.lat_off.size());
+  if (!p.lat_pair.empty())
+    std::memcpy(out.data() + L.off_latpair, p.lat_pair.data(), sizeof(int32_t) * p.lat_pair.size());
   if (!p.band_lo.empty()) std::memcpy(out.data() + L.off_band, p.band_lo.data(), sizeof(int32_t) * p.band_lo.size());
 }
 

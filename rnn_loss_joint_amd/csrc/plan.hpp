@@ -54,6 +54,10 @@ struct Plan {
   std::vector<GroupH> groups;
   std::vector<int32_t> gidx;
   std::vector<int64_t> lat_off;  // [B + 1] packed lattice block offsets (entries)
+  // [2 B] lattice sweep pairing: samples by T_b - 1 + U_b, longest first
+  // (ties by index); workgroup j sweeps alpha of the j-th longest and beta of
+  // the j-th shortest
+  std::vector<int32_t> lat_pair;
   int64_t total_rows = 0;
   int max_wave_rows = 0, max_wave_tiles = 0;
   int s6 = 1, s7a = 1, s7l = 1;  // split-K counts
@@ -68,6 +72,7 @@ struct Layout {
   size_t off_Tlen, off_Ulen, off_tiles, off_groups, off_gidx;
   size_t off_labels;  // int32 [B, U+1]: the labels the kernels read (range-checked copy)
   size_t off_latoff;  // int64 [B + 1]: packed lattice block offsets (part of the plan copy)
+  size_t off_latpair; // int32 [2 B]: lattice sweep pairing (part of the plan copy)
   size_t off_band;    // int32 [B, T]: the bands of a pruned lattice (part of the plan copy; 0 if none)
   size_t lat_entries; // entries of each lattice array (lat_off[B])
   size_t off_a, off_l, off_lse, off_phi, off_psi, off_alpha, off_beta, off_lnP;
