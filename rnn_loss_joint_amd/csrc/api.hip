@@ -764,6 +764,9 @@ static rnnt_status backward_impl(const rnnt_desc* desc, const void* hA, const vo
     ProfScope ps_("score_tables", st);
     RNNT_HIP(rnnt::launch_score_tables(WO, bO, at<char>(workspace, L.w_WOp), at<float>(workspace, L.w_bl), d.V, d.H,
                                        p.H_pad, p.nvt, st));
+  } else if (d.untiled && bf) {
+    ProfScope ps_("score_tables", st);
+    RNNT_HIP(rnnt::launch_bias_table(bO, at<float>(workspace, L.w_bl), d.V, p.nvt, st));
   }
   if (d.fp8 && p.H8 > p.H_pad) {
     ProfScope ps_("fill", st);
@@ -810,7 +813,7 @@ static rnnt_status backward_impl(const rnnt_desc* desc, const void* hA, const vo
       a3.V_pad = p.V_pad;
       a3.blank = d.blank;
       a3.logits = at<char>(sv.logits, (size_t)wv.row_begin * p.V_pad * 2);
-      a3.bO = bO;
+      a3.bl = at<float>(workspace, L.w_bl);
       a3.coefA = at<char>(workspace, L.w_coefA);
       a3.coefB = at<char>(workspace, L.w_coefB);
       a3.lse = sv.lse;

@@ -317,6 +317,8 @@ struct Scores3Args {
 hipError_t launch_scores3(const Scores3Args& a, bool bwd, hipStream_t st);
 hipError_t launch_score_tables(const void* WO, const void* bO, void* WOp, float* bl, int V, int H, int H_pad,
                                int nvt, hipStream_t st);
+// The bias table alone: bl[v] = b^O[v] log2 e for v < V, -1e30 up to nvt * 256.
+hipError_t launch_bias_table(const void* bO, float* bl, int V, int nvt, hipStream_t st);
 // fp8 output layer: ew = the largest e with max|W^O| 2^e <= 448 (0 if W^O is
 // all zero), WO8 = E4M3(W^O 2^e) as [nvt*256][H8] bytes (0 past V and H), the
 // bias table bl as launch_score_tables writes it.

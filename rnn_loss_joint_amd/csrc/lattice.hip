@@ -344,7 +344,8 @@ __device__ __attribute__((always_inline)) inline void lattice_body(const Lattice
 // the shorter sweep ends; after that the longer one has its SIMDs alone and
 // runs faster (about 1.6x per diagonal, measured). Pairing the longest
 // samples' sweeps with the shortest ones therefore shortens the longest
-// workgroup, which sets the launch's time.
+// workgroup, which sets the launch's time. Used when the 2 B sweeps
+// outnumber the CUs (with fewer, each unpaired sweep has a CU of its own).
 template <int NW, int SW, bool CLAMP>
 __global__ void __launch_bounds__(128 * NW) lattice_pair_kernel(LatticeArgs p) {
   constexpr int PF = 2;
@@ -370,12 +371,19 @@ __global__ void __launch_bounds__(64 * NW) lattice_kernel(LatticeArgs p) {
 }
 
 template <bool CLAMP>
-hipError_t launch_lattice_t(const LatticeArgs& a, int nw, hipStream_t st) {
+hipError_t launch_lattice_t(const LatticeArgs& a, int nw, bool paired, hipStream_t st) {
   const dim3 pairs(a.B), grid(a.B, 2);
-  if (nw <= 1) hipLaunchKernelGGL((lattice_pair_kernel<1, 16, CLAMP>), pairs, dim3(128), 0, st, a);
-  else if (nw <= 2) hipLaunchKernelGGL((lattice_pair_kernel<2, 16, CLAMP>), pairs, dim3(256), 0, st, a);
-  else if (nw <= 3) hipLaunchKernelGGL((lattice_pair_kernel<3, 16, CLAMP>), pairs, dim3(384), 0, st, a);
-  else if (nw <= 4) hipLaunchKernelGGL((lattice_pair_kernel<4, 16, CLAMP>), pairs, dim3(512), 0, st, a);
+  if (paired && nw <= 4) {
+    if (nw <= 1) hipLaunchKernelGGL((lattice_pair_kernel<1, 16, CLAMP>), pairs, dim3(128), 0, st, a);
+    else if (nw <= 2) hipLaunchKernelGGL((lattice_pair_kernel<2, 16, CLAMP>), pairs, dim3(256), 0, st, a);
+    else if (nw <= 3) hipLaunchKernelGGL((lattice_pair_kernel<3, 16, CLAMP>), pairs, dim3(384), 0, st, a);
+    else hipLaunchKernelGGL((lattice_pair_kernel<4, 16, CLAMP>), pairs, dim3(512), 0, st, a);
+    return hipGetLastError();
+  }
+  if (nw <= 1) hipLaunchKernelGGL((lattice_kernel<1, 16, CLAMP>), grid, dim3(64), 0, st, a);
+  else if (nw <= 2) hipLaunchKernelGGL((lattice_kernel<2, 16, CLAMP>), grid, dim3(128), 0, st, a);
+  else if (nw <= 3) hipLaunchKernelGGL((lattice_kernel<3, 16, CLAMP>), grid, dim3(192), 0, st, a);
+  else if (nw <= 4) hipLaunchKernelGGL((lattice_kernel<4, 16, CLAMP>), grid, dim3(256), 0, st, a);
   else if (nw <= 6) hipLaunchKernelGGL((lattice_kernel<6, 16, CLAMP>), grid, dim3(384), 0, st, a);
   else if (nw <= 8) hipLaunchKernelGGL((lattice_kernel<8, 16, CLAMP>), grid, dim3(512), 0, st, a);
   else if (nw <= 12) hipLaunchKernelGGL((lattice_kernel<12, 8, CLAMP>), grid, dim3(768), 0, st, a);
@@ -387,7 +395,13 @@ hipError_t launch_lattice_t(const LatticeArgs& a, int nw, hipStream_t st) {
 hipError_t launch_lattice(const LatticeArgs& a, int U1max, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   const int nw = (U1max + 63) / 64;
-  return a.clamp ? launch_lattice_t<true>(a, nw, st) : launch_lattice_t<false>(a, nw, st);
+  // pair the sweeps only when they outnumber the CUs: with fewer, each
+  // unpaired sweep gets a CU of its own
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipErrorInvalidDevice;
+  const bool paired = 2 * (int64_t)a.B > cus;
+  return a.clamp ? launch_lattice_t<true>(a, nw, paired, st) : launch_lattice_t<false>(a, nw, paired, st);
 }
 
 // Pruned lattice: the two log-probs of every cell outside its frame's band

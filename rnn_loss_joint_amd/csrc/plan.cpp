@@ -374,7 +374,7 @@ Layout make_layout(const Plan& p) {
   L.w_WOp = L.w_bl = L.w_coefA = L.w_coefB = 0;
   const bool s3 = persistent_scores(p);
   if (s3 && !d.fp8) L.w_WOp = take(2 * (size_t)p.nvt * 256 * p.H_pad);
-  if (s3) L.w_bl = take(4 * (size_t)p.nvt * 256);
+  if (s3 || (d.bf16 && d.untiled)) L.w_bl = take(4 * (size_t)p.nvt * 256);  // untiled: dh_logits reads it
   if (d.bf16 && (s3 || d.untiled)) {
     L.w_coefA = take(8 * wrows);
     L.w_coefB = take(16 * wrows);

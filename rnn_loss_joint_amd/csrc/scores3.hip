@@ -573,6 +573,13 @@ __global__ void bias_table_kernel(const bf16* __restrict__ bO, float* __restrict
   if (v < rows) bl[v] = v < V ? (float)bO[v] * kLog2e : -1e30f;
 }
 
+hipError_t launch_bias_table(const void* bO, float* bl, int V, int nvt, hipStream_t st) {
+  const int rows = nvt * 256;
+  hipLaunchKernelGGL(bias_table_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, reinterpret_cast<const bf16*>(bO),
+                     bl, V, rows);
+  return hipGetLastError();
+}
+
 hipError_t launch_score_tables(const void* WO, const void* bO, void* WOp, float* bl, int V, int H, int H_pad,
                                int nvt, hipStream_t st) {
   const int rows = nvt * 256;
@@ -776,7 +783,8 @@ hipError_t launch_dh_fix(const Scores3Args& a, hipStream_t st) {
 // fp16, rows of V_pad), written in place as bf16 (Eq. (10)): with
 // y = product + b^O log2 e (in fp32), dh = occ 2^(y - lse log2 e), minus the
 // blank and label terms of the row's coefficients. Eight consecutive scores
-// (16 bytes) per thread; past V the exponent is -inf, so dh is 0.
+// (16 bytes) per thread, their b^O log2 e from the bias table (two 16-byte
+// loads); past V the table holds -1e30, so dh is 0.
 __global__ void __launch_bounds__(256) dh_logits_kernel(Scores3Args p) {
   const int per_row = p.V_pad / 8;
   const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -786,14 +794,16 @@ __global__ void __launch_bounds__(256) dh_logits_kernel(Scores3Args p) {
   const f32x2 ca = reinterpret_cast<const f32x2*>(p.coefA)[rr];
   const f32x4 cb = reinterpret_cast<const f32x4*>(p.coefB)[rr];
   const int lab = (int)cb[2];
-  const bf16* bO = reinterpret_cast<const bf16*>(p.bO);
+  // b^O log2 e, and -1e30 past V (2^(w - 1e30 - lse) is exactly 0 there)
+  const f32x4 bl0 = reinterpret_cast<const f32x4*>(p.bl + v0)[0];
+  const f32x4 bl1 = reinterpret_cast<const f32x4*>(p.bl + v0)[1];
   char* row = reinterpret_cast<char*>(p.logits) + ((int64_t)rr * p.V_pad + v0) * 2;
   const f16x8 w = *reinterpret_cast<const f16x8*>(row);
   bf16x8 out;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int v = v0 + k;
-    const float yb = v < p.V ? (float)bO[v] * kLog2e : kNegInf;
+    const float yb = k < 4 ? bl0[k] : bl1[k - 4];
     float d = ca[1] * fexp2((float)w[k] + yb - ca[0]);
     if (v == p.blank) d -= cb[0];
     if (v == lab) d -= cb[1];
@@ -804,7 +814,7 @@ __global__ void __launch_bounds__(256) dh_logits_kernel(Scores3Args p) {
 
 hipError_t launch_dh_logits(const Scores3Args& a, hipStream_t st) {
   if (a.n_rows == 0) return hipSuccess;
-  if (a.V_pad % 8 != 0 || !a.logits || !a.coefA || !a.coefB || !a.bO) return hipErrorInvalidValue;
+  if (a.V_pad % 8 != 0 || !a.logits || !a.coefA || !a.coefB || !a.bl) return hipErrorInvalidValue;
   const int64_t n = (int64_t)a.n_rows * (a.V_pad / 8);
   hipLaunchKernelGGL(dh_logits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();

@@ -125,10 +125,22 @@ def lattice_layout(B, T, U1):
 
 @pytest.mark.parametrize("T,U,tr,ur", LATTICE_CASES)
 def test_lattice_kernel_matches_oracle(gpu_lib, T, U, tr, ur):
+    lattice_vs_oracle(gpu_lib, 5, T, U, tr, ur)
+
+
+@pytest.mark.parametrize("T,U,tr,ur", LATTICE_CASES[:4])
+def test_lattice_paired_sweeps_match_oracle(gpu_lib, T, U, tr, ur):
+    """More sweeps than CUs (B = 160 on 256 CUs): the paired kernel, one workgroup running an alpha
+    and a beta sweep of 1 to 4 waves each. Through rnnt_lattice (no host lengths, so no pairing
+    table) both halves sweep the same sample; the loss's pairing of long with short samples, whose
+    halves end at different steps, is checked by the B = 1024 and 40 s x 256 tests."""
+    lattice_vs_oracle(gpu_lib, 160, T, U, (1, T), (0, U))
+
+
+def lattice_vs_oracle(rl, B, T, U, tr, ur):
     import torch
 
-    rl = gpu_lib
-    B, U1 = 5, U + 1
+    U1 = U + 1
     n, ix_of = lattice_layout(B, T, U1)
     inp = make_inputs(B, T, U, 33, 8, 8, 8, dtype="f32", seed=31 + U, t_range=tr, u_range=ur)
     say(f"lattice kernel: B={B} T={T} U={U} ragged")
