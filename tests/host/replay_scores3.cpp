@@ -66,6 +66,25 @@ std::string run_case(const Dims& d, const std::vector<int32_t>& T_len, const std
   build_plan(d, T_len.data(), U_len.data(), ks * 16, p, band);
   if (!check_plan(p, err)) return "skip " + err;
   const Layout L = make_layout(p);
+  // the lattice sweep pairing: every sample once in the alpha role and once in
+  // the beta role, alpha longest first (T_b - 1 + U_b), beta the mirror order,
+  // and the table inside the plan copy
+  {
+    if ((int64_t)p.lat_pair.size() != 2 * (int64_t)d.B) return "FAIL pairing table size";
+    if (L.off_latpair + sizeof(int32_t) * p.lat_pair.size() > L.plan_bytes) return "FAIL pairing outside the plan copy";
+    std::vector<int> n_alpha(d.B, 0), n_beta(d.B, 0);
+    auto D = [&](int b) { return T_len[b] - 1 + U_len[b]; };
+    for (int j = 0; j < d.B; ++j) {
+      const int a = p.lat_pair[2 * j], b = p.lat_pair[2 * j + 1];
+      if (a < 0 || a >= d.B || b < 0 || b >= d.B) return "FAIL pairing index out of range";
+      ++n_alpha[a];
+      ++n_beta[b];
+      if (b != p.lat_pair[2 * (d.B - 1 - j)]) return "FAIL pairing not mirrored";
+      if (j > 0 && D(a) > D(p.lat_pair[2 * (j - 1)])) return "FAIL pairing not longest first";
+    }
+    for (int b = 0; b < d.B; ++b)
+      if (n_alpha[b] != 1 || n_beta[b] != 1) return "FAIL pairing not one sweep of each kind per sample";
+  }
   // the persistent score kernels run in bf16 mode with at least 8 k-steps of 64, and
   // always with the fp8 output layer (E4M3 rows of H8 >= 640 bytes)
   if (!persistent_scores(p)) return "skip not the persistent score path";
