@@ -359,7 +359,8 @@ __global__ void __launch_bounds__(128 * NW) lattice_pair_kernel(LatticeArgs p) {
   else lattice_body<NW, SW, PF, true, CLAMP>(p, ring + NW * SRING, bb, tid, nsteps);
 }
 
-// Longer sweeps: one workgroup per (sample, direction).
+// One workgroup per (sample, direction): sweeps of more than four waves, and
+// batches whose sweeps do not outnumber the CUs.
 template <int NW, int SW, bool CLAMP>
 __global__ void __launch_bounds__(64 * NW) lattice_kernel(LatticeArgs p) {
   constexpr int PF = 2;
