@@ -128,6 +128,16 @@ def test_lattice_kernel_matches_oracle(gpu_lib, T, U, tr, ur):
     lattice_vs_oracle(gpu_lib, 5, T, U, tr, ur)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_paired_sweeps_of_different_samples(gpu_lib, dtype):
+    """Through the loss with B = 160 (more sweeps than CUs): workgroup j sweeps alpha of the j-th
+    longest sample and beta of the j-th shortest, three waves each (U + 1 <= 192), with ragged
+    lengths so that the halves end at different steps; costs and gradients against the oracle."""
+    inp = make_inputs(160, 40, 150, 33, 16, 16, 16, dtype=dtype, seed=707, t_range=(1, 40), u_range=(0, 150))
+    say(f"paired sweeps of different samples {dtype}: B=160 T<=40 U<=150")
+    full_check(gpu_lib, inp)
+
+
 @pytest.mark.parametrize("T,U,tr,ur", LATTICE_CASES[:4])
 def test_lattice_paired_sweeps_match_oracle(gpu_lib, T, U, tr, ur):
     """More sweeps than CUs (B = 160 on 256 CUs): the paired kernel, one workgroup running an alpha
