@@ -297,7 +297,6 @@ struct Scores3Args {
   f32x2* stats;      // forward: [n_ct*128][nvt]
   void* dh;          // backward: [n_ct*128][V_pad] bf16
   void* logits;      // untiled mode: [n_rows][V_pad] fp16 (W^O z) log2 e (forward; null: not stored), dh in place (backward)
-  const void* bO;    // untiled backward: b^O [V] (bf16)
   void* coefA;       // [n_ct*128] (lse log2 e, occupancy)
   void* coefB;       // [n_ct*128] (cb, cl, label, 0)
   // fp8 output layer (WO8 non-null): E4M3 operands, rows of H8 bytes
