@@ -17,8 +17,9 @@
 //
 // NW waves serve one (sample, direction); wave w of them owns rows
 // u = 64 w + lane. A workgroup holds one such sweep, or two (the alpha sweep
-// of one sample and the beta sweep of another: lattice_pair_kernel). The sweep is cut into windows whose loads and stores are
-// the groups of SW diagonals from a multiple of SW (alpha computes diagonals
+// of one sample and the beta sweep of another: lattice_pair_kernel). The
+// sweep is cut into windows whose loads and stores are the groups of SW
+// diagonals from a multiple of SW (alpha computes diagonals
 // SW k + 1 .. SW k + SW in window k, upwards from the values on diagonal 0;
 // beta computes SW j + SW - 1 down to SW j, downwards from the window holding
 // D = T_b - 1 + U_b). The waves form a pipeline along u: alpha
